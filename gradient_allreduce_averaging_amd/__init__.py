@@ -1,0 +1,306 @@
+"""Python binding of libddp.so: bucketed gradient synchronisation on MI355X.
+
+Argument marshalling only -- every step runs in the HIP library through its
+C ABI (``include/ddp.h``).  PyTorch supplies device memory and streams:
+tensors are passed by ``data_ptr()``, streams by ``torch.cuda.Stream``
+handles.  Importing this module loads ``libddp.so`` and raises if it has not
+been built; there is no fallback implementation.
+
+Names follow the C ABI: ``plan_buckets``, ``plan_two_bucket``,
+``bind_params``, ``flatten``, ``bucket_allreduce_avg``,
+``sync_allreduce_avg``, ``unflatten``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddp.so")
+
+SEQUENTIAL = 0
+RING = 1
+_ORDERS = {"seq": SEQUENTIAL, "sequential": SEQUENTIAL, "ring": RING,
+           SEQUENTIAL: SEQUENTIAL, RING: RING}
+F32 = 0
+BF16 = 1
+_DTYPES = {"f32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16, F32: F32, BF16: BF16}
+
+REGION_BN_BIAS, REGION_BN_WEIGHT, REGION_FC_BIAS, REGION_FC_WEIGHT, REGION_FIRST, REGION_DEEP = range(6)
+
+STATUS = {0: "DDP_OK", 1: "DDP_ERR_INVALID_ARG", 2: "DDP_ERR_UNSUPPORTED", 3: "DDP_ERR_OVERFLOW",
+          4: "DDP_ERR_ALIAS", 5: "DDP_ERR_HIP", 6: "DDP_ERR_NOMEM"}
+
+
+class DDPError(RuntimeError):
+    def __init__(self, status: int, call: str, detail: str = ""):
+        self.status = status
+        msg = f"{call} failed: {STATUS.get(status, status)}"
+        super().__init__(msg + (f" ({detail})" if detail else ""))
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    # torch owns the device memory and streams handed to the library, so the
+    # library must run on torch's HIP runtime: load torch first, and the
+    # libamdhip64.so.7 dependency of libddp.so then resolves to the runtime
+    # torch already mapped instead of a second copy from /opt/rocm.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process "
+                          f"({sorted(runtimes)}); import torch before libddp.so")
+    c_i64p = ctypes.POINTER(ctypes.c_int64)
+    c_i32p = ctypes.POINTER(ctypes.c_int32)
+    vp = ctypes.c_void_p
+    sig = {
+        "ddp_plan_buckets": ([c_i64p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int,
+                              ctypes.POINTER(vp)], ctypes.c_int),
+        "ddp_plan_two_bucket": ([c_i64p, ctypes.POINTER(ctypes.c_uint8), ctypes.c_int32,
+                                 ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int),
+        "ddp_plan_free": ([vp], None),
+        "ddp_plan_num_buckets": ([vp], ctypes.c_int32),
+        "ddp_plan_total": ([vp], ctypes.c_int64),
+        "ddp_plan_bucket": ([vp, ctypes.c_int32, c_i64p, c_i64p, c_i32p, c_i32p], ctypes.c_int),
+        "ddp_plan_slot_param": ([vp, ctypes.c_int32, c_i32p], ctypes.c_int),
+        "ddp_plan_param": ([vp, ctypes.c_int32, c_i32p, c_i64p], ctypes.c_int),
+        "ddp_plan_prepare": ([vp], ctypes.c_int),
+        "ddp_bind_params": ([vp, ctypes.POINTER(vp), vp, ctypes.POINTER(vp)], ctypes.c_int),
+        "ddp_binding_free": ([vp], None),
+        "ddp_flatten": ([vp, vp, ctypes.c_int32, vp, ctypes.c_int, vp], ctypes.c_int),
+        "ddp_unflatten": ([vp, vp, ctypes.c_int32, vp, ctypes.c_int, vp], ctypes.c_int),
+        "ddp_bucket_allreduce_avg": ([ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp],
+                                     ctypes.c_int),
+        "ddp_sync_allreduce_avg": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int,
+                                    ctypes.c_int, vp, vp], ctypes.c_int),
+        "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "ddp_abi_version": ([], ctypes.c_int32),
+        "ddp_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        detail = lib.ddp_last_error().decode() if status == 5 else ""
+        raise DDPError(status, call, detail)
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    return (ctypes.c_void_p * len(ptrs))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+
+
+# ---------------------------------------------------------------- torch glue
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported gradient dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor is not contiguous")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------- plans
+
+class Plan:
+    """Owner of a ``ddp_plan_t``."""
+
+    def __init__(self, handle: ctypes.c_void_p, dtype: int, numel: Sequence[int]):
+        self._h = handle
+        self.dtype = dtype
+        self.numel = [int(n) for n in numel]
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and lib is not None:
+            lib.ddp_plan_free(h)
+
+    @property
+    def n_buckets(self) -> int:
+        return lib.ddp_plan_num_buckets(self._h)
+
+    @property
+    def total(self) -> int:
+        return lib.ddp_plan_total(self._h)
+
+    def bucket(self, b: int):
+        """(len, base, first_slot, n_slots) of bucket b."""
+        ln, base = ctypes.c_int64(), ctypes.c_int64()
+        fs, ns = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.ddp_plan_bucket(self._h, b, ctypes.byref(ln), ctypes.byref(base),
+                                   ctypes.byref(fs), ctypes.byref(ns)), "ddp_plan_bucket")
+        return ln.value, base.value, fs.value, ns.value
+
+    def slot_param(self, slot: int) -> int:
+        p = ctypes.c_int32()
+        _check(lib.ddp_plan_slot_param(self._h, slot, ctypes.byref(p)), "ddp_plan_slot_param")
+        return p.value
+
+    def param(self, p: int):
+        """(bucket, offset within bucket) of parameter p."""
+        b, off = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib.ddp_plan_param(self._h, p, ctypes.byref(b), ctypes.byref(off)), "ddp_plan_param")
+        return b.value, off.value
+
+    def buckets(self) -> List[List[int]]:
+        out = []
+        for b in range(self.n_buckets):
+            _, _, fs, ns = self.bucket(b)
+            out.append([self.slot_param(s) for s in range(fs, fs + ns)])
+        return out
+
+    def prepare(self):
+        _check(lib.ddp_plan_prepare(self._h), "ddp_plan_prepare")
+
+
+def plan_buckets(numel: Sequence[int], bucket_cap_bytes: int, dtype="f32") -> Plan:
+    arr = (ctypes.c_int64 * len(numel))(*numel)
+    h = ctypes.c_void_p()
+    dt = _DTYPES[dtype]
+    _check(lib.ddp_plan_buckets(arr, len(numel), int(bucket_cap_bytes), dt, ctypes.byref(h)),
+           "ddp_plan_buckets")
+    return Plan(h, dt, numel)
+
+
+def plan_two_bucket(numel: Sequence[int], region: Sequence[int], dtype="f32") -> Plan:
+    arr = (ctypes.c_int64 * len(numel))(*numel)
+    reg = (ctypes.c_uint8 * len(region))(*region)
+    h = ctypes.c_void_p()
+    dt = _DTYPES[dtype]
+    _check(lib.ddp_plan_two_bucket(arr, reg, len(numel), dt, ctypes.byref(h)),
+           "ddp_plan_two_bucket")
+    return Plan(h, dt, numel)
+
+
+# ---------------------------------------------------------------- bindings
+
+class Binding:
+    """Owner of a ``ddp_binding_t`` (one rank's parameter gradient pointers).
+    Keeps references to the tensors so their memory outlives the binding."""
+
+    def __init__(self, plan: Plan, grads: Sequence, stream=None):
+        self.plan = plan
+        self._grads = list(grads)
+        if len(self._grads) != len(plan.numel):
+            raise ValueError("one gradient tensor per parameter is required")
+        for g, n in zip(self._grads, plan.numel):
+            if g.numel() != n:
+                raise ValueError(f"gradient has {g.numel()} elements, the plan says {n}")
+        self.dtypes = {_dtype_code(g) for g in self._grads}
+        ptrs = _ptr_array([_dev_ptr(g) for g in self._grads])
+        h = ctypes.c_void_p()
+        _check(lib.ddp_bind_params(plan.handle, ptrs, ctypes.c_void_p(_stream_handle(stream)),
+                                   ctypes.byref(h)), "ddp_bind_params")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and lib is not None:
+            lib.ddp_binding_free(h)
+
+
+def bind_params(plan: Plan, grads: Sequence, stream=None) -> Binding:
+    return Binding(plan, grads, stream)
+
+
+def _check_flat(plan: Plan, binding: Binding, flat):
+    if flat.numel() < plan.total:
+        raise ValueError("flat buffer shorter than the plan")
+    if binding.dtypes != {_dtype_code(flat)}:
+        raise ValueError("flat buffer and parameter gradients differ in dtype")
+
+
+def flatten(plan: Plan, binding: Binding, flat, bucket: int = -1, stream=None):
+    _check_flat(plan, binding, flat)
+    _check(lib.ddp_flatten(plan.handle, binding.handle, bucket, _dev_ptr(flat), _dtype_code(flat),
+                           _stream_handle(stream)), "ddp_flatten")
+
+
+def unflatten(plan: Plan, binding: Binding, flat_out, bucket: int = -1, stream=None):
+    _check_flat(plan, binding, flat_out)
+    _check(lib.ddp_unflatten(plan.handle, binding.handle, bucket, _dev_ptr(flat_out),
+                             _dtype_code(flat_out), _stream_handle(stream)), "ddp_unflatten")
+
+
+# ---------------------------------------------------------------- reduce
+
+def bucket_allreduce_avg(rank_bufs: Sequence, out, order="ring", length: Optional[int] = None,
+                         stream=None):
+    """Average one bucket over len(rank_bufs) virtual ranks into ``out``."""
+    n = out.numel() if length is None else int(length)
+    in_dt = _dtype_code(rank_bufs[0])
+    for t in rank_bufs:
+        if _dtype_code(t) != in_dt or t.numel() < n:
+            raise ValueError("rank buffers differ in dtype or are too short")
+    if out.numel() < n:
+        raise ValueError("output too short")
+    ptrs = _ptr_array([_dev_ptr(t) for t in rank_bufs])
+    _check(lib.ddp_bucket_allreduce_avg(ptrs, len(rank_bufs), n, _ORDERS[order], in_dt,
+                                        _dtype_code(out), _dev_ptr(out), _stream_handle(stream)),
+           "ddp_bucket_allreduce_avg")
+
+
+def sync_allreduce_avg(plan: Plan, rank_flats: Sequence, out_flat, order="ring", stream=None):
+    """Average every bucket of ``plan`` in one launch."""
+    total = plan.total
+    for t in rank_flats:
+        if _dtype_code(t) != plan.dtype or t.numel() < total:
+            raise ValueError("rank flat buffers differ from the plan's dtype or size")
+    if out_flat.numel() < total:
+        raise ValueError("output too short")
+    ptrs = _ptr_array([_dev_ptr(t) for t in rank_flats])
+    _check(lib.ddp_sync_allreduce_avg(plan.handle, ptrs, len(rank_flats), _ORDERS[order],
+                                      _dtype_code(out_flat), _dev_ptr(out_flat),
+                                      _stream_handle(stream)), "ddp_sync_allreduce_avg")
+
+
+def status_string(status: int) -> str:
+    return lib.ddp_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return lib.ddp_abi_version()

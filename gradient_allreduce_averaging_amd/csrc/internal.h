@@ -1,0 +1,56 @@
+// Internal definitions shared by the host planner (plan.cpp) and the HIP
+// launch code (kernels.hip).  Not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "ddp.h"
+
+// Device-side copy of a plan's bucket table, for one device and one tile size.
+struct ddp_dev_tables {
+    int64_t *bucket_base = nullptr;   // [n_buckets + 1] flat start of each bucket, then total
+    int32_t *tile_bucket = nullptr;   // [n_tiles] bucket holding each tile's first element
+    int64_t n_tiles = 0;
+};
+
+struct ddp_plan {
+    ddp_dtype_t dtype = DDP_F32;
+    int32_t n_params = 0;
+    int64_t total = 0;                        // elements in the flat layout
+    std::vector<int64_t> numel;               // registration order
+    std::vector<int32_t> slot_param;          // parameter at each flat slot
+    std::vector<int32_t> param_bucket;        // bucket of each parameter
+    std::vector<int64_t> param_offset;        // element offset inside its bucket
+    std::vector<int64_t> bucket_base;         // [n_buckets + 1], last entry = total
+    std::vector<int32_t> bucket_first_slot;   // [n_buckets + 1], last entry = n_params
+
+    int32_t n_buckets() const { return (int32_t)bucket_base.size() - 1; }
+
+    std::mutex mu;                            // guards dev
+    std::map<std::pair<int, int64_t>, ddp_dev_tables> dev;   // (device, tile elements)
+};
+
+// One flatten/unflatten copy unit: `count` elements between a parameter's
+// gradient and the flat buffer.  Units are sorted by flat position, so the
+// units of bucket b are the range [bucket_first_unit[b], bucket_first_unit[b+1]).
+struct ddp_copy_unit {
+    uint64_t param_addr;   // device address of the parameter's gradient
+    int64_t param_elem;    // first element of this unit inside the parameter
+    int64_t flat_elem;     // first flat element of this unit
+    int64_t count;         // elements, 1..kCopyUnitElems
+};
+
+struct ddp_binding {
+    const ddp_plan *plan = nullptr;
+    int device = -1;
+    ddp_copy_unit *units = nullptr;           // device array
+    int64_t n_units = 0;
+    std::vector<int64_t> bucket_first_unit;   // [n_buckets + 1]
+};
+
+// Frees every device table of a plan (defined next to the kernels).
+void ddp_internal_free_plan_tables(ddp_plan *plan);

@@ -1,0 +1,740 @@
+// HIP kernels of libddp for gfx950 (MI355X) and the C-ABI entry points that
+// launch them.
+//
+// Pages: [DDP] "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel);
+//        [TR24] "(24) NCCL通信与分布式数据并行" (tech-renaissance.cn).
+//
+// Reduce + scale ([TR24] 一 and 九; [DDP] 2.10-2.11, 4.2).  Every output
+// element is owned by exactly one thread, which loads that element from all
+// N rank buffers, folds the N values in the fixed order in FP32, multiplies
+// by fl(1/N) and stores (optionally rounded to bf16, nearest-even).  There is
+// no cross-thread reduction, so the result does not depend on the grid.
+//
+// Layout and launch.  A block owns a tile of kThreads * kUnroll 16-byte
+// vectors; thread t takes vectors t, t + kThreads, ... so each wave load is
+// 64 contiguous 16-byte lanes (1 KiB) per rank.  All N * kUnroll loads of a
+// thread are issued before any add, to keep N * kUnroll * 16 bytes in flight
+// per lane.  The path is HBM-bound (0.22 flop/byte for FP32, N = 8): no LDS,
+// no MFMA, no cross-lane traffic.
+//
+// Ring order.  Element i of a bucket [base, end) sits in chunk
+// c = (i - base) / C with C = ceil((end - base) / N) and starts its fold at
+// rank (c + 1) mod N.  A tile resolves (uniformly, in scalar registers) the
+// chunk segment holding its first element and the segment after it, and
+// keeps two rotated pointer sets; a vector wholly inside either segment
+// takes the vector path, a vector straddling a chunk or bucket boundary (at
+// most a few per bucket) and the ragged tail take a per-element path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;             // 16-byte vectors per thread per tile
+constexpr int64_t kCopyUnitElems = 16384;
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct RankArgs {
+    const void *p[DDP_MAX_RANKS];
+};
+
+// Bucket boundaries as the kernels see them.  base == nullptr means a single
+// bucket [0, total).
+struct Buckets {
+    const int64_t *base;          // [n_buckets + 1]
+    const int32_t *tile_bucket;   // [n_tiles] bucket of each tile's first element
+    int32_t n_buckets;
+};
+
+// The chunk segments a tile may meet on the vector path.
+struct Segs {
+    int64_t a_lo, a_hi, b_lo, b_hi;
+    int sa, sb;
+    int32_t bucket;
+};
+
+__device__ __forceinline__ float widen_bf16(uint32_t h) { return __uint_as_float(h << 16); }
+
+// f32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet, sign kept).
+__device__ __forceinline__ uint32_t bf16_rne(float y)
+{
+    const uint32_t u = __float_as_uint(y);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Element e of a 16-byte vector, widened to FP32.
+template <int IN>
+__device__ __forceinline__ float lane(const u32x4 &v, int e)
+{
+    if (IN == kF32) return __uint_as_float(v[e]);
+    const uint32_t w = v[e >> 1];
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+template <int IN>
+__device__ __forceinline__ float load_elem(const void *p, int64_t i)
+{
+    if (IN == kF32) return static_cast<const float *>(p)[i];
+    return widen_bf16(static_cast<const uint16_t *>(p)[i]);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_elem(void *out, int64_t i, float y)
+{
+    if (OUT == kF32)
+        static_cast<float *>(out)[i] = y;
+    else
+        static_cast<uint16_t *>(out)[i] = (uint16_t)bf16_rne(y);
+}
+
+__device__ __forceinline__ int wrap(int r, int n) { return r >= n ? r - n : r; }
+
+// Ring start rank of element i (any bucket at or after b0).
+__device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int64_t total, int N,
+                                          int64_t i)
+{
+    int64_t base = 0, end = total;
+    if (bk.base) {
+        int32_t b = b0;
+        while (bk.base[b + 1] <= i) ++b;
+        base = bk.base[b];
+        end = bk.base[b + 1];
+    }
+    const int64_t C = (end - base + N - 1) / N;
+    return (int)(((i - base) / C + 1) % N);
+}
+
+// Per-element path: positions [i0, i0 + cnt) clipped to total.
+template <int IN, int OUT, bool RING>
+__device__ void reduce_elems(const RankArgs &ra, int N, int64_t total, const Buckets &bk,
+                             int32_t b0, float inv, void *out, int64_t i0, int cnt)
+{
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t i = i0 + e;
+        if (i >= total) break;
+        int r = RING ? ring_start(bk, b0, total, N, i) : 0;
+        float acc = load_elem<IN>(ra.p[r], i);
+        if (!RING) acc = 0.0f + acc;
+        for (int k = 1; k < N; ++k) {
+            r = wrap(r + 1, N);
+            acc = acc + load_elem<IN>(ra.p[r], i);
+        }
+        store_elem<OUT>(out, i, acc * inv);
+    }
+}
+
+// Segments of the tile starting at element tile0 (block-uniform values).
+template <bool RING>
+__device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int N, int64_t tile0)
+{
+    Segs s;
+    s.a_lo = 0;
+    s.a_hi = total;
+    s.b_lo = 0;
+    s.b_hi = 0;
+    s.sa = 0;
+    s.sb = 0;
+    s.bucket = 0;
+    if (!RING) return s;
+    const int32_t b = bk.tile_bucket ? bk.tile_bucket[blockIdx.x] : 0;
+    const int64_t base = bk.base ? bk.base[b] : 0;
+    const int64_t end = bk.base ? bk.base[b + 1] : total;
+    const int64_t C = (end - base + N - 1) / N;
+    const int64_t c = (tile0 - base) / C;
+    s.bucket = b;
+    s.a_lo = base + c * C;
+    s.a_hi = min(s.a_lo + C, end);
+    s.sa = (int)((c + 1) % N);
+    if (s.a_hi < end) {
+        s.b_lo = s.a_hi;
+        s.b_hi = min(s.b_lo + C, end);
+        s.sb = (int)((c + 2) % N);
+    } else if (bk.base && b + 1 < bk.n_buckets) {
+        const int64_t e2 = bk.base[b + 2];
+        const int64_t C2 = (e2 - end + N - 1) / N;
+        s.b_lo = end;
+        s.b_hi = min(end + C2, e2);
+        s.sb = 1 % N;
+    }
+    s.sa = __builtin_amdgcn_readfirstlane(s.sa);
+    s.sb = __builtin_amdgcn_readfirstlane(s.sb);
+    return s;
+}
+
+// Scale, convert and store one vector of accumulators at element i0.
+template <int IN, int OUT>
+__device__ __forceinline__ void store_vec(void *out, int64_t i0, const float *acc, float inv)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    if (OUT == kF32) {
+        u32x4 o;
+        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[e] * inv);
+        *reinterpret_cast<u32x4 *>(static_cast<float *>(out) + i0) = o;
+    } else if (VEC == 4) {
+        u32x2 o;
+        o[0] = bf16_rne(acc[0] * inv) | (bf16_rne(acc[1] * inv) << 16);
+        o[1] = bf16_rne(acc[2] * inv) | (bf16_rne(acc[3] * inv) << 16);
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(out) + i0) = o;
+    } else {
+        u32x4 o;
+        for (int w = 0; w < 4; ++w)
+            o[w] = bf16_rne(acc[2 * w] * inv) | (bf16_rne(acc[2 * w + 1] * inv) << 16);
+        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(out) + i0) = o;
+    }
+}
+
+// N known at compile time (2..8): all N * kUnroll vector loads in flight.
+template <int NR, bool RING, int IN, int OUT>
+__global__ void __launch_bounds__(kThreads)
+reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    const int64_t tile0 = (int64_t)blockIdx.x * (kThreads * kUnroll * VEC);
+    const Segs sg = tile_segs<RING>(bk, total, NR, tile0);
+
+    const char *qa[NR];
+    const char *qb[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        qa[k] = static_cast<const char *>(ra.p[wrap(sg.sa + k, NR)]);
+        qb[k] = RING ? static_cast<const char *>(ra.p[wrap(sg.sb + k, NR)]) : qa[k];
+    }
+
+    u32x4 v[kUnroll][NR];
+    int64_t i0[kUnroll];
+    bool fast[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        i0[u] = tile0 + ((int64_t)threadIdx.x + u * kThreads) * VEC;
+        const bool in_a = i0[u] >= sg.a_lo && i0[u] + VEC <= sg.a_hi;
+        const bool in_b = RING && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
+        fast[u] = in_a || in_b;
+        if (fast[u]) {
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const char *q = in_a ? qa[k] : qb[k];
+                v[u][k] = *reinterpret_cast<const u32x4 *>(q + i0[u] * ISZ);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (fast[u]) {
+            float acc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float x = lane<IN>(v[u][0], e);
+                acc[e] = RING ? x : 0.0f + x;
+            }
+#pragma unroll
+            for (int k = 1; k < NR; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[u][k], e);
+            store_vec<IN, OUT>(out, i0[u], acc, inv);
+        } else if (i0[u] < total) {
+            reduce_elems<IN, OUT, RING>(ra, NR, total, bk, sg.bucket, inv, out, i0[u], VEC);
+        }
+    }
+}
+
+// Any N up to DDP_MAX_RANKS: ranks walked in a loop.
+template <bool RING, int IN, int OUT>
+__global__ void __launch_bounds__(kThreads)
+reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    const int64_t tile0 = (int64_t)blockIdx.x * (kThreads * kUnroll * VEC);
+    const Segs sg = tile_segs<RING>(bk, total, N, tile0);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i0 = tile0 + ((int64_t)threadIdx.x + u * kThreads) * VEC;
+        const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
+        const bool in_b = RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+        if (in_a || in_b) {
+            int r = in_a ? sg.sa : sg.sb;
+            float acc[VEC];
+            u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(ra.p[r]) + i0 * ISZ);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float x = lane<IN>(w, e);
+                acc[e] = RING ? x : 0.0f + x;
+            }
+#pragma unroll 4
+            for (int k = 1; k < N; ++k) {
+                r = wrap(r + 1, N);
+                w = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(ra.p[r]) + i0 * ISZ);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(w, e);
+            }
+            store_vec<IN, OUT>(out, i0, acc, inv);
+        } else if (i0 < total) {
+            reduce_elems<IN, OUT, RING>(ra, N, total, bk, sg.bucket, inv, out, i0, VEC);
+        }
+    }
+}
+
+// One element per thread, element-aligned buffers of a single bucket.
+template <bool RING, int IN, int OUT>
+__global__ void __launch_bounds__(kThreads)
+reduce_scalar(RankArgs ra, int N, int64_t total, float inv, void *out)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    const Buckets single = {nullptr, nullptr, 1};
+    reduce_elems<IN, OUT, RING>(ra, N, total, single, 0, inv, out, i, 1);
+}
+
+// ---------------------------------------------------------------- copies
+
+__device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, int64_t hi)
+{
+    for (int64_t j = lo + 2 * (int64_t)threadIdx.x; j < hi; j += 2 * kThreads)
+        *reinterpret_cast<uint16_t *>(dst + j) = *reinterpret_cast<const uint16_t *>(src + j);
+}
+
+// Block-wide copy of nbytes (a multiple of 2) between 2-byte aligned addresses.
+__device__ void block_copy(char *dst, const char *src, int64_t nbytes)
+{
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src);
+    const int tid = threadIdx.x;
+    if (((d ^ s) & 15) == 0) {
+        const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
+        copy16b(dst, src, 0, head);
+        const int64_t nvec = (nbytes - head) >> 4;
+        const u32x4 *sv = reinterpret_cast<const u32x4 *>(src + head);
+        u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+        int64_t j = tid;
+        for (; j + 3 * kThreads < nvec; j += 4 * kThreads) {
+            const u32x4 a = sv[j], b = sv[j + kThreads], c = sv[j + 2 * kThreads],
+                        e = sv[j + 3 * kThreads];
+            dv[j] = a;
+            dv[j + kThreads] = b;
+            dv[j + 2 * kThreads] = c;
+            dv[j + 3 * kThreads] = e;
+        }
+        for (; j < nvec; j += kThreads) dv[j] = sv[j];
+        copy16b(dst, src, head + (nvec << 4), nbytes);
+    } else if (((d ^ s) & 3) == 0) {
+        const int64_t head = min<int64_t>((4 - (d & 3)) & 3, nbytes);
+        copy16b(dst, src, 0, head);
+        const int64_t nw = (nbytes - head) >> 2;
+        const uint32_t *sw = reinterpret_cast<const uint32_t *>(src + head);
+        uint32_t *dw = reinterpret_cast<uint32_t *>(dst + head);
+        int64_t j = tid;
+        for (; j + 3 * kThreads < nw; j += 4 * kThreads) {
+            const uint32_t a = sw[j], b = sw[j + kThreads], c = sw[j + 2 * kThreads],
+                           e = sw[j + 3 * kThreads];
+            dw[j] = a;
+            dw[j + kThreads] = b;
+            dw[j + 2 * kThreads] = c;
+            dw[j + 3 * kThreads] = e;
+        }
+        for (; j < nw; j += kThreads) dw[j] = sw[j];
+        copy16b(dst, src, head + (nw << 2), nbytes);
+    } else {
+        copy16b(dst, src, 0, nbytes);
+    }
+}
+
+// One copy unit per block; to_flat selects flatten (param -> flat) or
+// unflatten (flat -> param).
+__global__ void __launch_bounds__(kThreads)
+copy_units(const ddp_copy_unit *units, int64_t first, char *flat, int esize, int to_flat)
+{
+    const ddp_copy_unit u = units[first + blockIdx.x];
+    char *pp = reinterpret_cast<char *>(u.param_addr) + u.param_elem * esize;
+    char *fp = flat + u.flat_elem * esize;
+    const int64_t nbytes = u.count * esize;
+    if (to_flat)
+        block_copy(fp, pp, nbytes);
+    else
+        block_copy(pp, fp, nbytes);
+}
+
+// ---------------------------------------------------------------- host side
+
+thread_local char g_last_error[256] = "";
+
+// Records a failed HIP call for ddp_last_error() and maps it to a status.
+ddp_status_t hip_fail(const char *what, hipError_t e, ddp_status_t st = DDP_ERR_HIP)
+{
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return st;
+}
+
+ddp_status_t launched(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DDP_OK : hip_fail(what, e);
+}
+
+int dtype_size(int dt) { return dt == DDP_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == DDP_F32 || dt == DDP_BF16; }
+bool pair_ok(int in, int out)
+{
+    return (in == DDP_F32 && out == DDP_F32) || (in == DDP_BF16 && out == DDP_BF16) ||
+           (in == DDP_F32 && out == DDP_BF16);
+}
+int64_t vec_elems(int in) { return in == DDP_F32 ? 4 : 8; }
+int64_t tile_elems(int in) { return (int64_t)kThreads * kUnroll * vec_elems(in); }
+
+bool overlaps(uintptr_t a, int64_t na, uintptr_t b, int64_t nb)
+{
+    return a < b + (uintptr_t)nb && b < a + (uintptr_t)na;
+}
+
+// Output may be exactly one input (same dtype) or disjoint from all of them.
+ddp_status_t check_alias(const void *const *in, int n, int64_t len, int isz, const void *out,
+                         int osz)
+{
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out);
+    for (int r = 0; r < n; ++r) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(in[r]);
+        if (x == o && isz == osz) continue;
+        if (overlaps(x, len * isz, o, len * osz)) return DDP_ERR_ALIAS;
+    }
+    return DDP_OK;
+}
+
+template <bool RING, int IN, int OUT>
+ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Buckets &bk, float inv,
+                          void *out, hipStream_t st, bool vec_ok)
+{
+    if (vec_ok) {
+        const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
+        if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
+        const dim3 g((unsigned)tiles), b(kThreads);
+        switch (N) {
+        case 2: reduce_fast<2, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 3: reduce_fast<3, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 4: reduce_fast<4, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 5: reduce_fast<5, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 6: reduce_fast<6, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 7: reduce_fast<7, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 8: reduce_fast<8, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        default: reduce_many<RING, IN, OUT><<<g, b, 0, st>>>(ra, N, total, bk, inv, out); break;
+        }
+    } else {
+        const int64_t blocks = (total + kThreads - 1) / kThreads;
+        if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
+        reduce_scalar<RING, IN, OUT><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+            ra, N, total, inv, out);
+    }
+    return launched("reduce kernel launch");
+}
+
+ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
+                           const Buckets &bk, void *out, hipStream_t st, bool vec_ok)
+{
+    const float inv = 1.0f / (float)N;
+    const bool ring = order == DDP_ORDER_RING;
+    if (in == DDP_F32 && out_dt == DDP_F32)
+        return ring ? launch_typed<true, kF32, kF32>(ra, N, total, bk, inv, out, st, vec_ok)
+                    : launch_typed<false, kF32, kF32>(ra, N, total, bk, inv, out, st, vec_ok);
+    if (in == DDP_BF16 && out_dt == DDP_BF16)
+        return ring ? launch_typed<true, kBF16, kBF16>(ra, N, total, bk, inv, out, st, vec_ok)
+                    : launch_typed<false, kBF16, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
+    return ring ? launch_typed<true, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok)
+                : launch_typed<false, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Common validation of a reduce call.  Returns OK or an error code.
+ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int order, int in,
+                          int out_dt, const void *out)
+{
+    if (n < 1 || len < 0) return DDP_ERR_INVALID_ARG;
+    if (order != DDP_ORDER_SEQUENTIAL && order != DDP_ORDER_RING) return DDP_ERR_INVALID_ARG;
+    if (!dtype_ok(in) || !dtype_ok(out_dt)) return DDP_ERR_INVALID_ARG;
+    if (n > DDP_MAX_RANKS) return DDP_ERR_UNSUPPORTED;
+    if (!pair_ok(in, out_dt)) return DDP_ERR_UNSUPPORTED;
+    if (n == 1 && in != out_dt) return DDP_ERR_UNSUPPORTED;
+    if (len > INT64_MAX / 4) return DDP_ERR_OVERFLOW;
+    if (len == 0) return DDP_OK;   // nothing is read or written: pointers may be null
+    if (!ptrs || !out) return DDP_ERR_INVALID_ARG;
+    for (int r = 0; r < n; ++r) {
+        if (!ptrs[r]) return DDP_ERR_INVALID_ARG;
+        if (!aligned(ptrs[r], dtype_size(in))) return DDP_ERR_INVALID_ARG;
+    }
+    if (!aligned(out, dtype_size(out_dt))) return DDP_ERR_INVALID_ARG;
+    return check_alias(ptrs, n, len, dtype_size(in), out, dtype_size(out_dt));
+}
+
+// N == 1: the input is the result ([TR24] 九 skips the collective when
+// world_size <= 1).
+ddp_status_t copy_single(const void *in, int64_t len, int esize, void *out, hipStream_t st)
+{
+    if (in == out || len == 0) return DDP_OK;
+    const hipError_t e =
+        hipMemcpyAsync(out, in, (size_t)(len * esize), hipMemcpyDeviceToDevice, st);
+    return e == hipSuccess ? DDP_OK : hip_fail("hipMemcpyAsync (N == 1)", e);
+}
+
+// Device tables of `plan` for tiles of `tile` elements on the current device.
+ddp_status_t plan_tables(ddp_plan *plan, int64_t tile, const ddp_dev_tables **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    auto key = std::make_pair(dev, tile);
+    auto it = plan->dev.find(key);
+    if (it != plan->dev.end()) {
+        *out = &it->second;
+        return DDP_OK;
+    }
+    ddp_dev_tables t;
+    const int32_t nb = plan->n_buckets();
+    t.n_tiles = (plan->total + tile - 1) / tile;
+    std::vector<int32_t> tb;
+    try {
+        tb.resize((size_t)std::max<int64_t>(t.n_tiles, 1));
+    } catch (...) {
+        return DDP_ERR_NOMEM;
+    }
+    int32_t b = 0;
+    for (int64_t k = 0; k < t.n_tiles; ++k) {
+        const int64_t first = k * tile;
+        while (plan->bucket_base[b + 1] <= first) ++b;   // skips empty buckets
+        tb[k] = b;
+    }
+    const size_t base_bytes = sizeof(int64_t) * (size_t)(nb + 1);
+    const size_t tb_bytes = sizeof(int32_t) * tb.size();
+    if ((e = hipMalloc(&t.bucket_base, base_bytes)) != hipSuccess)
+        return hip_fail("hipMalloc (bucket table)", e, DDP_ERR_NOMEM);
+    if ((e = hipMalloc(&t.tile_bucket, tb_bytes)) != hipSuccess) {
+        (void)hipFree(t.bucket_base);
+        return hip_fail("hipMalloc (tile table)", e, DDP_ERR_NOMEM);
+    }
+    if ((e = hipMemcpy(t.bucket_base, plan->bucket_base.data(), base_bytes,
+                       hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t.tile_bucket, tb.data(), tb_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        (void)hipFree(t.bucket_base);
+        (void)hipFree(t.tile_bucket);
+        return hip_fail("hipMemcpy (plan tables)", e);
+    }
+    auto ins = plan->dev.emplace(key, t);
+    *out = &ins.first->second;
+    return DDP_OK;
+}
+
+}  // namespace
+
+void ddp_internal_free_plan_tables(ddp_plan *plan)
+{
+    std::lock_guard<std::mutex> lock(plan->mu);
+    if (plan->dev.empty()) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    for (auto &kv : plan->dev) {
+        (void)hipSetDevice(kv.first.first);
+        (void)hipFree(kv.second.bucket_base);
+        (void)hipFree(kv.second.tile_bucket);
+    }
+    plan->dev.clear();
+    if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+extern "C" {
+
+ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ranks, int64_t len,
+                                      ddp_order_t order, ddp_dtype_t in_dtype,
+                                      ddp_dtype_t out_dtype, void *out, void *stream)
+{
+    ddp_status_t stc = check_reduce(rank_ptrs, n_ranks, len, order, in_dtype, out_dtype, out);
+    if (stc != DDP_OK) return stc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (len == 0) return DDP_OK;
+    if (n_ranks == 1) return copy_single(rank_ptrs[0], len, dtype_size(in_dtype), out, st);
+    RankArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    bool vec_ok = aligned(out, 16);
+    for (int r = 0; r < n_ranks; ++r) {
+        ra.p[r] = rank_ptrs[r];
+        vec_ok = vec_ok && aligned(rank_ptrs[r], 16);
+    }
+    const Buckets single = {nullptr, nullptr, 1};
+    return launch_reduce(ra, n_ranks, len, order, in_dtype, out_dtype, single, out, st, vec_ok);
+}
+
+ddp_status_t ddp_plan_prepare(ddp_plan_t *plan)
+{
+    if (!plan) return DDP_ERR_INVALID_ARG;
+    const ddp_dev_tables *t = nullptr;
+    return plan_tables(plan, tile_elems(plan->dtype), &t);
+}
+
+ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
+                                    ddp_order_t order, ddp_dtype_t out_dtype, void *out_flat,
+                                    void *stream)
+{
+    if (!plan) return DDP_ERR_INVALID_ARG;
+    const int in = plan->dtype;
+    const int64_t total = plan->total;
+    ddp_status_t stc = check_reduce(rank_flat, n_ranks, total, order, in, out_dtype, out_flat);
+    if (stc != DDP_OK) return stc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (total == 0) return DDP_OK;
+    if (n_ranks == 1) return copy_single(rank_flat[0], total, dtype_size(in), out_flat, st);
+
+    RankArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    bool vec_ok = aligned(out_flat, 16);
+    for (int r = 0; r < n_ranks; ++r) {
+        ra.p[r] = rank_flat[r];
+        vec_ok = vec_ok && aligned(rank_flat[r], 16);
+    }
+    if (!vec_ok) {
+        // element-aligned buffers: one per-element launch per bucket
+        const int isz = dtype_size(in), osz = dtype_size(out_dtype);
+        for (int32_t b = 0; b < plan->n_buckets(); ++b) {
+            const int64_t base = plan->bucket_base[b], len = plan->bucket_base[b + 1] - base;
+            if (len == 0) continue;
+            RankArgs sub;
+            std::memset(&sub, 0, sizeof(sub));
+            for (int r = 0; r < n_ranks; ++r)
+                sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
+            const Buckets single = {nullptr, nullptr, 1};
+            ddp_status_t s2 = launch_reduce(sub, n_ranks, len, order, in, out_dtype, single,
+                                            static_cast<char *>(out_flat) + base * osz, st, false);
+            if (s2 != DDP_OK) return s2;
+        }
+        return DDP_OK;
+    }
+    if (order == DDP_ORDER_SEQUENTIAL) {
+        // the sequential fold does not depend on bucket boundaries
+        const Buckets single = {nullptr, nullptr, 1};
+        return launch_reduce(ra, n_ranks, total, order, in, out_dtype, single, out_flat, st, true);
+    }
+    const ddp_dev_tables *t = nullptr;
+    if ((stc = plan_tables(plan, tile_elems(in), &t)) != DDP_OK) return stc;
+    const Buckets bk = {t->bucket_base, t->tile_bucket, plan->n_buckets()};
+    return launch_reduce(ra, n_ranks, total, order, in, out_dtype, bk, out_flat, st, true);
+}
+
+ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, void *stream,
+                             ddp_binding_t **out)
+{
+    (void)stream;
+    if (!plan || !param_grads || !out) return DDP_ERR_INVALID_ARG;
+    for (int32_t p = 0; p < plan->n_params; ++p) {
+        if (plan->numel[p] > 0 && !param_grads[p]) return DDP_ERR_INVALID_ARG;
+        if (!aligned(param_grads[p], 2)) return DDP_ERR_INVALID_ARG;
+    }
+    ddp_binding *bd = new (std::nothrow) ddp_binding();
+    if (!bd) return DDP_ERR_NOMEM;
+    bd->plan = plan;
+    hipError_t e = hipGetDevice(&bd->device);
+    if (e != hipSuccess) {
+        delete bd;
+        return hip_fail("hipGetDevice", e);
+    }
+    std::vector<ddp_copy_unit> units;
+    try {
+        const int32_t nb = plan->n_buckets();
+        bd->bucket_first_unit.resize((size_t)nb + 1);
+        for (int32_t b = 0; b < nb; ++b) {
+            bd->bucket_first_unit[b] = (int64_t)units.size();
+            int64_t flat = plan->bucket_base[b];
+            for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
+                const int32_t p = plan->slot_param[s];
+                const int64_t n = plan->numel[p];
+                for (int64_t off = 0; off < n; off += kCopyUnitElems) {
+                    ddp_copy_unit u;
+                    u.param_addr = reinterpret_cast<uint64_t>(param_grads[p]);
+                    u.param_elem = off;
+                    u.flat_elem = flat + off;
+                    u.count = std::min<int64_t>(kCopyUnitElems, n - off);
+                    units.push_back(u);
+                }
+                flat += n;
+            }
+        }
+        bd->bucket_first_unit[nb] = (int64_t)units.size();
+    } catch (...) {
+        delete bd;
+        return DDP_ERR_NOMEM;
+    }
+    bd->n_units = (int64_t)units.size();
+    if (bd->n_units > 0) {
+        const size_t bytes = sizeof(ddp_copy_unit) * units.size();
+        if ((e = hipMalloc(&bd->units, bytes)) != hipSuccess) {
+            delete bd;
+            return hip_fail("hipMalloc (copy units)", e, DDP_ERR_NOMEM);
+        }
+        if ((e = hipMemcpy(bd->units, units.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+            (void)hipFree(bd->units);
+            delete bd;
+            return hip_fail("hipMemcpy (copy units)", e);
+        }
+    }
+    *out = bd;
+    return DDP_OK;
+}
+
+void ddp_binding_free(ddp_binding_t *binding)
+{
+    if (!binding) return;
+    if (binding->units) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(binding->device);
+        (void)hipFree(binding->units);
+        if (cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete binding;
+}
+
+static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, int32_t bucket,
+                             void *flat, int dtype, void *stream, int to_flat)
+{
+    if (!plan || !bd || !flat || bd->plan != plan || !dtype_ok(dtype)) return DDP_ERR_INVALID_ARG;
+    if (bucket < -1 || bucket >= plan->n_buckets()) return DDP_ERR_INVALID_ARG;
+    if (!aligned(flat, dtype_size(dtype))) return DDP_ERR_INVALID_ARG;
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev != bd->device) return DDP_ERR_INVALID_ARG;
+    const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
+    const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
+    if (last <= first) return DDP_OK;
+    if (last - first > INT_MAX) return DDP_ERR_OVERFLOW;
+    copy_units<<<dim3((unsigned)(last - first)), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
+        bd->units, first, static_cast<char *>(flat), dtype_size(dtype), to_flat);
+    return launched("copy kernel launch");
+}
+
+ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,
+                         void *flat_buf, ddp_dtype_t dtype, void *stream)
+{
+    return run_copy(plan, binding, bucket, flat_buf, dtype, stream, 1);
+}
+
+ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,
+                           const void *flat_out, ddp_dtype_t dtype, void *stream)
+{
+    return run_copy(plan, binding, bucket, const_cast<void *>(flat_out), dtype, stream, 0);
+}
+
+const char *ddp_last_error(void) { return g_last_error; }
+
+}  // extern "C"

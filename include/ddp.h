@@ -1,0 +1,230 @@
+/*
+ * ddp.h -- C ABI of libddp.so: bucketed gradient synchronisation on one
+ * MI355X (gfx950), with N virtual ranks whose gradients live in HBM.
+ *
+ * What the library computes (pages cited by title and section):
+ *   [DDP]  "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel)
+ *   [TR24] "(24) NCCL通信与分布式数据并行" (tech-renaissance.cn)
+ *   [TR16] "(16) DTensor：一张图纸，多卡共享的分布式张量抽象" (tech-renaissance.cn)
+ *   [DL]   "DDP分布式训练–数据加载和训练NCCL" (139.9.1.231)
+ *
+ *   1. plan      parameters are packed, last-registered first, into buckets of
+ *                at most bucket_cap bytes ([DDP] 3.2, 4.2), or split into the
+ *                two buckets DEEP_COMM / FIRST_COMM ([TR24] 八).
+ *   2. flatten   each rank's per-parameter gradients are copied into one
+ *                contiguous flat buffer per bucket ([DDP] 4.2, flat_grad).
+ *   3. reduce    every bucket element is summed over the N ranks in a fixed
+ *                FP32 order: SEQUENTIAL (zero, then ranks 0..N-1; [TR24] 一)
+ *                or RING (the ring reduce-scatter order of [DDP] 2.10-2.11:
+ *                chunk c = floor(i / ceil(L/N)) starts at rank (c+1) mod N).
+ *   4. scale     the sum is multiplied by fl(1/N) ([TR24] 九; [DDP] 4.2),
+ *                then stored as float32 or rounded to bf16 (nearest, ties to
+ *                even) -- fused into the reduce.
+ *   5. unflatten the averaged flat buffer is copied back to the per-parameter
+ *                gradient views ([DDP] 4.2, viewed back onto .grad).
+ *
+ * Conventions for every entry point
+ *   - Status codes, never exceptions or aborts.  Arguments are validated on
+ *     the host before any GPU work is queued; on a non-OK return nothing has
+ *     been enqueued (except DDP_ERR_HIP, returned when a launch fails).
+ *   - "stream" is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Device work is enqueued on it and runs asynchronously: an OK
+ *     return means "enqueued"; faults surface at the caller's next sync.
+ *   - Device pointers refer to memory of the current HIP device
+ *     (hipSetDevice / torch.cuda.set_device).  The caller owns all gradient
+ *     and output memory.  The library allocates device memory only for its
+ *     own descriptor tables (plans, bindings) and frees it in *_free.
+ *   - Element counts and offsets are int64 everywhere.
+ */
+#ifndef DDP_H
+#define DDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDP_ABI_VERSION 1
+/* Largest number of virtual ranks one call accepts. */
+#define DDP_MAX_RANKS 64
+
+typedef enum {
+    DDP_OK = 0,
+    DDP_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad index/enum */
+    DDP_ERR_UNSUPPORTED = 2,   /* dtype pair or rank count the library does not do */
+    DDP_ERR_OVERFLOW = 3,      /* a size that does not fit the int64 layout */
+    DDP_ERR_ALIAS = 4,         /* output overlaps an input other than exactly */
+    DDP_ERR_HIP = 5,           /* a HIP runtime call failed */
+    DDP_ERR_NOMEM = 6          /* host or device allocation failed */
+} ddp_status_t;
+
+typedef enum { DDP_F32 = 0, DDP_BF16 = 1 } ddp_dtype_t;
+
+typedef enum {
+    DDP_ORDER_SEQUENTIAL = 0,  /* acc = +0; acc += x_0; ...; acc += x_{N-1} */
+    DDP_ORDER_RING = 1         /* acc = x_s; acc += x_{s+1}; ... (indices mod N) */
+} ddp_order_t;
+
+/* Gradient regions of the two-bucket split, in memory order ([TR24] 七:
+ * G_BN_BIAS, G_BN_WEIGHT, G_FC_BIAS, G_FC_WEIGHT, G_FIRST_CONV, G_DEEP_CONV). */
+typedef enum {
+    DDP_REGION_BN_BIAS = 0,
+    DDP_REGION_BN_WEIGHT = 1,
+    DDP_REGION_FC_BIAS = 2,
+    DDP_REGION_FC_WEIGHT = 3,
+    DDP_REGION_FIRST = 4,
+    DDP_REGION_DEEP = 5
+} ddp_region_t;
+
+typedef struct ddp_plan ddp_plan_t;        /* opaque; host data + per-device tables */
+typedef struct ddp_binding ddp_binding_t;  /* opaque; one rank's parameter pointers */
+
+/* ------------------------------------------------------------------ plans
+ * Host-only calls: no GPU is touched, no device memory is allocated.
+ *
+ * Flat layout of a plan: buckets 0..B-1 back to back from element 0; inside
+ * a bucket its parameters back to back in "slot" order, with no padding.
+ */
+
+/* Cap-mode plan ([DDP] 3.2 and 4.2: parameters reversed, packed into buckets
+ * of about bucket_cap_mb; the last layer lands in the first bucket).
+ *   numel[n_params]   element count of each parameter, registration order, >= 0
+ *   bucket_cap_bytes  cap in bytes of `dtype` elements (25 MiB = 26214400), > 0
+ *   dtype             gradient element type (sets bytes per element)
+ *   out               receives a new plan; free it with ddp_plan_free
+ * Rule: walk parameters from last to first; close the current bucket when it
+ * is non-empty and adding the next parameter would exceed the cap; a lone
+ * parameter larger than the cap forms its own bucket.
+ * Errors: INVALID_ARG (null, n_params < 1, numel < 0, cap <= 0, bad dtype),
+ * OVERFLOW (total elements or bytes beyond int64), NOMEM. */
+ddp_status_t ddp_plan_buckets(const int64_t *numel, int32_t n_params,
+                              int64_t bucket_cap_bytes, ddp_dtype_t dtype,
+                              ddp_plan_t **out);
+
+/* Two-bucket plan ([TR24] 八, layout of [TR16] 四).
+ *   region[n_params]  one ddp_region_t per parameter
+ * Bucket 0 = DEEP_COMM: the DEEP parameters in registration order.
+ * Bucket 1 = FIRST_COMM: regions BN_BIAS, BN_WEIGHT, FC_BIAS, FC_WEIGHT,
+ * FIRST in that order, registration order inside each region.
+ * A bucket with no parameters is left out (the plan then has one bucket).
+ * Errors: as ddp_plan_buckets, plus INVALID_ARG for an unknown region tag. */
+ddp_status_t ddp_plan_two_bucket(const int64_t *numel, const uint8_t *region,
+                                 int32_t n_params, ddp_dtype_t dtype,
+                                 ddp_plan_t **out);
+
+/* Frees the plan and its device tables on every device they were uploaded
+ * to.  The caller must make sure no queued work still reads them. NULL is ok. */
+void ddp_plan_free(ddp_plan_t *plan);
+
+/* Number of buckets, or -1 for a NULL plan. */
+int32_t ddp_plan_num_buckets(const ddp_plan_t *plan);
+/* Total elements of the flat layout, or -1 for a NULL plan. */
+int64_t ddp_plan_total(const ddp_plan_t *plan);
+
+/* Bucket b: its length, its first element in the flat layout, and the range
+ * [first_slot, first_slot + n_slots) of slots it holds.  Any output pointer
+ * may be NULL.  Errors: INVALID_ARG (null plan, b out of range). */
+ddp_status_t ddp_plan_bucket(const ddp_plan_t *plan, int32_t b, int64_t *len,
+                             int64_t *base, int32_t *first_slot, int32_t *n_slots);
+
+/* Parameter held by flat slot `slot` (slots count 0..n_params-1 in flat order). */
+ddp_status_t ddp_plan_slot_param(const ddp_plan_t *plan, int32_t slot, int32_t *param);
+
+/* Bucket of parameter p and its element offset inside that bucket. */
+ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
+                            int64_t *offset);
+
+/* Uploads the plan's device tables (used by ddp_sync_allreduce_avg in RING
+ * order) to the current device, synchronously.  Optional: the first RING
+ * sync on a device does it by itself; call it beforehand when the sync will
+ * be captured into a HIP graph or must not allocate.
+ * Errors: INVALID_ARG, HIP, NOMEM. */
+ddp_status_t ddp_plan_prepare(ddp_plan_t *plan);
+
+/* ------------------------------------------------------------------ bindings
+ * One rank's per-parameter gradient buffers, resolved once (a static graph
+ * fixes every address up front: [DDP] 6.2; [TR24] 十 resolves addresses at
+ * capture time).
+ *   param_grads[n_params]  device pointer of each parameter's gradient, in
+ *                          registration order; each holds numel[p] elements
+ *                          of the element type flatten/unflatten are given.
+ *                          Pointers must be at least 2-byte aligned.
+ *   stream                 unused for now (the table upload is synchronous)
+ * The binding copies the pointer array; it does not own the gradients.
+ * Errors: INVALID_ARG (null plan/array/out, a null pointer for a parameter
+ * with numel > 0, misaligned pointer), HIP, NOMEM. */
+ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
+                             void *stream, ddp_binding_t **out);
+void ddp_binding_free(ddp_binding_t *binding);
+
+/* flat_buf[base_b + offset_p + j] = grad_p[j] for every parameter p of
+ * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch.
+ * flat_buf: device, ddp_plan_total(plan) elements, must not overlap any
+ * parameter buffer.  Errors: INVALID_ARG (null, bucket out of range, bad
+ * dtype, binding of another plan), HIP. */
+ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
+                         int32_t bucket, void *flat_buf, ddp_dtype_t dtype,
+                         void *stream);
+
+/* grad_p[j] = flat_out[base_b + offset_p + j]: the inverse copy, elements of
+ * `dtype` (the sync's output type).  Same arguments and errors. */
+ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
+                           int32_t bucket, const void *flat_out, ddp_dtype_t dtype,
+                           void *stream);
+
+/* ------------------------------------------------------------------ reduce
+ * One bucket's all-reduce + average, the operation of [TR24] 九 (sum with
+ * ncclSum, then dst *= 1/world_size) and of [DDP] 4.2 (all_reduce SUM, then
+ * flat_grad.div_(world_size)), on N buffers resident in one GPU.
+ *   rank_ptrs[n_ranks]  host array of device pointers; rank_ptrs[r] holds
+ *                       rank r's `len` elements of in_dtype
+ *   n_ranks             N, 1..DDP_MAX_RANKS
+ *   len                 elements in the bucket, >= 0 (0: nothing is done and
+ *                       the pointers are not looked at)
+ *   order               DDP_ORDER_SEQUENTIAL or DDP_ORDER_RING; for RING the
+ *                       chunks are C = ceil(len/N) elements from element 0
+ *   in_dtype, out_dtype f32->f32, bf16->bf16 or f32->bf16; bf16 inputs are
+ *                       widened exactly and summed in FP32
+ *   out                 device, `len` elements of out_dtype; every virtual
+ *                       rank's result (they are identical, [DDP] 2.5).  It may
+ *                       be exactly one of the inputs (in place, as ncclAllReduce
+ *                       with send == recv in [TR24] 九) when the dtypes match;
+ *                       any other overlap is rejected.
+ *   stream              hipStream_t
+ * N == 1: the result is the input, bit for bit ([TR24] 九 returns early for
+ * world_size <= 1); with out == rank_ptrs[0] nothing is launched.
+ * Pointers need only element alignment; 16-byte aligned buffers take the
+ * vector path, others a slower per-element path with identical results.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIAS, HIP. */
+ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ranks,
+                                      int64_t len, ddp_order_t order,
+                                      ddp_dtype_t in_dtype, ddp_dtype_t out_dtype,
+                                      void *out, void *stream);
+
+/* Every bucket of a plan in one launch (the whole synchronisation of one
+ * step; bit-identical to calling ddp_bucket_allreduce_avg per bucket on the
+ * bucket's sub-ranges).
+ *   rank_flat[n_ranks]  host array of device pointers to each rank's flat
+ *                       buffer (ddp_plan_total elements of the plan's dtype)
+ *   out_flat            device, ddp_plan_total elements of out_dtype
+ * RING chunks are computed per bucket (each bucket is its own all-reduce).
+ * The first RING call on a device uploads the plan's tables synchronously
+ * (see ddp_plan_prepare).  Errors: as ddp_bucket_allreduce_avg. */
+ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat,
+                                    int32_t n_ranks, ddp_order_t order,
+                                    ddp_dtype_t out_dtype, void *out_flat,
+                                    void *stream);
+
+/* ------------------------------------------------------------------ misc */
+const char *ddp_status_string(ddp_status_t status);
+/* Text of the last HIP failure seen by this thread ("" if none): the HIP call
+ * and the runtime's error string.  Valid until the thread's next failure. */
+const char *ddp_last_error(void);
+int32_t ddp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DDP_H */
