@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark: bucketed gradient synchronisation on one MI355X.
+
+Metric: effective HBM GB/s of one synchronisation, (N*P*b_in + P*b_out) /
+t_sync, and its fraction of the 8 TB/s HBM peak.  A step is one whole
+synchronisation of the workload: every bucket of the plan reduced over the N
+virtual ranks in the fixed order, scaled by 1/N and written -- one launch of
+ddp_sync_allreduce_avg.  Gradients sit in their bucket buffers (the
+gradient-as-bucket-view layout), so flatten and unflatten are not needed in
+the step; the same run also times the copy layout (flatten every rank, sync,
+unflatten) and reports it under "copy_path".
+
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload resnet50|gpt1p3b|gpt1p3b_two_bucket|many_small|llama7b|tiny]
+                       [--order ring|seq] [--no-cpu-baseline] [--no-copy-path]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective HBM GB/s (N·P·bytes read + P written) and % of peak per sync"
+KERNEL_SRC = os.path.join(ROOT, "gradient_allreduce_averaging_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, order, algorithmic_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they were taken on another version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(f"{workload}/{order}")
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="resnet50")
+    ap.add_argument("--order", default="ring", choices=["ring", "seq"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-path", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gradient_allreduce_averaging_amd as ddp
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    if args.calibrate:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
+        return
+    wl = W.workload(args.workload)
+    order = args.order
+    N = wl.n_ranks
+    if wl.two_bucket:
+        plan = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
+    else:
+        plan = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, wl.dtype)
+    P = plan.total
+    tin = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    tout = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    log(f"workload {wl.name}: N={N} P={P} buckets={plan.n_buckets} order={order} "
+        f"{wl.dtype}->{wl.out_dtype}")
+
+    flats = []
+    for r in range(N):
+        t = torch.empty(P, dtype=tin, device=dev)
+        W.device_normal_(t, r, wl.stream, wl.sigma)
+        flats.append(t)
+    out = torch.empty(P, dtype=tout, device=dev)
+    plan.prepare()
+    stream = torch.cuda.current_stream()
+    sync_bytes = wl.sync_bytes()
+
+    def sync(o=order):
+        ddp.sync_allreduce_avg(plan, flats, out, o, stream=stream)
+
+    # ---------------------------------------------------------------- timed
+    for _ in range(args.warmup):
+        sync()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        sync()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = float(np.mean(launch_ms))
+    value = sync_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = sync_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, kernel {kern_ms * 1e3:.1f} us avg "
+        f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
+
+    # ---------------------------------------------------------------- other order
+    other = {}
+    for o in ("seq", "ring"):
+        if o == order:
+            continue
+        for _ in range(5):
+            sync(o)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            sync(o)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        other[o] = {"ms_per_sync": round(ms, 5),
+                    "GBps": round(sync_bytes / (ms * 1e-3) / 1e9, 1)}
+
+    # ---------------------------------------------------------------- parity of the timed output
+    parity = None
+    cpu = None
+    if wl.total * N * wl.in_bytes <= (4 << 30) and not args.no_cpu_baseline:
+        import oracle
+        sync()
+        torch.cuda.synchronize()
+        got = out.view(torch.int32 if tout == torch.float32 else torch.int16).cpu().numpy()
+        host = [f.view(torch.int32 if tin == torch.float32 else torch.int16).cpu().numpy()
+                .view(np.float32 if tin == torch.float32 else np.uint16) for f in flats]
+        if wl.two_bucket:
+            oplan = oracle.plan_two_bucket(wl.numel, wl.regions)
+        else:
+            oplan = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, wl.in_bytes)
+        reps, t_cpu = 0, 0.0
+        want = None
+        while reps == 0 or t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            want = oracle.sync_avg(oplan, host, order, wl.dtype, wl.out_dtype)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        wv = want.view(np.int32 if tout == torch.float32 else np.int16)
+        same = got == wv
+        if tout == torch.float32:
+            both_nan = np.isnan(got.view(np.float32)) & np.isnan(want)
+        else:
+            both_nan = np.zeros_like(same)
+        parity = "bitwise equal to the CPU oracle" if bool((same | both_nan).all()) else \
+            f"MISMATCH in {int((~(same | both_nan)).sum())} elements"
+        cpu = {"value": round(sync_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the full {wl.name} synchronisation ({order} order, N={N}, P={P}), "
+                         f"{reps} repetition(s), {t_cpu:.1f} s single-threaded C oracle"}
+        log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps")
+
+    # ---------------------------------------------------------------- copy layout
+    copy_path = None
+    if not args.no_copy_path and not wl.two_bucket and N * P * wl.in_bytes <= (16 << 30):
+        # per-parameter gradients of every rank, holding the same values
+        grads = [[torch.empty(n, dtype=tin, device=dev) for n in wl.numel] for _ in range(N)]
+        binds = [ddp.bind_params(plan, grads[r]) for r in range(N)]
+        for r in range(N):
+            ddp.unflatten(plan, binds[r], flats[r], stream=stream)
+        res = [torch.empty(n, dtype=tout, device=dev) for n in wl.numel]
+        rbind = ddp.bind_params(plan, res)
+
+        def full_step():
+            for r in range(N):
+                ddp.flatten(plan, binds[r], flats[r], stream=stream)
+            sync()
+            ddp.unflatten(plan, rbind, out, stream=stream)
+
+        for _ in range(5):
+            full_step()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        reps = max(10, args.steps // 4)
+        tf = ts = tu = 0.0
+        for _ in range(reps):
+            e[0].record(stream)
+            for r in range(N):
+                ddp.flatten(plan, binds[r], flats[r], stream=stream)
+            e[1].record(stream)
+            sync()
+            e[2].record(stream)
+            ddp.unflatten(plan, rbind, out, stream=stream)
+            e[3].record(stream)
+            torch.cuda.synchronize()
+            tf += e[0].elapsed_time(e[1])
+            ts += e[1].elapsed_time(e[2])
+            tu += e[2].elapsed_time(e[3])
+        tf, ts, tu = tf / reps, ts / reps, tu / reps
+        fb = 2 * N * P * wl.in_bytes
+        ub = 2 * P * wl.out_bytes
+        copy_path = {
+            "ms_per_step": round(tf + ts + tu, 4),
+            "flatten_ms": round(tf, 4), "flatten_GBps": round(fb / (tf * 1e-3) / 1e9, 1),
+            "sync_ms": round(ts, 4),
+            "unflatten_ms": round(tu, 4), "unflatten_GBps": round(ub / (tu * 1e-3) / 1e9, 1),
+            "metric_GBps": round(sync_bytes / ((tf + ts + tu) * 1e-3) / 1e9, 1),
+            "launches": N + 2}
+        log(f"copy path: {copy_path}")
+        del grads, binds, res, rbind
+
+    traffic = measured_traffic(wl.name, order, sync_bytes)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {len(wl.params)} gradient tensors, "
+                               f"{P} elements, {N} virtual ranks, {plan.n_buckets} buckets",
+                   "virtual_ranks": N, "elements": P, "buckets": plan.n_buckets,
+                   "bucket_cap_bytes": wl.bucket_cap_bytes,
+                   "plan": "two-bucket" if wl.two_bucket else "cap",
+                   "order": order, "grad_dtype": wl.dtype, "out_dtype": wl.out_dtype,
+                   "grad_layout": "bucket view (gradients live in the per-rank flat buckets)",
+                   "bytes_per_sync": sync_bytes,
+                   "device": torch.cuda.get_device_name(0)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "reduce_fast (one launch per sync)",
+                     "kernel_ms": round(kern_ms, 5)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "other_orders": other,
+        "copy_path": copy_path,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,8 @@
 // Device-side copy of a plan's bucket table, for one device and one tile size.
 struct ddp_dev_tables {
     int64_t *bucket_base = nullptr;   // [n_buckets + 1] flat start of each bucket, then total
-    int32_t *tile_bucket = nullptr;   // [n_tiles] bucket holding each tile's first element
+    int32_t *tile_bucket = nullptr;   // bucket holding the first element of every
+                                      // 2^kTileTableShift-th tile
     int64_t n_tiles = 0;
 };
 

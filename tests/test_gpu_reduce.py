@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")]
 ORDERS = ["seq", "ring"]
-# f32 tiles hold 2048 elements, bf16 tiles 4096
+# lengths: empty, shorter than one 16-byte vector, ragged tails, one and many
+# tiles (a tile is 256 f32 or 512 bf16 elements)
 LENGTHS = [0, 1, 3, 5, 63, 2048, 2049, 4103, 3 * 4096 + 5, 100_003]
 RANKS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 64]
 
