@@ -120,26 +120,38 @@ def main():
         ddp.sync_allreduce_avg(plan, flats, out, o, stream=stream)
 
     # ---------------------------------------------------------------- timed
+    # K back-to-back steps, wall clock between two synchronisations; one event
+    # pair brackets the loop on the launch stream.
     for _ in range(args.warmup):
         sync()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    loop_a, loop_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    loop_a.record(stream)
+    for _ in range(args.steps):
+        sync()
+    loop_b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = loop_a.elapsed_time(loop_b) / args.steps
+    value = sync_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Per-launch duration of the reduce kernel: the same K steps again, each
+    # launch bracketed by its own event pair on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     for a, b in ev:
         a.record(stream)
         sync()
         b.record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     kern_ms = float(np.mean(launch_ms))
-    value = sync_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = sync_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, kernel {kern_ms * 1e3:.1f} us avg "
-        f"(min {min(launch_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
+    log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
+        f"stream, kernel {kern_ms * 1e3:.1f} us avg (min {min(launch_ms) * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s")
 
     # ---------------------------------------------------------------- other order
     other = {}
@@ -187,8 +199,14 @@ def main():
             both_nan = np.zeros_like(same)
         parity = "bitwise equal to the CPU oracle" if bool((same | both_nan).all()) else \
             f"MISMATCH in {int((~(same | both_nan)).sum())} elements"
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
         cpu = {"value": round(sync_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+               "kind": "oracle", "host_cpu": cpu_model, "host_threads": os.cpu_count(),
                "sample": f"the full {wl.name} synchronisation ({order} order, N={N}, P={P}), "
                          f"{reps} repetition(s), {t_cpu:.1f} s single-threaded C oracle"}
         log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps")
@@ -269,7 +287,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "reduce_fast (one launch per sync)",
-                     "kernel_ms": round(kern_ms, 5)},
+                     "kernel_ms": round(kern_ms, 5),
+                     "kernel_ms_min": round(min(launch_ms), 5),
+                     "stream_ms_per_step": round(gpu_ms_per_step, 5)},
         "cpu_baseline": cpu,
         "parity": parity,
         "other_orders": other,
