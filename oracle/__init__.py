@@ -73,24 +73,29 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def load_core(path: str):
+    """Load a compiled oracle core and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_rne_bf16.restype = ctypes.c_uint16
+    lib.oracle_rne_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_rne_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_bucket_avg.restype = ctypes.c_int
+    lib.oracle_bucket_avg.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.oracle_sampled_avg.restype = ctypes.c_int
+    lib.oracle_sampled_avg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
 def _core():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
-        lib.oracle_rne_bf16.restype = ctypes.c_uint16
-        lib.oracle_rne_bf16.argtypes = [ctypes.c_float]
-        lib.oracle_rne_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-        lib.oracle_bucket_avg.restype = ctypes.c_int
-        lib.oracle_bucket_avg.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
-                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                          ctypes.c_int, ctypes.c_void_p]
-        lib.oracle_sampled_avg.restype = ctypes.c_int
-        lib.oracle_sampled_avg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-        _lib = lib
+        _lib = load_core(_LIB)
     return _lib
 
 
