@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--order", default="ring", choices=["ring", "seq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-path", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-fused-sgd", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -152,6 +154,47 @@ def main():
     log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
         f"stream, kernel {kern_ms * 1e3:.1f} us avg (min {min(launch_ms) * 1e3:.1f}), "
         f"{achieved:.0f} GB/s")
+
+    # ---------------------------------------------------------------- access-pattern ceiling
+    # The same N input buffers read with the reduce's access pattern (N
+    # non-temporal 16-byte loads per lane, one-wave blocks) with and without
+    # the one store per lane, and no arithmetic: the ceiling of this pattern
+    # on this machine.  The probe's store covers the input byte count, so it runs
+    # only when input and output elements have the same size.
+    ceiling = None
+    if wl.in_bytes == wl.out_bytes and not args.no_ceiling:
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
+        probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        nvec = P * wl.in_bytes // 16
+        ptrs = (ctypes.c_void_p * N)(*[ctypes.c_void_p(f.data_ptr()) for f in flats])
+
+        def probe_run(write):
+            rc = probe.ddp_probe_stream(ptrs, N, ctypes.c_void_p(out.data_ptr()), nvec, write,
+                                        ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(stream.cuda_stream))
+            assert rc == 0, "probe launch failed"
+
+        res = {}
+        for write in (1, 0):
+            for _ in range(5):
+                probe_run(write)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                probe_run(write)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.steps
+            res[write] = nvec * 16 * (N + write) / (ms * 1e-3) / 1e9
+        ceiling = {"pattern_GBps": round(res[1], 1), "read_only_GBps": round(res[0], 1),
+                   "kernel_frac_of_pattern": round(achieved / res[1], 4),
+                   "probe": f"{N} non-temporal 16-byte loads + 1 store per lane on the same "
+                            "buffers, one-wave blocks, no arithmetic (read_only: without the store)"}
+        log(f"ceiling: {ceiling}")
 
     # ---------------------------------------------------------------- other order
     other = {}
@@ -259,6 +302,45 @@ def main():
         log(f"copy path: {copy_path}")
         del grads, binds, res, rbind
 
+    # ---------------------------------------------------------------- fused optimizer step
+    # The average folded into a momentum-SGD step (ddp_sync_sgd_update) against
+    # the unfused sequence it replaces: the synchronisation, then the optimizer
+    # reading the averaged gradient back (torch's in-place ops).
+    fused = None
+    if not args.no_fused_sgd and wl.out_dtype == "f32":
+        params = torch.empty(P, dtype=torch.float32, device=dev)
+        W.device_normal_(params, 99, 7, 1.0)
+        mbuf = torch.zeros(P, dtype=torch.float32, device=dev)
+        lr, mu = 0.01, 0.9
+
+        def fused_step():
+            ddp.sync_sgd_update(plan, flats, params, lr, order, momentum_buf=mbuf, momentum=mu,
+                                stream=stream)
+
+        def unfused_step():
+            sync()
+            mbuf.mul_(mu).add_(out)
+            params.add_(mbuf, alpha=-lr)
+
+        res = {}
+        for name, fn in (("fused", fused_step), ("unfused", unfused_step)):
+            for _ in range(5):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            res[name] = a.elapsed_time(b) / args.steps
+        fb = N * P * wl.in_bytes + 4 * P * 4
+        fused = {"ms": round(res["fused"], 5), "GBps": round(fb / (res["fused"] * 1e-3) / 1e9, 1),
+                 "bytes": fb, "unfused_ms": round(res["unfused"], 5),
+                 "speedup_vs_unfused": round(res["unfused"] / res["fused"], 3),
+                 "step": "momentum SGD (mu 0.9) on f32 parameters; unfused = sync + torch mul_/add_"}
+        log(f"fused sgd: {fused}")
+        del params, mbuf
+
     traffic = measured_traffic(wl.name, order, sync_bytes)
     line = {
         "metric": METRIC,
@@ -290,10 +372,12 @@ def main():
                      "kernel_ms": round(kern_ms, 5),
                      "kernel_ms_min": round(min(launch_ms), 5),
                      "stream_ms_per_step": round(gpu_ms_per_step, 5)},
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity": parity,
         "other_orders": other,
         "copy_path": copy_path,
+        "fused_sgd": fused,
     }
     print(json.dumps(line), flush=True)
 

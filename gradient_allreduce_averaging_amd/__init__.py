@@ -8,7 +8,7 @@ been built; there is no fallback implementation.
 
 Names follow the C ABI: ``plan_buckets``, ``plan_two_bucket``,
 ``bind_params``, ``flatten``, ``bucket_allreduce_avg``,
-``sync_allreduce_avg``, ``unflatten``.
+``sync_allreduce_avg``, ``sync_sgd_update``, ``unflatten``.
 """
 from __future__ import annotations
 
@@ -86,6 +86,8 @@ def _load():
                                      ctypes.c_int),
         "ddp_sync_allreduce_avg": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_int, vp, vp], ctypes.c_int),
+        "ddp_sync_sgd_update": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                 vp, vp, vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
         "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "ddp_abi_version": ([], ctypes.c_int32),
         "ddp_last_error": ([], ctypes.c_char_p),
@@ -296,6 +298,34 @@ def sync_allreduce_avg(plan: Plan, rank_flats: Sequence, out_flat, order="ring",
     _check(lib.ddp_sync_allreduce_avg(plan.handle, ptrs, len(rank_flats), _ORDERS[order],
                                       _dtype_code(out_flat), _dev_ptr(out_flat),
                                       _stream_handle(stream)), "ddp_sync_allreduce_avg")
+
+
+def sync_sgd_update(plan: Plan, rank_flats: Sequence, params, lr: float, order="ring",
+                    grad_out=None, momentum_buf=None, momentum: float = 0.0,
+                    out_dtype=None, stream=None):
+    """Average every bucket and apply one SGD step to the flat f32 ``params``
+    in the same launch (``ddp_sync_sgd_update``)."""
+    import torch
+    total = plan.total
+    for t in rank_flats:
+        if _dtype_code(t) != plan.dtype or t.numel() < total:
+            raise ValueError("rank flat buffers differ from the plan's dtype or size")
+    for t in (params, momentum_buf):
+        if t is not None and (t.dtype != torch.float32 or t.numel() < total):
+            raise ValueError("parameters and momentum must be float32 of the plan's size")
+    if grad_out is not None:
+        if grad_out.numel() < total:
+            raise ValueError("grad_out too short")
+        out_code = _dtype_code(grad_out)
+    else:
+        out_code = plan.dtype if out_dtype is None else _DTYPES[out_dtype]
+    ptrs = _ptr_array([_dev_ptr(t) for t in rank_flats])
+    _check(lib.ddp_sync_sgd_update(plan.handle, ptrs, len(rank_flats), _ORDERS[order], out_code,
+                                   None if grad_out is None else _dev_ptr(grad_out),
+                                   _dev_ptr(params),
+                                   None if momentum_buf is None else _dev_ptr(momentum_buf),
+                                   float(lr), float(momentum), _stream_handle(stream)),
+           "ddp_sync_sgd_update")
 
 
 def status_string(status: int) -> str:

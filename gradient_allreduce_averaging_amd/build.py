@@ -24,8 +24,24 @@ DEVICE = ["--offload-arch=" + ARCH, "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+PROBE_SRC = "probe.hip"
+PROBE_LIB = os.path.join(HERE, "libddp_probe.so")
+
+
+def _build_probe(verbose: bool) -> str:
+    """The benchmark's access-pattern probe, a library of its own."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-x", "hip"] + DEVICE + COMMON + ["-shared", os.path.join(CSRC, PROBE_SRC),
+                                                    "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libddp.so next to this file."""
+    """Compile every source and link libddp.so (and libddp_probe.so) next to this file."""
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
@@ -45,6 +61,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
+    _build_probe(verbose)
     return LIB
 
 

@@ -139,6 +139,21 @@ __device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int64_t
     return (int)(((i - base) / C + 1) % N);
 }
 
+// The scaled average of element i, one element at a time (N >= 2).
+template <int IN, bool RING>
+__device__ __forceinline__ float avg_elem(const RankArgs &ra, int N, int64_t total,
+                                          const Buckets &bk, int32_t b0, float inv, int64_t i)
+{
+    int r = RING ? ring_start(bk, b0, total, N, i) : 0;
+    float acc = load_elem<IN>(ra.p[r], i);
+    if (!RING) acc = 0.0f + acc;
+    for (int k = 1; k < N; ++k) {
+        r = wrap(r + 1, N);
+        acc = acc + load_elem<IN>(ra.p[r], i);
+    }
+    return acc * inv;
+}
+
 // Per-element path: positions [i0, i0 + cnt) clipped to total.
 template <int IN, int OUT, bool RING>
 __device__ void reduce_elems(const RankArgs &ra, int N, int64_t total, const Buckets &bk,
@@ -147,14 +162,56 @@ __device__ void reduce_elems(const RankArgs &ra, int N, int64_t total, const Buc
     for (int e = 0; e < cnt; ++e) {
         const int64_t i = i0 + e;
         if (i >= total) break;
-        int r = RING ? ring_start(bk, b0, total, N, i) : 0;
-        float acc = load_elem<IN>(ra.p[r], i);
-        if (!RING) acc = 0.0f + acc;
-        for (int k = 1; k < N; ++k) {
-            r = wrap(r + 1, N);
-            acc = acc + load_elem<IN>(ra.p[r], i);
+        store_elem<OUT>(out, i, avg_elem<IN, RING>(ra, N, total, bk, b0, inv, i));
+    }
+}
+
+// ---------------------------------------------------------------- SGD epilogue
+// The optimizer step the 1/N average can be folded into ([TR24] 九, note on
+// removing the separate scale kernel; update rule of [DDP] 5.3):
+//   g = the averaged gradient as stored (bf16: rounded, then widened back)
+//   momentum (optional): v = mu * m + g; m = v; g = v
+//   p = p - lr * g
+struct SgdArgs {
+    float *param;      // flat f32 parameters, updated in place
+    float *mom;        // flat f32 momentum buffer, or null
+    void *grad_out;    // flat averaged gradient (OUT elements), or null
+    float lr, mu;
+};
+
+template <bool MOM>
+__device__ __forceinline__ float sgd_elem(float p, float g, float &m, float lr, float mu)
+{
+    if (MOM) {
+        float v = mu * m;
+        v = v + g;
+        m = v;
+        g = v;
+    }
+    const float step = lr * g;
+    return p - step;
+}
+
+// Per-element fused path.  N == 1 takes the input as the average, bit for bit.
+template <int IN, int OUT, bool RING, bool MOM>
+__device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Buckets &bk, int32_t b0,
+                          float inv, const SgdArgs &sa, int64_t i0, int cnt)
+{
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t i = i0 + e;
+        if (i >= total) break;
+        const float y = N == 1 ? load_elem<IN>(ra.p[0], i) : avg_elem<IN, RING>(ra, N, total, bk, b0, inv, i);
+        float g = y;
+        if (OUT == kBF16) {
+            const uint32_t h = bf16_rne(y);
+            g = widen_bf16(h);
+            if (sa.grad_out) static_cast<uint16_t *>(sa.grad_out)[i] = (uint16_t)h;
+        } else if (sa.grad_out) {
+            static_cast<float *>(sa.grad_out)[i] = y;
         }
-        store_elem<OUT>(out, i, acc * inv);
+        float m = MOM ? sa.mom[i] : 0.0f;
+        sa.param[i] = sgd_elem<MOM>(sa.param[i], g, m, sa.lr, sa.mu);
+        if (MOM) sa.mom[i] = m;
     }
 }
 
@@ -205,26 +262,43 @@ __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int 
     return s;
 }
 
+// Convert and store one vector of scaled averages y at element i0; for a
+// bf16 output y is replaced by the stored value widened back to f32.
+template <int IN, int OUT>
+__device__ __forceinline__ void store_y(void *out, int64_t i0, float *y, bool write)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    if (OUT == kF32) {
+        u32x4 o;
+        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
+        if (write) st_stream(static_cast<float *>(out) + i0, o);
+    } else {
+        uint32_t h[VEC];
+        for (int e = 0; e < VEC; ++e) {
+            h[e] = bf16_rne(y[e]);
+            y[e] = widen_bf16(h[e]);
+        }
+        if (VEC == 4) {
+            u32x2 o;
+            o[0] = h[0] | (h[1] << 16);
+            o[1] = h[2] | (h[3] << 16);
+            if (write) st_stream(static_cast<uint16_t *>(out) + i0, o);
+        } else {
+            u32x4 o;
+            for (int w = 0; w < 4; ++w) o[w] = h[2 * w] | (h[2 * w + 1] << 16);
+            if (write) st_stream(static_cast<uint16_t *>(out) + i0, o);
+        }
+    }
+}
+
 // Scale, convert and store one vector of accumulators at element i0.
 template <int IN, int OUT>
 __device__ __forceinline__ void store_vec(void *out, int64_t i0, const float *acc, float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
-    if (OUT == kF32) {
-        u32x4 o;
-        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[e] * inv);
-        st_stream(static_cast<float *>(out) + i0, o);
-    } else if (VEC == 4) {
-        u32x2 o;
-        o[0] = bf16_rne(acc[0] * inv) | (bf16_rne(acc[1] * inv) << 16);
-        o[1] = bf16_rne(acc[2] * inv) | (bf16_rne(acc[3] * inv) << 16);
-        st_stream(static_cast<uint16_t *>(out) + i0, o);
-    } else {
-        u32x4 o;
-        for (int w = 0; w < 4; ++w)
-            o[w] = bf16_rne(acc[2 * w] * inv) | (bf16_rne(acc[2 * w + 1] * inv) << 16);
-        st_stream(static_cast<uint16_t *>(out) + i0, o);
-    }
+    float y[VEC];
+    for (int e = 0; e < VEC; ++e) y[e] = acc[e] * inv;
+    store_y<IN, OUT>(out, i0, y, true);
 }
 
 // N known at compile time (2..8): all N * kUnroll vector loads in flight.
@@ -285,6 +359,91 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
             reduce_elems<IN, OUT, RING>(ra, NR, total, bk, sg.bucket, inv, out, i0[u], VEC);
         }
     }
+}
+
+// Fused average + SGD step, N known at compile time (1..8).  Per lane: the N
+// gradient vectors and the lane's parameter (and momentum) vectors are loaded
+// together, the average is folded and scaled, optionally stored, and the
+// parameters updated in place.  Parameters are f32: one 16-byte vector per 4
+// elements, so a bf16 lane (8 elements) moves two.
+template <int NR, bool RING, int IN, int OUT, bool MOM>
+__global__ void __launch_bounds__(kThreads)
+reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
+{
+    static_assert(kUnroll == 1, "the fused kernel processes one vector per lane");
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    constexpr int PV = VEC / 4;
+    const int64_t tile = tile_of_block();
+    const int64_t tile0 = tile * (kThreads * VEC);
+    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
+    const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
+    const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
+    const bool fast = in_a || (RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi);
+
+    // rotated rank pointers for both segments, resolved in scalar registers
+    const char *qa[NR];
+    const char *qb[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        qa[k] = static_cast<const char *>(ra.p[wrap(sg.sa + k, NR)]);
+        qb[k] = RING ? static_cast<const char *>(ra.p[wrap(sg.sb + k, NR)]) : qa[k];
+    }
+    u32x4 v[NR], pv[PV], mv[PV];
+    if (total >= VEC) {   // unconditional loads, as in reduce_fast
+#pragma unroll
+        for (int k = 0; k < NR; ++k) v[k] = ld_stream((in_a ? qa[k] : qb[k]) + (fast ? i0 * ISZ : 0));
+        const int64_t po = fast ? i0 * 4 : 0;
+#pragma unroll
+        for (int j = 0; j < PV; ++j) {
+            pv[j] = ld_stream(reinterpret_cast<const char *>(sa.param) + po + 16 * j);
+            if (MOM) mv[j] = ld_stream(reinterpret_cast<const char *>(sa.mom) + po + 16 * j);
+        }
+    }
+    if (fast) {
+        float y[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float x = lane<IN>(v[0], e);
+            y[e] = (RING || NR == 1) ? x : 0.0f + x;
+        }
+#pragma unroll
+        for (int k = 1; k < NR; ++k)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) y[e] = y[e] + lane<IN>(v[k], e);
+        if (NR > 1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;
+        }
+        store_y<IN, OUT>(sa.grad_out, i0, y, sa.grad_out != nullptr);
+#pragma unroll
+        for (int j = 0; j < PV; ++j) {
+            u32x4 po, mo;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
+                po[w] = __float_as_uint(
+                    sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, sa.lr, sa.mu));
+                mo[w] = __float_as_uint(m);
+            }
+            st_stream(sa.param + i0 + 4 * j, po);
+            if (MOM) st_stream(sa.mom + i0 + 4 * j, mo);
+        }
+    } else if (i0 < total) {
+        sgd_elems<IN, OUT, RING, MOM>(ra, NR, total, bk, sg.bucket, inv, sa, i0, VEC);
+    }
+}
+
+// Fused average + SGD step, one element per thread, element-aligned buffers
+// of a single bucket, any N.
+template <bool RING, int IN, int OUT, bool MOM>
+__global__ void __launch_bounds__(kThreads)
+reduce_sgd_scalar(RankArgs ra, int N, int64_t total, float inv, SgdArgs sa)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    const Buckets single = {nullptr, nullptr, 1};
+    sgd_elems<IN, OUT, RING, MOM>(ra, N, total, single, 0, inv, sa, i, 1);
 }
 
 // Any N up to DDP_MAX_RANKS: ranks walked in a loop.
@@ -493,9 +652,61 @@ ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, 
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Common validation of a reduce call.  Returns OK or an error code.
+template <bool RING, int IN, int OUT, bool MOM>
+ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Buckets &bk,
+                              float inv, const SgdArgs &sa, hipStream_t st, bool vec_ok)
+{
+    if (vec_ok) {
+        const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
+        if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
+        const dim3 g((unsigned)tiles), b(kThreads);
+        switch (N) {
+        case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        default: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        }
+    } else {
+        const int64_t blocks = (total + kThreads - 1) / kThreads;
+        if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
+        reduce_sgd_scalar<RING, IN, OUT, MOM><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
+            ra, N, total, inv, sa);
+    }
+    return launched("fused SGD kernel launch");
+}
+
+template <bool RING, bool MOM>
+ddp_status_t launch_sgd_pair(const RankArgs &ra, int N, int64_t total, int in, int out_dt,
+                             const Buckets &bk, float inv, const SgdArgs &sa, hipStream_t st,
+                             bool vec_ok)
+{
+    if (in == DDP_F32 && out_dt == DDP_F32)
+        return launch_sgd_typed<RING, kF32, kF32, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
+    if (in == DDP_BF16 && out_dt == DDP_BF16)
+        return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
+    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
+}
+
+ddp_status_t launch_sgd(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
+                        const Buckets &bk, const SgdArgs &sa, hipStream_t st, bool vec_ok)
+{
+    const float inv = 1.0f / (float)N;
+    const bool ring = order == DDP_ORDER_RING, mom = sa.mom != nullptr;
+    if (ring)
+        return mom ? launch_sgd_pair<true, true>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok)
+                   : launch_sgd_pair<true, false>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok);
+    return mom ? launch_sgd_pair<false, true>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok)
+               : launch_sgd_pair<false, false>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok);
+}
+
+// Common validation of a reduce call.  Returns OK or an error code.  The
+// output may be null only when out_optional is set.
 ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int order, int in,
-                          int out_dt, const void *out)
+                          int out_dt, const void *out, bool out_optional = false)
 {
     if (n < 1 || len < 0) return DDP_ERR_INVALID_ARG;
     if (order != DDP_ORDER_SEQUENTIAL && order != DDP_ORDER_RING) return DDP_ERR_INVALID_ARG;
@@ -505,11 +716,12 @@ ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int o
     if (n == 1 && in != out_dt) return DDP_ERR_UNSUPPORTED;
     if (len > INT64_MAX / 4) return DDP_ERR_OVERFLOW;
     if (len == 0) return DDP_OK;   // nothing is read or written: pointers may be null
-    if (!ptrs || !out) return DDP_ERR_INVALID_ARG;
+    if (!ptrs || (!out && !out_optional)) return DDP_ERR_INVALID_ARG;
     for (int r = 0; r < n; ++r) {
         if (!ptrs[r]) return DDP_ERR_INVALID_ARG;
         if (!aligned(ptrs[r], dtype_size(in))) return DDP_ERR_INVALID_ARG;
     }
+    if (!out) return DDP_OK;
     if (!aligned(out, dtype_size(out_dt))) return DDP_ERR_INVALID_ARG;
     return check_alias(ptrs, n, len, dtype_size(in), out, dtype_size(out_dt));
 }
@@ -666,6 +878,72 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
     if ((stc = plan_tables(plan, tile_elems(in), &t)) != DDP_OK) return stc;
     const Buckets bk = {t->bucket_base, t->tile_bucket, plan->n_buckets()};
     return launch_reduce(ra, n_ranks, total, order, in, out_dtype, bk, out_flat, st, true);
+}
+
+ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
+                                 ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
+                                 float *param_flat, float *momentum_flat, float lr, float momentum,
+                                 void *stream)
+{
+    if (!plan) return DDP_ERR_INVALID_ARG;
+    const int in = plan->dtype;
+    const int64_t total = plan->total;
+    ddp_status_t stc =
+        check_reduce(rank_flat, n_ranks, total, order, in, out_dtype, grad_out, true);
+    if (stc != DDP_OK) return stc;
+    if (total == 0) return DDP_OK;
+    if (!param_flat || !aligned(param_flat, 4)) return DDP_ERR_INVALID_ARG;
+    if (momentum_flat && !aligned(momentum_flat, 4)) return DDP_ERR_INVALID_ARG;
+    const int isz = dtype_size(in), osz = dtype_size(out_dtype);
+    // parameters and momentum are written: they may overlap nothing else
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(param_flat);
+    const uintptr_t ma = reinterpret_cast<uintptr_t>(momentum_flat);
+    const uintptr_t ga = reinterpret_cast<uintptr_t>(grad_out);
+    for (int r = 0; r < n_ranks; ++r) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(rank_flat[r]);
+        if (overlaps(x, total * isz, pa, total * 4)) return DDP_ERR_ALIAS;
+        if (momentum_flat && overlaps(x, total * isz, ma, total * 4)) return DDP_ERR_ALIAS;
+    }
+    if (grad_out && overlaps(ga, total * osz, pa, total * 4)) return DDP_ERR_ALIAS;
+    if (momentum_flat && grad_out && overlaps(ga, total * osz, ma, total * 4)) return DDP_ERR_ALIAS;
+    if (momentum_flat && overlaps(pa, total * 4, ma, total * 4)) return DDP_ERR_ALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RankArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    bool vec_ok = n_ranks <= 8 && aligned(param_flat, 16) &&
+                  (!momentum_flat || aligned(momentum_flat, 16)) && (!grad_out || aligned(grad_out, 16));
+    for (int r = 0; r < n_ranks; ++r) {
+        ra.p[r] = rank_flat[r];
+        vec_ok = vec_ok && aligned(rank_flat[r], 16);
+    }
+    if (!vec_ok) {
+        // element-aligned buffers or N > 8: one per-element launch per bucket
+        for (int32_t b = 0; b < plan->n_buckets(); ++b) {
+            const int64_t base = plan->bucket_base[b], len = plan->bucket_base[b + 1] - base;
+            if (len == 0) continue;
+            RankArgs sub;
+            std::memset(&sub, 0, sizeof(sub));
+            for (int r = 0; r < n_ranks; ++r)
+                sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
+            SgdArgs sa = {param_flat + base, momentum_flat ? momentum_flat + base : nullptr,
+                          grad_out ? static_cast<char *>(grad_out) + base * osz : nullptr, lr,
+                          momentum};
+            const Buckets single = {nullptr, nullptr, 1};
+            ddp_status_t s2 = launch_sgd(sub, n_ranks, len, order, in, out_dtype, single, sa, st, false);
+            if (s2 != DDP_OK) return s2;
+        }
+        return DDP_OK;
+    }
+    const SgdArgs sa = {param_flat, momentum_flat, grad_out, lr, momentum};
+    if (order == DDP_ORDER_SEQUENTIAL) {
+        const Buckets single = {nullptr, nullptr, 1};
+        return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single, sa, st, true);
+    }
+    const ddp_dev_tables *t = nullptr;
+    if ((stc = plan_tables(plan, tile_elems(in), &t)) != DDP_OK) return stc;
+    const Buckets bk = {t->bucket_base, t->tile_bucket, plan->n_buckets()};
+    return launch_sgd(ra, n_ranks, total, order, in, out_dtype, bk, sa, st, true);
 }
 
 ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, void *stream,

@@ -217,6 +217,32 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
                                     ddp_dtype_t out_dtype, void *out_flat,
                                     void *stream);
 
+/* Every bucket's average folded into one SGD step on the flat parameters,
+ * in one launch: the optimizer update [TR24] 九 suggests absorbing the 1/N
+ * scale into, with the update rule theta <- theta - eta * g of [DDP] 5.3.
+ * Per element, with g the averaged gradient exactly as ddp_sync_allreduce_avg
+ * would store it (a bf16 average is rounded, then widened back to f32):
+ *     momentum_flat != NULL:  v = fl(fl(momentum * m) + g);  m = v;  g = v
+ *     param:                  p = fl(p - fl(lr * g))
+ * so the result equals ddp_sync_allreduce_avg followed by that step, bit for
+ * bit, while the average never makes a round trip through HBM.
+ *   rank_flat, n_ranks, order, out_dtype  as ddp_sync_allreduce_avg
+ *   grad_out       device, ddp_plan_total elements of out_dtype, or NULL to
+ *                  skip storing the average; may be exactly one of the inputs
+ *   param_flat     device, ddp_plan_total f32 parameters in the plan's flat
+ *                  layout, updated in place
+ *   momentum_flat  device, ddp_plan_total f32 momentum buffer updated in
+ *                  place (start from zeros), or NULL for plain SGD
+ *   lr, momentum   learning rate and momentum factor (f32)
+ * param_flat and momentum_flat may overlap no other buffer (DDP_ERR_ALIAS).
+ * N == 1 takes the input as the average, bit for bit.  16-byte aligned
+ * buffers and N <= 8 take the vector kernel, others a per-element kernel with
+ * identical results.  Errors: as ddp_sync_allreduce_avg. */
+ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
+                                 ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
+                                 float *param_flat, float *momentum_flat, float lr,
+                                 float momentum, void *stream);
+
 /* ------------------------------------------------------------------ misc */
 const char *ddp_status_string(ddp_status_t status);
 /* Text of the last HIP failure seen by this thread ("" if none): the HIP call

@@ -87,6 +87,9 @@ def load_core(path: str):
     lib.oracle_sampled_avg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.oracle_sgd_step.restype = ctypes.c_int
+    lib.oracle_sgd_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int64, ctypes.c_float, ctypes.c_float]
     return lib
 
 
@@ -236,6 +239,36 @@ def rne_bf16(y: np.ndarray) -> np.ndarray:
     out = np.empty(y.size, dtype=np.uint16)
     _core().oracle_rne_bf16_array(y.ctypes.data, y.size, out.ctypes.data)
     return out.reshape(y.shape)
+
+
+def sgd_step(param: np.ndarray, grad: np.ndarray, lr: float, grad_dtype: str = "f32",
+             momentum_buf: np.ndarray = None, momentum: float = 0.0):
+    """One SGD step in place on float32 ``param`` (and ``momentum_buf``):
+    theta <- theta - lr * g ([DDP] section 5.3), g the averaged gradient as
+    stored; with a momentum buffer v = mu * v + g first (see oracle_core.c)."""
+    assert param.dtype == np.float32 and param.flags.c_contiguous
+    g = np.ascontiguousarray(grad, dtype=_NP_DTYPE[grad_dtype])
+    if g.size != param.size:
+        raise ValueError("gradient and parameter sizes differ")
+    mptr = None
+    if momentum_buf is not None:
+        assert momentum_buf.dtype == np.float32 and momentum_buf.flags.c_contiguous
+        mptr = momentum_buf.ctypes.data
+    rc = _core().oracle_sgd_step(param.ctypes.data, mptr, g.ctypes.data, _DTYPE_CODE[grad_dtype],
+                                 param.size, np.float32(lr), np.float32(momentum))
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+
+
+def sync_sgd(plan: Plan, rank_flats: Sequence[np.ndarray], order: str, param: np.ndarray,
+             lr: float, in_dtype: str = "f32", out_dtype: str = None,
+             momentum_buf: np.ndarray = None, momentum: float = 0.0) -> np.ndarray:
+    """The synchronisation followed by one SGD step on the flat parameters
+    (updated in place); returns the averaged gradient."""
+    out_dtype = out_dtype or in_dtype
+    avg = sync_avg(plan, rank_flats, order, in_dtype, out_dtype)
+    sgd_step(param, avg, lr, out_dtype, momentum_buf, momentum)
+    return avg
 
 
 # ---------------------------------------------------------------------------

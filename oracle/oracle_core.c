@@ -26,6 +26,12 @@
  *   output      float32 y, or bf16 = y rounded to nearest, ties to even.
  *   N == 1      output = input, bit for bit ([TR24] section 九 returns early
  *               when world_size <= 1).
+ *   SGD step    (the optimizer update the average can be folded into, [TR24]
+ *               section 九 note; update rule theta <- theta - eta * g of [DDP]
+ *               section 5.3):  with momentum buffer m (optional):
+ *                   v = fl(fl(mu * m) + g);  m = v;  g = v
+ *               then  p = fl(p - fl(lr * g)),  where g is the averaged
+ *               gradient exactly as stored (bf16 widened back to f32).
  *
  * Built with -O2 -ffp-contract=off and no fast-math flag: every addition and
  * multiplication is one IEEE-754 binary32 operation (SSE on x86-64), denormals
@@ -150,6 +156,25 @@ int oracle_sampled_avg(const void *vals, const int64_t *pos, const int64_t *len,
         for (int r = 0; r < N; ++r) v[r] = load_elem(vals, in_dtype, s * N + r);
         float acc = fold(v, N, order, pos[s], len[s]);
         store_elem(out, out_dtype, s, acc * inv);
+    }
+    return 0;
+}
+
+/* One SGD step over n elements: p[i] -= lr * g[i] (g of dtype g_dtype),
+ * through the momentum buffer m when m != NULL. */
+int oracle_sgd_step(float *p, float *m, const void *g, int g_dtype, int64_t n, float lr, float mu)
+{
+    if ((g_dtype != ORACLE_F32 && g_dtype != ORACLE_BF16) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = load_elem(g, g_dtype, i);
+        if (m) {
+            float v = mu * m[i];
+            v = v + gi;
+            m[i] = v;
+            gi = v;
+        }
+        float step = lr * gi;
+        p[i] = p[i] - step;
     }
     return 0;
 }

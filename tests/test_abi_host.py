@@ -155,3 +155,21 @@ def test_flatten_argument_errors():
     assert L.ddp_flatten(None, None, -1, ctypes.c_void_p(0x1000), 0, None) == 1
     assert L.ddp_flatten(p.handle, None, -1, ctypes.c_void_p(0x1000), 0, None) == 1
     assert L.ddp_bind_params(p.handle, None, None, None) == 1
+
+
+def test_fused_sgd_argument_errors_are_host_side():
+    L = ddp.lib
+    P = lambda *a: (ctypes.c_void_p * len(a))(*[ctypes.c_void_p(x) for x in a])   # noqa: E731
+    p = ddp.plan_buckets([100, 28], 1 << 20)            # 128 f32 elements = 512 B
+    two = P(0x200000, 0x300000)
+    ok_param = ctypes.c_void_p(0x400000)
+    f = L.ddp_sync_sgd_update
+    assert f(None, two, 2, 0, 0, None, ok_param, None, 0.1, 0.0, None) == 1
+    assert f(p.handle, two, 2, 0, 0, None, None, None, 0.1, 0.0, None) == 1          # no params
+    assert f(p.handle, two, 2, 0, 0, None, ctypes.c_void_p(0x400002), None, 0.1, 0.0, None) == 1
+    assert f(p.handle, two, 2, 0, 0, None, ctypes.c_void_p(0x200100), None, 0.1, 0.0, None) == 4
+    assert f(p.handle, two, 2, 0, 0, None, ok_param, ctypes.c_void_p(0x400100), 0.1, 0.0, None) == 4
+    assert f(p.handle, two, 2, 0, 0, ctypes.c_void_p(0x400080), ok_param, None, 0.1, 0.0, None) == 4
+    assert f(p.handle, two, 2, 0, 0, None, ok_param, ctypes.c_void_p(0x300000), 0.1, 0.0, None) == 4
+    assert f(p.handle, P(0x200000), 1, 0, 1, None, ok_param, None, 0.1, 0.0, None) == 2   # N=1 f32->bf16
+    assert f(p.handle, two, 65, 0, 0, None, ok_param, None, 0.1, 0.0, None) == 2

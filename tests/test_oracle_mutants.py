@@ -151,7 +151,16 @@ def pin_p7_plans(o):
     return ok
 
 
-BATTERY = [pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
+def pin_sgd(o):
+    p = np.array([1.0, -2.0, 0.5], np.float32)
+    m = np.zeros(3, np.float32)
+    o.sgd_step(p, np.array([0.5, 0.25, -1.0], np.float32), 0.5, momentum_buf=m, momentum=0.5)
+    o.sgd_step(p, np.array([1.0, 1.0, 1.0], np.float32), 0.5, momentum_buf=m, momentum=0.5)
+    # v1 = g1; p1 = p0 - v1/2; v2 = v1/2 + g2; p2 = p1 - v2/2
+    return p.tolist() == [0.125, -2.6875, 0.75] and m.tolist() == [1.25, 1.125, 0.5]
+
+
+BATTERY = [pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
            pin_p9_scale, pin_p10_single, pin_bf16_path, pin_p7_plans]
 
 
@@ -184,6 +193,9 @@ C_MUTANTS = {
     "bad_bf16_widen": ("return bits_to_f32((uint32_t)h << 16);", "return bits_to_f32((uint32_t)h << 15);"),
     "single_rank_folds": ("    if (N == 1) {\n        if (in_dtype != out_dtype) return -1;\n        memcpy",
                           "    if (N == -1) {\n        if (in_dtype != out_dtype) return -1;\n        memcpy"),
+    "sgd_sign_flipped": ("p[i] = p[i] - step;", "p[i] = p[i] + step;"),
+    "sgd_momentum_terms_swapped": ("float v = mu * m[i];\n            v = v + gi;",
+                                   "float v = mu * gi;\n            v = v + m[i];"),
 }
 
 PY_MUTANTS = {
