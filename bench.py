@@ -66,6 +66,7 @@ def main():
     ap.add_argument("--no-copy-path", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-fused-sgd", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -265,11 +266,11 @@ def main():
         res = [torch.empty(n, dtype=tout, device=dev) for n in wl.numel]
         rbind = ddp.bind_params(plan, res)
 
-        def full_step():
+        def full_step(st=stream):
             for r in range(N):
-                ddp.flatten(plan, binds[r], flats[r], stream=stream)
-            sync()
-            ddp.unflatten(plan, rbind, out, stream=stream)
+                ddp.flatten(plan, binds[r], flats[r], stream=st)
+            ddp.sync_allreduce_avg(plan, flats, out, order, stream=st)
+            ddp.unflatten(plan, rbind, out, stream=st)
 
         for _ in range(5):
             full_step()
@@ -299,8 +300,30 @@ def main():
             "unflatten_ms": round(tu, 4), "unflatten_GBps": round(ub / (tu * 1e-3) / 1e9, 1),
             "metric_GBps": round(sync_bytes / ((tf + ts + tu) * 1e-3) / 1e9, 1),
             "launches": N + 2}
+        # the same step captured once into a HIP graph and replayed
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(stream)
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(graph, stream=cap_stream):
+                full_step(cap_stream)
+        torch.cuda.synchronize()
+        loop = {}
+        for name, fn in (("eager", full_step), ("graph", graph.replay)):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            loop[name] = a.elapsed_time(b) / reps
+        copy_path["eager_loop_ms_per_step"] = round(loop["eager"], 4)
+        copy_path["graph_replay_ms_per_step"] = round(loop["graph"], 4)
         log(f"copy path: {copy_path}")
-        del grads, binds, res, rbind
+        del grads, binds, res, rbind, graph
 
     # ---------------------------------------------------------------- fused optimizer step
     # The average folded into a momentum-SGD step (ddp_sync_sgd_update) against
@@ -341,6 +364,51 @@ def main():
         log(f"fused sgd: {fused}")
         del params, mbuf
 
+    # ---------------------------------------------------------------- two-bucket overlap
+    # The two-bucket plan of the same tensors: DEEP_COMM averaged on an update
+    # stream while a GEMM (standing in for the first layer's backward) runs on
+    # a compute stream; exposed = overlapped time - compute time.
+    overlap = None
+    if not args.no_overlap and wl.name == "resnet50":
+        tb = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
+        (dl, db, _, _), (fl_, fb_, _, _) = tb.bucket(0), tb.bucket(1)
+        mat_a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+        mat_b = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+        comp, upd = torch.cuda.Stream(), torch.cuda.Stream()
+        deep_in = [f[db:db + dl] for f in flats]
+        deep_out = out[db:db + dl]
+
+        def compute():
+            with torch.cuda.stream(comp):
+                torch.mm(mat_a, mat_b)
+
+        def deep():
+            ddp.bucket_allreduce_avg(deep_in, deep_out, order, stream=upd)
+
+        def timed(fns, reps=20):
+            for _ in range(3):
+                for f in fns:
+                    f()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                for f in fns:
+                    f()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / reps
+
+        t_comp = timed([compute])
+        t_deep = timed([deep])
+        t_both = timed([compute, deep])
+        overlap = {"plan": "two-bucket (DEEP_COMM %d, FIRST_COMM %d elements)" % (dl, fl_),
+                   "compute_ms": round(t_comp, 4), "deep_sync_ms": round(t_deep, 4),
+                   "overlapped_ms": round(t_both, 4),
+                   "exposed_sync_ms": round(max(t_both - t_comp, 0.0), 4),
+                   "hidden_fraction": round(1.0 - max(t_both - t_comp, 0.0) / t_deep, 3),
+                   "compute": "bf16 GEMM 4096^3 on a second stream"}
+        log(f"overlap: {overlap}")
+        del mat_a, mat_b, tb
+
     traffic = measured_traffic(wl.name, order, sync_bytes)
     line = {
         "metric": METRIC,
@@ -378,6 +446,7 @@ def main():
         "other_orders": other,
         "copy_path": copy_path,
         "fused_sgd": fused,
+        "overlap": overlap,
     }
     print(json.dumps(line), flush=True)
 
