@@ -67,6 +67,7 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-fused-sgd", action="store_true")
     ap.add_argument("--no-overlap", action="store_true")
+    ap.add_argument("--no-no-sync", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -409,6 +410,42 @@ def main():
         log(f"overlap: {overlap}")
         del mat_a, mat_b, tb
 
+    # ---------------------------------------------------------------- no_sync accumulation
+    # M micro-steps: with no_sync each rank accumulates locally (M - 1
+    # accumulates) and synchronises once; without it every micro-step also
+    # synchronises.  Separate buffers keep the benchmark's inputs untouched.
+    no_sync = None
+    if not args.no_no_sync and 2 * N * P * wl.in_bytes <= (16 << 30):
+        M = 4
+        local = [f.clone() for f in flats]
+        micro = [f.clone() for f in flats]
+
+        def acc():
+            ddp.accumulate(local, micro, stream=stream)
+
+        def sync_local():
+            ddp.sync_allreduce_avg(plan, local, out, order, stream=stream)
+
+        res = {}
+        for name, fn in (("acc", acc), ("sync", sync_local)):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            res[name] = a.elapsed_time(b) / args.steps
+        acc_bytes = 3 * N * P * wl.in_bytes
+        no_sync = {"micro_steps": M, "accumulate_ms": round(res["acc"], 5),
+                   "accumulate_GBps": round(acc_bytes / (res["acc"] * 1e-3) / 1e9, 1),
+                   "no_sync_ms": round((M - 1) * res["acc"] + res["sync"], 5),
+                   "sync_every_step_ms": round((M - 1) * res["acc"] + M * res["sync"], 5),
+                   "syncs_saved": M - 1}
+        log(f"no_sync: {no_sync}")
+        del local, micro
+
     traffic = measured_traffic(wl.name, order, sync_bytes)
     line = {
         "metric": METRIC,
@@ -447,6 +484,7 @@ def main():
         "copy_path": copy_path,
         "fused_sgd": fused,
         "overlap": overlap,
+        "no_sync": no_sync,
     }
     print(json.dumps(line), flush=True)
 

@@ -8,7 +8,7 @@ been built; there is no fallback implementation.
 
 Names follow the C ABI: ``plan_buckets``, ``plan_two_bucket``,
 ``bind_params``, ``flatten``, ``bucket_allreduce_avg``,
-``sync_allreduce_avg``, ``sync_sgd_update``, ``unflatten``.
+``sync_allreduce_avg``, ``sync_sgd_update``, ``accumulate``, ``unflatten``.
 """
 from __future__ import annotations
 
@@ -88,6 +88,8 @@ def _load():
                                     ctypes.c_int, vp, vp], ctypes.c_int),
         "ddp_sync_sgd_update": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+        "ddp_accumulate": ([ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_int, vp], ctypes.c_int),
         "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "ddp_abi_version": ([], ctypes.c_int32),
         "ddp_last_error": ([], ctypes.c_char_p),
@@ -326,6 +328,20 @@ def sync_sgd_update(plan: Plan, rank_flats: Sequence, params, lr: float, order="
                                    None if momentum_buf is None else _dev_ptr(momentum_buf),
                                    float(lr), float(momentum), _stream_handle(stream)),
            "ddp_sync_sgd_update")
+
+
+def accumulate(dst: Sequence, src: Sequence, length: Optional[int] = None, stream=None):
+    """dst[k] += src[k] for every pair, one launch (``ddp_accumulate``)."""
+    if len(dst) != len(src) or not dst:
+        raise ValueError("one source per destination is required")
+    dt = _dtype_code(dst[0])
+    n = dst[0].numel() if length is None else int(length)
+    for t in list(dst) + list(src):
+        if _dtype_code(t) != dt or t.numel() < n:
+            raise ValueError("buffers differ in dtype or are too short")
+    _check(lib.ddp_accumulate(_ptr_array([_dev_ptr(t) for t in dst]),
+                              _ptr_array([_dev_ptr(t) for t in src]), len(dst), n, dt,
+                              _stream_handle(stream)), "ddp_accumulate")
 
 
 def status_string(status: int) -> str:

@@ -243,6 +243,20 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
                                  float *param_flat, float *momentum_flat, float lr,
                                  float momentum, void *stream);
 
+/* Local gradient accumulation between synchronisations: the no_sync
+ * micro-steps of [DDP] 5.2, where backward adds each micro-batch's gradient
+ * into .grad and only the last micro-step synchronises.  For every pair k,
+ * in one launch:  dst[k][i] = fl(dst[k][i] + src[k][i])  (bf16: both widened,
+ * one f32 add, one round to nearest even).
+ *   dst[n_bufs], src[n_bufs]  host arrays of device pointers to len elements
+ *                             of dtype; n_bufs 1..DDP_MAX_RANKS (one pair
+ *                             per virtual rank)
+ * dst[k] may be exactly src[k]; any other overlap between the buffers is
+ * rejected (DDP_ERR_ALIAS).  len == 0 does nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, ALIAS, HIP. */
+ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
+                            ddp_dtype_t dtype, void *stream);
+
 /* ------------------------------------------------------------------ misc */
 const char *ddp_status_string(ddp_status_t status);
 /* Text of the last HIP failure seen by this thread ("" if none): the HIP call

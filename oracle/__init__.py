@@ -90,6 +90,8 @@ def load_core(path: str):
     lib.oracle_sgd_step.restype = ctypes.c_int
     lib.oracle_sgd_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_int64, ctypes.c_float, ctypes.c_float]
+    lib.oracle_accumulate.restype = ctypes.c_int
+    lib.oracle_accumulate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]
     return lib
 
 
@@ -269,6 +271,29 @@ def sync_sgd(plan: Plan, rank_flats: Sequence[np.ndarray], order: str, param: np
     avg = sync_avg(plan, rank_flats, order, in_dtype, out_dtype)
     sgd_step(param, avg, lr, out_dtype, momentum_buf, momentum)
     return avg
+
+
+def accumulate(dst: np.ndarray, src: np.ndarray, dtype: str = "f32"):
+    """dst += src in place: the local gradient accumulation of no_sync
+    micro-steps ([DDP] section 5.2)."""
+    assert dst.dtype == _NP_DTYPE[dtype] and dst.flags.c_contiguous
+    s = np.ascontiguousarray(src, dtype=_NP_DTYPE[dtype])
+    if s.size != dst.size:
+        raise ValueError("sizes differ")
+    if _core().oracle_accumulate(dst.ctypes.data, s.ctypes.data, _DTYPE_CODE[dtype], dst.size):
+        raise ValueError("oracle rejected the arguments")
+
+
+def no_sync_then_sync(plan: Plan, micro: Sequence[Sequence[np.ndarray]], order: str,
+                      dtype: str = "f32") -> np.ndarray:
+    """micro[m][r]: rank r's flat gradient of micro-step m.  Gradients are
+    accumulated per rank in micro-step order (no synchronisation), then the
+    accumulated buffers are synchronised once."""
+    local = [np.array(micro[0][r], copy=True) for r in range(len(micro[0]))]
+    for m in range(1, len(micro)):
+        for r in range(len(local)):
+            accumulate(local[r], micro[m][r], dtype)
+    return sync_avg(plan, local, order, dtype, dtype)
 
 
 # ---------------------------------------------------------------------------

@@ -32,6 +32,10 @@
  *                   v = fl(fl(mu * m) + g);  m = v;  g = v
  *               then  p = fl(p - fl(lr * g)),  where g is the averaged
  *               gradient exactly as stored (bf16 widened back to f32).
+ *   accumulate  local gradient accumulation between synchronisations ([DDP]
+ *               section 5.2, no_sync: backward adds into .grad):
+ *               dst = fl(dst + src), f32; for bf16 both widened, one f32 add,
+ *               one round to nearest even.
  *
  * Built with -O2 -ffp-contract=off and no fast-math flag: every addition and
  * multiplication is one IEEE-754 binary32 operation (SSE on x86-64), denormals
@@ -175,6 +179,19 @@ int oracle_sgd_step(float *p, float *m, const void *g, int g_dtype, int64_t n, f
         }
         float step = lr * gi;
         p[i] = p[i] - step;
+    }
+    return 0;
+}
+
+/* dst[i] = dst[i] + src[i] over n elements of dtype (bf16: widened, added in
+ * f32, rounded to nearest even). */
+int oracle_accumulate(void *dst, const void *src, int dtype, int64_t n)
+{
+    if ((dtype != ORACLE_F32 && dtype != ORACLE_BF16) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = load_elem(dst, dtype, i);
+        float b = load_elem(src, dtype, i);
+        store_elem(dst, dtype, i, a + b);
     }
     return 0;
 }

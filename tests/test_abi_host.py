@@ -173,3 +173,18 @@ def test_fused_sgd_argument_errors_are_host_side():
     assert f(p.handle, two, 2, 0, 0, None, ok_param, ctypes.c_void_p(0x300000), 0.1, 0.0, None) == 4
     assert f(p.handle, P(0x200000), 1, 0, 1, None, ok_param, None, 0.1, 0.0, None) == 2   # N=1 f32->bf16
     assert f(p.handle, two, 65, 0, 0, None, ok_param, None, 0.1, 0.0, None) == 2
+
+
+def test_accumulate_argument_errors_are_host_side():
+    L = ddp.lib
+    P = lambda *a: (ctypes.c_void_p * len(a))(*[ctypes.c_void_p(x) for x in a])   # noqa: E731
+    f = L.ddp_accumulate
+    assert f(P(0x1000), P(0x2000), 0, 16, 0, None) == 1
+    assert f(P(0x1000), P(0x2000), 1, -1, 0, None) == 1
+    assert f(P(0x1000), P(0x2000), 1, 16, 7, None) == 1
+    assert f(P(0x1000), P(0x2000), 65, 16, 0, None) == 2
+    assert f(None, None, 1, 0, 0, None) == 0                       # empty: nothing to do
+    assert f(P(0x1000), P(0x1010), 1, 16, 0, None) == 4           # partial overlap
+    assert f(P(0x1000, 0x1020), P(0x8000, 0x9000), 2, 16, 0, None) == 4   # dst overlap
+    assert f(P(0x1000, 0x2000), P(0x2000, 0x9000), 2, 16, 0, None) == 4   # dst[0] is src[1]
+    assert f(P(0x1002), P(0x2000), 1, 16, 0, None) == 1           # f32 misaligned to 2 B

@@ -160,7 +160,13 @@ def pin_sgd(o):
     return p.tolist() == [0.125, -2.6875, 0.75] and m.tolist() == [1.25, 1.125, 0.5]
 
 
-BATTERY = [pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
+def pin_accumulate(o):
+    d = np.array([1.0, 2.5, -3.0], np.float32)
+    o.accumulate(d, np.array([0.5, 0.5, 1.0], np.float32))
+    return d.tolist() == [1.5, 3.0, -2.0]
+
+
+BATTERY = [pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
            pin_p9_scale, pin_p10_single, pin_bf16_path, pin_p7_plans]
 
 
@@ -193,6 +199,7 @@ C_MUTANTS = {
     "bad_bf16_widen": ("return bits_to_f32((uint32_t)h << 16);", "return bits_to_f32((uint32_t)h << 15);"),
     "single_rank_folds": ("    if (N == 1) {\n        if (in_dtype != out_dtype) return -1;\n        memcpy",
                           "    if (N == -1) {\n        if (in_dtype != out_dtype) return -1;\n        memcpy"),
+    "accumulate_subtracts": ("store_elem(dst, dtype, i, a + b);", "store_elem(dst, dtype, i, a - b);"),
     "sgd_sign_flipped": ("p[i] = p[i] - step;", "p[i] = p[i] + step;"),
     "sgd_momentum_terms_swapped": ("float v = mu * m[i];\n            v = v + gi;",
                                    "float v = mu * gi;\n            v = v + m[i];"),
