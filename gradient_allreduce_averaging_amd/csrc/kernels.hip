@@ -46,7 +46,10 @@ constexpr int kThreads = 64;
 constexpr int kUnroll = 1;             // 16-byte vectors per lane per rank
 constexpr int kTileTableShift = 6;     // one bucket-table entry per 64 tiles
 constexpr int kCopyThreads = 256;      // flatten / unflatten blocks
-constexpr int64_t kCopyUnitElems = 16384;
+constexpr int64_t kCopyUnitElems = 16384;   // elements per copy-table entry
+constexpr int64_t kCopyBlockElems = 2048;   // elements per copy block: a unit gets
+constexpr int kCopyBlocksPerUnit = (int)(kCopyUnitElems / kCopyBlockElems);   // this many blocks
+static_assert(kCopyUnitElems % kCopyBlockElems == 0, "a copy unit splits into whole blocks");
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
@@ -564,15 +567,13 @@ __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
         const u32x4 *sv = reinterpret_cast<const u32x4 *>(src + head);
         u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
         int64_t j = tid;
-        for (; j + 3 * kCopyThreads < nvec; j += 4 * kCopyThreads) {
-            const u32x4 a = sv[j], b = sv[j + kCopyThreads], c = sv[j + 2 * kCopyThreads],
-                        e = sv[j + 3 * kCopyThreads];
-            dv[j] = a;
-            dv[j + kCopyThreads] = b;
-            dv[j + 2 * kCopyThreads] = c;
-            dv[j + 3 * kCopyThreads] = e;
+        for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {   // both loads before the stores
+            const u32x4 a = __builtin_nontemporal_load(sv + j);
+            const u32x4 b = __builtin_nontemporal_load(sv + j + kCopyThreads);
+            __builtin_nontemporal_store(a, dv + j);
+            __builtin_nontemporal_store(b, dv + j + kCopyThreads);
         }
-        for (; j < nvec; j += kCopyThreads) dv[j] = sv[j];
+        for (; j < nvec; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sv + j), dv + j);
         copy16b(dst, src, head + (nvec << 4), nbytes);
     } else if (((d ^ s) & 3) == 0) {
         const int64_t head = min<int64_t>((4 - (d & 3)) & 3, nbytes);
@@ -582,29 +583,37 @@ __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
         uint32_t *dw = reinterpret_cast<uint32_t *>(dst + head);
         int64_t j = tid;
         for (; j + 3 * kCopyThreads < nw; j += 4 * kCopyThreads) {
-            const uint32_t a = sw[j], b = sw[j + kCopyThreads], c = sw[j + 2 * kCopyThreads],
-                           e = sw[j + 3 * kCopyThreads];
-            dw[j] = a;
-            dw[j + kCopyThreads] = b;
-            dw[j + 2 * kCopyThreads] = c;
-            dw[j + 3 * kCopyThreads] = e;
+            const uint32_t a = __builtin_nontemporal_load(sw + j);
+            const uint32_t b = __builtin_nontemporal_load(sw + j + kCopyThreads);
+            const uint32_t c = __builtin_nontemporal_load(sw + j + 2 * kCopyThreads);
+            const uint32_t e = __builtin_nontemporal_load(sw + j + 3 * kCopyThreads);
+            __builtin_nontemporal_store(a, dw + j);
+            __builtin_nontemporal_store(b, dw + j + kCopyThreads);
+            __builtin_nontemporal_store(c, dw + j + 2 * kCopyThreads);
+            __builtin_nontemporal_store(e, dw + j + 3 * kCopyThreads);
         }
-        for (; j < nw; j += kCopyThreads) dw[j] = sw[j];
+        for (; j < nw; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sw + j), dw + j);
         copy16b(dst, src, head + (nw << 2), nbytes);
     } else {
         copy16b(dst, src, 0, nbytes);
     }
 }
 
-// One copy unit per block; to_flat selects flatten (param -> flat) or
-// unflatten (flat -> param).
+// kCopyBlocksPerUnit blocks per copy unit, each moving up to kCopyBlockElems
+// elements of it (parts past a short unit's end return at once); to_flat
+// selects flatten (param -> flat) or unflatten (flat -> param).  Short,
+// many blocks stream fastest here, as for the reduce; the table keeps one
+// entry per 16K elements.
 __global__ void __launch_bounds__(kCopyThreads)
 copy_units(const ddp_copy_unit *units, int64_t first, char *flat, int esize, int to_flat)
 {
-    const ddp_copy_unit u = units[first + blockIdx.x];
-    char *pp = reinterpret_cast<char *>(u.param_addr) + u.param_elem * esize;
-    char *fp = flat + u.flat_elem * esize;
-    const int64_t nbytes = u.count * esize;
+    const ddp_copy_unit u = units[first + blockIdx.x / kCopyBlocksPerUnit];
+    const int64_t lo = (int64_t)(blockIdx.x % kCopyBlocksPerUnit) * kCopyBlockElems;
+    if (lo >= u.count) return;
+    const int64_t n = min(u.count - lo, kCopyBlockElems);
+    char *pp = reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize;
+    char *fp = flat + (u.flat_elem + lo) * esize;
+    const int64_t nbytes = n * esize;
     if (to_flat)
         block_copy(fp, pp, nbytes);
     else
@@ -1123,8 +1132,8 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
-    if (last - first > INT_MAX) return DDP_ERR_OVERFLOW;
-    copy_units<<<dim3((unsigned)(last - first)), dim3(kCopyThreads), 0,
+    if ((last - first) * kCopyBlocksPerUnit > INT_MAX) return DDP_ERR_OVERFLOW;
+    copy_units<<<dim3((unsigned)((last - first) * kCopyBlocksPerUnit)), dim3(kCopyThreads), 0,
                  static_cast<hipStream_t>(stream)>>>(
         bd->units, first, static_cast<char *>(flat), dtype_size(dtype), to_flat);
     return launched("copy kernel launch");

@@ -144,3 +144,34 @@ def test_repeat_is_bitwise_stable(env):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     del flats, a, b
     torch.cuda.empty_cache()
+
+
+def test_single_bucket_beyond_2_pow_31_elements(env):
+    """One bucket of 2^31 + 3 f32 elements (8 GiB per rank) through the
+    per-bucket entry point: 64-bit element indexing, the ring chunk edge at
+    C = 2^30 + 2 and the ragged tail, on sampled elements."""
+    torch, ddp = env
+    L = (1 << 31) + 3
+    N = 2
+    xs = []
+    for r in range(N):
+        t = torch.empty(L, dtype=torch.float32, device="cuda:0")
+        W.device_normal_(t, r, 77, 1e-3)
+        xs.append(t)
+    out = torch.empty(L, dtype=torch.float32, device="cuda:0")
+    C = -(-L // N)
+    rng = np.random.default_rng(31)
+    pos = sorted({*(int(p) for p in rng.integers(0, L, 5000)),
+                  *[C + d for d in range(-9, 9)], *[(1 << 31) + d for d in range(-9, 3)],
+                  *range(L - 12, L), *range(0, 8)})
+    pos = np.array(pos, dtype=np.int64)
+    idx = torch.from_numpy(pos).to("cuda:0")
+    vals = np.stack([to_host(x.index_select(0, idx), torch) for x in xs], axis=1)
+    for order in ("seq", "ring"):
+        ddp.bucket_allreduce_avg(xs, out, order)
+        torch.cuda.synchronize()
+        got = to_host(out.index_select(0, idx), torch)
+        want = oracle.sampled_avg(vals, pos, np.full(pos.size, L, np.int64), order)
+        assert_bits_equal(got, want, f"2^31+3 {order}")
+    del xs, out
+    torch.cuda.empty_cache()
