@@ -120,8 +120,10 @@ def main():
     stream = torch.cuda.current_stream()
     sync_bytes = wl.sync_bytes()
 
+    prepared = {o: ddp.make_sync(plan, flats, out, o, stream=stream) for o in ("seq", "ring")}
+
     def sync(o=order):
-        ddp.sync_allreduce_avg(plan, flats, out, o, stream=stream)
+        prepared[o]()
 
     # ---------------------------------------------------------------- timed
     # K back-to-back steps, wall clock between two synchronisations; one event

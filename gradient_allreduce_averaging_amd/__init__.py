@@ -8,7 +8,8 @@ been built; there is no fallback implementation.
 
 Names follow the C ABI: ``plan_buckets``, ``plan_two_bucket``,
 ``bind_params``, ``flatten``, ``bucket_allreduce_avg``,
-``sync_allreduce_avg``, ``sync_sgd_update``, ``accumulate``, ``unflatten``.
+``sync_allreduce_avg``, ``sync_sgd_update``, ``accumulate``, ``unflatten``;
+``make_sync`` resolves a synchronisation once for repeated calls.
 """
 from __future__ import annotations
 
@@ -300,6 +301,39 @@ def sync_allreduce_avg(plan: Plan, rank_flats: Sequence, out_flat, order="ring",
     _check(lib.ddp_sync_allreduce_avg(plan.handle, ptrs, len(rank_flats), _ORDERS[order],
                                       _dtype_code(out_flat), _dev_ptr(out_flat),
                                       _stream_handle(stream)), "ddp_sync_allreduce_avg")
+
+
+class _PreparedSync:
+    """A synchronisation with every argument marshalled once; calling it
+    issues the one C call (see make_sync)."""
+
+    def __init__(self, plan: Plan, rank_flats: Sequence, out_flat, order, stream):
+        total = plan.total
+        for t in rank_flats:
+            if _dtype_code(t) != plan.dtype or t.numel() < total:
+                raise ValueError("rank flat buffers differ from the plan's dtype or size")
+        if out_flat.numel() < total:
+            raise ValueError("output too short")
+        self._keep = (plan, list(rank_flats), out_flat)   # keeps the memory alive
+        self._fn = lib.ddp_sync_allreduce_avg
+        self._args = (plan.handle, _ptr_array([_dev_ptr(t) for t in rank_flats]),
+                      len(rank_flats), _ORDERS[order], _dtype_code(out_flat),
+                      ctypes.c_void_p(_dev_ptr(out_flat)), ctypes.c_void_p(_stream_handle(stream)))
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            _check(status, "ddp_sync_allreduce_avg")
+
+
+def make_sync(plan: Plan, rank_flats: Sequence, out_flat, order="ring", stream=None):
+    """Resolve a synchronisation once -- buffers, order, stream -- and return a
+    zero-argument callable that enqueues it (a static graph fixes all of
+    these for every step).  The callable keeps its tensors alive; it launches
+    on the stream that was current (or given) when it was made."""
+    if _ORDERS[order] == RING:
+        plan.prepare()
+    return _PreparedSync(plan, rank_flats, out_flat, order, stream)
 
 
 def sync_sgd_update(plan: Plan, rank_flats: Sequence, params, lr: float, order="ring",

@@ -167,3 +167,21 @@ def test_same_result_on_repeat_and_on_a_side_stream(env):
         ddp.bucket_allreduce_avg(ts, out, "ring")
     s.synchronize()
     assert_bits_equal(to_host(out, torch), first, "side stream")
+
+
+def test_prepared_sync_matches_direct_call(env):
+    torch, ddp = env
+    import workloads as W
+    wl = W.workload("tiny")
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes)
+    xs = [W.host_rank_flat(wl, r) for r in range(wl.n_ranks)]
+    ts = [to_dev(x, torch) for x in xs]
+    a = torch.empty(lp.total, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for order in ORDERS:
+        call = ddp.make_sync(lp, ts, a, order)
+        call()
+        call()
+        ddp.sync_allreduce_avg(lp, ts, b, order)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_host(a, torch), to_host(b, torch), f"prepared {order}")
