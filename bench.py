@@ -412,6 +412,25 @@ def main():
         log(f"overlap: {overlap}")
         del mat_a, mat_b, tb
 
+    # ---------------------------------------------------------------- in place
+    # The all-reduce as the pages run it, in place (send buffer == receive
+    # buffer): the average overwrites rank 0's bucket buffer.  Runs after the
+    # parity leg because it rewrites rank 0's gradients.
+    in_place = {}
+    for o in ("ring", "seq"):
+        call = ddp.make_sync(plan, flats, flats[0], o, stream=stream)
+        for _ in range(3):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        in_place[o] = {"ms_per_sync": round(ms, 5), "GBps": round(sync_bytes / (ms * 1e-3) / 1e9, 1)}
+    log(f"in place: {in_place}")
+
     # ---------------------------------------------------------------- no_sync accumulation
     # M micro-steps: with no_sync each rank accumulates locally (M - 1
     # accumulates) and synchronises once; without it every micro-step also
@@ -485,6 +504,7 @@ def main():
         "other_orders": other,
         "copy_path": copy_path,
         "fused_sgd": fused,
+        "in_place": in_place,
         "overlap": overlap,
         "no_sync": no_sync,
     }
