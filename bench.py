@@ -68,6 +68,7 @@ def main():
     ap.add_argument("--no-fused-sgd", action="store_true")
     ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--no-no-sync", action="store_true")
+    ap.add_argument("--no-in-place", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -417,7 +418,7 @@ def main():
     # buffer): the average overwrites rank 0's bucket buffer.  Runs after the
     # parity leg because it rewrites rank 0's gradients.
     in_place = {}
-    for o in ("ring", "seq"):
+    for o in (() if args.no_in_place else ("ring", "seq")):
         call = ddp.make_sync(plan, flats, flats[0], o, stream=stream)
         for _ in range(3):
             call()
@@ -504,7 +505,7 @@ def main():
         "other_orders": other,
         "copy_path": copy_path,
         "fused_sgd": fused,
-        "in_place": in_place,
+        "in_place": in_place or None,
         "overlap": overlap,
         "no_sync": no_sync,
     }
