@@ -69,6 +69,7 @@ def main():
     ap.add_argument("--no-overlap", action="store_true")
     ap.add_argument("--no-no-sync", action="store_true")
     ap.add_argument("--no-in-place", action="store_true")
+    ap.add_argument("--no-rank-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -413,6 +414,37 @@ def main():
         log(f"overlap: {overlap}")
         del mat_a, mat_b, tb
 
+    # ---------------------------------------------------------------- rank sweep
+    # The same plan averaged over N = 2..32 virtual ranks (N > 8 takes the
+    # looped kernel): bandwidth against the number of concurrent streams.
+    rank_sweep = None
+    if not args.no_rank_sweep and wl.name == "resnet50":
+        extra = []
+        for r in range(N, 32):
+            t = torch.empty(P, dtype=tin, device=dev)
+            W.device_normal_(t, r, wl.stream, wl.sigma)
+            extra.append(t)
+        pool = flats + extra
+        sweep_out = torch.empty(P, dtype=tout, device=dev)
+        rank_sweep = {}
+        for n in (2, 4, 6, 8, 9, 12, 16, 32):
+            row = {}
+            for o in ("ring", "seq"):
+                call = ddp.make_sync(plan, pool[:n], sweep_out, o, stream=stream)
+                for _ in range(3):
+                    call()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(50):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / 50
+                row[o] = round((n * wl.in_bytes + wl.out_bytes) * P / (ms * 1e-3) / 1e9, 1)
+            rank_sweep[str(n)] = row
+        log(f"rank sweep (GB/s): {rank_sweep}")
+        del extra, pool, sweep_out
+
     # ---------------------------------------------------------------- in place
     # The all-reduce as the pages run it, in place (send buffer == receive
     # buffer): the average overwrites rank 0's bucket buffer.  Runs after the
@@ -506,6 +538,7 @@ def main():
         "copy_path": copy_path,
         "fused_sgd": fused,
         "in_place": in_place or None,
+        "rank_sweep_GBps": rank_sweep,
         "overlap": overlap,
         "no_sync": no_sync,
     }
