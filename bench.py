@@ -55,6 +55,33 @@ def measured_traffic(workload, order, algorithmic_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def run_environment(torch):
+    """ROCm release, HIP runtime and the device's peak clocks, for the record."""
+    env = {"hip_runtime": torch.version.hip, "torch": torch.__version__,
+           "launch": "direct launches (no graph) in the timed loop"}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has already loaded
+        # hipDeviceAttributeClockRate = 5 and ...MemoryClockRate = 60 (both kHz),
+        # ...MemoryBusWidth = 59 (bits), as numbered in ROCm 7's hip_runtime_api.h
+        for key, attr, div in (("sclk_peak_mhz", 5, 1000), ("mclk_peak_mhz", 60, 1000),
+                               ("mem_bus_bits", 59, 1)):
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+                env[key] = v.value // div
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    env["arch"] = getattr(props, "gcnArchName", "")
+    env["compute_units"] = props.multi_processor_count
+    return env
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +183,7 @@ def main():
     torch.cuda.synchronize()
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     kern_ms = float(np.mean(launch_ms))
+    kern_ms_median = float(np.median(launch_ms))
     achieved = sync_bytes / (kern_ms * 1e-3) / 1e9
     log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
         f"stream, kernel {kern_ms * 1e3:.1f} us avg (min {min(launch_ms) * 1e3:.1f}), "
@@ -259,6 +287,47 @@ def main():
                "sample": f"the full {wl.name} synchronisation ({order} order, N={N}, P={P}), "
                          f"{reps} repetition(s), {t_cpu:.1f} s single-threaded C oracle"}
         log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps")
+
+        # The oracle on all of this process's host cores: SEQ order, every
+        # bucket split into disjoint element ranges, one ctypes call per range
+        # (the call releases the GIL).  SEQ has no index dependence, so the
+        # split leaves every bit as it is; its result is checked against the
+        # GPU's SEQ output of the same buffers.
+        threads = min(16, len(os.sched_getaffinity(0)))
+        pieces = []
+        for base, ln in zip(oplan.bucket_base, oplan.bucket_len):
+            step = max(1, -(-ln // threads))
+            pieces += [(base + a, min(step, ln - a)) for a in range(0, ln, step)]
+        seq_want = np.empty(P, dtype=np.float32 if tout == torch.float32 else np.uint16)
+
+        def piece(pc):
+            a, n = pc
+            seq_want[a:a + n] = oracle.bucket_avg([h[a:a + n] for h in host], "seq",
+                                                  wl.dtype, wl.out_dtype)
+
+        from concurrent.futures import ThreadPoolExecutor
+        reps_mt, t_mt = 0, 0.0
+        with ThreadPoolExecutor(threads) as ex:
+            while reps_mt == 0 or t_mt < args.cpu_seconds / 2:
+                c0 = time.perf_counter()
+                list(ex.map(piece, pieces))
+                t_mt += time.perf_counter() - c0
+                reps_mt += 1
+        sync("seq")
+        torch.cuda.synchronize()
+        got_seq = out.view(torch.int32 if tout == torch.float32 else torch.int16).cpu().numpy()
+        sv = seq_want.view(got_seq.dtype)
+        ok = got_seq == sv
+        if tout == torch.float32:
+            ok |= np.isnan(got_seq.view(np.float32)) & np.isnan(seq_want)
+        cpu["all_cores"] = {
+            "value": round(sync_bytes * reps_mt / t_mt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "order": "seq", "parity_vs_gpu_seq": "bitwise equal" if bool(ok.all())
+            else f"MISMATCH in {int((~ok).sum())} elements",
+            "sample": f"{reps_mt} repetition(s) of the full synchronisation, {len(pieces)} element "
+                      f"ranges on {threads} threads, {t_mt:.1f} s"}
+        log(f"cpu oracle, {threads} threads (seq): {cpu['all_cores']['value']} GB/s; "
+            f"{cpu['all_cores']['parity_vs_gpu_seq']}")
 
     # ---------------------------------------------------------------- copy layout
     copy_path = None
@@ -529,6 +598,7 @@ def main():
                      "traffic": traffic,
                      "kernel": "reduce_fast (one launch per sync)",
                      "kernel_ms": round(kern_ms, 5),
+                     "kernel_ms_median": round(kern_ms_median, 5),
                      "kernel_ms_min": round(min(launch_ms), 5),
                      "stream_ms_per_step": round(gpu_ms_per_step, 5)},
         "ceiling": ceiling,
@@ -541,6 +611,7 @@ def main():
         "rank_sweep_GBps": rank_sweep,
         "overlap": overlap,
         "no_sync": no_sync,
+        "env": run_environment(torch),
     }
     print(json.dumps(line), flush=True)
 
