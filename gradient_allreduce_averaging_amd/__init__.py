@@ -78,6 +78,9 @@ def _load():
         "ddp_plan_slot_param": ([vp, ctypes.c_int32, c_i32p], ctypes.c_int),
         "ddp_plan_param": ([vp, ctypes.c_int32, c_i32p, c_i64p], ctypes.c_int),
         "ddp_plan_prepare": ([vp], ctypes.c_int),
+        "ddp_plan_prepare_ranks": ([vp, ctypes.c_int32], ctypes.c_int),
+        "ddp_set_occupancy": ([ctypes.c_int], ctypes.c_int),
+        "ddp_get_occupancy": ([], ctypes.c_int),
         "ddp_bind_params": ([vp, ctypes.POINTER(vp), vp, ctypes.POINTER(vp)], ctypes.c_int),
         "ddp_binding_free": ([vp], None),
         "ddp_flatten": ([vp, vp, ctypes.c_int32, vp, ctypes.c_int, vp], ctypes.c_int),
@@ -194,8 +197,14 @@ class Plan:
             out.append([self.slot_param(s) for s in range(fs, fs + ns)])
         return out
 
-    def prepare(self):
-        _check(lib.ddp_plan_prepare(self._h), "ddp_plan_prepare")
+    def prepare(self, n_ranks: Optional[int] = None):
+        """Upload the plan's device tables now (``ddp_plan_prepare``), and with
+        ``n_ranks`` also the RING table for that rank count
+        (``ddp_plan_prepare_ranks``), e.g. before capturing a graph."""
+        if n_ranks is None:
+            _check(lib.ddp_plan_prepare(self._h), "ddp_plan_prepare")
+        else:
+            _check(lib.ddp_plan_prepare_ranks(self._h, int(n_ranks)), "ddp_plan_prepare_ranks")
 
 
 def plan_buckets(numel: Sequence[int], bucket_cap_bytes: int, dtype="f32") -> Plan:
@@ -332,7 +341,7 @@ def make_sync(plan: Plan, rank_flats: Sequence, out_flat, order="ring", stream=N
     these for every step).  The callable keeps its tensors alive; it launches
     on the stream that was current (or given) when it was made."""
     if _ORDERS[order] == RING:
-        plan.prepare()
+        plan.prepare(len(rank_flats))
     return _PreparedSync(plan, rank_flats, out_flat, order, stream)
 
 
@@ -384,3 +393,22 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return lib.ddp_abi_version()
+
+
+OCCUPANCY_TUNED = 0
+OCCUPANCY_SHARED = 1
+_OCCUPANCY = {"tuned": OCCUPANCY_TUNED, "shared": OCCUPANCY_SHARED,
+              OCCUPANCY_TUNED: OCCUPANCY_TUNED, OCCUPANCY_SHARED: OCCUPANCY_SHARED}
+
+
+def set_occupancy(policy) -> None:
+    """``"tuned"`` (default): the streaming kernels run at their measured best
+    number of resident blocks per CU; ``"shared"``: no cap, for syncs that
+    overlap compute on other streams (``ddp_set_occupancy``).  Process-wide."""
+    if policy not in _OCCUPANCY:
+        raise ValueError(f"unknown occupancy policy {policy!r}")
+    _check(lib.ddp_set_occupancy(_OCCUPANCY[policy]), "ddp_set_occupancy")
+
+
+def get_occupancy() -> str:
+    return "tuned" if lib.ddp_get_occupancy() == OCCUPANCY_TUNED else "shared"

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -31,8 +32,10 @@ struct ddp_plan {
 
     int32_t n_buckets() const { return (int32_t)bucket_base.size() - 1; }
 
-    std::mutex mu;                            // guards dev
+    std::mutex mu;                            // guards dev and ring_desc
     std::map<std::pair<int, int64_t>, ddp_dev_tables> dev;   // (device, tile elements)
+    // (device, tile elements, ranks): device array of one ring-segment word per tile
+    std::map<std::tuple<int, int64_t, int>, uint32_t *> ring_desc;
 };
 
 // One flatten/unflatten copy unit: `count` elements between a parameter's

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <cstdio>
@@ -45,6 +46,8 @@ namespace {
 constexpr int kThreads = 64;
 constexpr int kUnroll = 1;             // 16-byte vectors per lane per rank
 constexpr int kTileTableShift = 6;     // one bucket-table entry per 64 tiles
+static_assert(kThreads * kUnroll * 8 <= 1023 && DDP_MAX_RANKS <= 64,
+              "a ring-segment word holds 10-bit tile offsets and 6-bit ranks");
 constexpr int kCopyThreads = 256;      // flatten / unflatten blocks
 constexpr int64_t kCopyUnitElems = 16384;   // elements per copy-table entry
 constexpr int64_t kCopyBlockElems = 2048;   // elements per copy block: a unit gets
@@ -67,14 +70,19 @@ struct Buckets {
     const int64_t *base;          // [n_buckets + 1]
     const int32_t *tile_bucket;   // [ceil(n_tiles / 2^kTileTableShift)] bucket of the
                                   // first element of every 2^kTileTableShift-th tile
+    const uint32_t *tile_desc;    // ring segments of every tile (encoding at tile_segs,
+                                  // layout at ring_tile_desc), or null for a single bucket
+    int64_t desc_stride;          // tiles per XCD stripe of tile_desc
     int32_t n_buckets;
 };
+
+// Workgroups are dealt to the XCDs round-robin, so tile t runs on XCD t % 8.
+constexpr int kXcds = 8;
 
 // The chunk segments a tile may meet on the vector path.
 struct Segs {
     int64_t a_lo, a_hi, b_lo, b_hi;
     int sa, sb;
-    int32_t bucket;
 };
 
 // Streaming 16-byte accesses of the reduce.  Every byte is touched once, so
@@ -221,7 +229,14 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
 // Tile processed by this block.
 __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 
-// Segments of tile `tile`, whose first element is tile0 (block-uniform values).
+// Ring segments of tile `tile`, whose first element is tile0 (block-uniform
+// values): segment a holds the tile's first element, segment b follows it;
+// a vector inside neither takes the per-element path.  With a plan the
+// segments come from one precomputed word per tile, so a wave makes a single
+// scalar load, issued while its vector loads are in flight:
+//   bits 0-5 start rank of a, 6-11 start rank of b,
+//   12-21 end of a and 22-31 end of b, both relative to tile0.
+// A single bucket [0, total) is computed here.
 template <bool RING>
 __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int N, int64_t tile,
                                           int64_t tile0)
@@ -233,36 +248,100 @@ __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int 
     s.b_hi = 0;
     s.sa = 0;
     s.sb = 0;
-    s.bucket = 0;
     if (!RING) return s;
-    int32_t b = 0;
-    if (bk.tile_bucket) {
-        // coarse table entry, then forward past bucket ends before tile0
-        b = bk.tile_bucket[tile >> kTileTableShift];
-        while (bk.base[b + 1] <= tile0) ++b;
-    }
-    const int64_t base = bk.base ? bk.base[b] : 0;
-    const int64_t end = bk.base ? bk.base[b + 1] : total;
-    const int64_t C = (end - base + N - 1) / N;
-    const int64_t c = (tile0 - base) / C;
-    s.bucket = b;
-    s.a_lo = base + c * C;
-    s.a_hi = min(s.a_lo + C, end);
-    s.sa = (int)((c + 1) % N);
-    if (s.a_hi < end) {
+    if (bk.tile_desc) {
+        const uint32_t d = bk.tile_desc[(tile % kXcds) * bk.desc_stride + tile / kXcds];
+        s.sa = (int)(d & 63u);
+        s.sb = (int)((d >> 6) & 63u);
+        s.a_lo = tile0;
+        s.a_hi = tile0 + (int64_t)((d >> 12) & 1023u);
         s.b_lo = s.a_hi;
-        s.b_hi = min(s.b_lo + C, end);
-        s.sb = (int)((c + 2) % N);
-    } else if (bk.base && b + 1 < bk.n_buckets) {
-        const int64_t e2 = bk.base[b + 2];
-        const int64_t C2 = (e2 - end + N - 1) / N;
-        s.b_lo = end;
-        s.b_hi = min(end + C2, e2);
-        s.sb = 1 % N;
+        s.b_hi = tile0 + (int64_t)(d >> 22);
+    } else {
+        const int64_t C = (total + N - 1) / N;
+        const int64_t c = tile0 / C;
+        s.a_lo = c * C;
+        s.a_hi = min(s.a_lo + C, total);
+        s.sa = (int)((c + 1) % N);
+        if (s.a_hi < total) {
+            s.b_lo = s.a_hi;
+            s.b_hi = min(s.b_lo + C, total);
+            s.sb = (int)((c + 2) % N);
+        }
     }
     s.sa = __builtin_amdgcn_readfirstlane(s.sa);
     s.sb = __builtin_amdgcn_readfirstlane(s.sb);
     return s;
+}
+
+// A bucket at or before the one holding tile0, where the per-element path
+// starts its forward search.
+__device__ __forceinline__ int32_t first_bucket(const Buckets &bk, int64_t tile)
+{
+    return bk.tile_bucket ? bk.tile_bucket[tile >> kTileTableShift] : 0;
+}
+
+// The fold of one lane's vectors, v[k] holding rank k's vector at the lane's
+// offset.  Ring order starting at rank R:
+//   acc = ((x_R + x_{R+1}) + ...) + x_{R-1}   (ranks mod NR)
+template <int NR, int IN, int R>
+__device__ __forceinline__ void fold_from(const u32x4 *v, float *acc)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = lane<IN>(v[R], e);
+#pragma unroll
+    for (int k = 1; k < NR; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[(R + k) % NR], e);
+}
+
+// Rotation R behind its branch: the inputs pass through an empty volatile asm
+// inside the branch, so the adds cannot be hoisted above it.  Without this
+// the compiler evaluates all NR rotations and selects one: NR times the adds
+// and twice the registers.
+template <int NR, int IN, int R>
+__device__ __forceinline__ void fold_from_here(const u32x4 *v, float *acc)
+{
+    u32x4 w[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        w[k] = v[k];
+        asm volatile("" : "+v"(w[k]));
+    }
+    fold_from<NR, IN, R>(w, acc);
+}
+
+// The same for a start rank s known at run time (wave-uniform): a branch
+// picks one of the NR compile-time rotations.
+template <int NR, int IN, int R = 0>
+__device__ __forceinline__ void fold_ring(const u32x4 *v, int s, float *acc)
+{
+    if constexpr (R + 1 < NR) {
+        if (s == R)
+            fold_from_here<NR, IN, R>(v, acc);
+        else
+            fold_ring<NR, IN, R + 1>(v, s, acc);
+    } else {
+        fold_from_here<NR, IN, R>(v, acc);
+    }
+}
+
+// Sequential order: acc = ((+0 + x_0) + x_1) + ... + x_{NR-1}; with one rank
+// the input itself.
+template <int NR, int IN>
+__device__ __forceinline__ void fold_seq(const u32x4 *v, float *acc)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const float x = lane<IN>(v[0], e);
+        acc[e] = NR == 1 ? x : 0.0f + x;
+    }
+#pragma unroll
+    for (int k = 1; k < NR; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[k], e);
 }
 
 // Convert and store one vector of scaled averages y at element i0; for a
@@ -313,53 +392,43 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     const int64_t tile = tile_of_block();
     const int64_t tile0 = tile * (kThreads * kUnroll * VEC);
-    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
 
-    const char *qa[NR];
-    const char *qb[NR];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        qa[k] = static_cast<const char *>(ra.p[wrap(sg.sa + k, NR)]);
-        qb[k] = RING ? static_cast<const char *>(ra.p[wrap(sg.sb + k, NR)]) : qa[k];
-    }
-
+    // Every rank's vector at the lane's offset, in rank order, in either
+    // summation order: the addresses depend on the tile alone, so all
+    // NR * kUnroll loads are in flight before the tile's ring segments are
+    // looked up below.  A lane whose vector runs past the end reads the first
+    // vector of each rank buffer instead (in bounds since total >= VEC) and
+    // never uses it.
     u32x4 v[kUnroll][NR];
     int64_t i0[kUnroll];
-    bool fast[kUnroll], in_a[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        i0[u] = tile0 + ((int64_t)threadIdx.x + u * kThreads) * VEC;
-        in_a[u] = i0[u] >= sg.a_lo && i0[u] + VEC <= sg.a_hi;
-        const bool in_b = RING && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
-        fast[u] = in_a[u] || in_b;
-    }
-    // The loads are unconditional so that all NR * kUnroll of them are in
-    // flight before the first wait; a lane whose vector is not on the vector
-    // path reads the first vector of a rank buffer instead (in bounds since
-    // total >= VEC) and never uses it.
+    for (int u = 0; u < kUnroll; ++u) i0[u] = tile0 + ((int64_t)threadIdx.x + u * kThreads) * VEC;
     if (total >= VEC) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
             for (int k = 0; k < NR; ++k)
-                v[u][k] = ld_stream((in_a[u] ? qa[k] : qb[k]) + (fast[u] ? i0[u] * ISZ : 0));
+                v[u][k] = ld_stream(static_cast<const char *>(ra.p[k]) +
+                                    (i0[u] + VEC <= total ? i0[u] * ISZ : 0));
     }
+
+    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (fast[u]) {
+        const bool in_a = i0[u] >= sg.a_lo && i0[u] + VEC <= sg.a_hi;
+        const bool in_b = RING && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
+        if (in_a || in_b) {
             float acc[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float x = lane<IN>(v[u][0], e);
-                acc[e] = RING ? x : 0.0f + x;
-            }
-#pragma unroll
-            for (int k = 1; k < NR; ++k)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[u][k], e);
+            if (!RING)
+                fold_seq<NR, IN>(v[u], acc);
+            else if (in_a)
+                fold_ring<NR, IN>(v[u], sg.sa, acc);
+            else
+                fold_ring<NR, IN>(v[u], sg.sb, acc);
             store_vec<IN, OUT>(out, i0[u], acc, inv);
         } else if (i0[u] < total) {
-            reduce_elems<IN, OUT, RING>(ra, NR, total, bk, sg.bucket, inv, out, i0[u], VEC);
+            reduce_elems<IN, OUT, RING>(ra, NR, total, bk, first_bucket(bk, tile), inv, out,
+                                            i0[u], VEC);
         }
     }
 }
@@ -379,41 +448,35 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
     constexpr int PV = VEC / 4;
     const int64_t tile = tile_of_block();
     const int64_t tile0 = tile * (kThreads * VEC);
-    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
-    const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
-    const bool fast = in_a || (RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi);
 
-    // rotated rank pointers for both segments, resolved in scalar registers
-    const char *qa[NR];
-    const char *qb[NR];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        qa[k] = static_cast<const char *>(ra.p[wrap(sg.sa + k, NR)]);
-        qb[k] = RING ? static_cast<const char *>(ra.p[wrap(sg.sb + k, NR)]) : qa[k];
-    }
+    // The lane's gradient vectors from every rank in rank order, and its
+    // parameter (and momentum) vectors, issued before the ring segments are
+    // looked up; a lane past the end reads the first vectors and drops them.
     u32x4 v[NR], pv[PV], mv[PV];
-    if (total >= VEC) {   // unconditional loads, as in reduce_fast
+    if (total >= VEC) {
+        const bool whole = i0 + VEC <= total;
+        const int64_t go = whole ? i0 * ISZ : 0, po = whole ? i0 * 4 : 0;
 #pragma unroll
-        for (int k = 0; k < NR; ++k) v[k] = ld_stream((in_a ? qa[k] : qb[k]) + (fast ? i0 * ISZ : 0));
-        const int64_t po = fast ? i0 * 4 : 0;
+        for (int k = 0; k < NR; ++k) v[k] = ld_stream(static_cast<const char *>(ra.p[k]) + go);
 #pragma unroll
         for (int j = 0; j < PV; ++j) {
             pv[j] = ld_stream(reinterpret_cast<const char *>(sa.param) + po + 16 * j);
             if (MOM) mv[j] = ld_stream(reinterpret_cast<const char *>(sa.mom) + po + 16 * j);
         }
     }
-    if (fast) {
+
+    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
+    const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
+    const bool in_b = RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+    if (in_a || in_b) {
         float y[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float x = lane<IN>(v[0], e);
-            y[e] = (RING || NR == 1) ? x : 0.0f + x;
-        }
-#pragma unroll
-        for (int k = 1; k < NR; ++k)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) y[e] = y[e] + lane<IN>(v[k], e);
+        if (!RING || NR == 1)
+            fold_seq<NR, IN>(v, y);
+        else if (in_a)
+            fold_ring<NR, IN>(v, sg.sa, y);
+        else
+            fold_ring<NR, IN>(v, sg.sb, y);
         if (NR > 1) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;
@@ -433,7 +496,7 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
             if (MOM) st_stream(sa.mom + i0 + 4 * j, mo);
         }
     } else if (i0 < total) {
-        sgd_elems<IN, OUT, RING, MOM>(ra, NR, total, bk, sg.bucket, inv, sa, i0, VEC);
+        sgd_elems<IN, OUT, RING, MOM>(ra, NR, total, bk, first_bucket(bk, tile), inv, sa, i0, VEC);
     }
 }
 
@@ -445,7 +508,7 @@ reduce_sgd_scalar(RankArgs ra, int N, int64_t total, float inv, SgdArgs sa)
 {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= total) return;
-    const Buckets single = {nullptr, nullptr, 1};
+    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
     sgd_elems<IN, OUT, RING, MOM>(ra, N, total, single, 0, inv, sa, i, 1);
 }
 
@@ -530,7 +593,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
             }
             store_vec<IN, OUT>(out, i0, acc, inv);
         } else if (i0 < total) {
-            reduce_elems<IN, OUT, RING>(ra, N, total, bk, sg.bucket, inv, out, i0, VEC);
+            reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
         }
     }
 }
@@ -542,7 +605,7 @@ reduce_scalar(RankArgs ra, int N, int64_t total, float inv, void *out)
 {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= total) return;
-    const Buckets single = {nullptr, nullptr, 1};
+    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
     reduce_elems<IN, OUT, RING>(ra, N, total, single, 0, inv, out, i, 1);
 }
 
@@ -647,6 +710,59 @@ bool pair_ok(int in, int out)
 int64_t vec_elems(int in) { return in == DDP_F32 ? 4 : 8; }
 int64_t tile_elems(int in) { return (int64_t)kThreads * kUnroll * vec_elems(in); }
 
+// ---------------------------------------------------------------- occupancy
+// These streaming kernels move the most bytes per second on gfx950 with fewer
+// resident blocks per CU than registers alone would allow (up to 32 of these
+// one-wave blocks): past a point, more concurrent waves only open more DRAM
+// rows at once.  Each launch is therefore capped at k resident blocks per CU
+// by asking for LDS_per_CU / k bytes of dynamic LDS, which the kernels do not
+// touch.  k was measured per kernel and rank count on ResNet-50, many-small,
+// GPT-1.3B and Llama-7B shapes; 0 means no cap.
+
+// Reduce, N = 2..8 (one 16-byte load per rank and lane, one store).
+int reduce_blocks_per_cu(int N)
+{
+    static const int k[9] = {0, 0, 0, 16, 14, 12, 10, 9, 8};
+    return N >= 0 && N <= 8 ? k[N] : 0;
+}
+
+// Fused average + SGD step, N = 1..8 (also the parameter, momentum loads and
+// stores).
+int sgd_blocks_per_cu(int N, bool mom)
+{
+    static const int with_mom[9] = {0, 20, 14, 10, 8, 8, 7, 7, 6};
+    static const int without[9] = {0, 0, 0, 0, 0, 10, 8, 8, 8};
+    if (N < 0 || N > 8) return 0;
+    return mom ? with_mom[N] : without[N];
+}
+
+// Flatten / unflatten (256-thread blocks).
+constexpr int kCopyBlocksPerCU = 7;
+
+constexpr int kMaxDevices = 64;
+
+// DDP_OCCUPANCY_TUNED or DDP_OCCUPANCY_SHARED, process-wide.
+std::atomic<int> g_occupancy{DDP_OCCUPANCY_TUNED};
+
+// Dynamic LDS bytes that leave room for k blocks per CU on the current device
+// (none under DDP_OCCUPANCY_SHARED).
+unsigned lds_for_blocks(int k)
+{
+    static std::atomic<int> lds_per_cu[kMaxDevices];   // 0: not queried yet, -1: unknown
+    if (k <= 0 || g_occupancy.load(std::memory_order_relaxed) != DDP_OCCUPANCY_TUNED) return 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            v <= 0)
+            v = -1;
+        lds_per_cu[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? (unsigned)(v / k) : 0;
+}
+
 bool overlaps(uintptr_t a, int64_t na, uintptr_t b, int64_t nb)
 {
     return a < b + (uintptr_t)nb && b < a + (uintptr_t)na;
@@ -673,14 +789,15 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
         const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
         if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
         const dim3 g((unsigned)tiles), b(kThreads);
+        const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N));
         switch (N) {
-        case 2: reduce_fast<2, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 3: reduce_fast<3, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 4: reduce_fast<4, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 5: reduce_fast<5, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 6: reduce_fast<6, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 7: reduce_fast<7, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
-        case 8: reduce_fast<8, RING, IN, OUT><<<g, b, 0, st>>>(ra, total, bk, inv, out); break;
+        case 2: reduce_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 3: reduce_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 4: reduce_fast<4, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 5: reduce_fast<5, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
+        case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
         default: reduce_many<RING, IN, OUT><<<g, b, 0, st>>>(ra, N, total, bk, inv, out); break;
         }
     } else {
@@ -717,15 +834,16 @@ ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Bu
         const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
         if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
         const dim3 g((unsigned)tiles), b(kThreads);
+        const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
         switch (N) {
-        case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
-        default: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, 0, st>>>(ra, total, bk, inv, sa); break;
+        case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        default: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
         }
     } else {
         const int64_t blocks = (total + kThreads - 1) / kThreads;
@@ -843,12 +961,93 @@ ddp_status_t plan_tables(ddp_plan *plan, int64_t tile, const ddp_dev_tables **ou
     return DDP_OK;
 }
 
+// Ring segments of every tile of a plan for n_ranks ranks, the word tile_segs
+// reads: start ranks of the segment holding the tile's first element and of
+// the next one, and where each ends inside the tile.  Segments are the
+// non-empty ring chunks of every bucket in flat order (chunk c of a bucket of
+// length L is [c*C, min((c+1)*C, L)) with C = ceil(L/N), started by rank
+// (c+1) mod N).  The words are striped by XCD -- tile t at
+// (t % 8) * stride + t / 8 -- so that each XCD's L2 fetches only lines of
+// its own tiles.  Built on the host and uploaded once per device, tile size
+// and rank count.
+int64_t desc_stride(int64_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds; }
+
+ddp_status_t ring_tile_desc(ddp_plan *plan, int64_t tile, int n_ranks, const uint32_t **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    const auto key = std::make_tuple(dev, tile, n_ranks);
+    auto it = plan->ring_desc.find(key);
+    if (it != plan->ring_desc.end()) {
+        *out = it->second;
+        return DDP_OK;
+    }
+    struct Seg {
+        int64_t lo, hi;
+        uint32_t start;
+    };
+    const int64_t total = plan->total, n_tiles = (total + tile - 1) / tile;
+    std::vector<Seg> segs;
+    std::vector<uint32_t> w;
+    try {
+        for (int32_t b = 0; b < plan->n_buckets(); ++b) {
+            const int64_t base = plan->bucket_base[b], end = plan->bucket_base[b + 1];
+            const int64_t C = (end - base + n_ranks - 1) / n_ranks;
+            for (int c = 0; c < n_ranks && base + c * C < end; ++c)
+                segs.push_back({base + c * C, std::min(base + (c + 1) * C, end),
+                                (uint32_t)((c + 1) % n_ranks)});
+        }
+        w.assign((size_t)std::max<int64_t>(kXcds * desc_stride(n_tiles), 1), 0u);
+    } catch (...) {
+        return DDP_ERR_NOMEM;
+    }
+    // the segments cover [0, total) in order, so one forward pass finds them
+    size_t j = 0;
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int64_t t0 = t * tile, t1 = std::min(t0 + tile, total);
+        while (segs[j].hi <= t0) ++j;
+        const uint32_t cut_a = (uint32_t)(std::min(segs[j].hi, t1) - t0);
+        uint32_t cut_b = cut_a, sb = 0;
+        if (segs[j].hi < t1) {
+            cut_b = (uint32_t)(std::min(segs[j + 1].hi, t1) - t0);
+            sb = segs[j + 1].start;
+        }
+        w[(size_t)((t % kXcds) * desc_stride(n_tiles) + t / kXcds)] =
+            segs[j].start | sb << 6 | cut_a << 12 | cut_b << 22;
+    }
+    uint32_t *d = nullptr;
+    const size_t bytes = sizeof(uint32_t) * w.size();
+    if ((e = hipMalloc(&d, bytes)) != hipSuccess)
+        return hip_fail("hipMalloc (ring segment table)", e, DDP_ERR_NOMEM);
+    if ((e = hipMemcpy(d, w.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail("hipMemcpy (ring segment table)", e);
+    }
+    plan->ring_desc.emplace(key, d);
+    *out = d;
+    return DDP_OK;
+}
+
+// The tables of a RING synchronisation over n_ranks ranks.
+ddp_status_t ring_buckets(ddp_plan *plan, int in, int n_ranks, Buckets *bk)
+{
+    const ddp_dev_tables *t = nullptr;
+    ddp_status_t st = plan_tables(plan, tile_elems(in), &t);
+    if (st != DDP_OK) return st;
+    const uint32_t *desc = nullptr;
+    if ((st = ring_tile_desc(plan, tile_elems(in), n_ranks, &desc)) != DDP_OK) return st;
+    *bk = {t->bucket_base, t->tile_bucket, desc, desc_stride(t->n_tiles), plan->n_buckets()};
+    return DDP_OK;
+}
+
 }  // namespace
 
 void ddp_internal_free_plan_tables(ddp_plan *plan)
 {
     std::lock_guard<std::mutex> lock(plan->mu);
-    if (plan->dev.empty()) return;
+    if (plan->dev.empty() && plan->ring_desc.empty()) return;
     int cur = -1;
     (void)hipGetDevice(&cur);
     for (auto &kv : plan->dev) {
@@ -856,7 +1055,12 @@ void ddp_internal_free_plan_tables(ddp_plan *plan)
         (void)hipFree(kv.second.bucket_base);
         (void)hipFree(kv.second.tile_bucket);
     }
+    for (auto &kv : plan->ring_desc) {
+        (void)hipSetDevice(std::get<0>(kv.first));
+        (void)hipFree(kv.second);
+    }
     plan->dev.clear();
+    plan->ring_desc.clear();
     if (cur >= 0) (void)hipSetDevice(cur);
 }
 
@@ -878,7 +1082,7 @@ ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ra
         ra.p[r] = rank_ptrs[r];
         vec_ok = vec_ok && aligned(rank_ptrs[r], 16);
     }
-    const Buckets single = {nullptr, nullptr, 1};
+    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
     return launch_reduce(ra, n_ranks, len, order, in_dtype, out_dtype, single, out, st, vec_ok);
 }
 
@@ -887,6 +1091,26 @@ ddp_status_t ddp_plan_prepare(ddp_plan_t *plan)
     if (!plan) return DDP_ERR_INVALID_ARG;
     const ddp_dev_tables *t = nullptr;
     return plan_tables(plan, tile_elems(plan->dtype), &t);
+}
+
+ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy)
+{
+    if (policy != DDP_OCCUPANCY_TUNED && policy != DDP_OCCUPANCY_SHARED) return DDP_ERR_INVALID_ARG;
+    g_occupancy.store(policy, std::memory_order_relaxed);
+    return DDP_OK;
+}
+
+ddp_occupancy_t ddp_get_occupancy(void)
+{
+    return static_cast<ddp_occupancy_t>(g_occupancy.load(std::memory_order_relaxed));
+}
+
+ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks)
+{
+    if (!plan || n_ranks < 1 || n_ranks > DDP_MAX_RANKS) return DDP_ERR_INVALID_ARG;
+    if (n_ranks == 1) return ddp_plan_prepare(plan);
+    Buckets bk;
+    return ring_buckets(plan, plan->dtype, n_ranks, &bk);
 }
 
 ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
@@ -919,7 +1143,7 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
             std::memset(&sub, 0, sizeof(sub));
             for (int r = 0; r < n_ranks; ++r)
                 sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
-            const Buckets single = {nullptr, nullptr, 1};
+            const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
             ddp_status_t s2 = launch_reduce(sub, n_ranks, len, order, in, out_dtype, single,
                                             static_cast<char *>(out_flat) + base * osz, st, false);
             if (s2 != DDP_OK) return s2;
@@ -928,12 +1152,11 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
     }
     if (order == DDP_ORDER_SEQUENTIAL) {
         // the sequential fold does not depend on bucket boundaries
-        const Buckets single = {nullptr, nullptr, 1};
+        const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
         return launch_reduce(ra, n_ranks, total, order, in, out_dtype, single, out_flat, st, true);
     }
-    const ddp_dev_tables *t = nullptr;
-    if ((stc = plan_tables(plan, tile_elems(in), &t)) != DDP_OK) return stc;
-    const Buckets bk = {t->bucket_base, t->tile_bucket, plan->n_buckets()};
+    Buckets bk;
+    if ((stc = ring_buckets(plan, in, n_ranks, &bk)) != DDP_OK) return stc;
     return launch_reduce(ra, n_ranks, total, order, in, out_dtype, bk, out_flat, st, true);
 }
 
@@ -986,20 +1209,20 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
             SgdArgs sa = {param_flat + base, momentum_flat ? momentum_flat + base : nullptr,
                           grad_out ? static_cast<char *>(grad_out) + base * osz : nullptr, lr,
                           momentum};
-            const Buckets single = {nullptr, nullptr, 1};
+            const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
             ddp_status_t s2 = launch_sgd(sub, n_ranks, len, order, in, out_dtype, single, sa, st, false);
             if (s2 != DDP_OK) return s2;
         }
         return DDP_OK;
     }
     const SgdArgs sa = {param_flat, momentum_flat, grad_out, lr, momentum};
-    if (order == DDP_ORDER_SEQUENTIAL) {
-        const Buckets single = {nullptr, nullptr, 1};
+    if (order == DDP_ORDER_SEQUENTIAL || n_ranks == 1) {
+        // neither depends on bucket boundaries (one rank: the input itself)
+        const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
         return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single, sa, st, true);
     }
-    const ddp_dev_tables *t = nullptr;
-    if ((stc = plan_tables(plan, tile_elems(in), &t)) != DDP_OK) return stc;
-    const Buckets bk = {t->bucket_base, t->tile_bucket, plan->n_buckets()};
+    Buckets bk;
+    if ((stc = ring_buckets(plan, in, n_ranks, &bk)) != DDP_OK) return stc;
     return launch_sgd(ra, n_ranks, total, order, in, out_dtype, bk, sa, st, true);
 }
 
@@ -1133,8 +1356,8 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
     if ((last - first) * kCopyBlocksPerUnit > INT_MAX) return DDP_ERR_OVERFLOW;
-    copy_units<<<dim3((unsigned)((last - first) * kCopyBlocksPerUnit)), dim3(kCopyThreads), 0,
-                 static_cast<hipStream_t>(stream)>>>(
+    copy_units<<<dim3((unsigned)((last - first) * kCopyBlocksPerUnit)), dim3(kCopyThreads),
+                 lds_for_blocks(kCopyBlocksPerCU), static_cast<hipStream_t>(stream)>>>(
         bd->units, first, static_cast<char *>(flat), dtype_size(dtype), to_flat);
     return launched("copy kernel launch");
 }

@@ -143,6 +143,18 @@ ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
  * Errors: INVALID_ARG, HIP, NOMEM. */
 ddp_status_t ddp_plan_prepare(ddp_plan_t *plan);
 
+/* ddp_plan_prepare, plus the table a RING synchronisation over n_ranks ranks
+ * reads: one 32-bit word per tile of the flat layout (4 bytes per 256 f32 or
+ * 512 bf16 elements) naming the ring chunks the tile meets.  RING chunks are
+ * per bucket and depend on n_ranks, so each rank count has its own table,
+ * kept on the device until ddp_plan_free.  Optional like ddp_plan_prepare:
+ * the first RING call (ddp_sync_allreduce_avg, ddp_sync_sgd_update) with a
+ * new rank count builds it synchronously; call this first when that call
+ * will be captured into a HIP graph or must not allocate.
+ *   n_ranks  1..DDP_MAX_RANKS (1 prepares only what ddp_plan_prepare does)
+ * Errors: INVALID_ARG, HIP, NOMEM. */
+ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
+
 /* ------------------------------------------------------------------ bindings
  * One rank's per-parameter gradient buffers, resolved once (a static graph
  * fixes every address up front: [DDP] 6.2; [TR24] 十 resolves addresses at
@@ -210,8 +222,9 @@ ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ra
  *                       buffer (ddp_plan_total elements of the plan's dtype)
  *   out_flat            device, ddp_plan_total elements of out_dtype
  * RING chunks are computed per bucket (each bucket is its own all-reduce).
- * The first RING call on a device uploads the plan's tables synchronously
- * (see ddp_plan_prepare).  Errors: as ddp_bucket_allreduce_avg. */
+ * The first RING call on a device with a given n_ranks uploads the plan's
+ * tables synchronously (see ddp_plan_prepare_ranks).
+ * Errors: as ddp_bucket_allreduce_avg. */
 ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat,
                                     int32_t n_ranks, ddp_order_t order,
                                     ddp_dtype_t out_dtype, void *out_flat,
@@ -256,6 +269,24 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, ALIAS, HIP. */
 ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
                             ddp_dtype_t dtype, void *stream);
+
+/* ------------------------------------------------------------------ occupancy
+ * How many blocks of the streaming kernels (reduce, fused SGD step, flatten /
+ * unflatten) may be resident on one CU.
+ *   DDP_OCCUPANCY_TUNED   (default) each launch is capped at the number of
+ *       resident blocks per CU measured fastest for its kernel and rank
+ *       count, by asking for an unused share of the CU's LDS.  Best for a
+ *       synchronisation that has the GPU to itself.
+ *   DDP_OCCUPANCY_SHARED  no cap.  The reserved LDS keeps other kernels'
+ *       LDS-using blocks (a GEMM's, say) off a CU while the reduce runs
+ *       there, so choose this when syncs overlap compute on other streams.
+ * The policy is process-wide and applies to launches made after the call.
+ * Results do not depend on it, only timing. */
+typedef enum { DDP_OCCUPANCY_TUNED = 0, DDP_OCCUPANCY_SHARED = 1 } ddp_occupancy_t;
+
+/* Errors: INVALID_ARG (not a ddp_occupancy_t value). */
+ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy);
+ddp_occupancy_t ddp_get_occupancy(void);
 
 /* ------------------------------------------------------------------ misc */
 const char *ddp_status_string(ddp_status_t status);

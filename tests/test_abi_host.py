@@ -111,6 +111,11 @@ def test_plan_errors():
     assert L.ddp_plan_bucket(p.handle, -1, ctypes.byref(ln), None, None, None) == 1
     assert L.ddp_plan_param(p.handle, 2, None, None) == 1
     assert L.ddp_plan_slot_param(p.handle, 0, None) == 1
+    # rank counts outside 1..64 and a null plan are rejected before any HIP call
+    assert L.ddp_plan_prepare_ranks(None, 2) == 1
+    assert L.ddp_plan_prepare_ranks(p.handle, 0) == 1
+    assert L.ddp_plan_prepare_ranks(p.handle, 65) == 1
+    assert L.ddp_plan_prepare(None) == 1
     with pytest.raises(ddp.DDPError):
         ddp.plan_buckets([1, 2], 0)
 
@@ -188,3 +193,16 @@ def test_accumulate_argument_errors_are_host_side():
     assert f(P(0x1000, 0x1020), P(0x8000, 0x9000), 2, 16, 0, None) == 4   # dst overlap
     assert f(P(0x1000, 0x2000), P(0x2000, 0x9000), 2, 16, 0, None) == 4   # dst[0] is src[1]
     assert f(P(0x1002), P(0x2000), 1, 16, 0, None) == 1           # f32 misaligned to 2 B
+
+
+def test_occupancy_policy_round_trip():
+    L = ddp.lib
+    assert ddp.get_occupancy() == "tuned"
+    assert L.ddp_set_occupancy(2) == 1
+    assert L.ddp_set_occupancy(-1) == 1
+    ddp.set_occupancy("shared")
+    assert ddp.get_occupancy() == "shared"
+    ddp.set_occupancy("tuned")
+    assert ddp.get_occupancy() == "tuned"
+    with pytest.raises(ValueError):
+        ddp.set_occupancy("fast")

@@ -33,7 +33,7 @@ def test_captured_step_replays_match_eager_and_oracle(env):
     N, cap = 4, 1 << 20
     lp = ddp.plan_buckets(sizes, cap, "f32")
     op = oracle.plan_cap(sizes, cap, 4)
-    lp.prepare()
+    lp.prepare(N)   # every table the captured RING syncs read, uploaded before capture
     dev = "cuda:0"
     grads = [[torch.empty(n, dtype=torch.float32, device=dev) for n in sizes] for _ in range(N)]
     flats = [torch.empty(lp.total, dtype=torch.float32, device=dev) for _ in range(N)]

@@ -169,6 +169,61 @@ def test_same_result_on_repeat_and_on_a_side_stream(env):
     assert_bits_equal(to_host(out, torch), first, "side stream")
 
 
+def test_one_plan_ring_tables_per_rank_count(env):
+    """The RING table of a plan is per rank count: one plan synchronised with
+    N = 2, 3, 5, 8, 12, then 3 and 8 again, matches the oracle every time."""
+    torch, ddp = env
+    rng = np.random.default_rng(31)
+    numel = [int(v) for v in rng.integers(1, 40000, 60)]
+    for dt, eb in (("f32", 4), ("bf16", 2)):
+        lp = ddp.plan_buckets(numel, 96 << 10, dt)
+        op = oracle.plan_cap(numel, 96 << 10, eb)
+        xs = random_inputs(rng, 12, op.total, dt)
+        ts = [to_dev(x, torch) for x in xs]
+        out = torch.empty(op.total, dtype=ts[0].dtype, device="cuda:0")
+        for n in (2, 3, 5, 8, 12, 3, 8):
+            print(f"{dt} N={n}", flush=True)
+            lp.prepare(n)
+            ddp.sync_allreduce_avg(lp, ts[:n], out, "ring")
+            torch.cuda.synchronize()
+            assert_bits_equal(to_host(out, torch), oracle.sync_avg(op, xs[:n], "ring", dt, dt),
+                              f"{dt} N={n}")
+
+
+def test_occupancy_policy_changes_no_bit(env):
+    """Both occupancy policies give the same bits (reduce in both orders, the
+    fused SGD step, flatten)."""
+    torch, ddp = env
+    rng = np.random.default_rng(5)
+    numel = [int(v) for v in rng.integers(1, 50000, 80)]
+    lp = ddp.plan_buckets(numel, 200 << 10)
+    op = oracle.plan_cap(numel, 200 << 10, 4)
+    xs = random_inputs(rng, 6, op.total, "f32")
+    ts = [to_dev(x, torch) for x in xs]
+    p0 = rng.standard_normal(op.total).astype(np.float32)
+    grads = [to_dev(g, torch) for g in random_inputs(rng, 1, op.total, "f32")[0:1]]
+    views = list(torch.split(grads[0], numel))
+    got = {}
+    try:
+        for policy in ("shared", "tuned"):
+            ddp.set_occupancy(policy)
+            for order in ("seq", "ring"):
+                out = torch.empty(op.total, dtype=torch.float32, device="cuda:0")
+                ddp.sync_allreduce_avg(lp, ts, out, order)
+                got[(policy, order)] = to_host(out, torch)
+            params, mom = to_dev(p0, torch), torch.zeros(op.total, device="cuda:0")
+            ddp.sync_sgd_update(lp, ts, params, 0.05, "ring", momentum_buf=mom, momentum=0.9)
+            got[(policy, "sgd")] = to_host(params, torch)
+            flat = torch.empty(op.total, dtype=torch.float32, device="cuda:0")
+            ddp.flatten(lp, ddp.bind_params(lp, views), flat)
+            got[(policy, "flatten")] = to_host(flat, torch)
+    finally:
+        ddp.set_occupancy("tuned")
+    for what in ("seq", "ring", "sgd", "flatten"):
+        assert_bits_equal(got[("shared", what)], got[("tuned", what)], what)
+    assert_bits_equal(got[("tuned", "ring")], oracle.sync_avg(op, xs, "ring"), "ring vs oracle")
+
+
 def test_prepared_sync_matches_direct_call(env):
     torch, ddp = env
     import workloads as W
