@@ -97,6 +97,7 @@ def main():
     ap.add_argument("--no-no-sync", action="store_true")
     ap.add_argument("--no-in-place", action="store_true")
     ap.add_argument("--no-rank-sweep", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -190,6 +191,31 @@ def main():
     log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
         f"stream ({achieved:.0f} GB/s); single launches between events: median "
         f"{np.median(launch_ms) * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us")
+
+    # ---------------------------------------------------------------- MALL flushed
+    # The same sync with a 512 MiB scratch buffer overwritten before each one,
+    # so that nothing of the previous sync is left in the 256 MB MALL; each
+    # sync bracketed by its own event pair (a few microseconds of event
+    # overhead included).
+    cold = None
+    if not args.no_cold:
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        reps = min(args.steps, 50)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            scratch.fill_(1.0)
+            a.record(stream)
+            sync()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in ev]
+        cold = {"GBps_median": round(sync_bytes / (float(np.median(ts)) * 1e-3) / 1e9, 1),
+                "GBps_best": round(sync_bytes / (min(ts) * 1e-3) / 1e9, 1),
+                "ms_median": round(float(np.median(ts)), 5), "syncs": reps,
+                "flush": "512 MiB written before every sync"}
+        log(f"MALL flushed: {cold}")
+        del scratch
 
     # ---------------------------------------------------------------- access-pattern ceiling
     # The same N input buffers read with the reduce's access pattern (N
@@ -616,6 +642,7 @@ def main():
                      "kernel_ms_source": "event pair around the K timed launches, / K",
                      "single_launch_ms_median": round(float(np.median(launch_ms)), 5),
                      "single_launch_ms_min": round(min(launch_ms), 5)},
+        "cold_mall": cold,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity": parity,
