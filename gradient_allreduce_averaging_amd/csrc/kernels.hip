@@ -49,7 +49,7 @@ constexpr int kTileTableShift = 6;     // one bucket-table entry per 64 tiles
 static_assert(kThreads * kUnroll * 8 <= 1023 && DDP_MAX_RANKS <= 64,
               "a ring-segment word holds 10-bit tile offsets and 6-bit ranks");
 constexpr int kCopyThreads = 256;      // flatten / unflatten blocks
-constexpr int64_t kCopyUnitElems = 16384;   // elements per copy-table entry
+constexpr int64_t kCopyUnitElems = 4096;    // elements per copy-table entry
 constexpr int64_t kCopyBlockElems = 2048;   // elements per copy block: a unit gets
 constexpr int kCopyBlocksPerUnit = (int)(kCopyUnitElems / kCopyBlockElems);   // this many blocks
 static_assert(kCopyUnitElems % kCopyBlockElems == 0, "a copy unit splits into whole blocks");
@@ -664,14 +664,20 @@ __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
 
 // kCopyBlocksPerUnit blocks per copy unit, each moving up to kCopyBlockElems
 // elements of it (parts past a short unit's end return at once); to_flat
-// selects flatten (param -> flat) or unflatten (flat -> param).  Short,
-// many blocks stream fastest here, as for the reduce; the table keeps one
-// entry per 16K elements.
+// selects flatten (param -> flat) or unflatten (flat -> param).  The blocks
+// of one unit run on one XCD (workgroups are dealt to the XCDs round-robin,
+// so block b runs on XCD b % 8), where the unit's table entry is then an L2
+// hit for all but the first of them.  Units hold 4K elements: with many
+// short parameters, bigger units mostly spawn blocks that find no work.
 __global__ void __launch_bounds__(kCopyThreads)
-copy_units(const ddp_copy_unit *units, int64_t first, char *flat, int esize, int to_flat)
+copy_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, char *flat, int esize,
+           int to_flat)
 {
-    const ddp_copy_unit u = units[first + blockIdx.x / kCopyBlocksPerUnit];
-    const int64_t lo = (int64_t)(blockIdx.x % kCopyBlocksPerUnit) * kCopyBlockElems;
+    const int64_t m = blockIdx.x / kXcds;
+    const int64_t ui = (m / kCopyBlocksPerUnit) * kXcds + blockIdx.x % kXcds;
+    if (ui >= n_units) return;
+    const ddp_copy_unit u = units[first + ui];
+    const int64_t lo = (m % kCopyBlocksPerUnit) * kCopyBlockElems;
     if (lo >= u.count) return;
     const int64_t n = min(u.count - lo, kCopyBlockElems);
     char *pp = reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize;
@@ -1355,10 +1361,13 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
-    if ((last - first) * kCopyBlocksPerUnit > INT_MAX) return DDP_ERR_OVERFLOW;
-    copy_units<<<dim3((unsigned)((last - first) * kCopyBlocksPerUnit)), dim3(kCopyThreads),
-                 lds_for_blocks(kCopyBlocksPerCU), static_cast<hipStream_t>(stream)>>>(
-        bd->units, first, static_cast<char *>(flat), dtype_size(dtype), to_flat);
+    // every XCD gets the same number of units (the last round padded)
+    const int64_t blocks = (last - first + kXcds - 1) / kXcds * kXcds * kCopyBlocksPerUnit;
+    if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
+    copy_units<<<dim3((unsigned)blocks), dim3(kCopyThreads), lds_for_blocks(kCopyBlocksPerCU),
+                 static_cast<hipStream_t>(stream)>>>(bd->units, first, last - first,
+                                                      static_cast<char *>(flat), dtype_size(dtype),
+                                                      to_flat);
     return launched("copy kernel launch");
 }
 

@@ -115,6 +115,7 @@ int main(void)
 
     void *dout;
     CHECK_HIP(hipMalloc(&dout, sizeof(float) * P));
+    CHECK_DDP(ddp_plan_prepare_ranks(plan, N));   /* the RING table for N ranks, up front */
     for (int order = DDP_ORDER_SEQUENTIAL; order <= DDP_ORDER_RING; ++order) {
         /* whole synchronisation in one launch */
         CHECK_DDP(ddp_sync_allreduce_avg(plan, cflat, N, (ddp_order_t)order, DDP_F32, dout, NULL));
@@ -139,6 +140,13 @@ int main(void)
         }
         CHECK_HIP(hipMemcpy(got, dout, sizeof(float) * P, hipMemcpyDeviceToHost));
         if (!same_bits(got, want, sizeof(float) * P, "per-bucket")) return 1;
+        /* the occupancy policy changes timing only */
+        if (ddp_get_occupancy() != DDP_OCCUPANCY_TUNED) return 1;
+        CHECK_DDP(ddp_set_occupancy(DDP_OCCUPANCY_SHARED));
+        CHECK_DDP(ddp_sync_allreduce_avg(plan, cflat, N, (ddp_order_t)order, DDP_F32, dout, NULL));
+        CHECK_DDP(ddp_set_occupancy(DDP_OCCUPANCY_TUNED));
+        CHECK_HIP(hipMemcpy(got, dout, sizeof(float) * P, hipMemcpyDeviceToHost));
+        if (!same_bits(got, want, sizeof(float) * P, "sync, shared occupancy")) return 1;
     }
 
     /* unflatten the ring average into fresh parameter buffers */
@@ -190,6 +198,8 @@ int main(void)
     if (ddp_sync_allreduce_avg(plan, cflat, 0, DDP_ORDER_RING, DDP_F32, dout, NULL) !=
         DDP_ERR_INVALID_ARG)
         return 1;
+    if (ddp_plan_prepare_ranks(plan, DDP_MAX_RANKS + 1) != DDP_ERR_INVALID_ARG) return 1;
+    if (ddp_set_occupancy((ddp_occupancy_t)7) != DDP_ERR_INVALID_ARG) return 1;
 
     ddp_binding_free(rbind);
     for (int r = 0; r < N; ++r) ddp_binding_free(bind[r]);
