@@ -560,42 +560,58 @@ __global__ void __launch_bounds__(kThreads) accumulate_scalar(AccArgs a, int64_t
     if (i < len) acc_elem<DT>(a.dst[blockIdx.y], a.src[blockIdx.y], i);
 }
 
-// Any N up to DDP_MAX_RANKS: ranks walked in a loop.
+// Any N up to DDP_MAX_RANKS: ranks walked in the fold order, eight loads in
+// flight at a time.  A wave makes one pass per ring segment its lanes lie in
+// (usually one), so the rank order -- and every rank pointer -- is
+// wave-uniform: pointers come from scalar loads, and a short last group is
+// cut by a uniform branch rather than dummy loads.
 template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
+    constexpr int G = 8;
+    static_assert(kUnroll == 1, "one vector per lane");
     const int64_t tile = tile_of_block();
-    const int64_t tile0 = tile * (kThreads * kUnroll * VEC);
+    const int64_t tile0 = tile * (kThreads * VEC);
+    const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
     const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
+    const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
+    const bool in_b = RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+#pragma unroll 1
+    for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+        const bool mine = pass == 0 ? in_a : in_b;
+        if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
+        const int s = pass == 0 ? sg.sa : sg.sb;           // wave-uniform start rank
+        const int64_t off = mine ? i0 * ISZ : 0;           // other lanes re-read vector 0
+        float acc[VEC];
+#pragma unroll 1
+        for (int k0 = 0; k0 < N; k0 += G) {
+            u32x4 v[G];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t i0 = tile0 + ((int64_t)threadIdx.x + u * kThreads) * VEC;
-        const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
-        const bool in_b = RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
-        if (in_a || in_b) {
-            int r = in_a ? sg.sa : sg.sb;
-            float acc[VEC];
-            u32x4 w = ld_stream(static_cast<const char *>(ra.p[r]) + i0 * ISZ);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float x = lane<IN>(w, e);
-                acc[e] = RING ? x : 0.0f + x;
+            for (int j = 0; j < G; ++j) {
+                if (k0 + j < N) {
+                    int r = s + k0 + j;
+                    r = r >= N ? r - N : r;
+                    v[j] = ld_stream(static_cast<const char *>(ra.p[r]) + off);
+                }
             }
-#pragma unroll 4
-            for (int k = 1; k < N; ++k) {
-                r = wrap(r + 1, N);
-                w = ld_stream(static_cast<const char *>(ra.p[r]) + i0 * ISZ);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(w, e);
+            for (int j = 0; j < G; ++j) {
+                if (k0 + j < N) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float x = lane<IN>(v[j], e);
+                        acc[e] = k0 + j > 0 ? acc[e] + x : (RING ? x : 0.0f + x);
+                    }
+                }
             }
-            store_vec<IN, OUT>(out, i0, acc, inv);
-        } else if (i0 < total) {
-            reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
         }
+        if (mine) store_vec<IN, OUT>(out, i0, acc, inv);
     }
+    if (!in_a && !in_b && i0 < total)
+        reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
 }
 
 // One element per thread, element-aligned buffers of a single bucket.
@@ -725,11 +741,14 @@ int64_t tile_elems(int in) { return (int64_t)kThreads * kUnroll * vec_elems(in);
 // touch.  k was measured per kernel and rank count on ResNet-50, many-small,
 // GPT-1.3B and Llama-7B shapes; 0 means no cap.
 
-// Reduce, N = 2..8 (one 16-byte load per rank and lane, one store).
-int reduce_blocks_per_cu(int N)
+// Reduce, N = 2..8 (one 16-byte load per rank and lane, one store); the
+// looped kernel for N > 8.
+int reduce_blocks_per_cu(int N, bool ring)
 {
     static const int k[9] = {0, 0, 0, 16, 14, 12, 10, 9, 8};
-    return N >= 0 && N <= 8 ? k[N] : 0;
+    if (N < 0) return 0;
+    if (N <= 8) return k[N];
+    return N <= 11 ? (ring ? 12 : 10) : 8;
 }
 
 // Fused average + SGD step, N = 1..8 (also the parameter, momentum loads and
@@ -795,7 +814,7 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
         const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
         if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
         const dim3 g((unsigned)tiles), b(kThreads);
-        const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N));
+        const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N, RING));
         switch (N) {
         case 2: reduce_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
         case 3: reduce_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
@@ -804,7 +823,7 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
         case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
         case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
         case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        default: reduce_many<RING, IN, OUT><<<g, b, 0, st>>>(ra, N, total, bk, inv, out); break;
+        default: reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, bk, inv, out); break;
         }
     } else {
         const int64_t blocks = (total + kThreads - 1) / kThreads;
