@@ -230,8 +230,10 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
 __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 
 // Ring segments of tile `tile`, whose first element is tile0 (block-uniform
-// values): segment a holds the tile's first element, segment b follows it;
-// a vector inside neither takes the per-element path.  With a plan the
+// values): segment a holds the tile's first element, segment b follows it
+// (b_lo == a_hi; b is empty when a reaches the end).  A vector inside one of
+// them folds with that segment's start rank; any other takes the
+// per-element path.  With a plan the
 // segments come from one precomputed word per tile, so a wave makes a single
 // scalar load, issued while its vector loads are in flight:
 //   bits 0-5 start rank of a, 6-11 start rank of b,
@@ -263,8 +265,8 @@ __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int 
         s.a_lo = c * C;
         s.a_hi = min(s.a_lo + C, total);
         s.sa = (int)((c + 1) % N);
+        s.b_lo = s.b_hi = s.a_hi;
         if (s.a_hi < total) {
-            s.b_lo = s.a_hi;
             s.b_hi = min(s.b_lo + C, total);
             s.sb = (int)((c + 2) % N);
         }
@@ -296,26 +298,23 @@ __device__ __forceinline__ void fold_from(const u32x4 *v, float *acc)
         for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[(R + k) % NR], e);
 }
 
-// Rotation R behind its branch: the inputs pass through an empty volatile asm
-// inside the branch, so the adds cannot be hoisted above it.  Without this
-// the compiler evaluates all NR rotations and selects one: NR times the adds
-// and twice the registers.
+// Rotation R behind its branch: an empty volatile asm inside the branch
+// claims to rewrite the inputs (in place, so no copies stay live), so the adds
+// that read them cannot be hoisted above it.  Without this the compiler
+// evaluates all NR rotations and selects one: NR times the adds and twice the
+// registers.  The values are untouched.
 template <int NR, int IN, int R>
-__device__ __forceinline__ void fold_from_here(const u32x4 *v, float *acc)
+__device__ __forceinline__ void fold_from_here(u32x4 *v, float *acc)
 {
-    u32x4 w[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-        w[k] = v[k];
-        asm volatile("" : "+v"(w[k]));
-    }
-    fold_from<NR, IN, R>(w, acc);
+    for (int k = 0; k < NR; ++k) asm volatile("" : "+v"(v[k]));
+    fold_from<NR, IN, R>(v, acc);
 }
 
 // The same for a start rank s known at run time (wave-uniform): a branch
 // picks one of the NR compile-time rotations.
 template <int NR, int IN, int R = 0>
-__device__ __forceinline__ void fold_ring(const u32x4 *v, int s, float *acc)
+__device__ __forceinline__ void fold_ring(u32x4 *v, int s, float *acc)
 {
     if constexpr (R + 1 < NR) {
         if (s == R)
@@ -421,10 +420,8 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
             float acc[VEC];
             if (!RING)
                 fold_seq<NR, IN>(v[u], acc);
-            else if (in_a)
-                fold_ring<NR, IN>(v[u], sg.sa, acc);
             else
-                fold_ring<NR, IN>(v[u], sg.sb, acc);
+                fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
             store_vec<IN, OUT>(out, i0[u], acc, inv);
         } else if (i0[u] < total) {
             reduce_elems<IN, OUT, RING>(ra, NR, total, bk, first_bucket(bk, tile), inv, out,
@@ -473,10 +470,8 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
         float y[VEC];
         if (!RING || NR == 1)
             fold_seq<NR, IN>(v, y);
-        else if (in_a)
-            fold_ring<NR, IN>(v, sg.sa, y);
         else
-            fold_ring<NR, IN>(v, sg.sb, y);
+            fold_ring<NR, IN>(v, in_a ? sg.sa : sg.sb, y);
         if (NR > 1) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;
