@@ -12,18 +12,21 @@
 //
 // Layout and launch.  A block is one wave and owns a tile of 64 16-byte
 // vectors (256 f32 or 512 bf16 elements): each wave load is 1 KiB contiguous
-// per rank.  All N loads of a lane are issued before any add, so N * 16 bytes
-// per lane are in flight; loads and stores are non-temporal.  The path is
-// HBM-bound (0.22 flop/byte for FP32, N = 8): no LDS, no MFMA, no cross-lane
-// traffic.
+// per rank.  A lane issues its N loads (every rank at its own offset, in rank
+// order) before anything else, so N * 16 bytes per lane are in flight; loads
+// and stores are non-temporal.  Launches cap the resident blocks per CU with
+// an unused dynamic-LDS reservation (see "occupancy").  The path is HBM-bound
+// (0.22 flop/byte for FP32, N = 8): no LDS traffic, no MFMA, no cross-lane
+// work.
 //
 // Ring order.  Element i of a bucket [base, end) sits in chunk
 // c = (i - base) / C with C = ceil((end - base) / N) and starts its fold at
-// rank (c + 1) mod N.  A tile resolves (uniformly, in scalar registers) the
-// chunk segment holding its first element and the segment after it, and
-// keeps two rotated pointer sets; a vector wholly inside either segment
-// takes the vector path, a vector straddling a chunk or bucket boundary (at
-// most a few per bucket) and the ragged tail take a per-element path.
+// rank (c + 1) mod N.  While its loads are in flight a tile reads one
+// precomputed word naming the chunk segment holding its first element and
+// the segment after it (start ranks and in-tile ends); a lane whose vector
+// lies wholly inside either folds from registers in that segment's rotated
+// order, and a vector straddling a chunk or bucket boundary (at most a few
+// per bucket) or the ragged tail takes a per-element path.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -232,10 +235,10 @@ __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 // Ring segments of tile `tile`, whose first element is tile0 (block-uniform
 // values): segment a holds the tile's first element, segment b follows it
 // (b_lo == a_hi; b is empty when a reaches the end).  A vector inside one of
-// them folds with that segment's start rank; any other takes the
-// per-element path.  With a plan the
-// segments come from one precomputed word per tile, so a wave makes a single
-// scalar load, issued while its vector loads are in flight:
+// them folds with that segment's start rank; any other takes the per-element
+// path.  With a plan the segments come from one precomputed word per tile,
+// so a wave makes a single scalar load, issued while its vector loads are in
+// flight:
 //   bits 0-5 start rank of a, 6-11 start rank of b,
 //   12-21 end of a and 22-31 end of b, both relative to tile0.
 // A single bucket [0, total) is computed here.
@@ -311,8 +314,9 @@ __device__ __forceinline__ void fold_from_here(u32x4 *v, float *acc)
     fold_from<NR, IN, R>(v, acc);
 }
 
-// The same for a start rank s known at run time (wave-uniform): a branch
-// picks one of the NR compile-time rotations.
+// The same for a start rank s known at run time (one of the tile's two, so
+// at most two of the branches run): a branch picks one of the NR
+// compile-time rotations.
 template <int NR, int IN, int R = 0>
 __device__ __forceinline__ void fold_ring(u32x4 *v, int s, float *acc)
 {

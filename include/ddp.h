@@ -164,7 +164,9 @@ ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
  *                          of the element type flatten/unflatten are given.
  *                          Pointers must be at least 2-byte aligned.
  *   stream                 unused for now (the table upload is synchronous)
- * The binding copies the pointer array; it does not own the gradients.
+ * The binding copies the pointer array; it does not own the gradients.  It
+ * keeps a device table of 32 bytes per 4096 elements of each parameter
+ * (rounded up per parameter) until ddp_binding_free.
  * Errors: INVALID_ARG (null plan/array/out, a null pointer for a parameter
  * with numel > 0, misaligned pointer), HIP, NOMEM. */
 ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
