@@ -18,6 +18,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -37,8 +38,14 @@ def log(*a):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with comments and blank lines removed
+    and each line stripped, so that only a change of code invalidates the
+    counter data taken on it."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+    code = "\n".join(line for line in lines if line)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload, order, algorithmic_bytes):
