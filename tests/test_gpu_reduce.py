@@ -240,3 +240,40 @@ def test_prepared_sync_matches_direct_call(env):
         ddp.sync_allreduce_avg(lp, ts, b, order)
         torch.cuda.synchronize()
         assert_bits_equal(to_host(a, torch), to_host(b, torch), f"prepared {order}")
+
+
+def test_concurrent_first_use_of_ring_tables(env):
+    """Four host threads synchronise one fresh plan at the same time, each with
+    its own rank count and stream, so the per-rank-count RING tables are built
+    concurrently (under the plan's lock); every result matches the oracle."""
+    import threading
+    torch, ddp = env
+    rng = np.random.default_rng(44)
+    numel = [int(v) for v in rng.integers(1, 30000, 70)]
+    lp = ddp.plan_buckets(numel, 120 << 10)
+    op = oracle.plan_cap(numel, 120 << 10, 4)
+    xs = random_inputs(rng, 8, op.total, "f32")
+    ts = [to_dev(x, torch) for x in xs]
+    counts = (3, 5, 7, 8)
+    outs = {n: torch.empty(op.total, dtype=torch.float32, device="cuda:0") for n in counts}
+    streams = {n: torch.cuda.Stream() for n in counts}
+    torch.cuda.synchronize()
+    start, errors = threading.Barrier(len(counts)), []
+
+    def run(n):
+        try:
+            start.wait()
+            for _ in range(3):
+                ddp.sync_allreduce_avg(lp, ts[:n], outs[n], "ring", stream=streams[n])
+            streams[n].synchronize()
+        except Exception as e:   # reported below, in the main thread
+            errors.append((n, e))
+
+    threads = [threading.Thread(target=run, args=(n,)) for n in counts]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for n in counts:
+        assert_bits_equal(to_host(outs[n], torch), oracle.sync_avg(op, xs[:n], "ring"), f"N={n}")
