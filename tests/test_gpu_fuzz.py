@@ -111,3 +111,32 @@ def test_two_plans_on_two_streams(env):
     torch.cuda.synchronize()
     for lp, op, xs, ts, out, s in cases:
         assert_bits_equal(to_host(out, torch), oracle.sync_avg(op, xs, "ring"), "two streams")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_plans_many_ranks(env, seed):
+    """N = 9..64 (the looped kernel): tiny caps, so chunks are shorter than a
+    tile and most tiles meet two or more ring segments."""
+    torch, ddp = env
+    rng = np.random.default_rng(9000 + seed)
+    for case in range(4):
+        n = int(rng.integers(1, 60))
+        numel = [int(v) for v in rng.integers(0, 4000, n)]
+        N = int(rng.choice([9, 11, 12, 16, 23, 33, 64]))
+        in_dt, out_dt = PAIRS[int(rng.integers(0, 3))]
+        eb = 4 if in_dt == "f32" else 2
+        cap = int(rng.choice([64, 1000, 4096, 20000]))
+        lp = ddp.plan_buckets(numel, cap, in_dt)
+        op = oracle.plan_cap(numel, cap, eb)
+        P = op.total
+        tag = f"seed={seed} case={case} N={N} {in_dt}->{out_dt} cap={cap} P={P} B={op.n_buckets}"
+        print(tag, flush=True)
+        xs = random_inputs(rng, N, P, in_dt)
+        ts = [to_dev(x, torch) for x in xs]
+        odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+        out = torch.empty(P, dtype=odt, device="cuda:0")
+        for order in ("seq", "ring"):
+            ddp.sync_allreduce_avg(lp, ts, out, order)
+            torch.cuda.synchronize()
+            assert_bits_equal(to_host(out, torch), oracle.sync_avg(op, xs, order, in_dt, out_dt),
+                              "sync " + tag)
