@@ -484,7 +484,8 @@ def main():
     # ---------------------------------------------------------------- two-bucket overlap
     # The two-bucket plan of the same tensors: DEEP_COMM averaged on an update
     # stream while a GEMM (standing in for the first layer's backward) runs on
-    # a compute stream; exposed = overlapped time - compute time.
+    # a compute stream; exposed = overlapped time - compute time.  Steps are
+    # timed back to back with both streams joined at every step boundary.
     overlap = None
     if not args.no_overlap and wl.name == "resnet50":
         tb = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
@@ -502,15 +503,27 @@ def main():
         def deep():
             ddp.bucket_allreduce_avg(deep_in, deep_out, order, stream=upd)
 
+        def step_barrier():
+            # a training step ends when both streams have: the next step's
+            # backward needs the averaged gradients, and the next syncs the
+            # next step's gradients
+            e_comp, e_upd = torch.cuda.Event(), torch.cuda.Event()
+            e_comp.record(comp)
+            e_upd.record(upd)
+            comp.wait_event(e_upd)
+            upd.wait_event(e_comp)
+
         def timed(fns, reps=20):
             for _ in range(3):
                 for f in fns:
                     f()
+                step_barrier()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(reps):
                 for f in fns:
                     f()
+                step_barrier()
             torch.cuda.synchronize()
             return (time.perf_counter() - t0) * 1e3 / reps
 
@@ -528,6 +541,48 @@ def main():
                                "exposed_sync_ms": round(max(t_both - t_comp, 0.0), 4),
                                "hidden_fraction": round(1.0 - max(t_both - t_comp, 0.0) / t_deep, 3)}
         ddp.set_occupancy("tuned")
+
+        # The bucket-by-bucket schedule of DDP ([DDP] 3.2, [TR24] 十一): bucket b
+        # (cap plan, last layers first) is averaged on the update stream as
+        # soon as a stand-in for the backward of its layers -- a bf16 GEMM
+        # with FLOPs in proportion to the bucket's share of the parameters,
+        # about 262 GFLOP in all (ResNet-50's backward at 32 images per GPU)
+        # -- has finished on the compute stream.
+        buckets = [plan.bucket(b) for b in range(plan.n_buckets)]
+        ks = [max(64, int(round(7808 * ln / P / 64)) * 64) for ln, _, _, _ in buckets]
+        lhs = [torch.randn(4096, k, device=dev, dtype=torch.bfloat16) for k in ks]
+        rhs = [torch.randn(k, 4096, device=dev, dtype=torch.bfloat16) for k in ks]
+        ready = [torch.cuda.Event() for _ in buckets]
+        ins = [[f[base:base + ln] for f in flats] for ln, base, _, _ in buckets]
+        outs_b = [out[base:base + ln] for ln, base, _, _ in buckets]
+
+        def backward():
+            with torch.cuda.stream(comp):
+                for a, b, e in zip(lhs, rhs, ready):
+                    torch.mm(a, b)
+                    e.record(comp)
+
+        def bucket_syncs(wait):
+            for b in range(len(buckets)):
+                if wait:
+                    upd.wait_event(ready[b])
+                ddp.bucket_allreduce_avg(ins[b], outs_b[b], order, stream=upd)
+
+        t_bwd = timed([backward])
+        gflop = sum(2 * 4096 * k * 4096 for k in ks) / 1e9
+        overlap["schedule"] = {"buckets": len(buckets), "backward_gflop": round(gflop, 1),
+                               "backward_ms": round(t_bwd, 4)}
+        for policy in ("tuned", "shared"):
+            ddp.set_occupancy(policy)
+            t_syncs = timed([lambda: bucket_syncs(False)])
+            t_sched = timed([backward, lambda: bucket_syncs(True)])
+            overlap["schedule"][policy] = {
+                "syncs_ms": round(t_syncs, 4), "serial_ms": round(t_bwd + t_syncs, 4),
+                "overlapped_ms": round(t_sched, 4),
+                "exposed_sync_ms": round(max(t_sched - t_bwd, 0.0), 4),
+                "hidden_fraction": round(1.0 - max(t_sched - t_bwd, 0.0) / t_syncs, 3)}
+        ddp.set_occupancy("tuned")
+        del lhs, rhs
         log(f"overlap: {overlap}")
         del mat_a, mat_b, tb
 
