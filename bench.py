@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--no-in-place", action="store_true")
     ap.add_argument("--no-rank-sweep", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--no-per-bucket", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -198,6 +199,46 @@ def main():
     log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
         f"stream ({achieved:.0f} GB/s); single launches between events: median "
         f"{np.median(launch_ms) * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us")
+
+    # ---------------------------------------------------------------- one launch per bucket
+    # The same sync as DDP issues it, one all-reduce call per bucket
+    # (ddp_bucket_allreduce_avg on each bucket's sub-ranges): driven from
+    # Python, and replayed from a HIP graph that captured those launches.
+    # Against the one-launch sync this is the launch overhead it saves.
+    per_bucket = None
+    if not args.no_per_bucket and 1 < plan.n_buckets <= 4096 and P < 10 ** 9:
+        spans = [plan.bucket(b)[:2] for b in range(plan.n_buckets)]
+        ins_b = [[f[base:base + ln] for f in flats] for ln, base in spans]
+        outs_b = [out[base:base + ln] for ln, base in spans]
+        side = torch.cuda.Stream()
+
+        def per_bucket_sync():
+            for xs_b, o_b in zip(ins_b, outs_b):
+                ddp.bucket_allreduce_avg(xs_b, o_b, order, stream=side)
+
+        def timed_side(fn, reps):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / reps
+
+        reps = 20
+        eager_ms = timed_side(per_bucket_sync, reps)
+        graph = torch.cuda.CUDAGraph()
+        per_bucket_sync()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            per_bucket_sync()
+        graph_ms = timed_side(graph.replay, reps)
+        del graph
+        per_bucket = {"launches": plan.n_buckets, "python_loop_ms": round(eager_ms, 4),
+                      "graph_replay_ms": round(graph_ms, 4), "one_launch_ms": round(ms_per_step, 4),
+                      "one_launch_speedup_vs_graph": round(graph_ms / ms_per_step, 3)}
+        log(f"per-bucket launches: {per_bucket}")
 
     # ---------------------------------------------------------------- MALL flushed
     # The same sync with a 512 MiB scratch buffer overwritten before each one,
@@ -704,6 +745,7 @@ def main():
                      "kernel_ms_source": "event pair around the K timed launches, / K",
                      "single_launch_ms_median": round(float(np.median(launch_ms)), 5),
                      "single_launch_ms_min": round(min(launch_ms), 5)},
+        "per_bucket": per_bucket,
         "cold_mall": cold,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
