@@ -10,17 +10,29 @@ gradient-as-bucket-view layout), so flatten and unflatten are not needed in
 the step; the same run also times the copy layout (flatten every rank, sync,
 unflatten) and reports it under "copy_path".
 
-Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits.
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
+Besides the metric and its roofline, the line carries (each can be skipped
+with its --no-... flag):
+  other_orders   the other summation order
+  per_bucket     the same sync as one launch per bucket (loop and graph)
+  cold_mall      the sync with the MALL flushed before each one
+  ceiling        a probe of the reduce's bare access pattern
+  cpu_baseline   the CPU oracle (one thread, and SEQ on all host cores)
+  copy_path      flatten + sync + unflatten (eager and graph-replayed)
+  fused_sgd      the average fused into a momentum-SGD step
+  overlap        syncs beside compute on a second stream
+  rank_sweep_GBps, in_place, no_sync, env
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload resnet50|gpt1p3b|gpt1p3b_two_bucket|many_small|llama7b|tiny]
-                       [--order ring|seq] [--no-cpu-baseline] [--no-copy-path]
+                       [--order ring|seq] [--cpu-seconds S] [--no-<section> ...]
+       python bench.py --calibrate   (the plain-copy run that scales the HBM counters)
 """
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 

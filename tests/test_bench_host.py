@@ -1,0 +1,48 @@
+"""bench.py on the host (no GPU): the one-GPU guard and the kernel-code hash
+that keys the committed HBM counter data."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("_bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_exits_with_2():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
+    b = _bench()
+    src = open(b.KERNEL_SRC, encoding="utf-8").read()
+    base = b.kernel_source_sha()
+    edited = tmp_path / "k.hip"
+    edited.write_text("// a new comment\n\n" + src.replace("\n{\n", "\n{   /* note */\n", 1) + "\n\n")
+    b.KERNEL_SRC = str(edited)
+    assert b.kernel_source_sha() == base
+    edited.write_text(src.replace("kThreads = 64", "kThreads = 128", 1))
+    assert b.kernel_source_sha() != base
+
+
+def test_traffic_is_reported_only_for_the_hashed_code(tmp_path):
+    b = _bench()
+    import json
+    rec = {"resnet50/ring": {"kernel_source_sha": b.kernel_source_sha(), "hbm_bytes_per_launch": 123}}
+    f = tmp_path / "t.json"
+    f.write_text(json.dumps(rec))
+    b.TRAFFIC_FILE = str(f)
+    assert b.measured_traffic("resnet50", "ring", 1) == 123
+    assert b.measured_traffic("resnet50", "seq", 1) is None
+    rec["resnet50/ring"]["kernel_source_sha"] = "0" * 16
+    f.write_text(json.dumps(rec))
+    assert b.measured_traffic("resnet50", "ring", 1) is None
