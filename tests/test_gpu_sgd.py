@@ -3,13 +3,14 @@ against the oracle's synchronisation followed by its SGD step, bit for bit:
 parameters, momentum buffer and the stored average, for every rank count
 1..9 (9: per-element kernel), all dtype pairs, both orders, with and without
 momentum and average output, misaligned buffers, in-place average output,
-and the ResNet-50 and many-small workloads at full size."""
+the ResNet-50 and many-small workloads at full size, and Llama-7B (bf16
+gradients, 27 GB of f32 parameters) on sampled positions."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_bits_equal, random_inputs, to_dev, to_host, torch_cuda
+from gpu_util import assert_bits_equal, random_inputs, sample_positions, to_dev, to_host, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +137,44 @@ def test_fused_sgd_rejects_overlaps(env):
     with pytest.raises(ddp.DDPError) as ei:
         ddp.sync_sgd_update(lp, [a[:128], b], m[:128], 0.1, momentum_buf=m[64:192])
     assert ei.value.status == 4
+
+
+def test_fused_sgd_llama_sampled(env):
+    """The fused step at the Llama-7B size: bf16 gradients of 8 ranks, f32
+    parameters and momentum (27 GB each), two momentum steps in both orders,
+    checked on positions covering every bucket and ring-chunk edge plus
+    random ones."""
+    torch, ddp = env
+    wl = W.workload("llama7b")
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "bf16")
+    op = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, 2)
+    P = op.total
+    flats = []
+    for r in range(wl.n_ranks):
+        t = torch.empty(P, dtype=torch.bfloat16, device="cuda:0")
+        W.device_normal_(t, r, wl.stream, wl.sigma)
+        flats.append(t)
+    params = torch.empty(P, dtype=torch.float32, device="cuda:0")
+    mbuf = torch.empty(P, dtype=torch.float32, device="cuda:0")
+    rng = np.random.default_rng(71)
+    pos = sample_positions(op.bucket_base, op.bucket_len, wl.n_ranks, P, rng)
+    idx = torch.from_numpy(pos).to("cuda:0")
+    vals = np.stack([to_host(f.index_select(0, idx), torch) for f in flats], axis=1)
+    base = np.array(op.bucket_base, dtype=np.int64)
+    lens = np.array(op.bucket_len, dtype=np.int64)
+    b_of = np.searchsorted(base, pos, side="right") - 1
+    for order in ("seq", "ring"):
+        print(f"llama7b fused SGD {order}", flush=True)
+        W.device_normal_(params, 99, 7, 1.0)
+        mbuf.zero_()
+        wp = to_host(params.index_select(0, idx), torch).copy()
+        wm = np.zeros(pos.size, np.float32)
+        avg = oracle.sampled_avg(vals, pos - base[b_of], lens[b_of], order, "bf16", "bf16")
+        for _ in range(2):
+            ddp.sync_sgd_update(lp, flats, params, 0.1, order, momentum_buf=mbuf, momentum=0.9)
+            oracle.sgd_step(wp, avg, 0.1, "bf16", wm, 0.9)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_host(params.index_select(0, idx), torch), wp, f"llama7b {order} params")
+        assert_bits_equal(to_host(mbuf.index_select(0, idx), torch), wm, f"llama7b {order} momentum")
+    del flats, params, mbuf, idx
+    torch.cuda.empty_cache()
