@@ -347,6 +347,41 @@ __device__ __forceinline__ void fold_seq(const u32x4 *v, float *acc)
         for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[k], e);
 }
 
+// Any N up to DDP_MAX_RANKS: the ranks walked in the fold order starting at
+// the wave-uniform rank s, eight loads in flight at a time.  Every rank
+// pointer is a scalar load, and a short last group is cut by a uniform
+// branch rather than dummy loads.  Lanes not taking part pass off = 0 and
+// re-read vector 0.
+template <int IN, bool RING>
+__device__ __forceinline__ void fold_looped(const RankArgs &ra, int N, int s, int64_t off,
+                                            float *acc)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int G = 8;
+#pragma unroll 1
+    for (int k0 = 0; k0 < N; k0 += G) {
+        u32x4 v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (k0 + j < N) {
+                int r = s + k0 + j;
+                r = r >= N ? r - N : r;
+                v[j] = ld_stream(static_cast<const char *>(ra.p[r]) + off);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (k0 + j < N) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float x = lane<IN>(v[j], e);
+                    acc[e] = k0 + j > 0 ? acc[e] + x : (RING ? x : 0.0f + x);
+                }
+            }
+        }
+    }
+}
+
 // Convert and store one vector of scaled averages y at element i0; for a
 // bf16 output y is replaced by the stored value widened back to f32.
 template <int IN, int OUT>
@@ -434,6 +469,30 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
     }
 }
 
+// The vector epilogue of the fused step: store the average y (bf16: y
+// becomes the stored value widened back), then update the lane's parameter
+// vectors pv (and momentum mv), already loaded, in place.
+template <int IN, int OUT, bool MOM>
+__device__ __forceinline__ void sgd_vec(const SgdArgs &sa, int64_t i0, float *y, const u32x4 *pv,
+                                        const u32x4 *mv)
+{
+    constexpr int PV = (IN == kF32 ? 4 : 8) / 4;
+    store_y<IN, OUT>(sa.grad_out, i0, y, sa.grad_out != nullptr);
+#pragma unroll
+    for (int j = 0; j < PV; ++j) {
+        u32x4 po, mo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
+            po[w] = __float_as_uint(
+                sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, sa.lr, sa.mu));
+            mo[w] = __float_as_uint(m);
+        }
+        st_stream(sa.param + i0 + 4 * j, po);
+        if (MOM) st_stream(sa.mom + i0 + 4 * j, mo);
+    }
+}
+
 // Fused average + SGD step, N known at compile time (1..8).  Per lane: the N
 // gradient vectors and the lane's parameter (and momentum) vectors are loaded
 // together, the average is folded and scaled, optionally stored, and the
@@ -480,20 +539,7 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;
         }
-        store_y<IN, OUT>(sa.grad_out, i0, y, sa.grad_out != nullptr);
-#pragma unroll
-        for (int j = 0; j < PV; ++j) {
-            u32x4 po, mo;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
-                po[w] = __float_as_uint(
-                    sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, sa.lr, sa.mu));
-                mo[w] = __float_as_uint(m);
-            }
-            st_stream(sa.param + i0 + 4 * j, po);
-            if (MOM) st_stream(sa.mom + i0 + 4 * j, mo);
-        }
+        sgd_vec<IN, OUT, MOM>(sa, i0, y, pv, mv);
     } else if (i0 < total) {
         sgd_elems<IN, OUT, RING, MOM>(ra, NR, total, bk, first_bucket(bk, tile), inv, sa, i0, VEC);
     }
@@ -559,18 +605,15 @@ __global__ void __launch_bounds__(kThreads) accumulate_scalar(AccArgs a, int64_t
     if (i < len) acc_elem<DT>(a.dst[blockIdx.y], a.src[blockIdx.y], i);
 }
 
-// Any N up to DDP_MAX_RANKS: ranks walked in the fold order, eight loads in
-// flight at a time.  A wave makes one pass per ring segment its lanes lie in
-// (usually one), so the rank order -- and every rank pointer -- is
-// wave-uniform: pointers come from scalar loads, and a short last group is
-// cut by a uniform branch rather than dummy loads.
+// Any N up to DDP_MAX_RANKS.  A wave makes one pass per ring segment its
+// lanes lie in (usually one), so the rank order of each pass is
+// wave-uniform, and folds with fold_looped.
 template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    constexpr int G = 8;
     static_assert(kUnroll == 1, "one vector per lane");
     const int64_t tile = tile_of_block();
     const int64_t tile0 = tile * (kThreads * VEC);
@@ -582,35 +625,54 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
         const bool mine = pass == 0 ? in_a : in_b;
         if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
-        const int s = pass == 0 ? sg.sa : sg.sb;           // wave-uniform start rank
-        const int64_t off = mine ? i0 * ISZ : 0;           // other lanes re-read vector 0
         float acc[VEC];
-#pragma unroll 1
-        for (int k0 = 0; k0 < N; k0 += G) {
-            u32x4 v[G];
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                if (k0 + j < N) {
-                    int r = s + k0 + j;
-                    r = r >= N ? r - N : r;
-                    v[j] = ld_stream(static_cast<const char *>(ra.p[r]) + off);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                if (k0 + j < N) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const float x = lane<IN>(v[j], e);
-                        acc[e] = k0 + j > 0 ? acc[e] + x : (RING ? x : 0.0f + x);
-                    }
-                }
-            }
-        }
+        fold_looped<IN, RING>(ra, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
         if (mine) store_vec<IN, OUT>(out, i0, acc, inv);
     }
     if (!in_a && !in_b && i0 < total)
         reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
+}
+
+// The fused average + SGD step for any N up to DDP_MAX_RANKS: the lane's
+// parameter (and momentum) vectors are issued first, then the ranks are
+// folded as in reduce_many and the epilogue of reduce_sgd_fast applied.
+template <bool RING, int IN, int OUT, bool MOM>
+__global__ void __launch_bounds__(kThreads)
+reduce_sgd_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArgs sa)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    constexpr int PV = VEC / 4;
+    static_assert(kUnroll == 1, "one vector per lane");
+    const int64_t tile = tile_of_block();
+    const int64_t tile0 = tile * (kThreads * VEC);
+    const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
+    u32x4 pv[PV], mv[PV];
+    if (total >= VEC) {   // a lane past the end reads the first vectors and drops them
+        const int64_t po = i0 + VEC <= total ? i0 * 4 : 0;
+#pragma unroll
+        for (int j = 0; j < PV; ++j) {
+            pv[j] = ld_stream(reinterpret_cast<const char *>(sa.param) + po + 16 * j);
+            if (MOM) mv[j] = ld_stream(reinterpret_cast<const char *>(sa.mom) + po + 16 * j);
+        }
+    }
+    const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
+    const bool in_a = i0 >= sg.a_lo && i0 + VEC <= sg.a_hi;
+    const bool in_b = RING && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+#pragma unroll 1
+    for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+        const bool mine = pass == 0 ? in_a : in_b;
+        if (!__builtin_amdgcn_ballot_w64(mine)) continue;
+        float y[VEC];
+        fold_looped<IN, RING>(ra, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, y);
+        if (mine) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;
+            sgd_vec<IN, OUT, MOM>(sa, i0, y, pv, mv);
+        }
+    }
+    if (!in_a && !in_b && i0 < total)
+        sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, first_bucket(bk, tile), inv, sa, i0, VEC);
 }
 
 // One element per thread, element-aligned buffers of a single bucket.
@@ -751,12 +813,13 @@ int reduce_blocks_per_cu(int N, bool ring)
 }
 
 // Fused average + SGD step, N = 1..8 (also the parameter, momentum loads and
-// stores).
+// stores); the looped kernel for N > 8.
 int sgd_blocks_per_cu(int N, bool mom)
 {
     static const int with_mom[9] = {0, 20, 14, 10, 8, 8, 7, 7, 6};
     static const int without[9] = {0, 0, 0, 0, 0, 10, 8, 8, 8};
-    if (N < 0 || N > 8) return 0;
+    if (N < 0) return 0;
+    if (N > 8) return N <= 11 ? (mom ? 10 : 12) : 8;
     return mom ? with_mom[N] : without[N];
 }
 
@@ -867,7 +930,8 @@ ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Bu
         case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
         case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
         case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        default: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        case 8: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
+        default: reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, bk, inv, sa); break;
         }
     } else {
         const int64_t blocks = (total + kThreads - 1) / kThreads;
@@ -1215,14 +1279,14 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
     hipStream_t st = static_cast<hipStream_t>(stream);
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    bool vec_ok = n_ranks <= 8 && aligned(param_flat, 16) &&
+    bool vec_ok = aligned(param_flat, 16) &&
                   (!momentum_flat || aligned(momentum_flat, 16)) && (!grad_out || aligned(grad_out, 16));
     for (int r = 0; r < n_ranks; ++r) {
         ra.p[r] = rank_flat[r];
         vec_ok = vec_ok && aligned(rank_flat[r], 16);
     }
     if (!vec_ok) {
-        // element-aligned buffers or N > 8: one per-element launch per bucket
+        // element-aligned buffers: one per-element launch per bucket
         for (int32_t b = 0; b < plan->n_buckets(); ++b) {
             const int64_t base = plan->bucket_base[b], len = plan->bucket_base[b + 1] - base;
             if (len == 0) continue;

@@ -251,8 +251,9 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
  *   lr, momentum   learning rate and momentum factor (f32)
  * param_flat and momentum_flat may overlap no other buffer (DDP_ERR_ALIAS).
  * N == 1 takes the input as the average, bit for bit.  16-byte aligned
- * buffers and N <= 8 take the vector kernel, others a per-element kernel with
- * identical results.  Errors: as ddp_sync_allreduce_avg. */
+ * buffers take the vector kernels (N <= 8 unrolled, N > 8 looped), others a
+ * per-element kernel with identical results.
+ * Errors: as ddp_sync_allreduce_avg. */
 ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
                                  float *param_flat, float *momentum_flat, float lr,

@@ -1,7 +1,7 @@
 """GPU parity of ddp_sync_sgd_update (average folded into one SGD step)
 against the oracle's synchronisation followed by its SGD step, bit for bit:
 parameters, momentum buffer and the stored average, for every rank count
-1..9 (9: per-element kernel), all dtype pairs, both orders, with and without
+1..9, 13, 16, 40 and 64 (N > 8: the looped kernel), all dtype pairs, both orders, with and without
 momentum and average output, misaligned buffers, in-place average output,
 the ResNet-50 and many-small workloads at full size, and Llama-7B (bf16
 gradients, 27 GB of f32 parameters) on sampled positions."""
@@ -73,7 +73,7 @@ SIZES = [1000, 3, 77, 5000, 1, 2049, 300, 12345]
 
 
 # N = 1 has no dtype change (DDP_ERR_UNSUPPORTED), so f32->bf16 starts at N = 2
-CASES = [(N, pair) for N in range(1, 10)
+CASES = [(N, pair) for N in list(range(1, 10)) + [13, 16, 40, 64]
          for pair in (("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"))
          if not (N == 1 and pair[0] != pair[1])]
 
