@@ -76,8 +76,17 @@ struct Buckets {
     const uint32_t *tile_desc;    // ring segments of every tile (encoding at tile_segs,
                                   // layout at ring_tile_desc), or null for a single bucket
     int64_t desc_stride;          // tiles per XCD stripe of tile_desc
+    int64_t lo, hi;               // base == nullptr: the one bucket is [lo, hi) in the
+                                  // launch's element numbering (lo < 0 when the launch
+                                  // starts past the bucket's first elements)
     int32_t n_buckets;
 };
+
+// One bucket spanning [lo, hi) of a launch's elements.
+__host__ __device__ inline Buckets single_bucket(int64_t lo, int64_t hi)
+{
+    return {nullptr, nullptr, nullptr, 0, lo, hi, 1};
+}
 
 // Workgroups are dealt to the XCDs round-robin, so tile t runs on XCD t % 8.
 constexpr int kXcds = 8;
@@ -142,7 +151,7 @@ __device__ __forceinline__ int wrap(int r, int n) { return r >= n ? r - n : r; }
 __device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int64_t total, int N,
                                           int64_t i)
 {
-    int64_t base = 0, end = total;
+    int64_t base = bk.lo, end = bk.hi;
     if (bk.base) {
         int32_t b = b0;
         while (bk.base[b + 1] <= i) ++b;
@@ -232,6 +241,24 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
 // Tile processed by this block.
 __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 
+// A single bucket that starts before the launch's element 0 (lo < 0: its
+// first -lo elements sit just before the 16-byte boundary the vector path
+// starts at) gets one extra block in front of the grid, which reduces those
+// elements one per lane while the tiles stream; the tiles then start at
+// block 1.
+__device__ __forceinline__ bool has_head(const Buckets &bk) { return !bk.base && bk.lo < 0; }
+
+// Runs the head block's work; true in that block.
+template <int IN, int OUT, bool RING>
+__device__ __forceinline__ bool head_block(const RankArgs &ra, int N, int64_t total,
+                                           const Buckets &bk, float inv, void *out)
+{
+    if (!has_head(bk) || blockIdx.x != 0) return false;
+    if (threadIdx.x < -bk.lo)
+        reduce_elems<IN, OUT, RING>(ra, N, total, bk, 0, inv, out, bk.lo + threadIdx.x, 1);
+    return true;
+}
+
 // Ring segments of tile `tile`, whose first element is tile0 (block-uniform
 // values): segment a holds the tile's first element, segment b follows it
 // (b_lo == a_hi; b is empty when a reaches the end).  A vector inside one of
@@ -241,7 +268,7 @@ __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 // flight:
 //   bits 0-5 start rank of a, 6-11 start rank of b,
 //   12-21 end of a and 22-31 end of b, both relative to tile0.
-// A single bucket [0, total) is computed here.
+// A single bucket [lo, hi) is computed here.
 template <bool RING>
 __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int N, int64_t tile,
                                           int64_t tile0)
@@ -263,14 +290,14 @@ __device__ __forceinline__ Segs tile_segs(const Buckets &bk, int64_t total, int 
         s.b_lo = s.a_hi;
         s.b_hi = tile0 + (int64_t)(d >> 22);
     } else {
-        const int64_t C = (total + N - 1) / N;
-        const int64_t c = tile0 / C;
-        s.a_lo = c * C;
-        s.a_hi = min(s.a_lo + C, total);
+        const int64_t C = (bk.hi - bk.lo + N - 1) / N;
+        const int64_t c = (tile0 - bk.lo) / C;
+        s.a_lo = bk.lo + c * C;
+        s.a_hi = min(s.a_lo + C, bk.hi);
         s.sa = (int)((c + 1) % N);
         s.b_lo = s.b_hi = s.a_hi;
-        if (s.a_hi < total) {
-            s.b_hi = min(s.b_lo + C, total);
+        if (s.a_hi < bk.hi) {
+            s.b_hi = min(s.b_lo + C, bk.hi);
             s.sb = (int)((c + 2) % N);
         }
     }
@@ -428,7 +455,8 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    const int64_t tile = tile_of_block();
+    if (head_block<IN, OUT, RING>(ra, NR, total, bk, inv, out)) return;
+    const int64_t tile = tile_of_block() - (has_head(bk) ? 1 : 0);
     const int64_t tile0 = tile * (kThreads * kUnroll * VEC);
 
     // Every rank's vector at the lane's offset, in rank order, in either
@@ -549,12 +577,11 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
 // of a single bucket, any N.
 template <bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
-reduce_sgd_scalar(RankArgs ra, int N, int64_t total, float inv, SgdArgs sa)
+reduce_sgd_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArgs sa)
 {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= total) return;
-    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-    sgd_elems<IN, OUT, RING, MOM>(ra, N, total, single, 0, inv, sa, i, 1);
+    sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, 0, inv, sa, i, 1);
 }
 
 // ---------------------------------------------------------------- accumulate
@@ -615,7 +642,8 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     static_assert(kUnroll == 1, "one vector per lane");
-    const int64_t tile = tile_of_block();
+    if (head_block<IN, OUT, RING>(ra, N, total, bk, inv, out)) return;
+    const int64_t tile = tile_of_block() - (has_head(bk) ? 1 : 0);
     const int64_t tile0 = tile * (kThreads * VEC);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
     const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
@@ -675,15 +703,15 @@ reduce_sgd_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArg
         sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, first_bucket(bk, tile), inv, sa, i0, VEC);
 }
 
-// One element per thread, element-aligned buffers of a single bucket.
+// One element per thread, element-aligned buffers: elements [0, total) of
+// the single bucket bk.
 template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
-reduce_scalar(RankArgs ra, int N, int64_t total, float inv, void *out)
+reduce_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
 {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= total) return;
-    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-    reduce_elems<IN, OUT, RING>(ra, N, total, single, 0, inv, out, i, 1);
+    reduce_elems<IN, OUT, RING>(ra, N, total, bk, 0, inv, out, i, 1);
 }
 
 // ---------------------------------------------------------------- copies
@@ -873,7 +901,8 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
                           void *out, hipStream_t st, bool vec_ok)
 {
     if (vec_ok) {
-        const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
+        const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN) +
+                              (!bk.base && bk.lo < 0 ? 1 : 0);   // + the head block
         if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
         const dim3 g((unsigned)tiles), b(kThreads);
         const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N, RING));
@@ -891,7 +920,7 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
         const int64_t blocks = (total + kThreads - 1) / kThreads;
         if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
         reduce_scalar<RING, IN, OUT><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
-            ra, N, total, inv, out);
+            ra, N, total, bk, inv, out);
     }
     return launched("reduce kernel launch");
 }
@@ -909,6 +938,48 @@ ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, 
                     : launch_typed<false, kBF16, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
     return ring ? launch_typed<true, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok)
                 : launch_typed<false, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
+}
+
+// One bucket of len elements.  The vector kernel wants its inputs 16-byte
+// aligned (the vector width) and streams best from 128-byte aligned tiles
+// (an L2 line: a misaligned 1 KiB wave load touches 9 lines instead of 8).
+// When every rank buffer sits at the same offset from a 128-byte boundary
+// -- a bucket at an unpadded offset into equally aligned flat buffers -- the
+// vector path starts at the next boundary, h elements in, and numbers the
+// bucket [-h, len - h) so that the ring chunks stay those of the whole
+// bucket; the launch's extra head block reduces the first h elements one by
+// one.  Sharing only the offset from a 16-byte boundary, it starts at the
+// next 16-byte boundary instead.  Otherwise the per-element kernel takes it
+// all.  The output must be aligned for the vector stores at the same point.
+ddp_status_t launch_one_bucket(const RankArgs &ra, int N, int64_t len, int order, int in,
+                               int out_dt, void *out, hipStream_t st)
+{
+    const int isz = dtype_size(in), osz = dtype_size(out_dt);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(ra.p[0]);
+    bool same128 = true, same16 = a0 % isz == 0;
+    for (int r = 1; r < N; ++r) {
+        const uintptr_t ar = reinterpret_cast<uintptr_t>(ra.p[r]);
+        same128 = same128 && ar % 128 == a0 % 128;
+        same16 = same16 && ar % 16 == a0 % 16;
+    }
+    const int64_t store_bytes = vec_elems(in) * osz;   // one lane's store: 16 or 8 bytes
+    const uintptr_t ao = reinterpret_cast<uintptr_t>(out);
+    int64_t h = -1;
+    for (const uintptr_t line : {uintptr_t(128), uintptr_t(16)}) {
+        if (!same16 || (line == 128 && !same128)) continue;
+        const int64_t hh = (int64_t)((line - a0 % line) % line) / isz;
+        if (hh < len && hh < kThreads && (ao + hh * osz) % store_bytes == 0) {
+            h = hh;
+            break;
+        }
+    }
+    if (h < 0)
+        return launch_reduce(ra, N, len, order, in, out_dt, single_bucket(0, len), out, st, false);
+    RankArgs rest;
+    std::memset(&rest, 0, sizeof(rest));
+    for (int r = 0; r < N; ++r) rest.p[r] = static_cast<const char *>(ra.p[r]) + h * isz;
+    return launch_reduce(rest, N, len - h, order, in, out_dt, single_bucket(-h, len - h),
+                         static_cast<char *>(out) + h * osz, st, true);
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -937,7 +1008,7 @@ ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Bu
         const int64_t blocks = (total + kThreads - 1) / kThreads;
         if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
         reduce_sgd_scalar<RING, IN, OUT, MOM><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
-            ra, N, total, inv, sa);
+            ra, N, total, bk, inv, sa);
     }
     return launched("fused SGD kernel launch");
 }
@@ -1126,7 +1197,8 @@ ddp_status_t ring_buckets(ddp_plan *plan, int in, int n_ranks, Buckets *bk)
     if (st != DDP_OK) return st;
     const uint32_t *desc = nullptr;
     if ((st = ring_tile_desc(plan, tile_elems(in), n_ranks, &desc)) != DDP_OK) return st;
-    *bk = {t->bucket_base, t->tile_bucket, desc, desc_stride(t->n_tiles), plan->n_buckets()};
+    *bk = {t->bucket_base, t->tile_bucket, desc, desc_stride(t->n_tiles), 0, plan->total,
+           plan->n_buckets()};
     return DDP_OK;
 }
 
@@ -1170,8 +1242,7 @@ ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ra
         ra.p[r] = rank_ptrs[r];
         vec_ok = vec_ok && aligned(rank_ptrs[r], 16);
     }
-    const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-    return launch_reduce(ra, n_ranks, len, order, in_dtype, out_dtype, single, out, st, vec_ok);
+    return launch_one_bucket(ra, n_ranks, len, order, in_dtype, out_dtype, out, st);
 }
 
 ddp_status_t ddp_plan_prepare(ddp_plan_t *plan)
@@ -1231,17 +1302,16 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
             std::memset(&sub, 0, sizeof(sub));
             for (int r = 0; r < n_ranks; ++r)
                 sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
-            const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-            ddp_status_t s2 = launch_reduce(sub, n_ranks, len, order, in, out_dtype, single,
-                                            static_cast<char *>(out_flat) + base * osz, st, false);
+            ddp_status_t s2 = launch_one_bucket(sub, n_ranks, len, order, in, out_dtype,
+                                                static_cast<char *>(out_flat) + base * osz, st);
             if (s2 != DDP_OK) return s2;
         }
         return DDP_OK;
     }
     if (order == DDP_ORDER_SEQUENTIAL) {
         // the sequential fold does not depend on bucket boundaries
-        const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-        return launch_reduce(ra, n_ranks, total, order, in, out_dtype, single, out_flat, st, true);
+        return launch_reduce(ra, n_ranks, total, order, in, out_dtype, single_bucket(0, total),
+                             out_flat, st, true);
     }
     Buckets bk;
     if ((stc = ring_buckets(plan, in, n_ranks, &bk)) != DDP_OK) return stc;
@@ -1297,8 +1367,8 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
             SgdArgs sa = {param_flat + base, momentum_flat ? momentum_flat + base : nullptr,
                           grad_out ? static_cast<char *>(grad_out) + base * osz : nullptr, lr,
                           momentum};
-            const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-            ddp_status_t s2 = launch_sgd(sub, n_ranks, len, order, in, out_dtype, single, sa, st, false);
+            ddp_status_t s2 = launch_sgd(sub, n_ranks, len, order, in, out_dtype,
+                                         single_bucket(0, len), sa, st, false);
             if (s2 != DDP_OK) return s2;
         }
         return DDP_OK;
@@ -1306,8 +1376,8 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
     const SgdArgs sa = {param_flat, momentum_flat, grad_out, lr, momentum};
     if (order == DDP_ORDER_SEQUENTIAL || n_ranks == 1) {
         // neither depends on bucket boundaries (one rank: the input itself)
-        const Buckets single = {nullptr, nullptr, nullptr, 0, 1};
-        return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single, sa, st, true);
+        return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single_bucket(0, total), sa, st,
+                          true);
     }
     Buckets bk;
     if ((stc = ring_buckets(plan, in, n_ranks, &bk)) != DDP_OK) return stc;

@@ -115,6 +115,51 @@ def test_misaligned_buffers_take_the_element_path(env, pair, order):
     assert_bits_equal(got, oracle.bucket_avg(xs, order, in_dt, out_dt), "misaligned")
 
 
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}-{p[1]}")
+@pytest.mark.parametrize("order", ORDERS)
+def test_shared_misalignment_peels_the_head(env, pair, order):
+    """Every rank buffer and the output start the same number of elements past
+    a 16-byte boundary (a bucket at an unpadded offset of equally aligned
+    flat buffers): the head goes element-wise, the rest to the vector
+    kernel, and ring chunks stay those of the whole bucket."""
+    torch, ddp = env
+    in_dt, out_dt = pair
+    rng = np.random.default_rng(6)
+    vec = 4 if in_dt == "f32" else 8
+    tdt = torch.float32 if in_dt == "f32" else torch.bfloat16
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    for N in (2, 3, 8, 12):
+        for off in range(1, vec):
+            for L in (1, vec - off, vec, 257, 4099, 70001):
+                xs = random_inputs(rng, N, L, in_dt)
+                ts = []
+                for x in xs:
+                    big = torch.empty(L + 16, dtype=tdt, device="cuda:0")
+                    big[off:off + L].copy_(to_dev(x, torch))
+                    ts.append(big[off:off + L])
+                obig = torch.empty(L + 16, dtype=odt, device="cuda:0")
+                tag = f"N={N} off={off} L={L}"
+                got, _ = _run(env, xs, order, in_dt, out_dt, out=obig[off:off + L], rank_tensors=ts)
+                want = oracle.bucket_avg(xs, order, in_dt, out_dt)
+                assert_bits_equal(got, want, tag)
+                if in_dt == out_dt:   # in place into rank 0's buffer
+                    ddp.bucket_allreduce_avg(ts, ts[0], order)
+                    torch.cuda.synchronize()
+                    assert_bits_equal(to_host(ts[0], torch), want, "in place " + tag)
+            # the same offset from a 16-byte boundary, different ones from a 128-byte one
+            L = 30011
+            xs = random_inputs(rng, N, L, in_dt)
+            ts = []
+            for r, x in enumerate(xs):
+                o = (r * vec) % 64 + 1
+                big = torch.empty(L + 80, dtype=tdt, device="cuda:0")
+                big[o:o + L].copy_(to_dev(x, torch))
+                ts.append(big[o:o + L])
+            obig = torch.empty(L + 16, dtype=odt, device="cuda:0")
+            got, _ = _run(env, xs, order, in_dt, out_dt, out=obig[1:1 + L], rank_tensors=ts)
+            assert_bits_equal(got, oracle.bucket_avg(xs, order, in_dt, out_dt), f"N={N} mixed")
+
+
 @pytest.mark.parametrize("order", ORDERS)
 @pytest.mark.parametrize("k", [0, 3])
 def test_in_place_output(env, order, k):
