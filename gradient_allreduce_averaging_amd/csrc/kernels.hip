@@ -242,21 +242,18 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
 __device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
 
 // A single bucket that starts before the launch's element 0 (lo < 0: its
-// first -lo elements sit just before the 16-byte boundary the vector path
-// starts at) gets one extra block in front of the grid, which reduces those
-// elements one per lane while the tiles stream; the tiles then start at
-// block 1.
-__device__ __forceinline__ bool has_head(const Buckets &bk) { return !bk.base && bk.lo < 0; }
-
-// Runs the head block's work; true in that block.
+// first -lo elements sit just before the aligned address the vector path
+// starts at) gets one extra block at the end of the grid.  Its tile lies past
+// the end, so the vector path finds no work there (its loads read the dummy
+// vector), and this reduces the head elements one per lane.  The check comes
+// after the vector path, so no other block waits on it before its loads.
 template <int IN, int OUT, bool RING>
-__device__ __forceinline__ bool head_block(const RankArgs &ra, int N, int64_t total,
+__device__ __forceinline__ void head_block(const RankArgs &ra, int N, int64_t total,
                                            const Buckets &bk, float inv, void *out)
 {
-    if (!has_head(bk) || blockIdx.x != 0) return false;
+    if (bk.base || bk.lo >= 0 || blockIdx.x != gridDim.x - 1) return;
     if (threadIdx.x < -bk.lo)
         reduce_elems<IN, OUT, RING>(ra, N, total, bk, 0, inv, out, bk.lo + threadIdx.x, 1);
-    return true;
 }
 
 // Ring segments of tile `tile`, whose first element is tile0 (block-uniform
@@ -455,8 +452,7 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    if (head_block<IN, OUT, RING>(ra, NR, total, bk, inv, out)) return;
-    const int64_t tile = tile_of_block() - (has_head(bk) ? 1 : 0);
+    const int64_t tile = tile_of_block();
     const int64_t tile0 = tile * (kThreads * kUnroll * VEC);
 
     // Every rank's vector at the lane's offset, in rank order, in either
@@ -495,6 +491,7 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
                                             i0[u], VEC);
         }
     }
+    head_block<IN, OUT, RING>(ra, NR, total, bk, inv, out);
 }
 
 // The vector epilogue of the fused step: store the average y (bf16: y
@@ -642,8 +639,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     static_assert(kUnroll == 1, "one vector per lane");
-    if (head_block<IN, OUT, RING>(ra, N, total, bk, inv, out)) return;
-    const int64_t tile = tile_of_block() - (has_head(bk) ? 1 : 0);
+    const int64_t tile = tile_of_block();
     const int64_t tile0 = tile * (kThreads * VEC);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
     const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
@@ -659,6 +655,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     }
     if (!in_a && !in_b && i0 < total)
         reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
+    head_block<IN, OUT, RING>(ra, N, total, bk, inv, out);
 }
 
 // The fused average + SGD step for any N up to DDP_MAX_RANKS: the lane's
