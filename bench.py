@@ -41,7 +41,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "effective HBM GB/s (N·P·bytes read + P written) and % of peak per sync"
-KERNEL_SRC = os.path.join(ROOT, "gradient_allreduce_averaging_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "gradient_allreduce_averaging_amd", "csrc")
+# the library's device and launch code: every kernel source and header but the
+# benchmark's own probe
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                        if f.endswith((".hip", ".h")) and f != "probe.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -50,14 +54,16 @@ def log(*a):
 
 
 def kernel_source_sha():
-    """sha256[:16] of the kernel source with comments and blank lines removed
-    and each line stripped, so that only a change of code invalidates the
-    counter data taken on it."""
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
-    code = "\n".join(line for line in lines if line)
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    """sha256[:16] of the kernel sources (in name order) with comments and
+    blank lines removed and each line stripped, so that only a change of code
+    invalidates the counter data taken on it."""
+    code = []
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+        code.append(os.path.basename(path) + "\n" + "\n".join(line for line in lines if line))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload, order, algorithmic_bytes):

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libddp.so")
-SOURCES = ["plan.cpp", "kernels.hip"]
+SOURCES = ["plan.cpp", "common.hip", "reduce.hip", "accumulate.hip", "copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,7 +46,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        cmd = [HIPCC] + COMMON + ["-c", path, "-o", obj]
+        # hidden visibility: only the DDP_API declarations of ddp.h are exported
+        cmd = [HIPCC] + COMMON + ["-fvisibility=hidden", "-c", path, "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"] + DEVICE
         if verbose:

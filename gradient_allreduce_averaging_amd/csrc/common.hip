@@ -1,0 +1,113 @@
+// Host-side helpers shared by libddp's launch code (declared in host.h),
+// and the entry points for the occupancy policy and error text.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+
+#include "host.h"
+
+namespace ddp_detail {
+
+thread_local char g_last_error[256] = "";
+
+ddp_status_t hip_fail(const char *what, hipError_t e, ddp_status_t st)
+{
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return st;
+}
+
+ddp_status_t launched(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DDP_OK : hip_fail(what, e);
+}
+
+// ---------------------------------------------------------------- occupancy
+// These streaming kernels move the most bytes per second on gfx950 with fewer
+// resident blocks per CU than registers alone would allow (up to 32 of these
+// one-wave blocks): past a point, more concurrent waves only open more DRAM
+// rows at once.  Each launch is therefore capped at k resident blocks per CU
+// by asking for LDS_per_CU / k bytes of dynamic LDS, which the kernels do not
+// touch.  k was measured per kernel and rank count on ResNet-50, many-small,
+// GPT-1.3B and Llama-7B shapes; 0 means no cap.
+
+// Reduce, N = 2..8 (one 16-byte load per rank and lane, one store); the
+// looped kernel for N > 8.
+int reduce_blocks_per_cu(int N, bool ring)
+{
+    static const int k[9] = {0, 0, 0, 16, 14, 12, 10, 9, 8};
+    if (N < 0) return 0;
+    if (N <= 8) return k[N];
+    return N <= 11 ? (ring ? 12 : 10) : 8;
+}
+
+// Fused average + SGD step, N = 1..8 (also the parameter, momentum loads and
+// stores); the looped kernel for N > 8.
+int sgd_blocks_per_cu(int N, bool mom)
+{
+    static const int with_mom[9] = {0, 20, 14, 10, 8, 8, 7, 7, 6};
+    static const int without[9] = {0, 0, 0, 0, 0, 10, 8, 8, 8};
+    if (N < 0) return 0;
+    if (N > 8) return N <= 11 ? (mom ? 10 : 12) : 8;
+    return mom ? with_mom[N] : without[N];
+}
+
+constexpr int kMaxDevices = 64;
+
+// DDP_OCCUPANCY_TUNED or DDP_OCCUPANCY_SHARED, process-wide.
+std::atomic<int> g_occupancy{DDP_OCCUPANCY_TUNED};
+
+// Dynamic LDS bytes that leave room for k blocks per CU on the current device
+// (none under DDP_OCCUPANCY_SHARED).
+unsigned lds_for_blocks(int k)
+{
+    static std::atomic<int> lds_per_cu[kMaxDevices];   // 0: not queried yet, -1: unknown
+    if (k <= 0 || g_occupancy.load(std::memory_order_relaxed) != DDP_OCCUPANCY_TUNED) return 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            v <= 0)
+            v = -1;
+        lds_per_cu[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? (unsigned)(v / k) : 0;
+}
+
+// Output may be exactly one input (same dtype) or disjoint from all of them.
+ddp_status_t check_alias(const void *const *in, int n, int64_t len, int isz, const void *out,
+                         int osz)
+{
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out);
+    for (int r = 0; r < n; ++r) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(in[r]);
+        if (x == o && isz == osz) continue;
+        if (overlaps(x, len * isz, o, len * osz)) return DDP_ERR_ALIAS;
+    }
+    return DDP_OK;
+}
+
+}  // namespace ddp_detail
+
+using namespace ddp_detail;
+
+extern "C" {
+
+ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy)
+{
+    if (policy != DDP_OCCUPANCY_TUNED && policy != DDP_OCCUPANCY_SHARED) return DDP_ERR_INVALID_ARG;
+    g_occupancy.store(policy, std::memory_order_relaxed);
+    return DDP_OK;
+}
+
+ddp_occupancy_t ddp_get_occupancy(void)
+{
+    return static_cast<ddp_occupancy_t>(g_occupancy.load(std::memory_order_relaxed));
+}
+
+const char *ddp_last_error(void) { return g_last_error; }
+
+}  // extern "C"

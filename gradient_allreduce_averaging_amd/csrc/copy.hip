@@ -1,0 +1,209 @@
+// Flatten and unflatten: per-parameter gradients <-> flat bucket buffers
+// (ddp_bind_params, ddp_flatten, ddp_unflatten).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <new>
+#include <vector>
+
+#include "host.h"
+#include "internal.h"
+
+using namespace ddp_detail;
+
+namespace {
+
+// ---------------------------------------------------------------- copies
+
+__device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, int64_t hi)
+{
+    for (int64_t j = lo + 2 * (int64_t)threadIdx.x; j < hi; j += 2 * kCopyThreads)
+        *reinterpret_cast<uint16_t *>(dst + j) = *reinterpret_cast<const uint16_t *>(src + j);
+}
+
+// Block-wide copy of nbytes (a multiple of 2) between 2-byte aligned addresses.
+__device__ void block_copy(char *dst, const char *src, int64_t nbytes)
+{
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src);
+    const int tid = threadIdx.x;
+    if (((d ^ s) & 15) == 0) {
+        const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
+        copy16b(dst, src, 0, head);
+        const int64_t nvec = (nbytes - head) >> 4;
+        const u32x4 *sv = reinterpret_cast<const u32x4 *>(src + head);
+        u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+        int64_t j = tid;
+        for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {   // both loads before the stores
+            const u32x4 a = __builtin_nontemporal_load(sv + j);
+            const u32x4 b = __builtin_nontemporal_load(sv + j + kCopyThreads);
+            __builtin_nontemporal_store(a, dv + j);
+            __builtin_nontemporal_store(b, dv + j + kCopyThreads);
+        }
+        for (; j < nvec; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sv + j), dv + j);
+        copy16b(dst, src, head + (nvec << 4), nbytes);
+    } else if (((d ^ s) & 3) == 0) {
+        const int64_t head = min<int64_t>((4 - (d & 3)) & 3, nbytes);
+        copy16b(dst, src, 0, head);
+        const int64_t nw = (nbytes - head) >> 2;
+        const uint32_t *sw = reinterpret_cast<const uint32_t *>(src + head);
+        uint32_t *dw = reinterpret_cast<uint32_t *>(dst + head);
+        int64_t j = tid;
+        for (; j + 3 * kCopyThreads < nw; j += 4 * kCopyThreads) {
+            const uint32_t a = __builtin_nontemporal_load(sw + j);
+            const uint32_t b = __builtin_nontemporal_load(sw + j + kCopyThreads);
+            const uint32_t c = __builtin_nontemporal_load(sw + j + 2 * kCopyThreads);
+            const uint32_t e = __builtin_nontemporal_load(sw + j + 3 * kCopyThreads);
+            __builtin_nontemporal_store(a, dw + j);
+            __builtin_nontemporal_store(b, dw + j + kCopyThreads);
+            __builtin_nontemporal_store(c, dw + j + 2 * kCopyThreads);
+            __builtin_nontemporal_store(e, dw + j + 3 * kCopyThreads);
+        }
+        for (; j < nw; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sw + j), dw + j);
+        copy16b(dst, src, head + (nw << 2), nbytes);
+    } else {
+        copy16b(dst, src, 0, nbytes);
+    }
+}
+
+// kCopyBlocksPerUnit blocks per copy unit, each moving up to kCopyBlockElems
+// elements of it (parts past a short unit's end return at once); to_flat
+// selects flatten (param -> flat) or unflatten (flat -> param).  The blocks
+// of one unit run on one XCD (workgroups are dealt to the XCDs round-robin,
+// so block b runs on XCD b % 8), where the unit's table entry is then an L2
+// hit for all but the first of them.  Units hold 4K elements: with many
+// short parameters, bigger units mostly spawn blocks that find no work.
+__global__ void __launch_bounds__(kCopyThreads)
+copy_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, char *flat, int esize,
+           int to_flat)
+{
+    const int64_t m = blockIdx.x / kXcds;
+    const int64_t ui = (m / kCopyBlocksPerUnit) * kXcds + blockIdx.x % kXcds;
+    if (ui >= n_units) return;
+    const ddp_copy_unit u = units[first + ui];
+    const int64_t lo = (m % kCopyBlocksPerUnit) * kCopyBlockElems;
+    if (lo >= u.count) return;
+    const int64_t n = min(u.count - lo, kCopyBlockElems);
+    char *pp = reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize;
+    char *fp = flat + (u.flat_elem + lo) * esize;
+    const int64_t nbytes = n * esize;
+    if (to_flat)
+        block_copy(fp, pp, nbytes);
+    else
+        block_copy(pp, fp, nbytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, void *stream,
+                             ddp_binding_t **out)
+{
+    (void)stream;
+    if (!plan || !param_grads || !out) return DDP_ERR_INVALID_ARG;
+    for (int32_t p = 0; p < plan->n_params; ++p) {
+        if (plan->numel[p] > 0 && !param_grads[p]) return DDP_ERR_INVALID_ARG;
+        if (!aligned(param_grads[p], 2)) return DDP_ERR_INVALID_ARG;
+    }
+    ddp_binding *bd = new (std::nothrow) ddp_binding();
+    if (!bd) return DDP_ERR_NOMEM;
+    bd->plan = plan;
+    hipError_t e = hipGetDevice(&bd->device);
+    if (e != hipSuccess) {
+        delete bd;
+        return hip_fail("hipGetDevice", e);
+    }
+    std::vector<ddp_copy_unit> units;
+    try {
+        const int32_t nb = plan->n_buckets();
+        bd->bucket_first_unit.resize((size_t)nb + 1);
+        for (int32_t b = 0; b < nb; ++b) {
+            bd->bucket_first_unit[b] = (int64_t)units.size();
+            int64_t flat = plan->bucket_base[b];
+            for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
+                const int32_t p = plan->slot_param[s];
+                const int64_t n = plan->numel[p];
+                for (int64_t off = 0; off < n; off += kCopyUnitElems) {
+                    ddp_copy_unit u;
+                    u.param_addr = reinterpret_cast<uint64_t>(param_grads[p]);
+                    u.param_elem = off;
+                    u.flat_elem = flat + off;
+                    u.count = std::min<int64_t>(kCopyUnitElems, n - off);
+                    units.push_back(u);
+                }
+                flat += n;
+            }
+        }
+        bd->bucket_first_unit[nb] = (int64_t)units.size();
+    } catch (...) {
+        delete bd;
+        return DDP_ERR_NOMEM;
+    }
+    bd->n_units = (int64_t)units.size();
+    if (bd->n_units > 0) {
+        const size_t bytes = sizeof(ddp_copy_unit) * units.size();
+        if ((e = hipMalloc(&bd->units, bytes)) != hipSuccess) {
+            delete bd;
+            return hip_fail("hipMalloc (copy units)", e, DDP_ERR_NOMEM);
+        }
+        if ((e = hipMemcpy(bd->units, units.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+            (void)hipFree(bd->units);
+            delete bd;
+            return hip_fail("hipMemcpy (copy units)", e);
+        }
+    }
+    *out = bd;
+    return DDP_OK;
+}
+
+void ddp_binding_free(ddp_binding_t *binding)
+{
+    if (!binding) return;
+    if (binding->units) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(binding->device);
+        (void)hipFree(binding->units);
+        if (cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete binding;
+}
+
+static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, int32_t bucket,
+                             void *flat, int dtype, void *stream, int to_flat)
+{
+    if (!plan || !bd || !flat || bd->plan != plan || !dtype_ok(dtype)) return DDP_ERR_INVALID_ARG;
+    if (bucket < -1 || bucket >= plan->n_buckets()) return DDP_ERR_INVALID_ARG;
+    if (!aligned(flat, dtype_size(dtype))) return DDP_ERR_INVALID_ARG;
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev != bd->device) return DDP_ERR_INVALID_ARG;
+    const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
+    const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
+    if (last <= first) return DDP_OK;
+    // every XCD gets the same number of units (the last round padded)
+    const int64_t blocks = (last - first + kXcds - 1) / kXcds * kXcds * kCopyBlocksPerUnit;
+    if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
+    copy_units<<<dim3((unsigned)blocks), dim3(kCopyThreads), lds_for_blocks(kCopyBlocksPerCU),
+                 static_cast<hipStream_t>(stream)>>>(bd->units, first, last - first,
+                                                      static_cast<char *>(flat), dtype_size(dtype),
+                                                      to_flat);
+    return launched("copy kernel launch");
+}
+
+ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,
+                         void *flat_buf, ddp_dtype_t dtype, void *stream)
+{
+    return run_copy(plan, binding, bucket, flat_buf, dtype, stream, 1);
+}
+
+ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,
+                           const void *flat_out, ddp_dtype_t dtype, void *stream)
+{
+    return run_copy(plan, binding, bucket, const_cast<void *>(flat_out), dtype, stream, 0);
+}
+
+}  // extern "C"

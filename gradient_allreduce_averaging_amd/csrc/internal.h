@@ -1,5 +1,5 @@
 // Internal definitions shared by the host planner (plan.cpp) and the HIP
-// launch code (kernels.hip).  Not part of the ABI.
+// launch code (reduce.hip, copy.hip).  Not part of the ABI.
 #pragma once
 
 #include <cstdint>

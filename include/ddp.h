@@ -42,6 +42,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The library's exported symbols: it is built with hidden visibility, so
+ * these declarations are the whole ABI. */
+#if defined(__GNUC__)
+#define DDP_API __attribute__((visibility("default")))
+#else
+#define DDP_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -99,7 +107,7 @@ typedef struct ddp_binding ddp_binding_t;  /* opaque; one rank's parameter point
  * parameter larger than the cap forms its own bucket.
  * Errors: INVALID_ARG (null, n_params < 1, numel < 0, cap <= 0, bad dtype),
  * OVERFLOW (total elements or bytes beyond int64), NOMEM. */
-ddp_status_t ddp_plan_buckets(const int64_t *numel, int32_t n_params,
+DDP_API ddp_status_t ddp_plan_buckets(const int64_t *numel, int32_t n_params,
                               int64_t bucket_cap_bytes, ddp_dtype_t dtype,
                               ddp_plan_t **out);
 
@@ -110,30 +118,30 @@ ddp_status_t ddp_plan_buckets(const int64_t *numel, int32_t n_params,
  * FIRST in that order, registration order inside each region.
  * A bucket with no parameters is left out (the plan then has one bucket).
  * Errors: as ddp_plan_buckets, plus INVALID_ARG for an unknown region tag. */
-ddp_status_t ddp_plan_two_bucket(const int64_t *numel, const uint8_t *region,
+DDP_API ddp_status_t ddp_plan_two_bucket(const int64_t *numel, const uint8_t *region,
                                  int32_t n_params, ddp_dtype_t dtype,
                                  ddp_plan_t **out);
 
 /* Frees the plan and its device tables on every device they were uploaded
  * to.  The caller must make sure no queued work still reads them. NULL is ok. */
-void ddp_plan_free(ddp_plan_t *plan);
+DDP_API void ddp_plan_free(ddp_plan_t *plan);
 
 /* Number of buckets, or -1 for a NULL plan. */
-int32_t ddp_plan_num_buckets(const ddp_plan_t *plan);
+DDP_API int32_t ddp_plan_num_buckets(const ddp_plan_t *plan);
 /* Total elements of the flat layout, or -1 for a NULL plan. */
-int64_t ddp_plan_total(const ddp_plan_t *plan);
+DDP_API int64_t ddp_plan_total(const ddp_plan_t *plan);
 
 /* Bucket b: its length, its first element in the flat layout, and the range
  * [first_slot, first_slot + n_slots) of slots it holds.  Any output pointer
  * may be NULL.  Errors: INVALID_ARG (null plan, b out of range). */
-ddp_status_t ddp_plan_bucket(const ddp_plan_t *plan, int32_t b, int64_t *len,
+DDP_API ddp_status_t ddp_plan_bucket(const ddp_plan_t *plan, int32_t b, int64_t *len,
                              int64_t *base, int32_t *first_slot, int32_t *n_slots);
 
 /* Parameter held by flat slot `slot` (slots count 0..n_params-1 in flat order). */
-ddp_status_t ddp_plan_slot_param(const ddp_plan_t *plan, int32_t slot, int32_t *param);
+DDP_API ddp_status_t ddp_plan_slot_param(const ddp_plan_t *plan, int32_t slot, int32_t *param);
 
 /* Bucket of parameter p and its element offset inside that bucket. */
-ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
+DDP_API ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
                             int64_t *offset);
 
 /* Uploads the plan's device tables (used by ddp_sync_allreduce_avg in RING
@@ -141,7 +149,7 @@ ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
  * sync on a device does it by itself; call it beforehand when the sync will
  * be captured into a HIP graph or must not allocate.
  * Errors: INVALID_ARG, HIP, NOMEM. */
-ddp_status_t ddp_plan_prepare(ddp_plan_t *plan);
+DDP_API ddp_status_t ddp_plan_prepare(ddp_plan_t *plan);
 
 /* ddp_plan_prepare, plus the table a RING synchronisation over n_ranks ranks
  * reads: one 32-bit word per tile of the flat layout (4 bytes per 256 f32 or
@@ -153,7 +161,7 @@ ddp_status_t ddp_plan_prepare(ddp_plan_t *plan);
  * will be captured into a HIP graph or must not allocate.
  *   n_ranks  1..DDP_MAX_RANKS (1 prepares only what ddp_plan_prepare does)
  * Errors: INVALID_ARG, HIP, NOMEM. */
-ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
+DDP_API ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
 
 /* ------------------------------------------------------------------ bindings
  * One rank's per-parameter gradient buffers, resolved once (a static graph
@@ -169,22 +177,22 @@ ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
  * (rounded up per parameter) until ddp_binding_free.
  * Errors: INVALID_ARG (null plan/array/out, a null pointer for a parameter
  * with numel > 0, misaligned pointer), HIP, NOMEM. */
-ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
+DDP_API ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
                              void *stream, ddp_binding_t **out);
-void ddp_binding_free(ddp_binding_t *binding);
+DDP_API void ddp_binding_free(ddp_binding_t *binding);
 
 /* flat_buf[base_b + offset_p + j] = grad_p[j] for every parameter p of
  * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch.
  * flat_buf: device, ddp_plan_total(plan) elements, must not overlap any
  * parameter buffer.  Errors: INVALID_ARG (null, bucket out of range, bad
  * dtype, binding of another plan), HIP. */
-ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
+DDP_API ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
                          int32_t bucket, void *flat_buf, ddp_dtype_t dtype,
                          void *stream);
 
 /* grad_p[j] = flat_out[base_b + offset_p + j]: the inverse copy, elements of
  * `dtype` (the sync's output type).  Same arguments and errors. */
-ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
+DDP_API ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
                            int32_t bucket, const void *flat_out, ddp_dtype_t dtype,
                            void *stream);
 
@@ -215,7 +223,7 @@ ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
  * per-element head; others take a slower per-element path.  Results are
  * identical either way.
  * Errors: INVALID_ARG, UNSUPPORTED, ALIAS, HIP. */
-ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ranks,
+DDP_API ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ranks,
                                       int64_t len, ddp_order_t order,
                                       ddp_dtype_t in_dtype, ddp_dtype_t out_dtype,
                                       void *out, void *stream);
@@ -230,7 +238,7 @@ ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ra
  * The first RING call on a device with a given n_ranks uploads the plan's
  * tables synchronously (see ddp_plan_prepare_ranks).
  * Errors: as ddp_bucket_allreduce_avg. */
-ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat,
+DDP_API ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat,
                                     int32_t n_ranks, ddp_order_t order,
                                     ddp_dtype_t out_dtype, void *out_flat,
                                     void *stream);
@@ -257,7 +265,7 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
  * buffers take the vector kernels (N <= 8 unrolled, N > 8 looped), others a
  * per-element kernel with identical results.
  * Errors: as ddp_sync_allreduce_avg. */
-ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
+DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
                                  float *param_flat, float *momentum_flat, float lr,
                                  float momentum, void *stream);
@@ -273,7 +281,7 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
  * dst[k] may be exactly src[k]; any other overlap between the buffers is
  * rejected (DDP_ERR_ALIAS).  len == 0 does nothing.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, ALIAS, HIP. */
-ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
+DDP_API ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
                             ddp_dtype_t dtype, void *stream);
 
 /* ------------------------------------------------------------------ occupancy
@@ -292,15 +300,15 @@ ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_
 typedef enum { DDP_OCCUPANCY_TUNED = 0, DDP_OCCUPANCY_SHARED = 1 } ddp_occupancy_t;
 
 /* Errors: INVALID_ARG (not a ddp_occupancy_t value). */
-ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy);
-ddp_occupancy_t ddp_get_occupancy(void);
+DDP_API ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy);
+DDP_API ddp_occupancy_t ddp_get_occupancy(void);
 
 /* ------------------------------------------------------------------ misc */
-const char *ddp_status_string(ddp_status_t status);
+DDP_API const char *ddp_status_string(ddp_status_t status);
 /* Text of the last HIP failure seen by this thread ("" if none): the HIP call
  * and the runtime's error string.  Valid until the thread's next failure. */
-const char *ddp_last_error(void);
-int32_t ddp_abi_version(void);
+DDP_API const char *ddp_last_error(void);
+DDP_API int32_t ddp_abi_version(void);
 
 #ifdef __cplusplus
 }

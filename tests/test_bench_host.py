@@ -24,13 +24,23 @@ def test_more_than_one_gpu_exits_with_2():
 
 def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
     b = _bench()
-    src = open(b.KERNEL_SRC, encoding="utf-8").read()
+    assert any(p.endswith("reduce.hip") for p in b.KERNEL_SOURCES)
+    assert any(p.endswith("device.h") for p in b.KERNEL_SOURCES)
+    assert not any(p.endswith("probe.hip") for p in b.KERNEL_SOURCES)
     base = b.kernel_source_sha()
-    edited = tmp_path / "k.hip"
-    edited.write_text("// a new comment\n\n" + src.replace("\n{\n", "\n{   /* note */\n", 1) + "\n\n")
-    b.KERNEL_SRC = str(edited)
+    copies = []
+    for path in b.KERNEL_SOURCES:
+        c = tmp_path / os.path.basename(path)
+        src = open(path, encoding="utf-8").read()
+        if path.endswith("device.h"):
+            src = "// a new comment\n\n" + src.replace("\n{\n", "\n{   /* note */\n", 1) + "\n\n"
+        c.write_text(src)
+        copies.append(str(c))
+    b.KERNEL_SOURCES = copies
     assert b.kernel_source_sha() == base
-    edited.write_text(src.replace("kThreads = 64", "kThreads = 128", 1))
+    dev = next(c for c in copies if c.endswith("device.h"))
+    text = open(dev, encoding="utf-8").read()
+    open(dev, "w", encoding="utf-8").write(text.replace("kThreads = 64", "kThreads = 128", 1))
     assert b.kernel_source_sha() != base
 
 
