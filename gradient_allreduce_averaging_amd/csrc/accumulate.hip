@@ -1,7 +1,6 @@
 // Local gradient accumulation between synchronisations (ddp_accumulate).
 #include <hip/hip_runtime.h>
 
-#include <climits>
 #include <cstring>
 
 #include "host.h"
@@ -26,13 +25,13 @@ __device__ __forceinline__ void acc_elem(char *d, const char *s, int64_t i)
 }
 
 template <int DT>
-__global__ void __launch_bounds__(kThreads) accumulate_vec(AccArgs a, int64_t len)
+__global__ void __launch_bounds__(kThreads) accumulate_vec(AccArgs a, int64_t len, int64_t first_block)
 {
     constexpr int VEC = DT == kF32 ? 4 : 8;
     constexpr int ISZ = DT == kF32 ? 4 : 2;
     char *d = a.dst[blockIdx.y];
     const char *s = a.src[blockIdx.y];
-    const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * VEC;
+    const int64_t i0 = ((first_block + blockIdx.x) * kThreads + threadIdx.x) * VEC;
     if (i0 + VEC <= len) {
         const u32x4 x = ld_stream(d + i0 * ISZ), y = ld_stream(s + i0 * ISZ);
         u32x4 o;
@@ -52,9 +51,10 @@ __global__ void __launch_bounds__(kThreads) accumulate_vec(AccArgs a, int64_t le
 }
 
 template <int DT>
-__global__ void __launch_bounds__(kThreads) accumulate_scalar(AccArgs a, int64_t len)
+__global__ void __launch_bounds__(kThreads) accumulate_scalar(AccArgs a, int64_t len,
+                                                             int64_t first_block)
 {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = (first_block + blockIdx.x) * kThreads + threadIdx.x;
     if (i < len) acc_elem<DT>(a.dst[blockIdx.y], a.src[blockIdx.y], i);
 }
 
@@ -92,17 +92,18 @@ ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t per = vec_ok ? (int64_t)kThreads * vec_elems(dtype) : kThreads;
-    const int64_t blocks = (len + per - 1) / per;
-    if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
-    const dim3 g((unsigned)blocks, (unsigned)n_bufs), b(kThreads);
-    if (dtype == DDP_F32) {
-        if (vec_ok) accumulate_vec<kF32><<<g, b, 0, st>>>(a, len);
-        else accumulate_scalar<kF32><<<g, b, 0, st>>>(a, len);
-    } else {
-        if (vec_ok) accumulate_vec<kBF16><<<g, b, 0, st>>>(a, len);
-        else accumulate_scalar<kBF16><<<g, b, 0, st>>>(a, len);
-    }
-    return launched("accumulate kernel launch");
+    const dim3 b(kThreads);
+    return launch_split((len + per - 1) / per, kThreads, "accumulate kernel launch",
+                        [&](int64_t b0, unsigned n) {
+                            const dim3 g(n, (unsigned)n_bufs);
+                            if (dtype == DDP_F32) {
+                                if (vec_ok) accumulate_vec<kF32><<<g, b, 0, st>>>(a, len, b0);
+                                else accumulate_scalar<kF32><<<g, b, 0, st>>>(a, len, b0);
+                            } else {
+                                if (vec_ok) accumulate_vec<kBF16><<<g, b, 0, st>>>(a, len, b0);
+                                else accumulate_scalar<kBF16><<<g, b, 0, st>>>(a, len, b0);
+                            }
+                        });
 }
 
 }  // extern "C"

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <cstdlib>
 
 #include "host.h"
 
@@ -21,6 +22,20 @@ ddp_status_t launched(const char *what)
 {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DDP_OK : hip_fail(what, e);
+}
+
+int64_t max_launch_items()
+{
+    static const int64_t items = [] {
+        int64_t v = int64_t(1) << 30;
+        if (const char *e = std::getenv("DDP_MAX_LAUNCH_ITEMS")) {
+            char *end = nullptr;
+            const long long x = std::strtoll(e, &end, 10);
+            if (end != e && x > 0 && x < v) v = x < 4096 ? 4096 : x;
+        }
+        return v / 4096 * 4096;
+    }();
+    return items;
 }
 
 // ---------------------------------------------------------------- occupancy

@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <climits>
 #include <new>
 #include <vector>
 
@@ -184,14 +183,21 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
-    // every XCD gets the same number of units (the last round padded)
-    const int64_t blocks = (last - first + kXcds - 1) / kXcds * kXcds * kCopyBlocksPerUnit;
-    if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
-    copy_units<<<dim3((unsigned)blocks), dim3(kCopyThreads), lds_for_blocks(kCopyBlocksPerCU),
-                 static_cast<hipStream_t>(stream)>>>(bd->units, first, last - first,
-                                                      static_cast<char *>(flat), dtype_size(dtype),
-                                                      to_flat);
-    return launched("copy kernel launch");
+    // Every XCD gets the same number of units (the last round padded).  A
+    // launch takes at most max_launch_items() work-items: a multiple of 4096,
+    // so of the kXcds * kCopyBlocksPerUnit blocks that one round of units
+    // spans.
+    const int64_t per = max_launch_items() / (kCopyThreads * kCopyBlocksPerUnit);
+    for (int64_t u0 = first; u0 < last; u0 += per) {
+        const int64_t n = std::min(per, last - u0);
+        const int64_t blocks = (n + kXcds - 1) / kXcds * kXcds * kCopyBlocksPerUnit;
+        copy_units<<<dim3((unsigned)blocks), dim3(kCopyThreads), lds_for_blocks(kCopyBlocksPerCU),
+                     static_cast<hipStream_t>(stream)>>>(bd->units, u0, n, static_cast<char *>(flat),
+                                                          dtype_size(dtype), to_flat);
+        const ddp_status_t st = launched("copy kernel launch");
+        if (st != DDP_OK) return st;
+    }
+    return DDP_OK;
 }
 
 ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,

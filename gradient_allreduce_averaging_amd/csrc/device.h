@@ -81,12 +81,14 @@ struct Buckets {
                                   // launch's element numbering (lo < 0 when the launch
                                   // starts past the bucket's first elements)
     int32_t n_buckets;
+    int64_t first_block;          // grid-wide index of this launch's block 0: a grid
+                                  // too large for one dispatch runs as several launches
 };
 
 // One bucket spanning [lo, hi) of a launch's elements.
 __host__ __device__ inline Buckets single_bucket(int64_t lo, int64_t hi)
 {
-    return {nullptr, nullptr, nullptr, 0, lo, hi, 1};
+    return {nullptr, nullptr, nullptr, 0, lo, hi, 1, 0};
 }
 
 // Workgroups are dealt to the XCDs round-robin, so tile t runs on XCD t % 8.
@@ -240,20 +242,26 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
     }
 }
 
-// Tile processed by this block.
-__device__ __forceinline__ int64_t tile_of_block() { return blockIdx.x; }
+// Tile (vector kernels) or group of kThreads elements (per-element kernels)
+// processed by this block.
+__device__ __forceinline__ int64_t tile_of_block(const Buckets &bk)
+{
+    return bk.first_block + blockIdx.x;
+}
 
 // A single bucket that starts before the launch's element 0 (lo < 0: its
 // first -lo elements sit just before the aligned address the vector path
-// starts at) gets one extra block at the end of the grid.  Its tile lies past
-// the end, so the vector path finds no work there (its loads read the dummy
-// vector), and this reduces the head elements one per lane.  The check comes
-// after the vector path, so no other block waits on it before its loads.
+// starts at) gets one extra block at the end of the grid.  Its tile, the
+// only one that starts at or past the end (tile0 >= total), gives the vector
+// path no work (its loads read the dummy vector), and this reduces the head
+// elements one per lane.  The check comes after the vector path, so no other
+// block waits on it before its loads.
 template <int IN, int OUT, bool RING>
 __device__ __forceinline__ void head_block(const RankArgs &ra, int N, int64_t total,
-                                           const Buckets &bk, float inv, void *out)
+                                           const Buckets &bk, float inv, void *out,
+                                           int64_t tile0)
 {
-    if (bk.base || bk.lo >= 0 || blockIdx.x != gridDim.x - 1) return;
+    if (bk.base || bk.lo >= 0 || tile0 < total) return;
     if (threadIdx.x < -bk.lo)
         reduce_elems<IN, OUT, RING>(ra, N, total, bk, 0, inv, out, bk.lo + threadIdx.x, 1);
 }

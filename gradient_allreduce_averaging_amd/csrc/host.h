@@ -38,6 +38,28 @@ inline bool overlaps(uintptr_t a, int64_t na, uintptr_t b, int64_t nb)
 ddp_status_t check_alias(const void *const *in, int n, int64_t len, int isz, const void *out,
                          int osz);
 
+// The most work-items one launch is given (a dispatch packet counts its grid
+// in 32-bit work-items): 2^30, or DDP_MAX_LAUNCH_ITEMS from the environment
+// when that is smaller (rounded down to a multiple of 4096, at least 4096).
+// A larger grid runs as several launches on the same stream, each told the
+// grid-wide index of its first block.
+int64_t max_launch_items();
+
+// Launches a grid of `blocks` blocks of `threads` threads as consecutive
+// launches of at most max_launch_items() work-items: launch(first_block, n)
+// enqueues blocks [first_block, first_block + n).
+template <class Launch>
+ddp_status_t launch_split(int64_t blocks, int threads, const char *what, Launch &&launch)
+{
+    const int64_t per = max_launch_items() / threads;
+    for (int64_t b0 = 0; b0 < blocks; b0 += per) {
+        launch(b0, (unsigned)(blocks - b0 < per ? blocks - b0 : per));
+        const ddp_status_t st = launched(what);
+        if (st != DDP_OK) return st;
+    }
+    return DDP_OK;
+}
+
 // Resident blocks per CU each kernel family is capped at (0: no cap), and
 // the dynamic-LDS request that imposes a cap of k (see common.hip).
 int reduce_blocks_per_cu(int N, bool ring);

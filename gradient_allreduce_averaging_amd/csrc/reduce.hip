@@ -7,7 +7,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <climits>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -28,7 +27,7 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    const int64_t tile = tile_of_block();
+    const int64_t tile = tile_of_block(bk);
     const int64_t tile0 = tile * (kThreads * kUnroll * VEC);
 
     // Every rank's vector at the lane's offset, in rank order, in either
@@ -67,7 +66,7 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
                                             i0[u], VEC);
         }
     }
-    head_block<IN, OUT, RING>(ra, NR, total, bk, inv, out);
+    head_block<IN, OUT, RING>(ra, NR, total, bk, inv, out, tile0);
 }
 
 // Fused average + SGD step, N known at compile time (1..8).  Per lane: the N
@@ -83,7 +82,7 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
-    const int64_t tile = tile_of_block();
+    const int64_t tile = tile_of_block(bk);
     const int64_t tile0 = tile * (kThreads * VEC);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
 
@@ -128,7 +127,7 @@ template <bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
 reduce_sgd_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArgs sa)
 {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = tile_of_block(bk) * kThreads + threadIdx.x;
     if (i >= total) return;
     sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, 0, inv, sa, i, 1);
 }
@@ -143,7 +142,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     static_assert(kUnroll == 1, "one vector per lane");
-    const int64_t tile = tile_of_block();
+    const int64_t tile = tile_of_block(bk);
     const int64_t tile0 = tile * (kThreads * VEC);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
     const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
@@ -159,7 +158,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     }
     if (!in_a && !in_b && i0 < total)
         reduce_elems<IN, OUT, RING>(ra, N, total, bk, first_bucket(bk, tile), inv, out, i0, VEC);
-    head_block<IN, OUT, RING>(ra, N, total, bk, inv, out);
+    head_block<IN, OUT, RING>(ra, N, total, bk, inv, out, tile0);
 }
 
 // The fused average + SGD step for any N up to DDP_MAX_RANKS: the lane's
@@ -173,7 +172,7 @@ reduce_sgd_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArg
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
     static_assert(kUnroll == 1, "one vector per lane");
-    const int64_t tile = tile_of_block();
+    const int64_t tile = tile_of_block(bk);
     const int64_t tile0 = tile * (kThreads * VEC);
     const int64_t i0 = tile0 + (int64_t)threadIdx.x * VEC;
     u32x4 pv[PV], mv[PV];
@@ -210,7 +209,7 @@ template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 reduce_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
 {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t i = tile_of_block(bk) * kThreads + threadIdx.x;
     if (i >= total) return;
     reduce_elems<IN, OUT, RING>(ra, N, total, bk, 0, inv, out, i, 1);
 }
@@ -221,29 +220,33 @@ template <bool RING, int IN, int OUT>
 ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Buckets &bk, float inv,
                           void *out, hipStream_t st, bool vec_ok)
 {
+    Buckets lb = bk;
+    const dim3 b(kThreads);
     if (vec_ok) {
         const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN) +
                               (!bk.base && bk.lo < 0 ? 1 : 0);   // + the head block
-        if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
-        const dim3 g((unsigned)tiles), b(kThreads);
         const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N, RING));
-        switch (N) {
-        case 2: reduce_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 3: reduce_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 4: reduce_fast<4, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 5: reduce_fast<5, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, bk, inv, out); break;
-        default: reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, bk, inv, out); break;
-        }
-    } else {
-        const int64_t blocks = (total + kThreads - 1) / kThreads;
-        if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
-        reduce_scalar<RING, IN, OUT><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
-            ra, N, total, bk, inv, out);
+        return launch_split(tiles, kThreads, "reduce kernel launch", [&](int64_t b0, unsigned n) {
+            lb.first_block = b0;
+            const dim3 g(n);
+            switch (N) {
+            case 2: reduce_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 3: reduce_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 4: reduce_fast<4, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 5: reduce_fast<5, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            default: reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, lb, inv, out); break;
+            }
+        });
     }
-    return launched("reduce kernel launch");
+    return launch_split((total + kThreads - 1) / kThreads, kThreads, "reduce kernel launch",
+                        [&](int64_t b0, unsigned n) {
+                            lb.first_block = b0;
+                            reduce_scalar<RING, IN, OUT><<<dim3(n), b, 0, st>>>(ra, N, total, lb,
+                                                                               inv, out);
+                        });
 }
 
 ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
@@ -307,29 +310,34 @@ template <bool RING, int IN, int OUT, bool MOM>
 ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Buckets &bk,
                               float inv, const SgdArgs &sa, hipStream_t st, bool vec_ok)
 {
+    Buckets lb = bk;
+    const dim3 b(kThreads);
+    const char *what = "fused SGD kernel launch";
     if (vec_ok) {
         const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
-        if (tiles > INT_MAX) return DDP_ERR_OVERFLOW;
-        const dim3 g((unsigned)tiles), b(kThreads);
         const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
-        switch (N) {
-        case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        case 8: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, bk, inv, sa); break;
-        default: reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, bk, inv, sa); break;
-        }
-    } else {
-        const int64_t blocks = (total + kThreads - 1) / kThreads;
-        if (blocks > INT_MAX) return DDP_ERR_OVERFLOW;
-        reduce_sgd_scalar<RING, IN, OUT, MOM><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(
-            ra, N, total, bk, inv, sa);
+        return launch_split(tiles, kThreads, what, [&](int64_t b0, unsigned n) {
+            lb.first_block = b0;
+            const dim3 g(n);
+            switch (N) {
+            case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            case 8: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
+            default: reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, lb, inv, sa); break;
+            }
+        });
     }
-    return launched("fused SGD kernel launch");
+    return launch_split((total + kThreads - 1) / kThreads, kThreads, what,
+                        [&](int64_t b0, unsigned n) {
+                            lb.first_block = b0;
+                            reduce_sgd_scalar<RING, IN, OUT, MOM><<<dim3(n), b, 0, st>>>(
+                                ra, N, total, lb, inv, sa);
+                        });
 }
 
 template <bool RING, bool MOM>
@@ -517,7 +525,7 @@ ddp_status_t ring_buckets(ddp_plan *plan, int in, int n_ranks, Buckets *bk)
     const uint32_t *desc = nullptr;
     if ((st = ring_tile_desc(plan, tile_elems(in), n_ranks, &desc)) != DDP_OK) return st;
     *bk = {t->bucket_base, t->tile_bucket, desc, desc_stride(t->n_tiles), 0, plan->total,
-           plan->n_buckets()};
+           plan->n_buckets(), 0};
     return DDP_OK;
 }
 

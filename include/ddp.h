@@ -34,7 +34,14 @@
  *     (hipSetDevice / torch.cuda.set_device).  The caller owns all gradient
  *     and output memory.  The library allocates device memory only for its
  *     own descriptor tables (plans, bindings) and frees it in *_free.
- *   - Element counts and offsets are int64 everywhere.
+ *   - Element counts and offsets are int64 everywhere.  A dispatch counts
+ *     its grid in 32-bit work-items, so a grid of more than 2^30 work-items
+ *     (a one-launch f32 reduce past 2^32 elements, a per-element one past
+ *     2^30) runs as consecutive launches on the same stream; results are
+ *     the same bits.  DDP_ERR_HIP from a later launch may follow earlier
+ *     ones already enqueued.  The environment variable DDP_MAX_LAUNCH_ITEMS,
+ *     read once per process, lowers the limit (at least 4096, rounded down
+ *     to a multiple of 4096), so that tests can split small grids.
  */
 #ifndef DDP_H
 #define DDP_H
