@@ -80,6 +80,38 @@ def measured_traffic(workload, order, algorithmic_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def side_by_side_streams(torch, tries=32):
+    """Two streams whose kernels run side by side, and the number of streams
+    tried.  HIP binds every stream to one of a few hardware queues
+    (GPU_MAX_HW_QUEUES, 4 by default), and two streams bound to one queue run
+    in submission order: a cross-stream wait in that queue holds back
+    everything queued behind it, so a compute stream and an update stream
+    that share a queue cannot overlap at all.  Checked by spinning a kernel
+    on the first stream and seeing a tiny kernel on the second finish before
+    it; torch hands out its pooled streams in turn, so the next candidate is
+    another stream."""
+    first = torch.cuda.Stream()
+    x = torch.zeros(1, device="cuda:0")
+    for k in range(1, tries + 1):
+        second = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        spun, tiny = torch.cuda.Event(), torch.cuda.Event()
+        with torch.cuda.stream(first):
+            torch.cuda._sleep(20_000_000)      # a bounded spin (clock cycles)
+            spun.record(first)
+        with torch.cuda.stream(second):
+            x.add_(1.0)
+            tiny.record(second)
+        while True:
+            t_done, s_done = tiny.query(), spun.query()
+            if t_done or s_done:
+                break
+        torch.cuda.synchronize()
+        if t_done and not s_done:
+            return first, second, k
+    return first, second, None
+
+
 def run_environment(torch):
     """ROCm release, HIP runtime and the device's peak clocks, for the record."""
     env = {"hip_runtime": torch.version.hip, "torch": torch.__version__,
@@ -551,7 +583,7 @@ def main():
         (dl, db, _, _), (fl_, fb_, _, _) = tb.bucket(0), tb.bucket(1)
         mat_a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
         mat_b = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-        comp, upd = torch.cuda.Stream(), torch.cuda.Stream()
+        comp, upd, tried = side_by_side_streams(torch)
         deep_in = [f[db:db + dl] for f in flats]
         deep_out = out[db:db + dl]
 
@@ -589,7 +621,9 @@ def main():
         t_comp = timed([compute])
         overlap = {"plan": "two-bucket (DEEP_COMM %d, FIRST_COMM %d elements)" % (dl, fl_),
                    "compute_ms": round(t_comp, 4),
-                   "compute": "bf16 GEMM 4096^3 on a second stream"}
+                   "compute": "bf16 GEMM 4096^3 on a second stream",
+                   "streams": ("side by side (hardware queues checked; %d tried)" % tried
+                               if tried else "not found side by side: results are serial")}
         # under both occupancy policies: the tuned cap reserves LDS that the
         # GEMM's blocks would need, "shared" leaves it free
         for policy in ("tuned", "shared"):
