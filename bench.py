@@ -18,7 +18,8 @@ with its --no-... flag):
   cold_mall      the sync with the MALL flushed before each one
   ceiling        a probe of the reduce's bare access pattern
   cpu_baseline   the CPU oracle (one thread, and SEQ on all host cores)
-  copy_path      flatten + sync + unflatten (eager and graph-replayed)
+  copy_path      flatten + sync + unflatten (eager and graph-replayed), and
+                 the same step as one kernel over per-parameter tensors
   fused_sgd      the average fused into a momentum-SGD step
   overlap        syncs beside compute on a second stream
   rank_sweep_GBps, in_place, no_sync, env
@@ -530,8 +531,33 @@ def main():
             loop[name] = a.elapsed_time(b) / reps
         copy_path["eager_loop_ms_per_step"] = round(loop["eager"], 4)
         copy_path["graph_replay_ms_per_step"] = round(loop["graph"], 4)
+
+        # the same step as one kernel over the per-parameter tensors
+        ps = ddp.param_sync(plan, binds, rbind, order)
+        for _ in range(5):
+            ps(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            ps(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t_ps = a.elapsed_time(b) / reps
+        chk = [torch.empty_like(t) for t in res]
+        ddp.unflatten(plan, ddp.bind_params(plan, chk), out, stream=stream)   # out holds this sync
+        torch.cuda.synchronize()
+        same = all(torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
+                               y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
+                   for x, y in zip(res, chk))
+        copy_path["param_sync"] = {
+            "ms_per_step": round(t_ps, 4), "GBps": round(sync_bytes / (t_ps * 1e-3) / 1e9, 1),
+            "speedup_vs_three_steps": round((tf + ts + tu) / t_ps, 2),
+            "same_bits_as_three_steps": bool(same),
+            "step": "every rank's per-parameter gradients averaged into per-parameter outputs "
+                    "in one launch (ddp_param_sync_run)"}
         log(f"copy path: {copy_path}")
-        del grads, binds, res, rbind, graph
+        del grads, binds, res, rbind, graph, ps, chk
 
     # ---------------------------------------------------------------- fused optimizer step
     # The average folded into a momentum-SGD step (ddp_sync_sgd_update) against

@@ -92,6 +92,10 @@ def _load():
                                     ctypes.c_int, vp, vp], ctypes.c_int),
         "ddp_sync_sgd_update": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+        "ddp_param_sync_create": ([vp, ctypes.POINTER(vp), ctypes.c_int32, vp, ctypes.c_int,
+                                   ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int),
+        "ddp_param_sync_run": ([vp, vp], ctypes.c_int),
+        "ddp_param_sync_free": ([vp], None),
         "ddp_accumulate": ([ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
                             ctypes.c_int, vp], ctypes.c_int),
         "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -259,6 +263,45 @@ class Binding:
 
 def bind_params(plan: Plan, grads: Sequence, stream=None) -> Binding:
     return Binding(plan, grads, stream)
+
+
+class ParamSync:
+    """Owner of a ``ddp_param_sync_t``: the synchronisation of one step over
+    per-parameter tensors -- every rank's bound gradients averaged straight
+    into the per-parameter outputs of ``out_binding``, in one launch, with the
+    bits of flatten + sync_allreduce_avg + unflatten.  Keeps the bindings (and
+    so their tensors) alive; calling it enqueues the sync."""
+
+    def __init__(self, plan: Plan, rank_bindings: Sequence[Binding], out_binding: Binding,
+                 order="ring"):
+        self.plan = plan
+        self._binds = list(rank_bindings)
+        self._out = out_binding
+        for bd in self._binds:
+            if bd.dtypes != {plan.dtype}:
+                raise ValueError("rank gradients must have the plan's dtype")
+        if len(out_binding.dtypes) != 1:
+            raise ValueError("the outputs must share one dtype")
+        self.out_dtype = next(iter(out_binding.dtypes))
+        handles = (ctypes.c_void_p * len(self._binds))(*[bd.handle for bd in self._binds])
+        h = ctypes.c_void_p()
+        _check(lib.ddp_param_sync_create(plan.handle, handles, len(self._binds),
+                                         out_binding.handle, _ORDERS[order], self.out_dtype,
+                                         ctypes.byref(h)), "ddp_param_sync_create")
+        self._h = h
+
+    def __call__(self, stream=None):
+        _check(lib.ddp_param_sync_run(self._h, _stream_handle(stream)), "ddp_param_sync_run")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and lib is not None:
+            lib.ddp_param_sync_free(h)
+
+
+def param_sync(plan: Plan, rank_bindings: Sequence[Binding], out_binding: Binding,
+               order="ring") -> ParamSync:
+    return ParamSync(plan, rank_bindings, out_binding, order)
 
 
 def _check_flat(plan: Plan, binding: Binding, flat):

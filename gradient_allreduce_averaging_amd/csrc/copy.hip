@@ -116,6 +116,9 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
     }
     std::vector<ddp_copy_unit> units;
     try {
+        bd->param_addr.resize((size_t)plan->n_params);
+        for (int32_t p = 0; p < plan->n_params; ++p)
+            bd->param_addr[p] = reinterpret_cast<uint64_t>(param_grads[p]);
         const int32_t nb = plan->n_buckets();
         bd->bucket_first_unit.resize((size_t)nb + 1);
         for (int32_t b = 0; b < nb; ++b) {

@@ -381,14 +381,28 @@ __device__ __forceinline__ void fold_seq(const u32x4 *v, float *acc)
         for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[k], e);
 }
 
+// A streaming 16-byte load at byte offset `off` from a rank's base: a
+// pointer (kernel arguments, which the compiler knows to be global memory)
+// or a 64-bit address read from a table, typed as global memory here so that
+// the load is a global rather than a flat instruction.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+
+__device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
+{
+    return ld_stream(static_cast<const char *>(p) + off);
+}
+__device__ __forceinline__ u32x4 ld_at(uint64_t a, int64_t off)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4 *>(a + (uint64_t)off));
+}
+
 // Any N up to DDP_MAX_RANKS: the ranks walked in the fold order starting at
-// the wave-uniform rank s, eight loads in flight at a time.  Every rank
-// pointer is a scalar load, and a short last group is cut by a uniform
-// branch rather than dummy loads.  Lanes not taking part pass off = 0 and
-// re-read vector 0.
-template <int IN, bool RING>
-__device__ __forceinline__ void fold_looped(const RankArgs &ra, int N, int s, int64_t off,
-                                            float *acc)
+// the wave-uniform rank s, eight loads in flight at a time.  p[r] is rank r's
+// base address (a pointer or a 64-bit address), read with a scalar load, and
+// a short last group is cut by a uniform branch rather than dummy loads.
+// Lanes not taking part pass off = 0 and re-read vector 0.
+template <int IN, bool RING, class Ptrs>
+__device__ __forceinline__ void fold_looped(const Ptrs &p, int N, int s, int64_t off, float *acc)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int G = 8;
@@ -400,7 +414,7 @@ __device__ __forceinline__ void fold_looped(const RankArgs &ra, int N, int s, in
             if (k0 + j < N) {
                 int r = s + k0 + j;
                 r = r >= N ? r - N : r;
-                v[j] = ld_stream(static_cast<const char *>(ra.p[r]) + off);
+                v[j] = ld_at(p[r], off);
             }
         }
 #pragma unroll

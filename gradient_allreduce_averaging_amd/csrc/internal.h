@@ -1,5 +1,5 @@
 // Internal definitions shared by the host planner (plan.cpp) and the HIP
-// launch code (reduce.hip, copy.hip).  Not part of the ABI.
+// launch code (reduce.hip, copy.hip, params.hip).  Not part of the ABI.
 #pragma once
 
 #include <cstdint>
@@ -54,6 +54,19 @@ struct ddp_binding {
     ddp_copy_unit *units = nullptr;           // device array
     int64_t n_units = 0;
     std::vector<int64_t> bucket_first_unit;   // [n_buckets + 1]
+    std::vector<uint64_t> param_addr;         // [n_params] the bound gradient pointers
+};
+
+// A synchronisation over per-parameter tensors (params.hip): one table entry
+// per tile of each parameter, with every rank's address and the output's.
+struct ddp_param_sync {
+    int device = -1;
+    int n_ranks = 0;
+    int order = 0;
+    int in = 0, out = 0;                      // ddp_dtype_t of inputs and outputs
+    char *table = nullptr;                    // device array, n_tiles * stride bytes
+    int64_t n_tiles = 0;
+    int64_t stride = 0;                       // bytes per entry
 };
 
 // Frees every device table of a plan (defined next to the kernels).

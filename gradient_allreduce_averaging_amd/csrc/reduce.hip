@@ -153,7 +153,7 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
         const bool mine = pass == 0 ? in_a : in_b;
         if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
         float acc[VEC];
-        fold_looped<IN, RING>(ra, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
+        fold_looped<IN, RING>(ra.p, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
         if (mine) store_vec<IN, OUT>(out, i0, acc, inv);
     }
     if (!in_a && !in_b && i0 < total)
@@ -192,7 +192,7 @@ reduce_sgd_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArg
         const bool mine = pass == 0 ? in_a : in_b;
         if (!__builtin_amdgcn_ballot_w64(mine)) continue;
         float y[VEC];
-        fold_looped<IN, RING>(ra, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, y);
+        fold_looped<IN, RING>(ra.p, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, y);
         if (mine) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) y[e] = y[e] * inv;

@@ -95,6 +95,7 @@ typedef enum {
 
 typedef struct ddp_plan ddp_plan_t;        /* opaque; host data + per-device tables */
 typedef struct ddp_binding ddp_binding_t;  /* opaque; one rank's parameter pointers */
+typedef struct ddp_param_sync ddp_param_sync_t;  /* opaque; a bound per-parameter sync */
 
 /* ------------------------------------------------------------------ plans
  * Host-only calls: no GPU is touched, no device memory is allocated.
@@ -276,6 +277,48 @@ DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *ra
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
                                  float *param_flat, float *momentum_flat, float lr,
                                  float momentum, void *stream);
+
+/* ------------------------------------------------------------ per-parameter
+ * The whole path of one step -- flatten every rank, average every bucket,
+ * unflatten ([DDP] 4.2) -- over per-parameter gradient tensors, in one
+ * kernel that reads each rank's gradients where they lie and writes the
+ * averages straight to per-parameter outputs.  The result equals
+ * ddp_flatten (every rank) + ddp_sync_allreduce_avg + ddp_unflatten, bit for
+ * bit, including the RING chunks, which follow the flat positions; the
+ * bytes moved are those of the sync alone.  It is what bucket views
+ * (gradient_as_bucket_view, [DDP] 4.2; [TR24] 八's region layout) give,
+ * without asking for that layout.
+ *
+ * ddp_param_sync_create resolves everything once (a static graph, [DDP] 6.2):
+ *   plan               the bucket plan; its dtype is the gradients' dtype
+ *   rank_bindings[n_ranks]  host array; rank r's gradients (ddp_bind_params
+ *                      with this plan, on the current device)
+ *   out_binding        the per-parameter outputs (ddp_bind_params with this
+ *                      plan): numel[p] elements of out_dtype each.  It may
+ *                      be one of rank_bindings (in place): an output may be
+ *                      exactly the same parameter's gradient of one rank
+ *                      and may overlap nothing else (DDP_ERR_ALIAS);
+ *                      outputs may not overlap each other
+ *   order, out_dtype   as ddp_sync_allreduce_avg (N == 1: the input, bit
+ *                      for bit, and out_dtype must equal the plan's dtype)
+ * It uploads a table with one entry per tile of each parameter (256 f32 or
+ * 512 bf16 elements): 8 * (n_ranks + 1) + 32 bytes rounded up to 16 (112
+ * for 8 ranks, about 0.5 % of the gradient bytes), held until
+ * ddp_param_sync_free.  The bindings' addresses are copied into it: bind
+ * again if a gradient moves.  Parameters whose gradients and output all sit
+ * on 16-byte boundaries take the vector path, others the per-element path
+ * (same results).
+ * ddp_param_sync_run enqueues the sync on `stream` (current device = the
+ * device it was created on); it allocates nothing, so it can be captured.
+ * Errors: INVALID_ARG (null arguments, a binding of another plan or device,
+ * misaligned pointers), UNSUPPORTED, ALIAS, OVERFLOW, HIP, NOMEM. */
+DDP_API ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan,
+                                           const ddp_binding_t *const *rank_bindings,
+                                           int32_t n_ranks, const ddp_binding_t *out_binding,
+                                           ddp_order_t order, ddp_dtype_t out_dtype,
+                                           ddp_param_sync_t **out);
+DDP_API ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *sync, void *stream);
+DDP_API void ddp_param_sync_free(ddp_param_sync_t *sync);
 
 /* Local gradient accumulation between synchronisations: the no_sync
  * micro-steps of [DDP] 5.2, where backward adds each micro-batch's gradient

@@ -165,6 +165,23 @@ int main(void)
         if (!same_bits(got, want + base + off, sizeof(float) * numel[p], "unflatten")) return 1;
     }
 
+    /* the same step in one kernel over the per-parameter gradients */
+    ddp_param_sync_t *ps;
+    CHECK_DDP(ddp_param_sync_create(plan, (const ddp_binding_t *const *)bind, N, rbind,
+                                    DDP_ORDER_RING, DDP_F32, &ps));
+    for (int p = 0; p < NP; ++p) CHECK_HIP(hipMemset(dres[p], 0xff, sizeof(float) * numel[p]));
+    CHECK_DDP(ddp_param_sync_run(ps, NULL));
+    CHECK_HIP(hipDeviceSynchronize());
+    for (int p = 0; p < NP; ++p) {
+        int32_t b;
+        int64_t off, base;
+        CHECK_DDP(ddp_plan_param(plan, p, &b, &off));
+        CHECK_DDP(ddp_plan_bucket(plan, b, NULL, &base, NULL, NULL));
+        CHECK_HIP(hipMemcpy(got, dres[p], sizeof(float) * numel[p], hipMemcpyDeviceToHost));
+        if (!same_bits(got, want + base + off, sizeof(float) * numel[p], "param sync")) return 1;
+    }
+    ddp_param_sync_free(ps);
+
     /* fused momentum-SGD step on flat parameters */
     float *hp = malloc(sizeof(float) * P), *hm = calloc((size_t)P, sizeof(float));
     for (int64_t i = 0; i < P; ++i) hp[i] = next_grad() * 1000.0f;

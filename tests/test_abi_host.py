@@ -195,6 +195,29 @@ def test_accumulate_argument_errors_are_host_side():
     assert f(P(0x1002), P(0x2000), 1, 16, 0, None) == 1           # f32 misaligned to 2 B
 
 
+def test_param_sync_argument_errors_are_host_side():
+    L = ddp.lib
+    p = ddp.plan_buckets([100, 28], 1 << 20)
+    pb = ddp.plan_buckets([100, 28], 1 << 20, "bf16")
+    ranks = (ctypes.c_void_p * 2)(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000))
+    outb = ctypes.c_void_p(0x3000)
+    res = ctypes.c_void_p()
+    f = L.ddp_param_sync_create
+    assert f(None, ranks, 2, outb, 1, 0, ctypes.byref(res)) == 1
+    assert f(p.handle, None, 2, outb, 1, 0, ctypes.byref(res)) == 1
+    assert f(p.handle, ranks, 2, None, 1, 0, ctypes.byref(res)) == 1
+    assert f(p.handle, ranks, 2, outb, 1, 0, None) == 1
+    assert f(p.handle, ranks, 0, outb, 1, 0, ctypes.byref(res)) == 1
+    assert f(p.handle, ranks, 2, outb, 7, 0, ctypes.byref(res)) == 1      # order
+    assert f(p.handle, ranks, 2, outb, 1, 9, ctypes.byref(res)) == 1      # dtype
+    assert f(p.handle, ranks, 65, outb, 1, 0, ctypes.byref(res)) == 2
+    assert f(pb.handle, ranks, 2, outb, 1, 0, ctypes.byref(res)) == 2     # bf16 -> f32
+    assert f(p.handle, ranks, 1, outb, 1, 1, ctypes.byref(res)) == 2      # one rank, f32 -> bf16
+    assert not res.value
+    assert L.ddp_param_sync_run(None, None) == 1
+    L.ddp_param_sync_free(None)
+
+
 def test_occupancy_policy_round_trip():
     L = ddp.lib
     assert ddp.get_occupancy() == "tuned"

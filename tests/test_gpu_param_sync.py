@@ -1,0 +1,279 @@
+"""GPU parity of the one-kernel synchronisation over per-parameter tensors
+(ddp_param_sync_create / _run) against the oracle's flatten, then sync, then
+unflatten ("DDP" section 4.2), bit for bit:
+
+* ResNet-50 (N = 8, both orders) and many-small (N = 4, ring) at full size,
+  every output element, and equal to the library's own three-step path;
+* random plans: parameter sizes around the tile edges, N from 1 to 12, all
+  three dtype pairs, tensors carved at every alignment (per-element path)
+  or on 16-byte boundaries (vector path);
+* in place (the outputs are rank 0's gradients), graph capture and replay,
+  and the rejected overlaps;
+* GPT-1.3B (N = 8, ring, f32), sampled positions at every bucket and
+  ring-chunk edge plus random ones, against the oracle's per-element fold.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_bits_equal, sample_positions, to_dev, to_host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = torch_cuda()
+    import gradient_allreduce_averaging_amd as ddp
+    return torch, ddp
+
+
+def _tdt(torch, dt):
+    return torch.float32 if dt == "f32" else torch.bfloat16
+
+
+def _carve(torch, sizes, tdt, rng, gaps):
+    """Parameter tensors cut from one buffer; with gaps, each starts 0..3
+    elements after the previous one ends (every alignment occurs)."""
+    offs, pos = [], 0
+    for n in sizes:
+        pos += int(rng.integers(0, 4)) if gaps else (-pos) % 8
+        offs.append(pos)
+        pos += n
+    big = torch.full((pos + 8,), -3.5, dtype=tdt, device="cuda:0")
+    return big, [big[o:o + n] for o, n in zip(offs, sizes)]
+
+
+def _host_grads(rng, sizes, dt):
+    out = []
+    for n in sizes:
+        x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        out.append(x if dt == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16))
+    return out
+
+
+def _want(op, host, order, dt, out_dt):
+    flats = [oracle.flatten(op, h) for h in host]
+    return oracle.unflatten(op, oracle.sync_avg(op, flats, order, dt, out_dt))
+
+
+def _run_case(torch, ddp, sizes, N, order, dt, out_dt, seed, gaps):
+    eb = 4 if dt == "f32" else 2
+    cap = 1 << 16
+    lp = ddp.plan_buckets(sizes, cap, dt)
+    op = oracle.plan_cap(sizes, cap, eb)
+    rng = np.random.default_rng(seed)
+    host = [_host_grads(rng, sizes, dt) for _ in range(N)]
+    keep, binds = [], []
+    for r in range(N):
+        big, views = _carve(torch, sizes, _tdt(torch, dt), rng, gaps)
+        for v, h in zip(views, host[r]):
+            v.copy_(to_dev(h, torch))
+        keep.append(big)
+        binds.append(ddp.bind_params(lp, views))
+    obig, outs = _carve(torch, sizes, _tdt(torch, out_dt), rng, gaps)
+    ps = ddp.param_sync(lp, binds, ddp.bind_params(lp, outs), order)
+    ps()
+    torch.cuda.synchronize()
+    want = _want(op, host, order, dt, out_dt)
+    for p in range(len(sizes)):
+        assert_bits_equal(to_host(outs[p], torch), want[p], f"N={N} {order} {dt}->{out_dt} p={p}")
+    return keep, obig
+
+
+@pytest.mark.parametrize("name,orders", [("resnet50", ("ring", "seq")), ("many_small", ("ring",))])
+def test_full_workload_bitwise(env, name, orders):
+    torch, ddp = env
+    wl = W.workload(name)
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "f32")
+    op = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, 4)
+    N = wl.n_ranks
+    grads = []
+    for r in range(N):
+        flat = torch.empty(lp.total, device="cuda:0")
+        W.device_normal_(flat, r, wl.stream, wl.sigma)
+        # separate tensors per parameter, as autograd leaves them
+        grads.append([flat[o:o + n].clone() for o, n in zip(np.cumsum([0] + wl.numel[:-1]), wl.numel)])
+        del flat
+    host = [[to_host(g, torch) for g in gr] for gr in grads]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    outs = [torch.empty(n, device="cuda:0") for n in wl.numel]
+    obind = ddp.bind_params(lp, outs)
+    flats = [torch.empty(lp.total, device="cuda:0") for _ in range(N)]
+    out_flat = torch.empty(lp.total, device="cuda:0")
+    res = [torch.empty(n, device="cuda:0") for n in wl.numel]
+    rbind = ddp.bind_params(lp, res)
+    for order in orders:
+        print(f"{name} {order}", flush=True)
+        ps = ddp.param_sync(lp, binds, obind, order)
+        for o in outs:
+            o.fill_(float("nan"))
+        ps()
+        # the library's three-step path on the same gradients
+        for r in range(N):
+            ddp.flatten(lp, binds[r], flats[r])
+        ddp.sync_allreduce_avg(lp, flats, out_flat, order)
+        ddp.unflatten(lp, rbind, out_flat)
+        torch.cuda.synchronize()
+        want = _want(op, host, order, "f32", "f32")
+        for p in range(len(wl.numel)):
+            got = to_host(outs[p], torch)
+            assert_bits_equal(got, want[p], f"{name} {order} p={p}")
+            assert_bits_equal(got, to_host(res[p], torch), f"{name} {order} p={p} vs three steps")
+    del grads, outs, flats, out_flat, res
+    torch.cuda.empty_cache()
+
+
+EDGE_SIZES = [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 1023, 1024,
+              1025, 4095, 4096, 4097, 9001, 20000]
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 9, 12])
+@pytest.mark.parametrize("gaps", [False, True])
+def test_random_plans(env, pair, N, gaps):
+    torch, ddp = env
+    dt, out_dt = pair
+    if N == 1 and dt != out_dt:
+        pytest.skip("one rank keeps the input dtype")
+    rng = np.random.default_rng(N * 7 + gaps)
+    sizes = list(EDGE_SIZES) + [int(x) for x in rng.integers(1, 70000, 40)]
+    rng.shuffle(sizes)
+    for order in ("ring", "seq"):
+        _run_case(torch, ddp, sizes, N, order, dt, out_dt, 100 * N + gaps, gaps)
+
+
+@pytest.mark.parametrize("order", ["ring", "seq"])
+def test_in_place_on_rank_zero(env, order):
+    torch, ddp = env
+    rng = np.random.default_rng(5)
+    sizes = list(EDGE_SIZES)
+    N = 4
+    lp = ddp.plan_buckets(sizes, 1 << 15, "f32")
+    op = oracle.plan_cap(sizes, 1 << 15, 4)
+    host = [_host_grads(rng, sizes, "f32") for _ in range(N)]
+    grads = [[to_dev(h, torch) for h in hr] for hr in host]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    ps = ddp.param_sync(lp, binds, binds[0], order)
+    ps()
+    torch.cuda.synchronize()
+    want = _want(op, host, order, "f32", "f32")
+    for p in range(len(sizes)):
+        assert_bits_equal(to_host(grads[0][p], torch), want[p], f"in place p={p}")
+        assert_bits_equal(to_host(grads[1][p], torch), host[1][p], f"rank 1 untouched p={p}")
+
+
+def test_graph_replays_match_eager(env):
+    torch, ddp = env
+    rng = np.random.default_rng(9)
+    sizes = [p.numel for p in W.many_small(n=600)]
+    N = 8
+    lp = ddp.plan_buckets(sizes, 1 << 20, "f32")
+    op = oracle.plan_cap(sizes, 1 << 20, 4)
+    grads = [[torch.empty(n, device="cuda:0") for n in sizes] for _ in range(N)]
+    outs = [torch.empty(n, device="cuda:0") for n in sizes]
+    ps = ddp.param_sync(lp, [ddp.bind_params(lp, g) for g in grads], ddp.bind_params(lp, outs),
+                        "ring")
+
+    def fill():
+        host = [_host_grads(rng, sizes, "f32") for _ in range(N)]
+        for g, h in zip(grads, host):
+            for t, x in zip(g, h):
+                t.copy_(to_dev(x, torch))
+        torch.cuda.synchronize()
+        return host
+
+    fill()
+    ps()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ps()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        host = fill()
+        g.replay()
+        torch.cuda.synchronize()
+        replay = [to_host(o, torch).copy() for o in outs]
+        ps()
+        torch.cuda.synchronize()
+        want = _want(op, host, "ring", "f32", "f32")
+        for p in range(0, len(sizes), 5):
+            assert_bits_equal(replay[p], to_host(outs[p], torch), f"replay {rep} p={p} vs eager")
+            assert_bits_equal(replay[p], want[p], f"replay {rep} p={p} vs oracle")
+
+
+def test_overlaps_are_rejected(env):
+    torch, ddp = env
+    sizes = [1000, 2000, 3000]
+    lp = ddp.plan_buckets(sizes, 1 << 20, "f32")
+    grads = [[torch.zeros(n, device="cuda:0") for n in sizes] for _ in range(2)]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    big = torch.zeros(7000, device="cuda:0")
+    disjoint = ddp.bind_params(lp, [big[0:1000], big[1000:3000], big[3000:6000]])
+    ddp.param_sync(lp, binds, disjoint)                    # accepted
+    # an output that overlaps rank 0's parameter 0 without being it
+    shared = torch.zeros(1010, device="cuda:0")
+    binds_ov = [ddp.bind_params(lp, [shared[10:1010], grads[0][1], grads[0][2]]),
+                ddp.bind_params(lp, grads[1])]
+    out_ov = ddp.bind_params(lp, [shared[0:1000], big[1000:3000], big[3000:6000]])
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.param_sync(lp, binds_ov, out_ov)
+    assert e.value.status == 4                             # DDP_ERR_ALIAS
+    # outputs overlapping each other
+    out_self = ddp.bind_params(lp, [big[0:1000], big[500:2500], big[3000:6000]])
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.param_sync(lp, binds, out_self)
+    assert e.value.status == 4
+    # an output on another parameter's gradient of a rank
+    out_cross = ddp.bind_params(lp, [grads[0][1][:1000], big[1000:3000], big[3000:6000]])
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.param_sync(lp, binds, out_cross)
+    assert e.value.status == 4
+    # in place on the same parameter of one rank: accepted
+    ddp.param_sync(lp, binds, ddp.bind_params(lp, [grads[1][0], big[1000:3000], big[3000:6000]]))
+
+
+def test_gpt_sampled(env):
+    torch, ddp = env
+    wl = W.workload("gpt1p3b")
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "f32")
+    op = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, 4)
+    N, P = wl.n_ranks, op.total
+    reg_off = np.cumsum([0] + wl.numel[:-1]).astype(np.int64)   # registration-order storage
+    stores = []
+    for r in range(N):
+        t = torch.empty(P, device="cuda:0")
+        W.device_normal_(t, r, wl.stream, wl.sigma)
+        stores.append(t)
+    grads = [[t[o:o + n] for o, n in zip(reg_off, wl.numel)] for t in stores]
+    out_store = torch.empty(P, device="cuda:0")
+    outs = [out_store[o:o + n] for o, n in zip(reg_off, wl.numel)]
+    ps = ddp.param_sync(lp, [ddp.bind_params(lp, g) for g in grads], ddp.bind_params(lp, outs),
+                        "ring")
+    print("gpt1p3b param sync ring", flush=True)
+    ps()
+    torch.cuda.synchronize()
+    # sampled flat positions of the plan -> (parameter, element)
+    rng = np.random.default_rng(13)
+    pos = sample_positions(op.bucket_base, op.bucket_len, N, P, rng)
+    base = np.array(op.bucket_base, dtype=np.int64)
+    flat_off = np.array([base[b] + off for b, off in op.param_location()], dtype=np.int64)
+    by_flat = np.argsort(flat_off, kind="stable")
+    nz = by_flat[np.array(wl.numel, dtype=np.int64)[by_flat] > 0]
+    p_of = nz[np.searchsorted(flat_off[nz], pos, side="right") - 1]
+    src = torch.from_numpy(reg_off[p_of] + (pos - flat_off[p_of])).to("cuda:0")
+    vals = np.stack([to_host(t.index_select(0, src), torch) for t in stores], axis=1)
+    lens = np.array(op.bucket_len, dtype=np.int64)
+    b_of = np.searchsorted(base, pos, side="right") - 1
+    while (lens[b_of] == 0).any():
+        b_of[lens[b_of] == 0] += 1
+    want = oracle.sampled_avg(vals, pos - base[b_of], lens[b_of], "ring")
+    assert_bits_equal(to_host(out_store.index_select(0, src), torch), want, "gpt1p3b sampled")
+    del stores, grads, outs, out_store, src
+    torch.cuda.empty_cache()
