@@ -2,6 +2,7 @@
 // and the entry points for the occupancy policy and error text.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -66,6 +67,19 @@ int sgd_blocks_per_cu(int N, bool mom)
     if (N < 0) return 0;
     if (N > 8) return N <= 11 ? (mom ? 10 : 12) : 8;
     return mom ? with_mom[N] : without[N];
+}
+
+// The per-parameter sync (params.hip): the reduce's pattern behind one
+// table entry per block, whose scalar-load latency more resident blocks
+// hide.  Measured at N = 4 (many-small: 16) and N = 8 (ResNet-50 and
+// GPT-1.3B in f32: 10; Llama-7B in bf16: 12); other N take the reduce's cap
+// plus two.
+int params_blocks_per_cu(int N, bool ring, bool bf16)
+{
+    if (N == 4) return 16;
+    if (N == 8) return bf16 ? 12 : 10;
+    const int k = reduce_blocks_per_cu(N, ring);
+    return k > 0 ? std::min(k + 2, 16) : 0;
 }
 
 constexpr int kMaxDevices = 64;

@@ -64,6 +64,7 @@ ddp_status_t launch_split(int64_t blocks, int threads, const char *what, Launch 
 // the dynamic-LDS request that imposes a cap of k (see common.hip).
 int reduce_blocks_per_cu(int N, bool ring);
 int sgd_blocks_per_cu(int N, bool mom);
+int params_blocks_per_cu(int N, bool ring, bool bf16);
 constexpr int kCopyBlocksPerCU = 7;   // flatten / unflatten (256-thread blocks)
 unsigned lds_for_blocks(int k);
 

@@ -26,10 +26,16 @@ using namespace ddp_detail;
 
 namespace {
 
-// A parameter is cut into tiles of kThreads * VEC elements from its own
-// start (the last one shorter), so every address inside a tile has the
-// alignment of the parameter's address.  One table entry per tile, `stride`
-// bytes (16-byte aligned):
+// Vectors per lane: a tile is kThreads * kPsUnroll vectors.  Two (half as
+// many entries and blocks) measured 3-5 % slower than one at every cap.
+constexpr int kPsUnroll = 1;
+
+inline int64_t ps_tile_elems(int in) { return (int64_t)kThreads * kPsUnroll * vec_elems(in); }
+
+// A parameter is cut into tiles of ps_tile_elems elements from its own start
+// (the last one shorter), so every address inside a tile has the alignment
+// of the parameter's address.  One table entry per tile, `stride` bytes
+// (16-byte aligned):
 //   uint64_t addr[N + 1]   ranks 0..N-1, then the output, at the tile's first element
 //   PsMeta                 below
 struct PsMeta {
@@ -37,10 +43,10 @@ struct PsMeta {
     int64_t blen;     // length of that bucket
     uint32_t count;   // elements in the tile, 1..tile
     uint32_t vec;     // 1: every address of the parameter 16-byte aligned
-    uint32_t ring;    // the ring chunks the tile meets: bits 0-5 start rank of
-                      // chunk a, 6-11 of chunk b, 12-21 end of a and 22-31 end
-                      // of b relative to the tile's first element
-    uint32_t pad;
+    uint32_t starts;  // the ring chunks the tile meets: start rank of chunk a
+                      // (bits 0-5) and of chunk b (bits 6-11) ...
+    uint32_t cuts;    // ... and where a (bits 0-15) and b (bits 16-31) end,
+                      // relative to the tile's first element
 };
 
 int64_t ps_stride(int N) { return (8 * (int64_t)(N + 1) + (int64_t)sizeof(PsMeta) + 15) / 16 * 16; }
@@ -146,21 +152,21 @@ __device__ __forceinline__ PsSegs ps_segs(const PsMeta &m)
     s.a_hi = s.b_lo = s.b_hi = m.count;
     s.sa = s.sb = 0;
     if (RING) {
-        s.sa = __builtin_amdgcn_readfirstlane((int)(m.ring & 63u));
-        s.sb = __builtin_amdgcn_readfirstlane((int)((m.ring >> 6) & 63u));
-        s.a_hi = s.b_lo = (int64_t)((m.ring >> 12) & 1023u);
-        s.b_hi = (int64_t)(m.ring >> 22);
+        s.sa = __builtin_amdgcn_readfirstlane((int)(m.starts & 63u));
+        s.sb = __builtin_amdgcn_readfirstlane((int)((m.starts >> 6) & 63u));
+        s.a_hi = s.b_lo = (int64_t)(m.cuts & 0xffffu);
+        s.b_hi = (int64_t)(m.cuts >> 16);
     }
     return s;
 }
 
 // N known at compile time (1..8).  The tile's entry (one batch of scalar
-// loads) gives every address; then all NR vector loads of the lane go out
-// before the ring chunks are looked at, as in the flat reduce.  A lane past
-// the tile's end reads the tile's first vector and drops it.  The loads are
-// not behind a branch (a branch would wait for the entry's flags before
-// fetching its addresses): a tile without the vector path reads 16 bytes
-// of its own entry instead, and drops them.
+// loads) gives every address; then all NR * kPsUnroll vector loads of the
+// lane go out before the ring chunks are looked at, as in the flat reduce.
+// A lane's vector past the tile's end reads the tile's first vector and
+// drops it.  The loads are not behind a branch (a branch would wait for the
+// entry's flags before fetching its addresses): a tile without the vector
+// path reads 16 bytes of its own entry instead, and drops them.
 template <int NR, bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, float inv)
@@ -177,29 +183,37 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
     // before any of them is used
 #pragma unroll
     for (int k = 0; k <= NR; ++k) asm volatile("" : "+s"(ad[k]));
-    const int64_t i0 = (int64_t)threadIdx.x * VEC, cnt = m.count;
+    const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
-    const int64_t off = i0 + VEC <= cnt ? i0 * ISZ : 0;
-    u32x4 v[NR];
+    int64_t i0[kPsUnroll];
+    u32x4 v[kPsUnroll][NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k)
-        v[k] = gld_stream(vec ? ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(e));
+    for (int u = 0; u < kPsUnroll; ++u) {
+        i0[u] = ((int64_t)u * kThreads + threadIdx.x) * VEC;
+        const int64_t off = i0[u] + VEC <= cnt ? i0[u] * ISZ : 0;
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+            v[u][k] = gld_stream(vec ? ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(e));
+    }
     const PsSegs sg = ps_segs<RING>(m);
-    const bool in_a = vec && i0 + VEC <= sg.a_hi;
-    const bool in_b = RING && vec && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
-    if (in_a || in_b) {
-        if constexpr (NR == 1 && IN == OUT) {
-            gst_stream(ad[1] + (uint64_t)(i0 * ISZ), v[0]);
-        } else {
-            float acc[VEC];
-            if (!RING)
-                fold_seq<NR, IN>(v, acc);
-            else
-                fold_ring<NR, IN>(v, in_a ? sg.sa : sg.sb, acc);
-            gstore_vec<IN, OUT>(ad[NR], i0, acc, inv);
+#pragma unroll
+    for (int u = 0; u < kPsUnroll; ++u) {
+        const bool in_a = vec && i0[u] + VEC <= sg.a_hi;
+        const bool in_b = RING && vec && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
+        if (in_a || in_b) {
+            if constexpr (NR == 1 && IN == OUT) {
+                gst_stream(ad[1] + (uint64_t)(i0[u] * ISZ), v[u][0]);
+            } else {
+                float acc[VEC];
+                if (!RING)
+                    fold_seq<NR, IN>(v[u], acc);
+                else
+                    fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
+                gstore_vec<IN, OUT>(ad[NR], i0[u], acc, inv);
+            }
+        } else if (i0[u] < cnt) {
+            params_elems<IN, OUT, RING>(a, NR, m, inv, i0[u], VEC);
         }
-    } else if (i0 < cnt) {
-        params_elems<IN, OUT, RING>(a, NR, m, inv, i0, VEC);
     }
 }
 
@@ -214,20 +228,24 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
     const char *e = table + (first_block + blockIdx.x) * stride;
     const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
     const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + 1));
-    const int64_t i0 = (int64_t)threadIdx.x * VEC, cnt = m.count;
+    const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     const PsSegs sg = ps_segs<RING>(m);
-    const bool in_a = vec && i0 + VEC <= sg.a_hi;
-    const bool in_b = RING && vec && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
 #pragma unroll 1
-    for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
-        const bool mine = pass == 0 ? in_a : in_b;
-        if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
-        float acc[VEC];
-        fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
-        if (mine) gstore_vec<IN, OUT>(a[N], i0, acc, inv);
+    for (int u = 0; u < kPsUnroll; ++u) {
+        const int64_t i0 = ((int64_t)u * kThreads + threadIdx.x) * VEC;
+        const bool in_a = vec && i0 + VEC <= sg.a_hi;
+        const bool in_b = RING && vec && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+#pragma unroll 1
+        for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+            const bool mine = pass == 0 ? in_a : in_b;
+            if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
+            float acc[VEC];
+            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
+            if (mine) gstore_vec<IN, OUT>(a[N], i0, acc, inv);
+        }
+        if (!in_a && !in_b && i0 < cnt) params_elems<IN, OUT, RING>(a, N, m, inv, i0, VEC);
     }
-    if (!in_a && !in_b && i0 < cnt) params_elems<IN, OUT, RING>(a, N, m, inv, i0, VEC);
 }
 
 template <bool RING, int IN, int OUT>
@@ -237,7 +255,7 @@ ddp_status_t launch_params_typed(const ddp_param_sync *ps, hipStream_t st)
     const float inv = 1.0f / (float)N;
     const char *tb = ps->table;
     const int64_t sd = ps->stride;
-    const unsigned lds = lds_for_blocks(reduce_blocks_per_cu(N, RING));
+    const unsigned lds = lds_for_blocks(params_blocks_per_cu(N, RING, IN == kBF16));
     const dim3 b(kThreads);
     return launch_split(ps->n_tiles, kThreads, "parameter sync kernel launch",
                         [&](int64_t b0, unsigned n) {
@@ -304,9 +322,9 @@ ddp_status_t check_param_alias(const ddp_plan *plan, const ddp_binding_t *const 
     return DDP_OK;
 }
 
-// The ring chunks of bucket positions [t0, t0 + count) of a bucket of blen
-// elements over N ranks, as the entry's word.
-uint32_t ring_word(int64_t t0, int64_t count, int64_t blen, int N)
+// The ring chunks met by bucket positions [t0, t0 + count) of a bucket of
+// blen elements over N ranks: the entry's starts and cuts words.
+void ring_words(int64_t t0, int64_t count, int64_t blen, int N, uint32_t *starts, uint32_t *cuts)
 {
     const int64_t C = (blen + N - 1) / N, t1 = t0 + count;
     const int64_t ca = t0 / C, a_end = std::min((ca + 1) * C, blen);
@@ -316,7 +334,8 @@ uint32_t ring_word(int64_t t0, int64_t count, int64_t blen, int N)
         cut_b = (uint32_t)(std::min(std::min((ca + 2) * C, blen), t1) - t0);
         sb = (uint32_t)((ca + 2) % N);
     }
-    return (uint32_t)((ca + 1) % N) | sb << 6 | cut_a << 12 | cut_b << 22;
+    *starts = (uint32_t)((ca + 1) % N) | sb << 6;
+    *cuts = cut_a | cut_b << 16;
 }
 
 }  // namespace
@@ -349,7 +368,7 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
     ddp_status_t st = check_param_alias(plan, R, n_ranks, out_binding, isz, osz);
     if (st != DDP_OK) return st;
 
-    const int64_t T = tile_elems(in), stride = ps_stride(n_ranks);
+    const int64_t T = ps_tile_elems(in), stride = ps_stride(n_ranks);
     int64_t n_tiles = 0;
     for (int32_t p = 0; p < plan->n_params; ++p) n_tiles += (plan->numel[p] + T - 1) / T;
     if (n_tiles > INT64_MAX / stride) return DDP_ERR_OVERFLOW;
@@ -409,7 +428,7 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
                 m.blen = blen;
                 m.count = (uint32_t)std::min(T, n - j0);
                 m.vec = vec ? 1u : 0u;
-                m.ring = ring ? ring_word(m.pos, m.count, blen, n_ranks) : 0u;
+                if (ring) ring_words(m.pos, m.count, blen, n_ranks, &m.starts, &m.cuts);
                 std::memcpy(ent + 8 * (n_ranks + 1), &m, sizeof(m));
                 if (++fill == per_chunk && (st = flush()) != DDP_OK) {
                     ddp_param_sync_free(ps);
