@@ -20,7 +20,8 @@ with its --no-... flag):
   cpu_baseline   the CPU oracle (one thread, and SEQ on all host cores)
   copy_path      flatten + sync + unflatten (eager and graph-replayed), and
                  the same step as one kernel over per-parameter tensors
-  fused_sgd      the average fused into a momentum-SGD step
+  fused_sgd      the average fused into a momentum-SGD step (flat and
+                 per-parameter tensors)
   overlap        syncs beside compute on a second stream
   rank_sweep_GBps, in_place, no_sync, env
 
@@ -595,6 +596,32 @@ def main():
                  "bytes": fb, "unfused_ms": round(res["unfused"], 5),
                  "speedup_vs_unfused": round(res["unfused"] / res["fused"], 3),
                  "step": "momentum SGD (mu 0.9) on f32 parameters; unfused = sync + torch mul_/add_"}
+        # the same step on per-parameter tensors (gradients, parameters and
+        # momentum buffers as autograd and the optimizer keep them)
+        if N * P * wl.in_bytes <= (16 << 30):
+            gviews = []
+            for r in range(N):
+                g = [torch.empty(n, dtype=tin, device=dev) for n in wl.numel]
+                ddp.unflatten(plan, ddp.bind_params(plan, g), flats[r], stream=stream)
+                gviews.append(g)
+            pp = [torch.empty(n, dtype=torch.float32, device=dev).normal_() for n in wl.numel]
+            pm = [torch.zeros(n, dtype=torch.float32, device=dev) for n in wl.numel]
+            step = ddp.param_sgd(plan, [ddp.bind_params(plan, g) for g in gviews],
+                                 ddp.bind_params(plan, pp), ddp.bind_params(plan, pm), None, order)
+            for _ in range(5):
+                step(lr, mu, stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                step(lr, mu, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t_p = a.elapsed_time(b) / args.steps
+            fused["per_parameter"] = {
+                "ms": round(t_p, 5), "GBps": round(fb / (t_p * 1e-3) / 1e9, 1),
+                "step": "the same step on per-parameter gradients, parameters and momentum "
+                        "(ddp_param_sgd_run)"}
+            del gviews, pp, pm, step
         log(f"fused sgd: {fused}")
         del params, mbuf
 

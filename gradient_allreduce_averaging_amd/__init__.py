@@ -96,6 +96,9 @@ def _load():
                                    ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int),
         "ddp_param_sync_run": ([vp, vp], ctypes.c_int),
         "ddp_param_sync_free": ([vp], None),
+        "ddp_param_sgd_create": ([vp, ctypes.POINTER(vp), ctypes.c_int32, vp, vp, vp, ctypes.c_int,
+                                  ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int),
+        "ddp_param_sgd_run": ([vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
         "ddp_accumulate": ([ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
                             ctypes.c_int, vp], ctypes.c_int),
         "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -302,6 +305,57 @@ class ParamSync:
 def param_sync(plan: Plan, rank_bindings: Sequence[Binding], out_binding: Binding,
                order="ring") -> ParamSync:
     return ParamSync(plan, rank_bindings, out_binding, order)
+
+
+class ParamSGD:
+    """Owner of a ``ddp_param_sync_t`` made by ``ddp_param_sgd_create``: every
+    rank's bound gradients averaged and folded into an SGD step on the bound
+    per-parameter f32 ``params`` (and ``momentum`` buffers), optionally storing
+    the average in ``grad_out``.  Calling it with (lr, momentum) enqueues one
+    step.  Keeps every binding (and so its tensors) alive."""
+
+    def __init__(self, plan: Plan, rank_bindings: Sequence[Binding], params: Binding,
+                 momentum: Optional[Binding] = None, grad_out: Optional[Binding] = None,
+                 order="ring", out_dtype=None):
+        self.plan = plan
+        self._keep = [list(rank_bindings), params, momentum, grad_out]
+        for bd in rank_bindings:
+            if bd.dtypes != {plan.dtype}:
+                raise ValueError("rank gradients must have the plan's dtype")
+        for bd in (params, momentum):
+            if bd is not None and bd.dtypes != {F32}:
+                raise ValueError("parameters and momentum must be float32")
+        if grad_out is not None:
+            if len(grad_out.dtypes) != 1:
+                raise ValueError("the averaged gradients must share one dtype")
+            out_dt = next(iter(grad_out.dtypes))
+        else:
+            out_dt = plan.dtype if out_dtype is None else (BF16 if out_dtype == "bf16" else F32)
+        self.out_dtype = out_dt
+        handles = (ctypes.c_void_p * len(rank_bindings))(*[bd.handle for bd in rank_bindings])
+        h = ctypes.c_void_p()
+        _check(lib.ddp_param_sgd_create(plan.handle, handles, len(rank_bindings),
+                                        grad_out.handle if grad_out is not None else None,
+                                        params.handle,
+                                        momentum.handle if momentum is not None else None,
+                                        _ORDERS[order], out_dt, ctypes.byref(h)),
+               "ddp_param_sgd_create")
+        self._h = h
+
+    def __call__(self, lr: float, momentum: float = 0.0, stream=None):
+        _check(lib.ddp_param_sgd_run(self._h, lr, momentum, _stream_handle(stream)),
+               "ddp_param_sgd_run")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and lib is not None:
+            lib.ddp_param_sync_free(h)
+
+
+def param_sgd(plan: Plan, rank_bindings: Sequence[Binding], params: Binding,
+              momentum: Optional[Binding] = None, grad_out: Optional[Binding] = None,
+              order="ring", out_dtype=None) -> ParamSGD:
+    return ParamSGD(plan, rank_bindings, params, momentum, grad_out, order, out_dtype)
 
 
 def _check_flat(plan: Plan, binding: Binding, flat):

@@ -58,12 +58,15 @@ struct ddp_binding {
 };
 
 // A synchronisation over per-parameter tensors (params.hip): one table entry
-// per tile of each parameter, with every rank's address and the output's.
+// per tile of each parameter, with every rank's address and those of the
+// tensors it writes.
 struct ddp_param_sync {
     int device = -1;
     int n_ranks = 0;
     int order = 0;
     int in = 0, out = 0;                      // ddp_dtype_t of inputs and outputs
+    bool sgd = false;                         // built by ddp_param_sgd_create
+    bool momentum = false;                    // sgd: with a momentum buffer
     char *table = nullptr;                    // device array, n_tiles * stride bytes
     int64_t n_tiles = 0;
     int64_t stride = 0;                       // bytes per entry

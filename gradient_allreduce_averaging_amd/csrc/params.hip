@@ -1,17 +1,22 @@
-// The synchronisation over per-parameter gradient tensors in one kernel
-// (ddp_param_sync_create / _run / _free).  Every rank's gradients are read
-// where they lie, with no flatten, folded in the fixed order their flat
-// positions define, scaled, and written to per-parameter outputs, with no
-// unflatten.  The result is that of flatten, then ddp_sync_allreduce_avg,
-// then unflatten, bit for bit; the bytes moved are those of the sync alone
-// (N reads and one write per element), where the three steps move
-// 2N + N + 1 + 2 element-widths per element.
+// The synchronisation over per-parameter tensors in one kernel.
+//
+// ddp_param_sync_*: every rank's gradients are read where they lie, with no
+// flatten, folded in the fixed order their flat positions define, scaled,
+// and written to per-parameter outputs, with no unflatten.  The result is
+// that of flatten, then ddp_sync_allreduce_avg, then unflatten, bit for bit;
+// the bytes moved are those of the sync alone (N reads and one write per
+// element), where the three steps move 2N + N + 1 + 2 element-widths.
+//
+// ddp_param_sgd_*: the same average folded into a (momentum) SGD step on
+// per-parameter f32 parameters, the per-parameter form of
+// ddp_sync_sgd_update.
 //
 // Pages: [DDP] "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel) 4.2 (the
 //        gradients are copied into a flat bucket, averaged, and viewed back;
-//        gradient_as_bucket_view drops a copy);
+//        gradient_as_bucket_view drops a copy), 5.3 (the update rule);
 //        [TR24] "(24) NCCL通信与分布式数据并行" (tech-renaissance.cn) 八
-//        (gradients laid out by region so that no copy is needed).
+//        (gradients laid out by region so that no copy is needed), 九 (the
+//        scale could be absorbed into the optimizer update).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,7 +41,12 @@ inline int64_t ps_tile_elems(int in) { return (int64_t)kThreads * kPsUnroll * ve
 // (the last one shorter), so every address inside a tile has the alignment
 // of the parameter's address.  One table entry per tile, `stride` bytes
 // (16-byte aligned):
-//   uint64_t addr[N + 1]   ranks 0..N-1, then the output, at the tile's first element
+//   uint64_t addr[N + X]   ranks 0..N-1, then the X tensors written, at the
+//                          tile's first element:
+//                            sync: the output (X = 1)
+//                            SGD:  the averaged gradient (0 if not stored),
+//                                  the parameters, the momentum (0 if none)
+//                                  (X = 3)
 //   PsMeta                 below
 struct PsMeta {
     int64_t pos;      // position of the tile's first element inside its bucket
@@ -49,10 +59,15 @@ struct PsMeta {
                       // relative to the tile's first element
 };
 
-int64_t ps_stride(int N) { return (8 * (int64_t)(N + 1) + (int64_t)sizeof(PsMeta) + 15) / 16 * 16; }
+constexpr int kSyncExtra = 1, kSgdExtra = 3;
 
-// Streaming accesses at an address read from the table, typed as global
-// memory so that they compile to global (not flat) instructions.
+int64_t ps_stride(int N, int extra)
+{
+    return (8 * (int64_t)(N + extra) + (int64_t)sizeof(PsMeta) + 15) / 16 * 16;
+}
+
+// Accesses at addresses read from the table, typed as global memory so that
+// they compile to global (not flat) instructions.
 typedef __attribute__((address_space(1))) u32x2 g_u32x2;
 typedef __attribute__((address_space(1))) float g_f32;
 typedef __attribute__((address_space(1))) uint32_t g_u32;
@@ -68,31 +83,68 @@ __device__ __forceinline__ void gst_stream(uint64_t addr, const u32x2 &v)
     __builtin_nontemporal_store(v, reinterpret_cast<g_u32x2 *>(addr));
 }
 
-// Scale, convert and store one vector of accumulators at tile element i0 of
-// the output at `out` (the flat kernels' store_vec, on a table address).
+// Convert and store one vector of averages y at tile element i0 of the
+// tensor at `out` (when `write`); for a bf16 output y becomes the stored
+// value widened back to f32 either way.
+template <int IN, int OUT>
+__device__ __forceinline__ void gstore_y(uint64_t out, int64_t i0, float *y, bool write)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    if (OUT == kF32) {
+        u32x4 o;
+        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
+        if (write) gst_stream(out + (uint64_t)i0 * 4, o);
+    } else {
+        uint32_t h[VEC];
+        for (int e = 0; e < VEC; ++e) {
+            h[e] = bf16_rne(y[e]);
+            y[e] = widen_bf16(h[e]);
+        }
+        if (VEC == 4) {
+            u32x2 o;
+            o[0] = h[0] | (h[1] << 16);
+            o[1] = h[2] | (h[3] << 16);
+            if (write) gst_stream(out + (uint64_t)i0 * 2, o);
+        } else {
+            u32x4 o;
+            for (int w = 0; w < 4; ++w) o[w] = h[2 * w] | (h[2 * w + 1] << 16);
+            if (write) gst_stream(out + (uint64_t)i0 * 2, o);
+        }
+    }
+}
+
+// Scale, convert and store one vector of accumulators.
 template <int IN, int OUT>
 __device__ __forceinline__ void gstore_vec(uint64_t out, int64_t i0, const float *acc, float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     float y[VEC];
     for (int e = 0; e < VEC; ++e) y[e] = acc[e] * inv;
-    if (OUT == kF32) {
-        u32x4 o;
-        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
-        gst_stream(out + (uint64_t)i0 * 4, o);
-    } else {
-        uint32_t h[VEC];
-        for (int e = 0; e < VEC; ++e) h[e] = bf16_rne(y[e]);
-        if (VEC == 4) {
-            u32x2 o;
-            o[0] = h[0] | (h[1] << 16);
-            o[1] = h[2] | (h[3] << 16);
-            gst_stream(out + (uint64_t)i0 * 2, o);
-        } else {
-            u32x4 o;
-            for (int w = 0; w < 4; ++w) o[w] = h[2 * w] | (h[2 * w + 1] << 16);
-            gst_stream(out + (uint64_t)i0 * 2, o);
+    gstore_y<IN, OUT>(out, i0, y, true);
+}
+
+// The SGD epilogue on one vector of averages y (the flat kernels' sgd_vec,
+// on table addresses): y stored to grad_out when that is not 0 (bf16: y
+// becomes the stored value widened back), then the lane's parameter vectors
+// pv (and momentum mv), already loaded, updated and stored.
+template <int IN, int OUT, bool MOM>
+__device__ __forceinline__ void gsgd_vec(uint64_t gout, uint64_t param, uint64_t mom, int64_t i0,
+                                         float *y, const u32x4 *pv, const u32x4 *mv, float lr,
+                                         float mu)
+{
+    constexpr int PV = (IN == kF32 ? 4 : 8) / 4;
+    gstore_y<IN, OUT>(gout, i0, y, gout != 0);
+#pragma unroll
+    for (int j = 0; j < PV; ++j) {
+        u32x4 po, mo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
+            po[w] = __float_as_uint(sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, lr, mu));
+            mo[w] = __float_as_uint(m);
         }
+        gst_stream(param + (uint64_t)(i0 + 4 * j) * 4, po);
+        if (MOM) gst_stream(mom + (uint64_t)(i0 + 4 * j) * 4, mo);
     }
 }
 
@@ -103,7 +155,26 @@ __device__ __forceinline__ float gload_elem(uint64_t a, int64_t i)
     return widen_bf16(*reinterpret_cast<const g_u16 *>(a + (uint64_t)i * 2));
 }
 
-// Per-element path: tile elements [i0, i0 + cnt) clipped to the tile.
+// The scaled average of tile element i, one element at a time (N >= 2).
+template <int IN, bool RING>
+__device__ __forceinline__ float ps_avg_elem(const uint64_t *a, int N, const PsMeta &m, float inv,
+                                             int64_t i)
+{
+    int r = 0;
+    if (RING) {
+        const int64_t C = (m.blen + N - 1) / N;
+        r = (int)(((m.pos + i) / C + 1) % N);
+    }
+    float acc = gload_elem<IN>(a[r], i);
+    if (!RING) acc = 0.0f + acc;
+    for (int k = 1; k < N; ++k) {
+        r = wrap(r + 1, N);
+        acc = acc + gload_elem<IN>(a[r], i);
+    }
+    return acc * inv;
+}
+
+// Per-element path of the sync: tile elements [i0, i0 + cnt) clipped to the tile.
 template <int IN, int OUT, bool RING>
 __device__ void params_elems(const uint64_t *a, int N, const PsMeta &m, float inv, int64_t i0,
                              int cnt)
@@ -121,22 +192,36 @@ __device__ void params_elems(const uint64_t *a, int N, const PsMeta &m, float in
                     *reinterpret_cast<const g_u16 *>(a[0] + (uint64_t)i * 2);
             continue;
         }
-        int r = 0;
-        if (RING) {
-            const int64_t C = (m.blen + N - 1) / N;
-            r = (int)(((m.pos + i) / C + 1) % N);
-        }
-        float acc = gload_elem<IN>(a[r], i);
-        if (!RING) acc = 0.0f + acc;
-        for (int k = 1; k < N; ++k) {
-            r = wrap(r + 1, N);
-            acc = acc + gload_elem<IN>(a[r], i);
-        }
-        const float y = acc * inv;
+        const float y = ps_avg_elem<IN, RING>(a, N, m, inv, i);
         if (OUT == kF32)
             *reinterpret_cast<g_f32 *>(out + (uint64_t)i * 4) = y;
         else
             *reinterpret_cast<g_u16 *>(out + (uint64_t)i * 2) = (uint16_t)bf16_rne(y);
+    }
+}
+
+// Per-element path of the SGD step.  N == 1 takes the input as the average.
+template <int IN, int OUT, bool RING, bool MOM>
+__device__ void params_sgd_elems(const uint64_t *a, int N, const PsMeta &m, float inv, float lr,
+                                 float mu, int64_t i0, int cnt)
+{
+    const uint64_t gout = a[N], param = a[N + 1], mom = a[N + 2];
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t i = i0 + e;
+        if (i >= (int64_t)m.count) break;
+        const float y = N == 1 ? gload_elem<IN>(a[0], i) : ps_avg_elem<IN, RING>(a, N, m, inv, i);
+        float g = y;
+        if (OUT == kBF16) {
+            const uint32_t h = bf16_rne(y);
+            g = widen_bf16(h);
+            if (gout) *reinterpret_cast<g_u16 *>(gout + (uint64_t)i * 2) = (uint16_t)h;
+        } else if (gout) {
+            *reinterpret_cast<g_f32 *>(gout + (uint64_t)i * 4) = y;
+        }
+        g_f32 *pp = reinterpret_cast<g_f32 *>(param + (uint64_t)i * 4);
+        float mm = MOM ? *reinterpret_cast<const g_f32 *>(mom + (uint64_t)i * 4) : 0.0f;
+        *pp = sgd_elem<MOM>(*pp, g, mm, lr, mu);
+        if (MOM) *reinterpret_cast<g_f32 *>(mom + (uint64_t)i * 4) = mm;
     }
 }
 
@@ -160,13 +245,34 @@ __device__ __forceinline__ PsSegs ps_segs(const PsMeta &m)
     return s;
 }
 
-// N known at compile time (1..8).  The tile's entry (one batch of scalar
-// loads) gives every address; then all NR * kPsUnroll vector loads of the
-// lane go out before the ring chunks are looked at, as in the flat reduce.
-// A lane's vector past the tile's end reads the tile's first vector and
-// drops it.  The loads are not behind a branch (a branch would wait for the
-// entry's flags before fetching its addresses): a tile without the vector
-// path reads 16 bytes of its own entry instead, and drops them.
+// The tile's entry: every address and the metadata, fetched in one batch of
+// scalar loads before any of them is used (a use behind a branch would
+// otherwise wait for the flags before fetching its address).
+template <int NA>
+struct PsEntry {
+    uint64_t ad[NA];
+    PsMeta m;
+};
+
+template <int NA>
+__device__ __forceinline__ PsEntry<NA> ps_entry(const char *e)
+{
+    PsEntry<NA> t;
+    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
+#pragma unroll
+    for (int k = 0; k < NA; ++k) t.ad[k] = a[k];
+    t.m = *reinterpret_cast<const PsMeta *>(e + 8 * NA);
+#pragma unroll
+    for (int k = 0; k < NA; ++k) asm volatile("" : "+s"(t.ad[k]));
+    return t;
+}
+
+// Sync, N known at compile time (1..8).  After the entry, all NR *
+// kPsUnroll vector loads of the lane go out before the ring chunks are
+// looked at, as in the flat reduce.  A lane's vector past the tile's end
+// reads the tile's first vector and drops it; a tile without the vector
+// path reads 16 bytes of its own entry instead, and drops them (the loads
+// are not behind a branch).
 template <int NR, bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, float inv)
@@ -174,15 +280,8 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     const char *e = table + (first_block + blockIdx.x) * stride;
-    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
-    uint64_t ad[NR + 1];
-#pragma unroll
-    for (int k = 0; k <= NR; ++k) ad[k] = a[k];
-    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (NR + 1));
-    // every address is fetched in the entry's one batch of scalar loads,
-    // before any of them is used
-#pragma unroll
-    for (int k = 0; k <= NR; ++k) asm volatile("" : "+s"(ad[k]));
+    const PsEntry<NR + kSyncExtra> t = ps_entry<NR + kSyncExtra>(e);
+    const PsMeta &m = t.m;
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     int64_t i0[kPsUnroll];
@@ -193,7 +292,7 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
         const int64_t off = i0[u] + VEC <= cnt ? i0[u] * ISZ : 0;
 #pragma unroll
         for (int k = 0; k < NR; ++k)
-            v[u][k] = gld_stream(vec ? ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(e));
+            v[u][k] = gld_stream(vec ? t.ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(e));
     }
     const PsSegs sg = ps_segs<RING>(m);
 #pragma unroll
@@ -202,23 +301,24 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
         const bool in_b = RING && vec && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
         if (in_a || in_b) {
             if constexpr (NR == 1 && IN == OUT) {
-                gst_stream(ad[1] + (uint64_t)(i0[u] * ISZ), v[u][0]);
+                gst_stream(t.ad[1] + (uint64_t)(i0[u] * ISZ), v[u][0]);
             } else {
                 float acc[VEC];
                 if (!RING)
                     fold_seq<NR, IN>(v[u], acc);
                 else
                     fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
-                gstore_vec<IN, OUT>(ad[NR], i0[u], acc, inv);
+                gstore_vec<IN, OUT>(t.ad[NR], i0[u], acc, inv);
             }
         } else if (i0[u] < cnt) {
-            params_elems<IN, OUT, RING>(a, NR, m, inv, i0[u], VEC);
+            params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(e), NR, m, inv, i0[u],
+                                        VEC);
         }
     }
 }
 
-// Any N up to DDP_MAX_RANKS: one pass per ring chunk the wave's lanes meet,
-// folded with fold_looped from the entry's addresses.
+// Sync, any N up to DDP_MAX_RANKS: one pass per ring chunk the wave's lanes
+// meet, folded with fold_looped from the entry's addresses.
 template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first_block, float inv)
@@ -227,7 +327,7 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     const char *e = table + (first_block + blockIdx.x) * stride;
     const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
-    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + 1));
+    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + kSyncExtra));
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     const PsSegs sg = ps_segs<RING>(m);
@@ -248,8 +348,114 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
     }
 }
 
+// SGD, N known at compile time (1..8): the gradient vectors of every rank
+// and the lane's parameter (and momentum) vectors are loaded together, the
+// average folded and scaled, optionally stored, and the parameters updated.
+// Parameters are f32: one 16-byte vector per 4 elements, so a bf16 lane (8
+// elements) moves two.
+template <int NR, bool RING, int IN, int OUT, bool MOM>
+__global__ void __launch_bounds__(kThreads)
+params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, float inv,
+                float lr, float mu)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    constexpr int PV = VEC / 4;
+    const char *e = table + (first_block + blockIdx.x) * stride;
+    const PsEntry<NR + kSgdExtra> t = ps_entry<NR + kSgdExtra>(e);
+    const PsMeta &m = t.m;
+    const uint64_t gout = t.ad[NR], param = t.ad[NR + 1], mom = t.ad[NR + 2];
+    const uint64_t dummy = reinterpret_cast<uint64_t>(e);
+    const int64_t cnt = m.count;
+    const bool vec = m.vec && cnt >= VEC;
+    int64_t i0[kPsUnroll];
+    u32x4 v[kPsUnroll][NR], pv[kPsUnroll][PV], mv[kPsUnroll][PV];
+#pragma unroll
+    for (int u = 0; u < kPsUnroll; ++u) {
+        i0[u] = ((int64_t)u * kThreads + threadIdx.x) * VEC;
+        const bool whole = i0[u] + VEC <= cnt;
+        const int64_t go = whole ? i0[u] * ISZ : 0, po = whole ? i0[u] * 4 : 0;
+#pragma unroll
+        for (int k = 0; k < NR; ++k) v[u][k] = gld_stream(vec ? t.ad[k] + (uint64_t)go : dummy);
+#pragma unroll
+        for (int j = 0; j < PV; ++j) {
+            pv[u][j] = gld_stream(vec ? param + (uint64_t)(po + 16 * j) : dummy);
+            if (MOM) mv[u][j] = gld_stream(vec ? mom + (uint64_t)(po + 16 * j) : dummy);
+        }
+    }
+    const PsSegs sg = ps_segs<RING>(m);
+#pragma unroll
+    for (int u = 0; u < kPsUnroll; ++u) {
+        const bool in_a = vec && i0[u] + VEC <= sg.a_hi;
+        const bool in_b = RING && vec && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
+        if (in_a || in_b) {
+            float y[VEC];
+            if (!RING || NR == 1)
+                fold_seq<NR, IN>(v[u], y);
+            else
+                fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, y);
+            if (NR > 1) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
+            }
+            gsgd_vec<IN, OUT, MOM>(gout, param, mom, i0[u], y, pv[u], mv[u], lr, mu);
+        } else if (i0[u] < cnt) {
+            params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(e), NR, m, inv,
+                                                 lr, mu, i0[u], VEC);
+        }
+    }
+}
+
+// SGD, any N up to DDP_MAX_RANKS: the lane's parameter (and momentum)
+// vectors first, then the ranks folded as in params_many.
+template <bool RING, int IN, int OUT, bool MOM>
+__global__ void __launch_bounds__(kThreads)
+params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t first_block,
+                float inv, float lr, float mu)
+{
+    constexpr int VEC = IN == kF32 ? 4 : 8;
+    constexpr int ISZ = IN == kF32 ? 4 : 2;
+    constexpr int PV = VEC / 4;
+    const char *e = table + (first_block + blockIdx.x) * stride;
+    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
+    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + kSgdExtra));
+    const uint64_t gout = a[N], param = a[N + 1], mom = a[N + 2];
+    const int64_t cnt = m.count;
+    const bool vec = m.vec && cnt >= VEC;
+    const PsSegs sg = ps_segs<RING>(m);
+#pragma unroll 1
+    for (int u = 0; u < kPsUnroll; ++u) {
+        const int64_t i0 = ((int64_t)u * kThreads + threadIdx.x) * VEC;
+        const bool in_a = vec && i0 + VEC <= sg.a_hi;
+        const bool in_b = RING && vec && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
+        u32x4 pv[PV], mv[PV];
+        if (vec) {   // a lane past the end reads the tile's first vectors and drops them
+            const int64_t po = i0 + VEC <= cnt ? i0 * 4 : 0;
+#pragma unroll
+            for (int j = 0; j < PV; ++j) {
+                pv[j] = gld_stream(param + (uint64_t)(po + 16 * j));
+                if (MOM) mv[j] = gld_stream(mom + (uint64_t)(po + 16 * j));
+            }
+        }
+#pragma unroll 1
+        for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+            const bool mine = pass == 0 ? in_a : in_b;
+            if (!__builtin_amdgcn_ballot_w64(mine)) continue;
+            float y[VEC];
+            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, y);
+            if (mine) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
+                gsgd_vec<IN, OUT, MOM>(gout, param, mom, i0, y, pv, mv, lr, mu);
+            }
+        }
+        if (!in_a && !in_b && i0 < cnt)
+            params_sgd_elems<IN, OUT, RING, MOM>(a, N, m, inv, lr, mu, i0, VEC);
+    }
+}
+
 template <bool RING, int IN, int OUT>
-ddp_status_t launch_params_typed(const ddp_param_sync *ps, hipStream_t st)
+ddp_status_t launch_sync_typed(const ddp_param_sync *ps, hipStream_t st)
 {
     const int N = ps->n_ranks;
     const float inv = 1.0f / (float)N;
@@ -274,32 +480,78 @@ ddp_status_t launch_params_typed(const ddp_param_sync *ps, hipStream_t st)
     });
 }
 
-template <bool RING>
-ddp_status_t launch_params(const ddp_param_sync *ps, hipStream_t st)
+template <bool RING, int IN, int OUT, bool MOM>
+ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, float lr, float mu, hipStream_t st)
 {
-    if (ps->in == DDP_F32 && ps->out == DDP_F32) return launch_params_typed<RING, kF32, kF32>(ps, st);
-    if (ps->in == DDP_BF16) return launch_params_typed<RING, kBF16, kBF16>(ps, st);
-    return launch_params_typed<RING, kF32, kBF16>(ps, st);
+    const int N = ps->n_ranks;
+    const float inv = 1.0f / (float)N;
+    const char *tb = ps->table;
+    const int64_t sd = ps->stride;
+    const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
+    const dim3 b(kThreads);
+    return launch_split(ps->n_tiles, kThreads, "parameter SGD kernel launch",
+                        [&](int64_t b0, unsigned n) {
+        const dim3 g(n);
+        switch (N) {
+        case 1: params_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 2: params_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 3: params_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 4: params_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 5: params_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 6: params_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 7: params_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        case 8: params_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
+        default: params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, N, b0, inv, lr, mu); break;
+        }
+    });
 }
 
-// The outputs may not overlap each other, and may overlap an input only as
-// the same parameter's gradient of one rank, exactly (in place: each element
-// is read before it is written, by the same thread).  Inputs may overlap
-// each other: they are only read.
+template <bool RING>
+ddp_status_t launch_sync(const ddp_param_sync *ps, hipStream_t st)
+{
+    if (ps->in == DDP_F32 && ps->out == DDP_F32) return launch_sync_typed<RING, kF32, kF32>(ps, st);
+    if (ps->in == DDP_BF16) return launch_sync_typed<RING, kBF16, kBF16>(ps, st);
+    return launch_sync_typed<RING, kF32, kBF16>(ps, st);
+}
+
+template <bool RING, bool MOM>
+ddp_status_t launch_sgd(const ddp_param_sync *ps, float lr, float mu, hipStream_t st)
+{
+    if (ps->in == DDP_F32 && ps->out == DDP_F32)
+        return launch_sgd_typed<RING, kF32, kF32, MOM>(ps, lr, mu, st);
+    if (ps->in == DDP_BF16) return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ps, lr, mu, st);
+    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ps, lr, mu, st);
+}
+
+// A set of per-parameter tensors the kernel writes.
+struct Written {
+    const ddp_binding_t *bd;   // null: not used
+    int esz;                   // element size
+    bool in_place_ok;          // may be exactly the same parameter's gradient of one rank
+};
+
+// Written tensors may not overlap each other, and may overlap an input only
+// as the same parameter's gradient of one rank, exactly, where the set
+// allows it (in place: each element is read before it is written, by the
+// same thread).  Inputs may overlap each other: they are only read.
 ddp_status_t check_param_alias(const ddp_plan *plan, const ddp_binding_t *const *ranks, int N,
-                               const ddp_binding_t *out, int isz, int osz)
+                               int isz, const Written *w, int nw)
 {
     struct Iv {
         uint64_t lo, hi;
         int32_t p;
+        bool in_place_ok;
     };
     std::vector<Iv> outs;
     try {
-        outs.reserve((size_t)plan->n_params);
-        for (int32_t p = 0; p < plan->n_params; ++p) {
-            if (plan->numel[p] == 0) continue;
-            const uint64_t lo = out->param_addr[p];
-            outs.push_back({lo, lo + (uint64_t)plan->numel[p] * (uint64_t)osz, p});
+        for (int k = 0; k < nw; ++k) {
+            if (!w[k].bd) continue;
+            for (int32_t p = 0; p < plan->n_params; ++p) {
+                if (plan->numel[p] == 0) continue;
+                const uint64_t lo = w[k].bd->param_addr[p];
+                outs.push_back({lo, lo + (uint64_t)plan->numel[p] * (uint64_t)w[k].esz, p,
+                                w[k].in_place_ok});
+            }
         }
     } catch (...) {
         return DDP_ERR_NOMEM;
@@ -307,7 +559,7 @@ ddp_status_t check_param_alias(const ddp_plan *plan, const ddp_binding_t *const 
     std::sort(outs.begin(), outs.end(), [](const Iv &x, const Iv &y) { return x.lo < y.lo; });
     for (size_t k = 1; k < outs.size(); ++k)
         if (outs[k].lo < outs[k - 1].hi) return DDP_ERR_ALIAS;
-    // outs are disjoint and sorted, so their ends are sorted too
+    // written intervals are disjoint and sorted, so their ends are sorted too
     for (int r = 0; r < N; ++r) {
         for (int32_t p = 0; p < plan->n_params; ++p) {
             if (plan->numel[p] == 0) continue;
@@ -316,7 +568,8 @@ ddp_status_t check_param_alias(const ddp_plan *plan, const ddp_binding_t *const 
             auto it = std::upper_bound(outs.begin(), outs.end(), lo,
                                        [](uint64_t v, const Iv &x) { return v < x.hi; });
             for (; it != outs.end() && it->lo < hi; ++it)
-                if (!(it->lo == lo && it->hi == hi && it->p == p)) return DDP_ERR_ALIAS;
+                if (!(it->in_place_ok && it->lo == lo && it->hi == hi && it->p == p))
+                    return DDP_ERR_ALIAS;
         }
     }
     return DDP_OK;
@@ -338,16 +591,12 @@ void ring_words(int64_t t0, int64_t count, int64_t blen, int N, uint32_t *starts
     *cuts = cut_a | cut_b << 16;
 }
 
-}  // namespace
-
-extern "C" {
-
-ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *const *rank_bindings,
-                                   int32_t n_ranks, const ddp_binding_t *out_binding,
-                                   ddp_order_t order, ddp_dtype_t out_dtype,
-                                   ddp_param_sync_t **out)
+// Validates the bindings and builds the device table of a per-parameter
+// sync (w: the written sets, in entry order).
+ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32_t n_ranks,
+                    const Written *w, int nw, ddp_order_t order, ddp_dtype_t out_dtype, bool sgd,
+                    ddp_param_sync_t **out)
 {
-    if (!plan || !rank_bindings || !out_binding || !out) return DDP_ERR_INVALID_ARG;
     if (n_ranks < 1 || !dtype_ok(out_dtype)) return DDP_ERR_INVALID_ARG;
     if (order != DDP_ORDER_SEQUENTIAL && order != DDP_ORDER_RING) return DDP_ERR_INVALID_ARG;
     if (n_ranks > DDP_MAX_RANKS) return DDP_ERR_UNSUPPORTED;
@@ -356,19 +605,21 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
     int dev = -1;
     hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) return hip_fail("hipGetDevice", he);
-    const int isz = dtype_size(in), osz = dtype_size(out_dtype);
-    const ddp_binding_t *const *R = rank_bindings;
-    for (int r = 0; r <= n_ranks; ++r) {
-        const ddp_binding_t *bd = r < n_ranks ? R[r] : out_binding;
-        if (!bd || bd->plan != plan || bd->device != dev) return DDP_ERR_INVALID_ARG;
-        const int esz = r < n_ranks ? isz : osz;
+    const int isz = dtype_size(in);
+    auto usable = [&](const ddp_binding_t *bd, int esz) {
+        if (bd->plan != plan || bd->device != dev) return false;
         for (int32_t p = 0; p < plan->n_params; ++p)
-            if (plan->numel[p] > 0 && bd->param_addr[p] % (uint64_t)esz) return DDP_ERR_INVALID_ARG;
-    }
-    ddp_status_t st = check_param_alias(plan, R, n_ranks, out_binding, isz, osz);
+            if (plan->numel[p] > 0 && bd->param_addr[p] % (uint64_t)esz) return false;
+        return true;
+    };
+    for (int r = 0; r < n_ranks; ++r)
+        if (!R[r] || !usable(R[r], isz)) return DDP_ERR_INVALID_ARG;
+    for (int k = 0; k < nw; ++k)
+        if (w[k].bd && !usable(w[k].bd, w[k].esz)) return DDP_ERR_INVALID_ARG;
+    ddp_status_t st = check_param_alias(plan, R, n_ranks, isz, w, nw);
     if (st != DDP_OK) return st;
 
-    const int64_t T = ps_tile_elems(in), stride = ps_stride(n_ranks);
+    const int64_t T = ps_tile_elems(in), stride = ps_stride(n_ranks, nw);
     int64_t n_tiles = 0;
     for (int32_t p = 0; p < plan->n_params; ++p) n_tiles += (plan->numel[p] + T - 1) / T;
     if (n_tiles > INT64_MAX / stride) return DDP_ERR_OVERFLOW;
@@ -379,6 +630,8 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
     ps->order = order;
     ps->in = in;
     ps->out = out_dtype;
+    ps->sgd = sgd;
+    ps->momentum = sgd && w[2].bd != nullptr;
     ps->n_tiles = n_tiles;
     ps->stride = stride;
     if (n_tiles == 0) {
@@ -414,14 +667,17 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
         for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
             const int32_t p = plan->slot_param[s];
             const int64_t n = plan->numel[p];
-            bool vec = out_binding->param_addr[p] % 16 == 0;
+            bool vec = true;
             for (int r = 0; r < n_ranks; ++r) vec = vec && R[r]->param_addr[p] % 16 == 0;
+            for (int k = 0; k < nw; ++k) vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 16 == 0);
             for (int64_t j0 = 0; j0 < n; j0 += T) {
                 char *ent = host.data() + fill * stride;
                 uint64_t *addr = reinterpret_cast<uint64_t *>(ent);
                 for (int r = 0; r < n_ranks; ++r)
                     addr[r] = R[r]->param_addr[p] + (uint64_t)(j0 * isz);
-                addr[n_ranks] = out_binding->param_addr[p] + (uint64_t)(j0 * osz);
+                for (int k = 0; k < nw; ++k)
+                    addr[n_ranks + k] =
+                        w[k].bd ? w[k].bd->param_addr[p] + (uint64_t)(j0 * w[k].esz) : 0;
                 PsMeta m;
                 std::memset(&m, 0, sizeof(m));
                 m.pos = plan->param_offset[p] + j0;
@@ -429,7 +685,7 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
                 m.count = (uint32_t)std::min(T, n - j0);
                 m.vec = vec ? 1u : 0u;
                 if (ring) ring_words(m.pos, m.count, blen, n_ranks, &m.starts, &m.cuts);
-                std::memcpy(ent + 8 * (n_ranks + 1), &m, sizeof(m));
+                std::memcpy(ent + 8 * (n_ranks + nw), &m, sizeof(m));
                 if (++fill == per_chunk && (st = flush()) != DDP_OK) {
                     ddp_param_sync_free(ps);
                     return st;
@@ -445,17 +701,61 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
     return DDP_OK;
 }
 
-ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *ps, void *stream)
+ddp_status_t check_run(const ddp_param_sync_t *ps, bool sgd)
 {
-    if (!ps) return DDP_ERR_INVALID_ARG;
+    if (!ps || ps->sgd != sgd) return DDP_ERR_INVALID_ARG;
     int dev = -1;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-    if (dev != ps->device) return DDP_ERR_INVALID_ARG;
-    if (ps->n_tiles == 0) return DDP_OK;
+    return dev == ps->device ? DDP_OK : DDP_ERR_INVALID_ARG;
+}
+
+}  // namespace
+
+extern "C" {
+
+ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *const *rank_bindings,
+                                   int32_t n_ranks, const ddp_binding_t *out_binding,
+                                   ddp_order_t order, ddp_dtype_t out_dtype,
+                                   ddp_param_sync_t **out)
+{
+    if (!plan || !rank_bindings || !out_binding || !out) return DDP_ERR_INVALID_ARG;
+    const Written w[kSyncExtra] = {{out_binding, dtype_size(out_dtype), true}};
+    return create(plan, rank_bindings, n_ranks, w, kSyncExtra, order, out_dtype, false, out);
+}
+
+ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *ps, void *stream)
+{
+    const ddp_status_t s = check_run(ps, false);
+    if (s != DDP_OK || ps->n_tiles == 0) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return ps->order == DDP_ORDER_RING && ps->n_ranks > 1 ? launch_params<true>(ps, st)
-                                                          : launch_params<false>(ps, st);
+    return ps->order == DDP_ORDER_RING && ps->n_ranks > 1 ? launch_sync<true>(ps, st)
+                                                          : launch_sync<false>(ps, st);
+}
+
+ddp_status_t ddp_param_sgd_create(const ddp_plan_t *plan, const ddp_binding_t *const *rank_bindings,
+                                  int32_t n_ranks, const ddp_binding_t *grad_out,
+                                  const ddp_binding_t *params, const ddp_binding_t *momentum,
+                                  ddp_order_t order, ddp_dtype_t out_dtype, ddp_param_sync_t **out)
+{
+    if (!plan || !rank_bindings || !params || !out) return DDP_ERR_INVALID_ARG;
+    const Written w[kSgdExtra] = {{grad_out, dtype_size(out_dtype), true},
+                                  {params, 4, false},
+                                  {momentum, 4, false}};
+    return create(plan, rank_bindings, n_ranks, w, kSgdExtra, order, out_dtype, true, out);
+}
+
+ddp_status_t ddp_param_sgd_run(const ddp_param_sync_t *ps, float lr, float momentum, void *stream)
+{
+    const ddp_status_t s = check_run(ps, true);
+    if (s != DDP_OK || ps->n_tiles == 0) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool ring = ps->order == DDP_ORDER_RING && ps->n_ranks > 1;
+    if (ring)
+        return ps->momentum ? launch_sgd<true, true>(ps, lr, momentum, st)
+                            : launch_sgd<true, false>(ps, lr, momentum, st);
+    return ps->momentum ? launch_sgd<false, true>(ps, lr, momentum, st)
+                        : launch_sgd<false, false>(ps, lr, momentum, st);
 }
 
 void ddp_param_sync_free(ddp_param_sync_t *ps)

@@ -318,6 +318,38 @@ DDP_API ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan,
                                            ddp_order_t order, ddp_dtype_t out_dtype,
                                            ddp_param_sync_t **out);
 DDP_API ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *sync, void *stream);
+
+/* The same average folded into an SGD step on per-parameter f32 parameters:
+ * ddp_sync_sgd_update for tensors that are not in the flat layout.  Per
+ * element, with g the averaged gradient exactly as ddp_param_sync_run would
+ * store it (a bf16 average rounded, then widened back):
+ *     momentum != NULL:  v = fl(fl(mu * m) + g);  m = v;  g = v
+ *     params:            p = fl(p - fl(lr * g))
+ * bit for bit ddp_param_sync_run followed by that step, in one pass.
+ *   rank_bindings, n_ranks, order, out_dtype  as ddp_param_sync_create
+ *   grad_out   binding of per-parameter outputs for the averaged gradient
+ *              (out_dtype), or NULL not to store it; may be one rank's
+ *              binding (in place, as ddp_param_sync_create)
+ *   params     binding of the f32 parameters (ddp_bind_params with this
+ *              plan; numel[p] f32 each), updated in place
+ *   momentum   binding of f32 momentum buffers (start from zeros), updated
+ *              in place, or NULL for plain SGD
+ * params and momentum may overlap no other tensor (DDP_ERR_ALIAS).  The
+ * table holds 8 * (n_ranks + 3) + 32 bytes per tile, rounded up to 16.
+ * ddp_param_sgd_run enqueues one step with learning rate lr and momentum
+ * factor mu; it allocates nothing.  A sync made by one create function is
+ * refused by the other's run function (DDP_ERR_INVALID_ARG).
+ * Errors: as ddp_param_sync_create. */
+DDP_API ddp_status_t ddp_param_sgd_create(const ddp_plan_t *plan,
+                                          const ddp_binding_t *const *rank_bindings,
+                                          int32_t n_ranks, const ddp_binding_t *grad_out,
+                                          const ddp_binding_t *params,
+                                          const ddp_binding_t *momentum, ddp_order_t order,
+                                          ddp_dtype_t out_dtype, ddp_param_sync_t **out);
+DDP_API ddp_status_t ddp_param_sgd_run(const ddp_param_sync_t *sync, float lr, float mu,
+                                       void *stream);
+
+/* Frees a sync made by ddp_param_sync_create or ddp_param_sgd_create. */
 DDP_API void ddp_param_sync_free(ddp_param_sync_t *sync);
 
 /* Local gradient accumulation between synchronisations: the no_sync

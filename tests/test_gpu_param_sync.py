@@ -277,3 +277,153 @@ def test_gpt_sampled(env):
     assert_bits_equal(to_host(out_store.index_select(0, src), torch), want, "gpt1p3b sampled")
     del stores, grads, outs, out_store, src
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ fused SGD step
+# ddp_param_sgd_*: the per-parameter average folded into a (momentum) SGD step
+# ("DDP" section 5.3), against the oracle's average then its SGD step per
+# parameter, bit for bit.
+
+def _want_sgd(op, host, order, dt, out_dt, params0, lr, mu, steps):
+    avg = _want(op, host, order, dt, out_dt)
+    params = [p.copy() for p in params0]
+    moms = [np.zeros_like(p) for p in params0] if mu is not None else None
+    for _ in range(steps):
+        for p in range(len(params)):
+            oracle.sgd_step(params[p], avg[p], lr, out_dt, moms[p] if moms else None, mu or 0.0)
+    return avg, params, moms
+
+
+def _run_sgd_case(torch, ddp, sizes, N, order, dt, out_dt, seed, gaps, mom, store):
+    eb = 4 if dt == "f32" else 2
+    cap = 1 << 16
+    lp = ddp.plan_buckets(sizes, cap, dt)
+    op = oracle.plan_cap(sizes, cap, eb)
+    rng = np.random.default_rng(seed)
+    host = [_host_grads(rng, sizes, dt) for _ in range(N)]
+    keep, binds = [], []
+    for r in range(N):
+        big, views = _carve(torch, sizes, _tdt(torch, dt), rng, gaps)
+        for v, h in zip(views, host[r]):
+            v.copy_(to_dev(h, torch))
+        keep.append(big)
+        binds.append(ddp.bind_params(lp, views))
+    p0 = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    pbig, params = _carve(torch, sizes, torch.float32, rng, gaps)
+    for t, h in zip(params, p0):
+        t.copy_(to_dev(h, torch))
+    mbig, moms = _carve(torch, sizes, torch.float32, rng, gaps)
+    for t in moms:
+        t.zero_()
+    obig, outs = _carve(torch, sizes, _tdt(torch, out_dt), rng, gaps)
+    mu = 0.9 if mom else None
+    step = ddp.param_sgd(lp, binds, ddp.bind_params(lp, params),
+                         ddp.bind_params(lp, moms) if mom else None,
+                         ddp.bind_params(lp, outs) if store else None, order,
+                         out_dtype=out_dt)
+    for _ in range(2):
+        step(0.1, mu or 0.0)
+    torch.cuda.synchronize()
+    avg, wp, wm = _want_sgd(op, host, order, dt, out_dt, p0, 0.1, mu, 2)
+    what = f"N={N} {order} {dt}->{out_dt} mom={mom} store={store}"
+    for p in range(len(sizes)):
+        assert_bits_equal(to_host(params[p], torch), wp[p], f"{what} params p={p}")
+        if mom:
+            assert_bits_equal(to_host(moms[p], torch), wm[p], f"{what} momentum p={p}")
+        if store:
+            assert_bits_equal(to_host(outs[p], torch), avg[p], f"{what} average p={p}")
+    return keep, pbig, mbig, obig
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
+@pytest.mark.parametrize("N", [1, 2, 8, 12])
+@pytest.mark.parametrize("gaps", [False, True])
+def test_sgd_random_plans(env, pair, N, gaps):
+    torch, ddp = env
+    dt, out_dt = pair
+    if N == 1 and dt != out_dt:
+        pytest.skip("one rank keeps the input dtype")
+    rng = np.random.default_rng(N * 11 + gaps)
+    sizes = list(EDGE_SIZES) + [int(x) for x in rng.integers(1, 50000, 25)]
+    rng.shuffle(sizes)
+    for order, mom, store in (("ring", True, True), ("seq", True, False), ("ring", False, False)):
+        _run_sgd_case(torch, ddp, sizes, N, order, dt, out_dt, 300 * N + gaps, gaps, mom, store)
+
+
+def test_sgd_resnet50_matches_flat_fused_step(env):
+    torch, ddp = env
+    wl = W.workload("resnet50")
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "f32")
+    op = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, 4)
+    N = wl.n_ranks
+    offs = np.cumsum([0] + wl.numel[:-1])
+    grads, flats = [], []
+    for r in range(N):
+        flat = torch.empty(lp.total, device="cuda:0")
+        W.device_normal_(flat, r, wl.stream, wl.sigma)
+        grads.append([flat[o:o + n].clone() for o, n in zip(offs, wl.numel)])
+        del flat
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    for r in range(N):                       # the same values in the flat layout
+        f = torch.empty(lp.total, device="cuda:0")
+        ddp.flatten(lp, binds[r], f)
+        flats.append(f)
+    params = [torch.empty(n, device="cuda:0").normal_(0, 1) for n in wl.numel]
+    p0 = [to_host(t, torch).copy() for t in params]
+    moms = [torch.zeros(n, device="cuda:0") for n in wl.numel]
+    pflat = torch.empty(lp.total, device="cuda:0")
+    mflat = torch.zeros(lp.total, device="cuda:0")
+    pbind = ddp.bind_params(lp, params)
+    ddp.flatten(lp, pbind, pflat)
+    step = ddp.param_sgd(lp, binds, pbind, ddp.bind_params(lp, moms), None, "ring")
+    for _ in range(2):
+        step(0.05, 0.9)
+        ddp.sync_sgd_update(lp, flats, pflat, 0.05, "ring", momentum_buf=mflat, momentum=0.9)
+    torch.cuda.synchronize()
+    back_p = [torch.empty(n, device="cuda:0") for n in wl.numel]
+    back_m = [torch.empty(n, device="cuda:0") for n in wl.numel]
+    ddp.unflatten(lp, ddp.bind_params(lp, back_p), pflat)
+    ddp.unflatten(lp, ddp.bind_params(lp, back_m), mflat)
+    torch.cuda.synchronize()
+    for p in range(len(wl.numel)):
+        assert_bits_equal(to_host(params[p], torch), to_host(back_p[p], torch), f"params p={p}")
+        assert_bits_equal(to_host(moms[p], torch), to_host(back_m[p], torch), f"momentum p={p}")
+    # and against the oracle for a few parameters
+    host = [[to_host(g, torch) for g in gr] for gr in grads]
+    avg = _want(op, host, "ring", "f32", "f32")
+    for p in (0, 1, len(wl.numel) // 2, len(wl.numel) - 1):
+        wp, wm = p0[p].copy(), np.zeros(wl.numel[p], np.float32)
+        for _ in range(2):
+            oracle.sgd_step(wp, avg[p], 0.05, "f32", wm, 0.9)
+        assert_bits_equal(to_host(params[p], torch), wp, f"oracle params p={p}")
+        assert_bits_equal(to_host(moms[p], torch), wm, f"oracle momentum p={p}")
+    del grads, flats, params, moms, pflat, mflat, back_p, back_m
+    torch.cuda.empty_cache()
+
+
+def test_sgd_overlaps_and_kinds_are_checked(env):
+    torch, ddp = env
+    sizes = [1000, 2000]
+    lp = ddp.plan_buckets(sizes, 1 << 20, "f32")
+    grads = [[torch.zeros(n, device="cuda:0") for n in sizes] for _ in range(2)]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    params = [torch.zeros(n, device="cuda:0") for n in sizes]
+    pb = ddp.bind_params(lp, params)
+    # parameters on a rank's gradients
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.param_sgd(lp, binds, binds[0])
+    assert e.value.status == 4
+    # momentum overlapping the parameters
+    with pytest.raises(ddp.DDPError) as e:
+        ddp.param_sgd(lp, binds, pb, pb)
+    assert e.value.status == 4
+    # the average stored in place on rank 1: accepted
+    step = ddp.param_sgd(lp, binds, pb, None, binds[1])
+    step(0.1)
+    # a sync object is refused by the SGD run function and the other way round
+    sync = ddp.param_sync(lp, binds, ddp.bind_params(lp, [torch.zeros(n, device="cuda:0")
+                                                          for n in sizes]))
+    assert ddp.lib.ddp_param_sgd_run(sync._h, 0.1, 0.0, None) == 1
+    assert ddp.lib.ddp_param_sync_run(step._h, None) == 1
+    torch.cuda.synchronize()

@@ -10,7 +10,7 @@ These tests check that the split changes no bit:
   synchronisation, an unaligned single bucket (head block in the last
   launch), the per-element kernel, the fused SGD step, accumulate and
   flatten, each replay equal to the eager call;
-* the parity suites once more in a child process whose limit is 4096
+* the parity suites (flat and per-parameter) once more in a child process whose limit is 4096
   work-items (64 reduce blocks, 8 copy units per launch), so that every
   small case spans many launches and is compared with the oracle there;
 * at the real limit: N = 2 f32 ranks of 4.3 G elements (past element 2^32,
@@ -194,9 +194,10 @@ def test_parity_suites_with_split_launches(env):
     torch.cuda.empty_cache()
     suites = ["tests/test_gpu_reduce.py", "tests/test_gpu_sgd.py", "tests/test_gpu_accumulate.py",
               "tests/test_gpu_flatten.py", "tests/test_gpu_fuzz.py",
-              "tests/test_gpu_graph_overlap.py", "tests/test_gpu_split_launch.py"]
+              "tests/test_gpu_graph_overlap.py", "tests/test_gpu_param_sync.py",
+              "tests/test_gpu_split_launch.py"]
     cmd = [sys.executable, "-u", "-m", "pytest", "-x", "-q", "-m", "gpu", "-p", "no:cacheprovider",
-           "-k", "not llama and not real_limit", *suites]
+           "-k", "not llama and not real_limit and not gpt", *suites]
     child_env = dict(os.environ, **{ENV: str(CHILD_LIMIT)})
     print("child:", " ".join(cmd[3:]), f"with {ENV}={CHILD_LIMIT}", flush=True)
     r = subprocess.run(cmd, cwd=ROOT, env=child_env, capture_output=True, text=True, timeout=420)
