@@ -65,6 +65,7 @@ ddp_status_t launch_split(int64_t blocks, int threads, const char *what, Launch 
 int reduce_blocks_per_cu(int N, bool ring);
 int sgd_blocks_per_cu(int N, bool mom);
 int params_blocks_per_cu(int N, bool ring, bool bf16);
+int params_sgd_blocks_per_cu(int N, bool mom);
 constexpr int kCopyBlocksPerCU = 7;   // flatten / unflatten (256-thread blocks)
 unsigned lds_for_blocks(int k);
 

@@ -487,7 +487,7 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, float lr, float mu, hipS
     const float inv = 1.0f / (float)N;
     const char *tb = ps->table;
     const int64_t sd = ps->stride;
-    const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
+    const unsigned lds = lds_for_blocks(params_sgd_blocks_per_cu(N, MOM));
     const dim3 b(kThreads);
     return launch_split(ps->n_tiles, kThreads, "parameter SGD kernel launch",
                         [&](int64_t b0, unsigned n) {
