@@ -199,6 +199,45 @@ int main(void)
     CHECK_HIP(hipMemcpy(got, dm, sizeof(float) * P, hipMemcpyDeviceToHost));
     if (!same_bits(got, hm, sizeof(float) * P, "sgd momentum")) return 1;
 
+    /* the same step on per-parameter parameters and momentum buffers */
+    void *dpp[NP], *dpm[NP];
+    float *hpp = malloc(sizeof(float) * P), *hpm = calloc((size_t)P, sizeof(float));
+    for (int p = 0; p < NP; ++p) {
+        int32_t b;
+        int64_t off, base;
+        CHECK_DDP(ddp_plan_param(plan, p, &b, &off));
+        CHECK_DDP(ddp_plan_bucket(plan, b, NULL, &base, NULL, NULL));
+        for (int64_t j = 0; j < numel[p]; ++j) hpp[base + off + j] = next_grad() * 1000.0f;
+        CHECK_HIP(hipMalloc(&dpp[p], sizeof(float) * numel[p]));
+        CHECK_HIP(hipMalloc(&dpm[p], sizeof(float) * numel[p]));
+        CHECK_HIP(hipMemcpy(dpp[p], hpp + base + off, sizeof(float) * numel[p],
+                            hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemset(dpm[p], 0, sizeof(float) * numel[p]));
+    }
+    ddp_binding_t *pbind, *mbind;
+    CHECK_DDP(ddp_bind_params(plan, dpp, NULL, &pbind));
+    CHECK_DDP(ddp_bind_params(plan, dpm, NULL, &mbind));
+    ddp_param_sync_t *psgd;
+    CHECK_DDP(ddp_param_sgd_create(plan, (const ddp_binding_t *const *)bind, N, NULL, pbind, mbind,
+                                   DDP_ORDER_RING, DDP_F32, &psgd));
+    CHECK_DDP(ddp_param_sgd_run(psgd, 0.1f, 0.9f, NULL));
+    CHECK_HIP(hipDeviceSynchronize());
+    oracle_sgd_step(hpp, hpm, want, 0, P, 0.1f, 0.9f);   /* flat order: want is the flat average */
+    for (int p = 0; p < NP; ++p) {
+        int32_t b;
+        int64_t off, base;
+        CHECK_DDP(ddp_plan_param(plan, p, &b, &off));
+        CHECK_DDP(ddp_plan_bucket(plan, b, NULL, &base, NULL, NULL));
+        CHECK_HIP(hipMemcpy(got, dpp[p], sizeof(float) * numel[p], hipMemcpyDeviceToHost));
+        if (!same_bits(got, hpp + base + off, sizeof(float) * numel[p], "param sgd params")) return 1;
+        CHECK_HIP(hipMemcpy(got, dpm[p], sizeof(float) * numel[p], hipMemcpyDeviceToHost));
+        if (!same_bits(got, hpm + base + off, sizeof(float) * numel[p], "param sgd momentum")) return 1;
+    }
+    if (ddp_param_sync_run(psgd, NULL) != DDP_ERR_INVALID_ARG) return 1;   /* wrong kind */
+    ddp_param_sync_free(psgd);
+    ddp_binding_free(pbind);
+    ddp_binding_free(mbind);
+
     /* accumulate rank 1 into rank 0 and rank 3 into rank 2 */
     void *adst[2] = {dflat[0], dflat[2]};
     const void *asrc[2] = {dflat[1], dflat[3]};
