@@ -99,6 +99,9 @@ def _load():
         "ddp_param_sgd_create": ([vp, ctypes.POINTER(vp), ctypes.c_int32, vp, vp, vp, ctypes.c_int,
                                   ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int),
         "ddp_param_sgd_run": ([vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+        "ddp_param_sync_run_buckets": ([vp, ctypes.c_int32, ctypes.c_int32, vp], ctypes.c_int),
+        "ddp_param_sgd_run_buckets": ([vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                       ctypes.c_float, vp], ctypes.c_int),
         "ddp_accumulate": ([ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
                             ctypes.c_int, vp], ctypes.c_int),
         "ddp_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -293,8 +296,14 @@ class ParamSync:
                                          ctypes.byref(h)), "ddp_param_sync_create")
         self._h = h
 
-    def __call__(self, stream=None):
-        _check(lib.ddp_param_sync_run(self._h, _stream_handle(stream)), "ddp_param_sync_run")
+    def __call__(self, stream=None, buckets=None):
+        """Enqueues the sync; buckets=(first, count) limits it to those buckets."""
+        if buckets is None:
+            _check(lib.ddp_param_sync_run(self._h, _stream_handle(stream)), "ddp_param_sync_run")
+        else:
+            _check(lib.ddp_param_sync_run_buckets(self._h, int(buckets[0]), int(buckets[1]),
+                                                  _stream_handle(stream)),
+                   "ddp_param_sync_run_buckets")
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None
@@ -329,8 +338,12 @@ class ParamSGD:
             if len(grad_out.dtypes) != 1:
                 raise ValueError("the averaged gradients must share one dtype")
             out_dt = next(iter(grad_out.dtypes))
+        elif out_dtype is None:
+            out_dt = plan.dtype
+        elif out_dtype in ("f32", "bf16"):
+            out_dt = BF16 if out_dtype == "bf16" else F32
         else:
-            out_dt = plan.dtype if out_dtype is None else (BF16 if out_dtype == "bf16" else F32)
+            raise ValueError(f"unknown out_dtype {out_dtype!r}")
         self.out_dtype = out_dt
         handles = (ctypes.c_void_p * len(rank_bindings))(*[bd.handle for bd in rank_bindings])
         h = ctypes.c_void_p()
@@ -342,9 +355,15 @@ class ParamSGD:
                "ddp_param_sgd_create")
         self._h = h
 
-    def __call__(self, lr: float, momentum: float = 0.0, stream=None):
-        _check(lib.ddp_param_sgd_run(self._h, lr, momentum, _stream_handle(stream)),
-               "ddp_param_sgd_run")
+    def __call__(self, lr: float, momentum: float = 0.0, stream=None, buckets=None):
+        """One step; buckets=(first, count) limits it to those buckets."""
+        if buckets is None:
+            _check(lib.ddp_param_sgd_run(self._h, lr, momentum, _stream_handle(stream)),
+                   "ddp_param_sgd_run")
+        else:
+            _check(lib.ddp_param_sgd_run_buckets(self._h, int(buckets[0]), int(buckets[1]), lr,
+                                                 momentum, _stream_handle(stream)),
+                   "ddp_param_sgd_run_buckets")
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None

@@ -70,6 +70,7 @@ struct ddp_param_sync {
     char *table = nullptr;                    // device array, n_tiles * stride bytes
     int64_t n_tiles = 0;
     int64_t stride = 0;                       // bytes per entry
+    std::vector<int64_t> bucket_tile;         // [n_buckets + 1] first entry of each bucket
 };
 
 // Frees every device table of a plan (defined next to the kernels).

@@ -454,8 +454,13 @@ params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t f
     }
 }
 
+// Entries [first, first + count) of a table: whole buckets.
+struct TileRange {
+    int64_t first, count;
+};
+
 template <bool RING, int IN, int OUT>
-ddp_status_t launch_sync_typed(const ddp_param_sync *ps, hipStream_t st)
+ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream_t st)
 {
     const int N = ps->n_ranks;
     const float inv = 1.0f / (float)N;
@@ -463,9 +468,10 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, hipStream_t st)
     const int64_t sd = ps->stride;
     const unsigned lds = lds_for_blocks(params_blocks_per_cu(N, RING, IN == kBF16));
     const dim3 b(kThreads);
-    return launch_split(ps->n_tiles, kThreads, "parameter sync kernel launch",
-                        [&](int64_t b0, unsigned n) {
+    return launch_split(tr.count, kThreads, "parameter sync kernel launch",
+                        [&](int64_t i, unsigned n) {
         const dim3 g(n);
+        const int64_t b0 = tr.first + i;
         switch (N) {
         case 1: params_fast<1, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
         case 2: params_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
@@ -481,7 +487,8 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, hipStream_t st)
 }
 
 template <bool RING, int IN, int OUT, bool MOM>
-ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, float lr, float mu, hipStream_t st)
+ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, TileRange tr, float lr, float mu,
+                              hipStream_t st)
 {
     const int N = ps->n_ranks;
     const float inv = 1.0f / (float)N;
@@ -489,9 +496,10 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, float lr, float mu, hipS
     const int64_t sd = ps->stride;
     const unsigned lds = lds_for_blocks(params_sgd_blocks_per_cu(N, MOM));
     const dim3 b(kThreads);
-    return launch_split(ps->n_tiles, kThreads, "parameter SGD kernel launch",
-                        [&](int64_t b0, unsigned n) {
+    return launch_split(tr.count, kThreads, "parameter SGD kernel launch",
+                        [&](int64_t i, unsigned n) {
         const dim3 g(n);
+        const int64_t b0 = tr.first + i;
         switch (N) {
         case 1: params_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
         case 2: params_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
@@ -507,20 +515,21 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, float lr, float mu, hipS
 }
 
 template <bool RING>
-ddp_status_t launch_sync(const ddp_param_sync *ps, hipStream_t st)
+ddp_status_t launch_sync(const ddp_param_sync *ps, TileRange tr, hipStream_t st)
 {
-    if (ps->in == DDP_F32 && ps->out == DDP_F32) return launch_sync_typed<RING, kF32, kF32>(ps, st);
-    if (ps->in == DDP_BF16) return launch_sync_typed<RING, kBF16, kBF16>(ps, st);
-    return launch_sync_typed<RING, kF32, kBF16>(ps, st);
+    if (ps->in == DDP_F32 && ps->out == DDP_F32)
+        return launch_sync_typed<RING, kF32, kF32>(ps, tr, st);
+    if (ps->in == DDP_BF16) return launch_sync_typed<RING, kBF16, kBF16>(ps, tr, st);
+    return launch_sync_typed<RING, kF32, kBF16>(ps, tr, st);
 }
 
 template <bool RING, bool MOM>
-ddp_status_t launch_sgd(const ddp_param_sync *ps, float lr, float mu, hipStream_t st)
+ddp_status_t launch_sgd(const ddp_param_sync *ps, TileRange tr, float lr, float mu, hipStream_t st)
 {
     if (ps->in == DDP_F32 && ps->out == DDP_F32)
-        return launch_sgd_typed<RING, kF32, kF32, MOM>(ps, lr, mu, st);
-    if (ps->in == DDP_BF16) return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ps, lr, mu, st);
-    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ps, lr, mu, st);
+        return launch_sgd_typed<RING, kF32, kF32, MOM>(ps, tr, lr, mu, st);
+    if (ps->in == DDP_BF16) return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ps, tr, lr, mu, st);
+    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ps, tr, lr, mu, st);
 }
 
 // A set of per-parameter tensors the kernel writes.
@@ -634,6 +643,18 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
     ps->momentum = sgd && w[2].bd != nullptr;
     ps->n_tiles = n_tiles;
     ps->stride = stride;
+    try {
+        ps->bucket_tile.assign((size_t)plan->n_buckets() + 1, 0);
+    } catch (...) {
+        delete ps;
+        return DDP_ERR_NOMEM;
+    }
+    for (int32_t b = 0; b < plan->n_buckets(); ++b) {
+        int64_t t = 0;
+        for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s)
+            t += (plan->numel[plan->slot_param[s]] + T - 1) / T;
+        ps->bucket_tile[b + 1] = ps->bucket_tile[b] + t;
+    }
     if (n_tiles == 0) {
         *out = ps;
         return DDP_OK;
@@ -701,13 +722,49 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
     return DDP_OK;
 }
 
-ddp_status_t check_run(const ddp_param_sync_t *ps, bool sgd)
+// Checks a run call and finds the entries of buckets [b0, b0 + nb) (nb < 0:
+// every bucket).
+ddp_status_t check_run(const ddp_param_sync_t *ps, bool sgd, int32_t b0, int32_t nb, TileRange *tr)
 {
     if (!ps || ps->sgd != sgd) return DDP_ERR_INVALID_ARG;
+    const int32_t n_buckets = (int32_t)ps->bucket_tile.size() - 1;
+    if (nb < 0) {
+        b0 = 0;
+        nb = n_buckets;
+    }
+    if (b0 < 0 || b0 > n_buckets || nb > n_buckets - b0) return DDP_ERR_INVALID_ARG;
     int dev = -1;
     const hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-    return dev == ps->device ? DDP_OK : DDP_ERR_INVALID_ARG;
+    if (dev != ps->device) return DDP_ERR_INVALID_ARG;
+    tr->first = ps->bucket_tile[b0];
+    tr->count = ps->bucket_tile[b0 + nb] - tr->first;
+    return DDP_OK;
+}
+
+ddp_status_t run_sync(const ddp_param_sync_t *ps, int32_t b0, int32_t nb, void *stream)
+{
+    TileRange tr;
+    const ddp_status_t s = check_run(ps, false, b0, nb, &tr);
+    if (s != DDP_OK || tr.count == 0) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return ps->order == DDP_ORDER_RING && ps->n_ranks > 1 ? launch_sync<true>(ps, tr, st)
+                                                          : launch_sync<false>(ps, tr, st);
+}
+
+ddp_status_t run_sgd(const ddp_param_sync_t *ps, int32_t b0, int32_t nb, float lr, float mu,
+                     void *stream)
+{
+    TileRange tr;
+    const ddp_status_t s = check_run(ps, true, b0, nb, &tr);
+    if (s != DDP_OK || tr.count == 0) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool ring = ps->order == DDP_ORDER_RING && ps->n_ranks > 1;
+    if (ring)
+        return ps->momentum ? launch_sgd<true, true>(ps, tr, lr, mu, st)
+                            : launch_sgd<true, false>(ps, tr, lr, mu, st);
+    return ps->momentum ? launch_sgd<false, true>(ps, tr, lr, mu, st)
+                        : launch_sgd<false, false>(ps, tr, lr, mu, st);
 }
 
 }  // namespace
@@ -726,11 +783,14 @@ ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan, const ddp_binding_t *
 
 ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *ps, void *stream)
 {
-    const ddp_status_t s = check_run(ps, false);
-    if (s != DDP_OK || ps->n_tiles == 0) return s;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    return ps->order == DDP_ORDER_RING && ps->n_ranks > 1 ? launch_sync<true>(ps, st)
-                                                          : launch_sync<false>(ps, st);
+    return run_sync(ps, 0, -1, stream);
+}
+
+ddp_status_t ddp_param_sync_run_buckets(const ddp_param_sync_t *ps, int32_t first_bucket,
+                                        int32_t n_buckets, void *stream)
+{
+    if (n_buckets < 0) return DDP_ERR_INVALID_ARG;
+    return run_sync(ps, first_bucket, n_buckets, stream);
 }
 
 ddp_status_t ddp_param_sgd_create(const ddp_plan_t *plan, const ddp_binding_t *const *rank_bindings,
@@ -747,15 +807,14 @@ ddp_status_t ddp_param_sgd_create(const ddp_plan_t *plan, const ddp_binding_t *c
 
 ddp_status_t ddp_param_sgd_run(const ddp_param_sync_t *ps, float lr, float momentum, void *stream)
 {
-    const ddp_status_t s = check_run(ps, true);
-    if (s != DDP_OK || ps->n_tiles == 0) return s;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool ring = ps->order == DDP_ORDER_RING && ps->n_ranks > 1;
-    if (ring)
-        return ps->momentum ? launch_sgd<true, true>(ps, lr, momentum, st)
-                            : launch_sgd<true, false>(ps, lr, momentum, st);
-    return ps->momentum ? launch_sgd<false, true>(ps, lr, momentum, st)
-                        : launch_sgd<false, false>(ps, lr, momentum, st);
+    return run_sgd(ps, 0, -1, lr, momentum, stream);
+}
+
+ddp_status_t ddp_param_sgd_run_buckets(const ddp_param_sync_t *ps, int32_t first_bucket,
+                                       int32_t n_buckets, float lr, float momentum, void *stream)
+{
+    if (n_buckets < 0) return DDP_ERR_INVALID_ARG;
+    return run_sgd(ps, first_bucket, n_buckets, lr, momentum, stream);
 }
 
 void ddp_param_sync_free(ddp_param_sync_t *ps)

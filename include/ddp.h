@@ -319,6 +319,15 @@ DDP_API ddp_status_t ddp_param_sync_create(const ddp_plan_t *plan,
                                            ddp_param_sync_t **out);
 DDP_API ddp_status_t ddp_param_sync_run(const ddp_param_sync_t *sync, void *stream);
 
+/* ddp_param_sync_run for buckets [first_bucket, first_bucket + n_buckets)
+ * only: DDP's schedule ([DDP] 3.2; [TR24] 十一) averages each bucket as soon
+ * as backward has produced its gradients, last layers first, so a caller
+ * runs bucket 0, then 1, ..., each when it is ready.  The buckets of one
+ * step together give the bits of one ddp_param_sync_run.
+ * Errors: INVALID_ARG (range outside the plan's buckets), HIP. */
+DDP_API ddp_status_t ddp_param_sync_run_buckets(const ddp_param_sync_t *sync, int32_t first_bucket,
+                                                int32_t n_buckets, void *stream);
+
 /* The same average folded into an SGD step on per-parameter f32 parameters:
  * ddp_sync_sgd_update for tensors that are not in the flat layout.  Per
  * element, with g the averaged gradient exactly as ddp_param_sync_run would
@@ -348,6 +357,11 @@ DDP_API ddp_status_t ddp_param_sgd_create(const ddp_plan_t *plan,
                                           ddp_dtype_t out_dtype, ddp_param_sync_t **out);
 DDP_API ddp_status_t ddp_param_sgd_run(const ddp_param_sync_t *sync, float lr, float mu,
                                        void *stream);
+/* The SGD step of buckets [first_bucket, first_bucket + n_buckets) only, as
+ * ddp_param_sync_run_buckets. */
+DDP_API ddp_status_t ddp_param_sgd_run_buckets(const ddp_param_sync_t *sync, int32_t first_bucket,
+                                               int32_t n_buckets, float lr, float mu,
+                                               void *stream);
 
 /* Frees a sync made by ddp_param_sync_create or ddp_param_sgd_create. */
 DDP_API void ddp_param_sync_free(ddp_param_sync_t *sync);

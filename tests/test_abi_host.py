@@ -215,6 +215,10 @@ def test_param_sync_argument_errors_are_host_side():
     assert f(p.handle, ranks, 1, outb, 1, 1, ctypes.byref(res)) == 2      # one rank, f32 -> bf16
     assert not res.value
     assert L.ddp_param_sync_run(None, None) == 1
+    assert L.ddp_param_sync_run_buckets(None, 0, 1, None) == 1
+    assert L.ddp_param_sgd_run(None, 0.1, 0.0, None) == 1
+    assert L.ddp_param_sgd_run_buckets(None, 0, 1, 0.1, 0.0, None) == 1
+    assert L.ddp_param_sgd_create(p.handle, ranks, 2, None, None, None, 1, 0, ctypes.byref(res)) == 1
     L.ddp_param_sync_free(None)
 
 

@@ -427,3 +427,56 @@ def test_sgd_overlaps_and_kinds_are_checked(env):
     assert ddp.lib.ddp_param_sgd_run(sync._h, 0.1, 0.0, None) == 1
     assert ddp.lib.ddp_param_sync_run(step._h, None) == 1
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ bucket by bucket
+# ddp_param_sync_run_buckets / ddp_param_sgd_run_buckets: DDP's schedule
+# averages each bucket when backward has produced it ("DDP" section 3.2);
+# the buckets of one step together give the bits of the whole call.
+
+@pytest.mark.parametrize("order", ["ring", "seq"])
+def test_bucket_by_bucket_equals_whole(env, order):
+    torch, ddp = env
+    rng = np.random.default_rng(21)
+    sizes = [p.numel for p in W.many_small(n=500)] + list(EDGE_SIZES)
+    N = 4
+    cap = 1 << 18
+    lp = ddp.plan_buckets(sizes, cap, "f32")
+    op = oracle.plan_cap(sizes, cap, 4)
+    B = lp.n_buckets
+    assert B > 8
+    host = [_host_grads(rng, sizes, "f32") for _ in range(N)]
+    grads = [[to_dev(h, torch) for h in hr] for hr in host]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    outs = [torch.full((n,), float("nan"), device="cuda:0") for n in sizes]
+    ps = ddp.param_sync(lp, binds, ddp.bind_params(lp, outs), order)
+    want = _want(op, host, order, "f32", "f32")
+    for groups in ([(b, 1) for b in range(B)], [(b, min(3, B - b)) for b in range(0, B, 3)]):
+        for o in outs:
+            o.fill_(float("nan"))
+        for b0, nb in groups:
+            ps(buckets=(b0, nb))
+        torch.cuda.synchronize()
+        for p in range(len(sizes)):
+            assert_bits_equal(to_host(outs[p], torch), want[p], f"{order} buckets p={p}")
+    # an empty range does nothing; a range past the plan is refused
+    ps(buckets=(B, 0))
+    for bad in ((0, B + 1), (B, 1), (-1, 1)):
+        assert ddp.lib.ddp_param_sync_run_buckets(ps._h, bad[0], bad[1], None) == 1
+
+    # the SGD step bucket by bucket, two steps, against the whole step
+    p0 = [rng.standard_normal(n).astype(np.float32) for n in sizes]
+    pa = [to_dev(x, torch) for x in p0]
+    pb = [to_dev(x, torch) for x in p0]
+    ma = [torch.zeros(n, device="cuda:0") for n in sizes]
+    mb = [torch.zeros(n, device="cuda:0") for n in sizes]
+    whole = ddp.param_sgd(lp, binds, ddp.bind_params(lp, pa), ddp.bind_params(lp, ma), None, order)
+    parts = ddp.param_sgd(lp, binds, ddp.bind_params(lp, pb), ddp.bind_params(lp, mb), None, order)
+    for _ in range(2):
+        whole(0.1, 0.9)
+        for b in range(B):
+            parts(0.1, 0.9, buckets=(b, 1))
+    torch.cuda.synchronize()
+    for p in range(len(sizes)):
+        assert_bits_equal(to_host(pb[p], torch), to_host(pa[p], torch), f"{order} sgd params p={p}")
+        assert_bits_equal(to_host(mb[p], torch), to_host(ma[p], torch), f"{order} sgd momentum p={p}")
