@@ -17,7 +17,7 @@ SOURCES = ["plan.cpp", "common.hip", "reduce.hip", "accumulate.hip", "copy.hip",
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wshadow",
           "-ffp-contract=off", "-fno-fast-math",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-fno-gpu-flush-denormals-to-zero",

@@ -152,8 +152,7 @@ __device__ __forceinline__ void store_elem(void *out, int64_t i, float y)
 __device__ __forceinline__ int wrap(int r, int n) { return r >= n ? r - n : r; }
 
 // Ring start rank of element i (any bucket at or after b0).
-__device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int64_t total, int N,
-                                          int64_t i)
+__device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int N, int64_t i)
 {
     int64_t base = bk.lo, end = bk.hi;
     if (bk.base) {
@@ -171,7 +170,7 @@ template <int IN, bool RING>
 __device__ __forceinline__ float avg_elem(const RankArgs &ra, int N, int64_t total,
                                           const Buckets &bk, int32_t b0, float inv, int64_t i)
 {
-    int r = RING ? ring_start(bk, b0, total, N, i) : 0;
+    int r = RING ? ring_start(bk, b0, N, i) : 0;
     float acc = load_elem<IN>(ra.p[r], i);
     if (!RING) acc = 0.0f + acc;
     for (int k = 1; k < N; ++k) {
