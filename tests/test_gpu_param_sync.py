@@ -10,7 +10,9 @@ unflatten ("DDP" section 4.2), bit for bit:
 * in place (the outputs are rank 0's gradients), graph capture and replay,
   and the rejected overlaps;
 * GPT-1.3B (N = 8, ring, f32), sampled positions at every bucket and
-  ring-chunk edge plus random ones, against the oracle's per-element fold.
+  ring-chunk edge plus random ones, against the oracle's per-element fold;
+* the fused SGD step (ddp_param_sgd_*): random plans, the flat fused step on
+  ResNet-50, bucket-by-bucket runs, and Llama-7B (bf16, sampled).
 """
 import numpy as np
 import pytest
@@ -480,3 +482,50 @@ def test_bucket_by_bucket_equals_whole(env, order):
     for p in range(len(sizes)):
         assert_bits_equal(to_host(pb[p], torch), to_host(pa[p], torch), f"{order} sgd params p={p}")
         assert_bits_equal(to_host(mb[p], torch), to_host(ma[p], torch), f"{order} sgd momentum p={p}")
+
+
+def test_sgd_llama_sampled(env):
+    """The per-parameter fused step at the Llama-7B size: bf16 gradients of 8
+    ranks, f32 parameters and momentum per parameter, two momentum steps in
+    ring order, checked on positions at every bucket and ring-chunk edge plus
+    random ones against the oracle's per-element average and SGD step."""
+    torch, ddp = env
+    wl = W.workload("llama7b")
+    lp = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "bf16")
+    op = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, 2)
+    N, P = wl.n_ranks, op.total
+    reg_off = np.cumsum([0] + wl.numel[:-1]).astype(np.int64)
+    stores = []
+    for r in range(N):
+        t = torch.empty(P, dtype=torch.bfloat16, device="cuda:0")
+        W.device_normal_(t, r, wl.stream, wl.sigma)
+        stores.append(t)
+    pstore = torch.empty(P, dtype=torch.float32, device="cuda:0")
+    W.device_normal_(pstore, 99, 7, 1.0)
+    mstore = torch.zeros(P, dtype=torch.float32, device="cuda:0")
+    views = lambda t: [t[o:o + n] for o, n in zip(reg_off, wl.numel)]   # noqa: E731
+    step = ddp.param_sgd(lp, [ddp.bind_params(lp, views(t)) for t in stores],
+                         ddp.bind_params(lp, views(pstore)), ddp.bind_params(lp, views(mstore)),
+                         None, "ring")
+    rng = np.random.default_rng(77)
+    pos = sample_positions(op.bucket_base, op.bucket_len, N, P, rng)
+    base = np.array(op.bucket_base, dtype=np.int64)
+    flat_off = np.array([base[b] + off for b, off in op.param_location()], dtype=np.int64)
+    by_flat = np.argsort(flat_off, kind="stable")
+    p_of = by_flat[np.searchsorted(flat_off[by_flat], pos, side="right") - 1]
+    src = torch.from_numpy(reg_off[p_of] + (pos - flat_off[p_of])).to("cuda:0")
+    vals = np.stack([to_host(t.index_select(0, src), torch) for t in stores], axis=1)
+    lens = np.array(op.bucket_len, dtype=np.int64)
+    b_of = np.searchsorted(base, pos, side="right") - 1
+    wp = to_host(pstore.index_select(0, src), torch).copy()
+    wm = np.zeros(pos.size, np.float32)
+    avg = oracle.sampled_avg(vals, pos - base[b_of], lens[b_of], "ring", "bf16", "bf16")
+    print("llama7b per-parameter fused SGD ring", flush=True)
+    for _ in range(2):
+        step(0.1, 0.9)
+        oracle.sgd_step(wp, avg, 0.1, "bf16", wm, 0.9)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(pstore.index_select(0, src), torch), wp, "llama7b params")
+    assert_bits_equal(to_host(mstore.index_select(0, src), torch), wm, "llama7b momentum")
+    del stores, pstore, mstore, step, src
+    torch.cuda.empty_cache()
