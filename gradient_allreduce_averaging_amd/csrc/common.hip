@@ -48,14 +48,17 @@ int64_t max_launch_items()
 // touch.  k was measured per kernel and rank count on ResNet-50, many-small,
 // GPT-1.3B and Llama-7B shapes; 0 means no cap.
 
-// Reduce, N = 2..8 (one 16-byte load per rank and lane, one store); the
-// looped kernel for N > 8.
+// Reduce, N = 2..16 (one 16-byte load per rank and lane, one store): for
+// N = 9..12, 7 (8 for sequential order at N = 9, 10), and 6 for 13..16
+// (ResNet-50 plan, swept 4-12); the looped kernel for N > 16.
 int reduce_blocks_per_cu(int N, bool ring)
 {
     static const int k[9] = {0, 0, 0, 16, 14, 12, 10, 9, 8};
     if (N < 0) return 0;
     if (N <= 8) return k[N];
-    return N <= 11 ? (ring ? 12 : 10) : 8;
+    if (N <= 10) return ring ? 7 : 8;
+    if (N <= 12) return 7;
+    return N <= 16 ? 6 : 8;
 }
 
 // Fused average + SGD step, N = 1..8 (also the parameter, momentum loads and
@@ -72,12 +75,13 @@ int sgd_blocks_per_cu(int N, bool mom)
 // The per-parameter sync (params.hip): the reduce's pattern behind one
 // table entry per block, whose scalar-load latency more resident blocks
 // hide.  Measured at N = 4 (many-small: 16) and N = 8 (ResNet-50 and
-// GPT-1.3B in f32: 10; Llama-7B in bf16: 12); other N take the reduce's cap
-// plus two.
+// GPT-1.3B in f32: 10; Llama-7B in bf16: 12); other N take the cap of the
+// flat kernel of the same shape (unrolled up to 8, looped above) plus two.
 int params_blocks_per_cu(int N, bool ring, bool bf16)
 {
     if (N == 4) return 16;
     if (N == 8) return bf16 ? 12 : 10;
+    if (N > 8) return N <= 11 ? (ring ? 14 : 12) : 10;   // the looped kernel's caps + 2
     const int k = reduce_blocks_per_cu(N, ring);
     return k > 0 ? std::min(k + 2, 16) : 0;
 }

@@ -20,7 +20,8 @@ using namespace ddp_detail;
 
 namespace {
 
-// N known at compile time (2..8): all N * kUnroll vector loads in flight.
+// N known at compile time (2..16): all N * kUnroll vector loads in flight,
+// the fold done from registers in any rotation.
 template <int NR, bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
 reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
@@ -132,7 +133,7 @@ reduce_sgd_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdA
     sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, 0, inv, sa, i, 1);
 }
 
-// Any N up to DDP_MAX_RANKS.  A wave makes one pass per ring segment its
+// Any N up to DDP_MAX_RANKS (launched for N > 16).  A wave makes one pass per ring segment its
 // lanes lie in (usually one), so the rank order of each pass is
 // wave-uniform, and folds with fold_looped.
 template <bool RING, int IN, int OUT>
@@ -237,6 +238,14 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
             case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
             case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
             case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 9: reduce_fast<9, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 10: reduce_fast<10, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 11: reduce_fast<11, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 12: reduce_fast<12, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 13: reduce_fast<13, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 14: reduce_fast<14, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 15: reduce_fast<15, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
+            case 16: reduce_fast<16, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
             default: reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, lb, inv, out); break;
             }
         });
