@@ -529,3 +529,32 @@ def test_sgd_llama_sampled(env):
     assert_bits_equal(to_host(mstore.index_select(0, src), torch), wm, "llama7b momentum")
     del stores, pstore, mstore, step, src
     torch.cuda.empty_cache()
+
+
+def test_zero_size_parameters(env):
+    """Parameters with no elements get no tiles; their (empty) tensors are
+    never touched, and the others are averaged as usual."""
+    torch, ddp = env
+    sizes = [0, 5, 0, 300, 4096, 0, 1]
+    N = 3
+    lp = ddp.plan_buckets(sizes, 1 << 20, "f32")
+    op = oracle.plan_cap(sizes, 1 << 20, 4)
+    rng = np.random.default_rng(3)
+    host = [_host_grads(rng, sizes, "f32") for _ in range(N)]
+    grads = [[to_dev(h, torch) for h in hr] for hr in host]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    outs = [torch.full((n,), float("nan"), device="cuda:0") for n in sizes]
+    for order in ("ring", "seq"):
+        ddp.param_sync(lp, binds, ddp.bind_params(lp, outs), order)()
+        torch.cuda.synchronize()
+        want = _want(op, host, order, "f32", "f32")
+        for p in range(len(sizes)):
+            assert_bits_equal(to_host(outs[p], torch), want[p], f"{order} p={p}")
+    params = [torch.ones(n, device="cuda:0") for n in sizes]
+    ddp.param_sgd(lp, binds, ddp.bind_params(lp, params))(0.5)
+    torch.cuda.synchronize()
+    want = _want(op, host, "ring", "f32", "f32")
+    for p in range(len(sizes)):
+        wp = np.ones(sizes[p], np.float32)
+        oracle.sgd_step(wp, want[p], 0.5, "f32")
+        assert_bits_equal(to_host(params[p], torch), wp, f"sgd p={p}")
