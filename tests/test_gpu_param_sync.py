@@ -558,3 +558,15 @@ def test_zero_size_parameters(env):
         wp = np.ones(sizes[p], np.float32)
         oracle.sgd_step(wp, want[p], 0.5, "f32")
         assert_bits_equal(to_host(params[p], torch), wp, f"sgd p={p}")
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
+def test_most_ranks(env, pair):
+    """DDP_MAX_RANKS ranks: the looped kernels, a 560-byte table entry."""
+    torch, ddp = env
+    dt, out_dt = pair
+    sizes = list(EDGE_SIZES)
+    for order in ("ring", "seq"):
+        _run_case(torch, ddp, sizes, 64, order, dt, out_dt, 640, False)
+        _run_sgd_case(torch, ddp, sizes, 64, order, dt, out_dt, 641, True, True, True)
