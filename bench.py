@@ -786,14 +786,18 @@ def main():
                     upd.wait_event(ready[b])
                 pps(upd, buckets=(b, 1))
 
-        t_psyncs = timed([lambda: param_syncs(False)])
-        t_psched = timed([backward, lambda: param_syncs(True)])
-        overlap["schedule"]["per_parameter"] = {
-            "syncs_ms": round(t_psyncs, 4), "serial_ms": round(t_bwd + t_psyncs, 4),
-            "overlapped_ms": round(t_psched, 4),
-            "exposed_sync_ms": round(max(t_psched - t_bwd, 0.0), 4),
-            "hidden_fraction": round(1.0 - max(t_psched - t_bwd, 0.0) / t_psyncs, 3),
-            "sync": "ddp_param_sync_run_buckets, one bucket per launch, default occupancy"}
+        per_param = {"sync": "ddp_param_sync_run_buckets, one bucket per launch"}
+        for policy in ("tuned", "shared"):
+            ddp.set_occupancy(policy)
+            t_psyncs = timed([lambda: param_syncs(False)])
+            t_psched = timed([backward, lambda: param_syncs(True)])
+            per_param[policy] = {
+                "syncs_ms": round(t_psyncs, 4), "serial_ms": round(t_bwd + t_psyncs, 4),
+                "overlapped_ms": round(t_psched, 4),
+                "exposed_sync_ms": round(max(t_psched - t_bwd, 0.0), 4),
+                "hidden_fraction": round(1.0 - max(t_psched - t_bwd, 0.0) / t_psyncs, 3)}
+        ddp.set_occupancy("tuned")
+        overlap["schedule"]["per_parameter"] = per_param
         del lhs, rhs, pg, pout, pps
         log(f"overlap: {overlap}")
         del mat_a, mat_b, tb

@@ -390,7 +390,8 @@ DDP_API ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, in
  *   DDP_OCCUPANCY_SHARED  no cap.  The reserved LDS keeps other kernels'
  *       LDS-using blocks (a GEMM's, say) off a CU while the reduce runs
  *       there; when syncs overlap compute on other streams this policy
- *       shortens the overlapped step by a few percent.
+ *       shortens the overlapped step by a few percent (more for the
+ *       per-parameter sync, whose tuned cap is higher).
  * The policy is process-wide and applies to launches made after the call.
  * Results do not depend on it, only timing. */
 typedef enum { DDP_OCCUPANCY_TUNED = 0, DDP_OCCUPANCY_SHARED = 1 } ddp_occupancy_t;
