@@ -102,10 +102,16 @@ struct Segs {
 
 // Streaming 16-byte accesses of the reduce.  Every byte is touched once, so
 // they are non-temporal (the `nt` cache policy): on gfx950 this lifts a pure
-// streaming read from ~6.5 to ~7.2 TB/s and the reduce by ~15 %.
+// streaming read from ~6.5 to ~7.2 TB/s and the reduce by ~15 %.  Loads need
+// only element alignment (2 bytes): gfx9 and later global loads take any
+// address, and the under-aligned type tells the compiler so (the instruction
+// is the same global_load_dwordx4).  Rank buffers of a bucket therefore need
+// not share their offset from a 16-byte boundary.
+typedef u32x4 u32x4_ua __attribute__((aligned(2)));
+
 __device__ __forceinline__ u32x4 ld_stream(const char *p)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_ua *>(p));
 }
 
 template <typename V>
@@ -385,6 +391,7 @@ __device__ __forceinline__ void fold_seq(const u32x4 *v, float *acc)
 // or a 64-bit address read from a table, typed as global memory here so that
 // the load is a global rather than a flat instruction.
 typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) u32x4_ua g_u32x4_ua;
 
 __device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
 {
@@ -392,7 +399,7 @@ __device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
 }
 __device__ __forceinline__ u32x4 ld_at(uint64_t a, int64_t off)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4 *>(a + (uint64_t)off));
+    return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4_ua *>(a + (uint64_t)off));
 }
 
 // Any N up to DDP_MAX_RANKS: the ranks walked in the fold order starting at

@@ -273,23 +273,24 @@ ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, 
                 : launch_typed<false, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
 }
 
-// One bucket of len elements.  The vector kernel wants its inputs 16-byte
-// aligned (the vector width) and streams best from 128-byte aligned tiles
-// (an L2 line: a misaligned 1 KiB wave load touches 9 lines instead of 8).
-// When every rank buffer sits at the same offset from a 128-byte boundary
-// -- a bucket at an unpadded offset into equally aligned flat buffers -- the
-// vector path starts at the next boundary, h elements in, and numbers the
-// bucket [-h, len - h) so that the ring chunks stay those of the whole
-// bucket; the launch's extra head block reduces the first h elements one by
-// one.  Sharing only the offset from a 16-byte boundary, it starts at the
-// next 16-byte boundary instead.  Otherwise the per-element kernel takes it
-// all.  The output must be aligned for the vector stores at the same point.
+// One bucket of len elements.  The vector kernel streams best from 128-byte
+// aligned tiles (an L2 line: a misaligned 1 KiB wave load touches 9 lines
+// instead of 8), and its stores want the output aligned to a lane's store
+// width.  It starts h < 64 elements into the bucket and numbers the bucket
+// [-h, len - h), so that the ring chunks stay those of the whole bucket; the
+// launch's extra head block reduces the first h elements one by one.  h puts
+// every rank buffer on a 128-byte (else 16-byte) boundary when they all sit
+// at the same offset from one -- a bucket at an unpadded offset into equally
+// aligned flat buffers -- and the output can follow; otherwise it puts the
+// output on a 128-byte boundary and the rank loads run at whatever element
+// alignment they have (the loads accept any).  Only a bucket shorter than
+// that head takes the per-element kernel alone.
 ddp_status_t launch_one_bucket(const RankArgs &ra, int N, int64_t len, int order, int in,
                                int out_dt, void *out, hipStream_t st)
 {
     const int isz = dtype_size(in), osz = dtype_size(out_dt);
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(ra.p[0]);
-    bool same128 = true, same16 = a0 % isz == 0;
+    bool same128 = true, same16 = true;
     for (int r = 1; r < N; ++r) {
         const uintptr_t ar = reinterpret_cast<uintptr_t>(ra.p[r]);
         same128 = same128 && ar % 128 == a0 % 128;
@@ -305,6 +306,10 @@ ddp_status_t launch_one_bucket(const RankArgs &ra, int N, int64_t len, int order
             h = hh;
             break;
         }
+    }
+    if (h < 0) {   // the output's 128-byte boundary (out is element-aligned)
+        const int64_t hh = (int64_t)((128 - ao % 128) % 128) / osz;
+        if (hh < len) h = hh;
     }
     if (h < 0)
         return launch_reduce(ra, N, len, order, in, out_dt, single_bucket(0, len), out, st, false);

@@ -225,11 +225,12 @@ DDP_API ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *
  *   stream              hipStream_t
  * N == 1: the result is the input, bit for bit ([TR24] 九 returns early for
  * world_size <= 1); with out == rank_ptrs[0] nothing is launched.
- * Pointers need only element alignment.  Buffers that all sit at the same
- * offset from a 16-byte boundary (a bucket at an unpadded offset into
- * equally aligned flat buffers) take the vector path after a short
- * per-element head; others take a slower per-element path.  Results are
- * identical either way.
+ * Pointers need only element alignment.  The vector kernel starts after a
+ * short per-element head that puts every rank buffer on a 128-byte boundary
+ * when they all sit at the same offset from one (a bucket at an unpadded
+ * offset into equally aligned flat buffers), else the output; rank buffers
+ * at different offsets are then read at their element alignment (a little
+ * slower).  Results are identical either way.
  * Errors: INVALID_ARG, UNSUPPORTED, ALIAS, HIP. */
 DDP_API ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ranks,
                                       int64_t len, ddp_order_t order,

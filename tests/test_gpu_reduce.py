@@ -95,7 +95,7 @@ def test_special_values(env, N, order):
 
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0]}-{p[1]}")
 @pytest.mark.parametrize("order", ORDERS)
-def test_misaligned_buffers_take_the_element_path(env, pair, order):
+def test_ranks_at_different_offsets(env, pair, order):
     torch, ddp = env
     in_dt, out_dt = pair
     rng = np.random.default_rng(5)

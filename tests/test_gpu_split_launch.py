@@ -8,14 +8,15 @@ These tests check that the split changes no bit:
 
 * the launch count: kernel nodes of captured graphs, for the one-launch
   synchronisation, an unaligned single bucket (head block in the last
-  launch), the per-element kernel, the fused SGD step, accumulate and
-  flatten, each replay equal to the eager call;
+  launch), ranks at mixed offsets, the fused SGD step (vector and
+  per-element), accumulate and flatten, each replay equal to the eager call;
 * the parity suites (flat and per-parameter) once more in a child process whose limit is 4096
   work-items (64 reduce blocks, 8 copy units per launch), so that every
   small case spans many launches and is compared with the oracle there;
 * at the real limit: N = 2 f32 ranks of 4.3 G elements (past element 2^32,
-  where the one-launch sync, the head-peeled bucket, the fused step and
-  accumulate split) and a per-element launch past element 2^30, checked on
+  where the one-launch sync, the head-peeled and mixed-offset buckets, the
+  fused step and accumulate split) and a per-element fused SGD launch past
+  element 2^30, checked on
   sampled positions around every launch edge, bucket edge and ring-chunk
   edge against the oracle.
 """
@@ -139,12 +140,13 @@ def test_launch_count_follows_the_item_limit(env):
     assert k == launches(-(-(L - 29) // 256) + 1, 64), ("head", k)
     _replay_equals_eager(torch, g, head, [out], "head replay")
 
-    # ranks at different offsets from a 16-byte boundary: the per-element kernel
-    def scalar():
+    # ranks at different offsets from a 16-byte boundary: the vector kernel on
+    # the output's alignment (here 0 head elements), loads at element alignment
+    def mixed():
         ddp.bucket_allreduce_avg([f[r:] for r, f in enumerate(flats)], out, "ring", length=L)
-    k, g = _kernel_nodes(torch, scalar)
-    assert k == launches(-(-L // 64), 64), ("scalar", k)
-    _replay_equals_eager(torch, g, scalar, [out], "per-element replay")
+    k, g = _kernel_nodes(torch, mixed)
+    assert k == launches(-(-L // 256), 64), ("mixed offsets", k)
+    _replay_equals_eager(torch, g, mixed, [out], "mixed-offset replay")
 
     params = torch.empty(P, device=dev).normal_(0, 1, generator=gen)
     mom = torch.zeros(P, device=dev)
@@ -161,6 +163,16 @@ def test_launch_count_follows_the_item_limit(env):
     k, g = _kernel_nodes(torch, sgd)
     assert k == launches(-(-P // 256), 64), ("sgd", k)
     _replay_equals_eager(torch, g, sgd, [params, mom], "fused SGD replay", sgd_reset)
+
+    # flat buffers off a 16-byte boundary: the per-element fused kernel, one
+    # grid per bucket
+    def sgd_elems():
+        ddp.sync_sgd_update(lp, [f[1:P + 1] for f in flats], params, 0.1, "ring",
+                            momentum_buf=mom, momentum=0.9)
+    k, g = _kernel_nodes(torch, sgd_elems)
+    lens = [lp.bucket(b)[0] for b in range(lp.n_buckets)]
+    assert k == sum(launches(-(-n // 64), 64) for n in lens if n), ("per-element sgd", k)
+    _replay_equals_eager(torch, g, sgd_elems, [params, mom], "per-element SGD replay", sgd_reset)
 
     acc_dst = [torch.empty(P, device=dev) for _ in range(2)]
 
@@ -272,10 +284,10 @@ def test_real_limit_past_element_2_32(env):
                       "head-peeled bucket")
     del jidx
 
-    print("real limit: per-element kernel past element 2^30", flush=True)
-    L2 = 1_100_000_000
+    print("real limit: ranks at different offsets from a 16-byte boundary", flush=True)
+    L2 = P - 2
     spos = set(int(x) for x in rng.integers(0, L2, 4000))
-    spos |= _near([1 << 30, 0, L2 - 1, L2 // 2], 0, L2)
+    spos |= _near([1 << 32, 0, L2 - 1, L2 // 2], 0, L2)
     spos = np.array(sorted(spos), dtype=np.int64)
     sv = np.stack([to_host(flats[r].index_select(0, torch.from_numpy(spos + 1 + r).to(dev)), torch)
                    for r in range(N)], axis=1)
@@ -283,8 +295,31 @@ def test_real_limit_past_element_2_32(env):
     torch.cuda.synchronize()
     assert_bits_equal(to_host(out.index_select(0, torch.from_numpy(spos).to(dev)), torch),
                       oracle.sampled_avg(sv, spos, np.full(spos.size, L2), "ring"),
-                      "per-element kernel")
+                      "mixed offsets")
     del out
+    torch.cuda.empty_cache()
+
+    print("real limit: per-element fused SGD kernel past element 2^30", flush=True)
+    L3 = 1_100_000_000
+    lp3 = ddp.plan_buckets([L3], 25 << 20, "f32")
+    p3 = torch.empty(L3, dtype=torch.float32, device=dev)
+    W.device_normal_(p3, 78, 3, 1.0)
+    m3 = torch.zeros(L3, dtype=torch.float32, device=dev)
+    tpos = set(int(x) for x in rng.integers(0, L3, 4000))
+    tpos |= _near([1 << 30, 0, L3 - 1, L3 // 2], 0, L3)
+    tpos = np.array(sorted(tpos), dtype=np.int64)
+    tidx = torch.from_numpy(tpos).to(dev)
+    tv = np.stack([to_host(flats[r].index_select(0, tidx + 1), torch) for r in range(N)], axis=1)
+    wp3 = to_host(p3.index_select(0, tidx), torch).copy()
+    wm3 = np.zeros(tpos.size, np.float32)
+    avg3 = oracle.sampled_avg(tv, tpos, np.full(tpos.size, L3), "ring")
+    ddp.sync_sgd_update(lp3, [f[1:L3 + 1] for f in flats], p3, 0.1, "ring", momentum_buf=m3,
+                        momentum=0.9)
+    oracle.sgd_step(wp3, avg3, 0.1, "f32", wm3, 0.9)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(p3.index_select(0, tidx), torch), wp3, "per-element SGD params")
+    assert_bits_equal(to_host(m3.index_select(0, tidx), torch), wm3, "per-element SGD momentum")
+    del p3, m3, tidx
     torch.cuda.empty_cache()
 
     print("real limit: fused SGD step with momentum", flush=True)
