@@ -52,7 +52,7 @@ struct PsMeta {
     int64_t pos;      // position of the tile's first element inside its bucket
     int64_t blen;     // length of that bucket
     uint32_t count;   // elements in the tile, 1..tile
-    uint32_t vec;     // 1: every address of the parameter 16-byte aligned
+    uint32_t vec;     // 1: every written tensor of the parameter 16-byte aligned
     uint32_t starts;  // the ring chunks the tile meets: start rank of chunk a
                       // (bits 0-5) and of chunk b (bits 6-11) ...
     uint32_t cuts;    // ... and where a (bits 0-15) and b (bits 16-31) end,
@@ -688,8 +688,9 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
         for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
             const int32_t p = plan->slot_param[s];
             const int64_t n = plan->numel[p];
+            // the vector path stores 16-byte vectors to the written tensors;
+            // the gradients are read at whatever element alignment they have
             bool vec = true;
-            for (int r = 0; r < n_ranks; ++r) vec = vec && R[r]->param_addr[p] % 16 == 0;
             for (int k = 0; k < nw; ++k) vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 16 == 0);
             for (int64_t j0 = 0; j0 < n; j0 += T) {
                 char *ent = host.data() + fill * stride;

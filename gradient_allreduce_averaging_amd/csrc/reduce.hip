@@ -578,11 +578,7 @@ ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int32_t n_ra
     if (n_ranks == 1) return copy_single(rank_ptrs[0], len, dtype_size(in_dtype), out, st);
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    bool vec_ok = aligned(out, 16);
-    for (int r = 0; r < n_ranks; ++r) {
-        ra.p[r] = rank_ptrs[r];
-        vec_ok = vec_ok && aligned(rank_ptrs[r], 16);
-    }
+    for (int r = 0; r < n_ranks; ++r) ra.p[r] = rank_ptrs[r];
     return launch_one_bucket(ra, n_ranks, len, order, in_dtype, out_dtype, out, st);
 }
 
@@ -616,13 +612,13 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
 
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    bool vec_ok = aligned(out_flat, 16);
-    for (int r = 0; r < n_ranks; ++r) {
-        ra.p[r] = rank_flat[r];
-        vec_ok = vec_ok && aligned(rank_flat[r], 16);
-    }
+    // the vector stores want the output on a 16-byte boundary; the rank
+    // buffers are read at whatever element alignment they have
+    const bool vec_ok = aligned(out_flat, 16);
+    for (int r = 0; r < n_ranks; ++r) ra.p[r] = rank_flat[r];
     if (!vec_ok) {
-        // element-aligned buffers: one per-element launch per bucket
+        // an output off a 16-byte boundary: one launch per bucket, each
+        // aligned to its own part of the output
         const int isz = dtype_size(in), osz = dtype_size(out_dtype);
         for (int32_t b = 0; b < plan->n_buckets(); ++b) {
             const int64_t base = plan->bucket_base[b], len = plan->bucket_base[b + 1] - base;
@@ -678,12 +674,11 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
     hipStream_t st = static_cast<hipStream_t>(stream);
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    bool vec_ok = aligned(param_flat, 16) &&
-                  (!momentum_flat || aligned(momentum_flat, 16)) && (!grad_out || aligned(grad_out, 16));
-    for (int r = 0; r < n_ranks; ++r) {
-        ra.p[r] = rank_flat[r];
-        vec_ok = vec_ok && aligned(rank_flat[r], 16);
-    }
+    // the written buffers must sit on 16-byte boundaries for the vector
+    // kernels; the rank buffers are read at whatever element alignment they have
+    const bool vec_ok = aligned(param_flat, 16) && (!momentum_flat || aligned(momentum_flat, 16)) &&
+                        (!grad_out || aligned(grad_out, 16));
+    for (int r = 0; r < n_ranks; ++r) ra.p[r] = rank_flat[r];
     if (!vec_ok) {
         // element-aligned buffers: one per-element launch per bucket
         for (int32_t b = 0; b < plan->n_buckets(); ++b) {

@@ -245,7 +245,10 @@ DDP_API ddp_status_t ddp_bucket_allreduce_avg(const void *const *rank_ptrs, int3
  *   out_flat            device, ddp_plan_total elements of out_dtype
  * RING chunks are computed per bucket (each bucket is its own all-reduce).
  * The first RING call on a device with a given n_ranks uploads the plan's
- * tables synchronously (see ddp_plan_prepare_ranks).
+ * tables synchronously (see ddp_plan_prepare_ranks).  One launch needs
+ * out_flat on a 16-byte boundary (rank buffers need only element
+ * alignment); otherwise each bucket is launched on its own, as
+ * ddp_bucket_allreduce_avg.
  * Errors: as ddp_bucket_allreduce_avg. */
 DDP_API ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_flat,
                                     int32_t n_ranks, ddp_order_t order,
@@ -270,9 +273,10 @@ DDP_API ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const 
  *                  place (start from zeros), or NULL for plain SGD
  *   lr, momentum   learning rate and momentum factor (f32)
  * param_flat and momentum_flat may overlap no other buffer (DDP_ERR_ALIAS).
- * N == 1 takes the input as the average, bit for bit.  16-byte aligned
- * buffers take the vector kernels (N <= 8 unrolled, N > 8 looped), others a
- * per-element kernel with identical results.
+ * N == 1 takes the input as the average, bit for bit.  With param_flat,
+ * momentum_flat and grad_out on 16-byte boundaries the vector kernels run
+ * (N <= 8 unrolled, N > 8 looped; the rank buffers need only element
+ * alignment), otherwise a per-element kernel with identical results.
  * Errors: as ddp_sync_allreduce_avg. */
 DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
@@ -306,9 +310,10 @@ DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *ra
  * 512 bf16 elements): 8 * (n_ranks + 1) + 32 bytes rounded up to 16 (112
  * for 8 ranks, 1.2 % of the 9 KiB such a tile reads and writes), held until
  * ddp_param_sync_free.  The bindings' addresses are copied into it: bind
- * again if a gradient moves.  Parameters whose gradients and output all sit
- * on 16-byte boundaries take the vector path, others the per-element path
- * (same results).
+ * again if a gradient moves.  Parameters whose written tensors (outputs;
+ * parameters, momentum and stored average of the SGD step) sit on 16-byte
+ * boundaries take the vector path, reading the gradients at any element
+ * alignment; others take the per-element path (same results).
  * ddp_param_sync_run enqueues the sync on `stream` (current device = the
  * device it was created on); it allocates nothing, so it can be captured.
  * Errors: INVALID_ARG (null arguments, a binding of another plan or device,

@@ -164,15 +164,31 @@ def test_launch_count_follows_the_item_limit(env):
     assert k == launches(-(-P // 256), 64), ("sgd", k)
     _replay_equals_eager(torch, g, sgd, [params, mom], "fused SGD replay", sgd_reset)
 
-    # flat buffers off a 16-byte boundary: the per-element fused kernel, one
-    # grid per bucket
-    def sgd_elems():
+    # rank buffers off a 16-byte boundary: still the vector kernel
+    def sgd_mixed():
         ddp.sync_sgd_update(lp, [f[1:P + 1] for f in flats], params, 0.1, "ring",
                             momentum_buf=mom, momentum=0.9)
+    k, g = _kernel_nodes(torch, sgd_mixed)
+    assert k == launches(-(-P // 256), 64), ("sgd, ranks off 16 B", k)
+    _replay_equals_eager(torch, g, sgd_mixed, [params, mom], "SGD replay, ranks off 16 B", sgd_reset)
+
+    # parameters off a 16-byte boundary: the per-element fused kernel, one
+    # grid per bucket
+    pbig = torch.empty(P + 4, device=dev)
+    p_off = pbig[1:P + 1]
+
+    def p_reset():
+        p_off.copy_(p0)
+        mom.zero_()
+        torch.cuda.synchronize()
+
+    def sgd_elems():
+        ddp.sync_sgd_update(lp, [f[:P] for f in flats], p_off, 0.1, "ring", momentum_buf=mom,
+                            momentum=0.9)
     k, g = _kernel_nodes(torch, sgd_elems)
     lens = [lp.bucket(b)[0] for b in range(lp.n_buckets)]
     assert k == sum(launches(-(-n // 64), 64) for n in lens if n), ("per-element sgd", k)
-    _replay_equals_eager(torch, g, sgd_elems, [params, mom], "per-element SGD replay", sgd_reset)
+    _replay_equals_eager(torch, g, sgd_elems, [p_off, mom], "per-element SGD replay", p_reset)
 
     acc_dst = [torch.empty(P, device=dev) for _ in range(2)]
 
@@ -302,7 +318,8 @@ def test_real_limit_past_element_2_32(env):
     print("real limit: per-element fused SGD kernel past element 2^30", flush=True)
     L3 = 1_100_000_000
     lp3 = ddp.plan_buckets([L3], 25 << 20, "f32")
-    p3 = torch.empty(L3, dtype=torch.float32, device=dev)
+    p3big = torch.empty(L3 + 4, dtype=torch.float32, device=dev)
+    p3 = p3big[1:L3 + 1]                          # off a 16-byte boundary
     W.device_normal_(p3, 78, 3, 1.0)
     m3 = torch.zeros(L3, dtype=torch.float32, device=dev)
     tpos = set(int(x) for x in rng.integers(0, L3, 4000))
@@ -319,7 +336,7 @@ def test_real_limit_past_element_2_32(env):
     torch.cuda.synchronize()
     assert_bits_equal(to_host(p3.index_select(0, tidx), torch), wp3, "per-element SGD params")
     assert_bits_equal(to_host(m3.index_select(0, tidx), torch), wm3, "per-element SGD momentum")
-    del p3, m3, tidx
+    del p3, p3big, m3, tidx
     torch.cuda.empty_cache()
 
     print("real limit: fused SGD step with momentum", flush=True)
