@@ -1,7 +1,8 @@
 // Device-side building blocks of libddp's kernels for gfx950 (MI355X):
 // launch shape constants, the argument structs, streaming loads and stores,
-// bf16 conversion, the ring-segment lookup and the fixed-order folds.  Shared
-// by reduce.hip, accumulate.hip and copy.hip; not part of the ABI.
+// bf16 conversion, the ring-segment lookup, the fixed-order folds and the
+// store epilogues.  Shared by reduce.hip, params.hip, accumulate.hip and
+// copy.hip; not part of the ABI.
 //
 //
 // Pages: [DDP] "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel);
@@ -120,6 +121,60 @@ __device__ __forceinline__ void st_stream(void *p, const V &v)
     __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
 }
 
+// The same accesses at a base that is either a pointer (a kernel argument,
+// which the compiler knows to be global memory) or a 64-bit address read
+// from a table, typed as global memory here so that the access is a global
+// rather than a flat instruction.  Loads take a byte offset.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) u32x4_ua g_u32x4_ua;
+
+__device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
+{
+    return ld_stream(static_cast<const char *>(p) + off);
+}
+__device__ __forceinline__ u32x4 ld_at(uint64_t a, int64_t off)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4_ua *>(a + (uint64_t)off));
+}
+
+// Stores take the element index i of a T array at the base.
+template <typename T, typename V>
+__device__ __forceinline__ void st_at(void *p, int64_t i, const V &v)
+{
+    st_stream(static_cast<T *>(p) + i, v);
+}
+template <typename T, typename V>
+__device__ __forceinline__ void st_at(uint64_t a, int64_t i, const V &v)
+{
+    typedef __attribute__((address_space(1))) V GV;
+    __builtin_nontemporal_store(v, reinterpret_cast<GV *>(a + (uint64_t)i * sizeof(T)));
+}
+
+// Plain (cached) accesses of element i of a T array at either kind of base,
+// for the per-element paths.
+template <typename T>
+__device__ __forceinline__ T ld_elem(const void *p, int64_t i)
+{
+    return static_cast<const T *>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ T ld_elem(uint64_t a, int64_t i)
+{
+    typedef __attribute__((address_space(1))) T GT;
+    return *reinterpret_cast<const GT *>(a + (uint64_t)i * sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ void st_elem(void *p, int64_t i, T v)
+{
+    static_cast<T *>(p)[i] = v;
+}
+template <typename T>
+__device__ __forceinline__ void st_elem(uint64_t a, int64_t i, T v)
+{
+    typedef __attribute__((address_space(1))) T GT;
+    *reinterpret_cast<GT *>(a + (uint64_t)i * sizeof(T)) = v;
+}
+
 __device__ __forceinline__ float widen_bf16(uint32_t h) { return __uint_as_float(h << 16); }
 
 // f32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet, sign kept).
@@ -139,20 +194,20 @@ __device__ __forceinline__ float lane(const u32x4 &v, int e)
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
 }
 
-template <int IN>
-__device__ __forceinline__ float load_elem(const void *p, int64_t i)
+template <int IN, class A>
+__device__ __forceinline__ float load_elem(A p, int64_t i)
 {
-    if (IN == kF32) return static_cast<const float *>(p)[i];
-    return widen_bf16(static_cast<const uint16_t *>(p)[i]);
+    if (IN == kF32) return ld_elem<float>(p, i);
+    return widen_bf16(ld_elem<uint16_t>(p, i));
 }
 
-template <int OUT>
-__device__ __forceinline__ void store_elem(void *out, int64_t i, float y)
+template <int OUT, class A>
+__device__ __forceinline__ void store_elem(A out, int64_t i, float y)
 {
     if (OUT == kF32)
-        static_cast<float *>(out)[i] = y;
+        st_elem<float>(out, i, y);
     else
-        static_cast<uint16_t *>(out)[i] = (uint16_t)bf16_rne(y);
+        st_elem<uint16_t>(out, i, (uint16_t)bf16_rne(y));
 }
 
 __device__ __forceinline__ int wrap(int r, int n) { return r >= n ? r - n : r; }
@@ -171,19 +226,25 @@ __device__ __forceinline__ int ring_start(const Buckets &bk, int32_t b0, int N, 
     return (int)(((i - base) / C + 1) % N);
 }
 
-// The scaled average of element i, one element at a time (N >= 2).
+// The scaled average of element i of the ranks at bases p[0..N-1] (N >= 2),
+// folded from rank r (RING: the element's ring start; SEQ: 0, after +0).
+template <int IN, bool RING, class A>
+__device__ __forceinline__ float avg_at(const A *p, int N, int r, float inv, int64_t i)
+{
+    float acc = load_elem<IN>(p[r], i);
+    if (!RING) acc = 0.0f + acc;
+    for (int k = 1; k < N; ++k) {
+        r = wrap(r + 1, N);
+        acc = acc + load_elem<IN>(p[r], i);
+    }
+    return acc * inv;
+}
+
 template <int IN, bool RING>
 __device__ __forceinline__ float avg_elem(const RankArgs &ra, int N, int64_t total,
                                           const Buckets &bk, int32_t b0, float inv, int64_t i)
 {
-    int r = RING ? ring_start(bk, b0, N, i) : 0;
-    float acc = load_elem<IN>(ra.p[r], i);
-    if (!RING) acc = 0.0f + acc;
-    for (int k = 1; k < N; ++k) {
-        r = wrap(r + 1, N);
-        acc = acc + load_elem<IN>(ra.p[r], i);
-    }
-    return acc * inv;
+    return avg_at<IN, RING>(ra.p, N, RING ? ring_start(bk, b0, N, i) : 0, inv, i);
 }
 
 // Per-element path: positions [i0, i0 + cnt) clipped to total.
@@ -224,6 +285,27 @@ __device__ __forceinline__ float sgd_elem(float p, float g, float &m, float lr, 
     return p - step;
 }
 
+// Per-element epilogue of the fused step at element i: the average y stored
+// to gout unless gout is null (bf16: rounded, and the step takes the rounded
+// value), then the parameter (and momentum) updated.  Bases are pointers or
+// table addresses.
+template <int OUT, bool MOM, class A>
+__device__ __forceinline__ void sgd_at(A gout, A param, A mom, int64_t i, float y, float lr,
+                                       float mu)
+{
+    float g = y;
+    if (OUT == kBF16) {
+        const uint32_t h = bf16_rne(y);
+        g = widen_bf16(h);
+        if (gout != A()) st_elem<uint16_t>(gout, i, (uint16_t)h);
+    } else if (gout != A()) {
+        st_elem<float>(gout, i, y);
+    }
+    float m = MOM ? ld_elem<float>(mom, i) : 0.0f;
+    st_elem<float>(param, i, sgd_elem<MOM>(ld_elem<float>(param, i), g, m, lr, mu));
+    if (MOM) st_elem<float>(mom, i, m);
+}
+
 // Per-element fused path.  N == 1 takes the input as the average, bit for bit.
 template <int IN, int OUT, bool RING, bool MOM>
 __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Buckets &bk, int32_t b0,
@@ -233,17 +315,8 @@ __device__ void sgd_elems(const RankArgs &ra, int N, int64_t total, const Bucket
         const int64_t i = i0 + e;
         if (i >= total) break;
         const float y = N == 1 ? load_elem<IN>(ra.p[0], i) : avg_elem<IN, RING>(ra, N, total, bk, b0, inv, i);
-        float g = y;
-        if (OUT == kBF16) {
-            const uint32_t h = bf16_rne(y);
-            g = widen_bf16(h);
-            if (sa.grad_out) static_cast<uint16_t *>(sa.grad_out)[i] = (uint16_t)h;
-        } else if (sa.grad_out) {
-            static_cast<float *>(sa.grad_out)[i] = y;
-        }
-        float m = MOM ? sa.mom[i] : 0.0f;
-        sa.param[i] = sgd_elem<MOM>(sa.param[i], g, m, sa.lr, sa.mu);
-        if (MOM) sa.mom[i] = m;
+        sgd_at<OUT, MOM>(sa.grad_out, static_cast<void *>(sa.param), static_cast<void *>(sa.mom), i,
+                         y, sa.lr, sa.mu);
     }
 }
 
@@ -386,22 +459,6 @@ __device__ __forceinline__ void fold_seq(const u32x4 *v, float *acc)
         for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + lane<IN>(v[k], e);
 }
 
-// A streaming 16-byte load at byte offset `off` from a rank's base: a
-// pointer (kernel arguments, which the compiler knows to be global memory)
-// or a 64-bit address read from a table, typed as global memory here so that
-// the load is a global rather than a flat instruction.
-typedef __attribute__((address_space(1))) u32x4 g_u32x4;
-typedef __attribute__((address_space(1))) u32x4_ua g_u32x4_ua;
-
-__device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
-{
-    return ld_stream(static_cast<const char *>(p) + off);
-}
-__device__ __forceinline__ u32x4 ld_at(uint64_t a, int64_t off)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4_ua *>(a + (uint64_t)off));
-}
-
 // Any N up to DDP_MAX_RANKS: the ranks walked in the fold order starting at
 // the wave-uniform rank s, eight loads in flight at a time.  p[r] is rank r's
 // base address (a pointer or a 64-bit address), read with a scalar load, and
@@ -436,16 +493,18 @@ __device__ __forceinline__ void fold_looped(const Ptrs &p, int N, int s, int64_t
     }
 }
 
-// Convert and store one vector of scaled averages y at element i0; for a
-// bf16 output y is replaced by the stored value widened back to f32.
-template <int IN, int OUT>
-__device__ __forceinline__ void store_y(void *out, int64_t i0, float *y, bool write)
+// Convert and store one vector of scaled averages y at element i0 of the
+// tensor at `out` (a pointer or a table address; nothing is written unless
+// `write`); for a bf16 output y becomes the stored value widened back to f32
+// either way.
+template <int IN, int OUT, class A>
+__device__ __forceinline__ void store_y(A out, int64_t i0, float *y, bool write)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     if (OUT == kF32) {
         u32x4 o;
         for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
-        if (write) st_stream(static_cast<float *>(out) + i0, o);
+        if (write) st_at<float>(out, i0, o);
     } else {
         uint32_t h[VEC];
         for (int e = 0; e < VEC; ++e) {
@@ -456,18 +515,18 @@ __device__ __forceinline__ void store_y(void *out, int64_t i0, float *y, bool wr
             u32x2 o;
             o[0] = h[0] | (h[1] << 16);
             o[1] = h[2] | (h[3] << 16);
-            if (write) st_stream(static_cast<uint16_t *>(out) + i0, o);
+            if (write) st_at<uint16_t>(out, i0, o);
         } else {
             u32x4 o;
             for (int w = 0; w < 4; ++w) o[w] = h[2 * w] | (h[2 * w + 1] << 16);
-            if (write) st_stream(static_cast<uint16_t *>(out) + i0, o);
+            if (write) st_at<uint16_t>(out, i0, o);
         }
     }
 }
 
 // Scale, convert and store one vector of accumulators at element i0.
-template <int IN, int OUT>
-__device__ __forceinline__ void store_vec(void *out, int64_t i0, const float *acc, float inv)
+template <int IN, int OUT, class A>
+__device__ __forceinline__ void store_vec(A out, int64_t i0, const float *acc, float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     float y[VEC];
@@ -475,28 +534,38 @@ __device__ __forceinline__ void store_vec(void *out, int64_t i0, const float *ac
     store_y<IN, OUT>(out, i0, y, true);
 }
 
-// The vector epilogue of the fused step: store the average y (bf16: y
-// becomes the stored value widened back), then update the lane's parameter
-// vectors pv (and momentum mv), already loaded, in place.
-template <int IN, int OUT, bool MOM>
-__device__ __forceinline__ void sgd_vec(const SgdArgs &sa, int64_t i0, float *y, const u32x4 *pv,
-                                        const u32x4 *mv)
+// The vector epilogue of the fused step: store the average y to gout unless
+// gout is null (bf16: y becomes the stored value widened back), then update
+// the lane's parameter vectors pv (and momentum mv), already loaded, and
+// store them to param (and mom).  The three bases are pointers or table
+// addresses.
+template <int IN, int OUT, bool MOM, class A>
+__device__ __forceinline__ void sgd_vec(A gout, A param, A mom, int64_t i0, float *y,
+                                        const u32x4 *pv, const u32x4 *mv, float lr, float mu)
 {
     constexpr int PV = (IN == kF32 ? 4 : 8) / 4;
-    store_y<IN, OUT>(sa.grad_out, i0, y, sa.grad_out != nullptr);
+    store_y<IN, OUT>(gout, i0, y, gout != A());
 #pragma unroll
     for (int j = 0; j < PV; ++j) {
         u32x4 po, mo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
-            po[w] = __float_as_uint(
-                sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, sa.lr, sa.mu));
+            po[w] = __float_as_uint(sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, lr, mu));
             mo[w] = __float_as_uint(m);
         }
-        st_stream(sa.param + i0 + 4 * j, po);
-        if (MOM) st_stream(sa.mom + i0 + 4 * j, mo);
+        st_at<float>(param, i0 + 4 * j, po);
+        if (MOM) st_at<float>(mom, i0 + 4 * j, mo);
     }
+}
+
+// The same on the flat buffers of SgdArgs.
+template <int IN, int OUT, bool MOM>
+__device__ __forceinline__ void sgd_vec(const SgdArgs &sa, int64_t i0, float *y, const u32x4 *pv,
+                                        const u32x4 *mv)
+{
+    sgd_vec<IN, OUT, MOM>(sa.grad_out, static_cast<void *>(sa.param),
+                          static_cast<void *>(sa.mom), i0, y, pv, mv, sa.lr, sa.mu);
 }
 
 }  // namespace ddp_detail

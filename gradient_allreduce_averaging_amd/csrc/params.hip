@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "host.h"
@@ -66,94 +67,7 @@ int64_t ps_stride(int N, int extra)
     return (8 * (int64_t)(N + extra) + (int64_t)sizeof(PsMeta) + 15) / 16 * 16;
 }
 
-// Accesses at addresses read from the table, typed as global memory so that
-// they compile to global (not flat) instructions.
-typedef __attribute__((address_space(1))) u32x2 g_u32x2;
-typedef __attribute__((address_space(1))) float g_f32;
-typedef __attribute__((address_space(1))) uint32_t g_u32;
-typedef __attribute__((address_space(1))) uint16_t g_u16;
-
 __device__ __forceinline__ u32x4 gld_stream(uint64_t addr) { return ld_at(addr, 0); }
-__device__ __forceinline__ void gst_stream(uint64_t addr, const u32x4 &v)
-{
-    __builtin_nontemporal_store(v, reinterpret_cast<g_u32x4 *>(addr));
-}
-__device__ __forceinline__ void gst_stream(uint64_t addr, const u32x2 &v)
-{
-    __builtin_nontemporal_store(v, reinterpret_cast<g_u32x2 *>(addr));
-}
-
-// Convert and store one vector of averages y at tile element i0 of the
-// tensor at `out` (when `write`); for a bf16 output y becomes the stored
-// value widened back to f32 either way.
-template <int IN, int OUT>
-__device__ __forceinline__ void gstore_y(uint64_t out, int64_t i0, float *y, bool write)
-{
-    constexpr int VEC = IN == kF32 ? 4 : 8;
-    if (OUT == kF32) {
-        u32x4 o;
-        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
-        if (write) gst_stream(out + (uint64_t)i0 * 4, o);
-    } else {
-        uint32_t h[VEC];
-        for (int e = 0; e < VEC; ++e) {
-            h[e] = bf16_rne(y[e]);
-            y[e] = widen_bf16(h[e]);
-        }
-        if (VEC == 4) {
-            u32x2 o;
-            o[0] = h[0] | (h[1] << 16);
-            o[1] = h[2] | (h[3] << 16);
-            if (write) gst_stream(out + (uint64_t)i0 * 2, o);
-        } else {
-            u32x4 o;
-            for (int w = 0; w < 4; ++w) o[w] = h[2 * w] | (h[2 * w + 1] << 16);
-            if (write) gst_stream(out + (uint64_t)i0 * 2, o);
-        }
-    }
-}
-
-// Scale, convert and store one vector of accumulators.
-template <int IN, int OUT>
-__device__ __forceinline__ void gstore_vec(uint64_t out, int64_t i0, const float *acc, float inv)
-{
-    constexpr int VEC = IN == kF32 ? 4 : 8;
-    float y[VEC];
-    for (int e = 0; e < VEC; ++e) y[e] = acc[e] * inv;
-    gstore_y<IN, OUT>(out, i0, y, true);
-}
-
-// The SGD epilogue on one vector of averages y (the flat kernels' sgd_vec,
-// on table addresses): y stored to grad_out when that is not 0 (bf16: y
-// becomes the stored value widened back), then the lane's parameter vectors
-// pv (and momentum mv), already loaded, updated and stored.
-template <int IN, int OUT, bool MOM>
-__device__ __forceinline__ void gsgd_vec(uint64_t gout, uint64_t param, uint64_t mom, int64_t i0,
-                                         float *y, const u32x4 *pv, const u32x4 *mv, float lr,
-                                         float mu)
-{
-    constexpr int PV = (IN == kF32 ? 4 : 8) / 4;
-    gstore_y<IN, OUT>(gout, i0, y, gout != 0);
-#pragma unroll
-    for (int j = 0; j < PV; ++j) {
-        u32x4 po, mo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
-            po[w] = __float_as_uint(sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, lr, mu));
-            mo[w] = __float_as_uint(m);
-        }
-        gst_stream(param + (uint64_t)(i0 + 4 * j) * 4, po);
-        if (MOM) gst_stream(mom + (uint64_t)(i0 + 4 * j) * 4, mo);
-    }
-}
-
-template <int IN>
-__device__ __forceinline__ float gload_elem(uint64_t a, int64_t i)
-{
-    if (IN == kF32) return *reinterpret_cast<const g_f32 *>(a + (uint64_t)i * 4);
-    return widen_bf16(*reinterpret_cast<const g_u16 *>(a + (uint64_t)i * 2));
-}
 
 // The scaled average of tile element i, one element at a time (N >= 2).
 template <int IN, bool RING>
@@ -165,13 +79,7 @@ __device__ __forceinline__ float ps_avg_elem(const uint64_t *a, int N, const PsM
         const int64_t C = (m.blen + N - 1) / N;
         r = (int)(((m.pos + i) / C + 1) % N);
     }
-    float acc = gload_elem<IN>(a[r], i);
-    if (!RING) acc = 0.0f + acc;
-    for (int k = 1; k < N; ++k) {
-        r = wrap(r + 1, N);
-        acc = acc + gload_elem<IN>(a[r], i);
-    }
-    return acc * inv;
+    return avg_at<IN, RING>(a, N, r, inv, i);
 }
 
 // Per-element path of the sync: tile elements [i0, i0 + cnt) clipped to the tile.
@@ -185,18 +93,12 @@ __device__ void params_elems(const uint64_t *a, int N, const PsMeta &m, float in
         if (i >= (int64_t)m.count) break;
         if (N == 1) {   // the input, bit for bit (inputs and outputs share a dtype)
             if (IN == kF32)
-                *reinterpret_cast<g_u32 *>(out + (uint64_t)i * 4) =
-                    *reinterpret_cast<const g_u32 *>(a[0] + (uint64_t)i * 4);
+                st_elem<uint32_t>(out, i, ld_elem<uint32_t>(a[0], i));
             else
-                *reinterpret_cast<g_u16 *>(out + (uint64_t)i * 2) =
-                    *reinterpret_cast<const g_u16 *>(a[0] + (uint64_t)i * 2);
+                st_elem<uint16_t>(out, i, ld_elem<uint16_t>(a[0], i));
             continue;
         }
-        const float y = ps_avg_elem<IN, RING>(a, N, m, inv, i);
-        if (OUT == kF32)
-            *reinterpret_cast<g_f32 *>(out + (uint64_t)i * 4) = y;
-        else
-            *reinterpret_cast<g_u16 *>(out + (uint64_t)i * 2) = (uint16_t)bf16_rne(y);
+        store_elem<OUT>(out, i, ps_avg_elem<IN, RING>(a, N, m, inv, i));
     }
 }
 
@@ -205,23 +107,11 @@ template <int IN, int OUT, bool RING, bool MOM>
 __device__ void params_sgd_elems(const uint64_t *a, int N, const PsMeta &m, float inv, float lr,
                                  float mu, int64_t i0, int cnt)
 {
-    const uint64_t gout = a[N], param = a[N + 1], mom = a[N + 2];
     for (int e = 0; e < cnt; ++e) {
         const int64_t i = i0 + e;
         if (i >= (int64_t)m.count) break;
-        const float y = N == 1 ? gload_elem<IN>(a[0], i) : ps_avg_elem<IN, RING>(a, N, m, inv, i);
-        float g = y;
-        if (OUT == kBF16) {
-            const uint32_t h = bf16_rne(y);
-            g = widen_bf16(h);
-            if (gout) *reinterpret_cast<g_u16 *>(gout + (uint64_t)i * 2) = (uint16_t)h;
-        } else if (gout) {
-            *reinterpret_cast<g_f32 *>(gout + (uint64_t)i * 4) = y;
-        }
-        g_f32 *pp = reinterpret_cast<g_f32 *>(param + (uint64_t)i * 4);
-        float mm = MOM ? *reinterpret_cast<const g_f32 *>(mom + (uint64_t)i * 4) : 0.0f;
-        *pp = sgd_elem<MOM>(*pp, g, mm, lr, mu);
-        if (MOM) *reinterpret_cast<g_f32 *>(mom + (uint64_t)i * 4) = mm;
+        const float y = N == 1 ? load_elem<IN>(a[0], i) : ps_avg_elem<IN, RING>(a, N, m, inv, i);
+        sgd_at<OUT, MOM>(a[N], a[N + 1], a[N + 2], i, y, lr, mu);
     }
 }
 
@@ -301,14 +191,14 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
         const bool in_b = RING && vec && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
         if (in_a || in_b) {
             if constexpr (NR == 1 && IN == OUT) {
-                gst_stream(t.ad[1] + (uint64_t)(i0[u] * ISZ), v[u][0]);
+                st_at<std::conditional_t<IN == kF32, float, uint16_t>>(t.ad[1], i0[u], v[u][0]);
             } else {
                 float acc[VEC];
                 if (!RING)
                     fold_seq<NR, IN>(v[u], acc);
                 else
                     fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
-                gstore_vec<IN, OUT>(t.ad[NR], i0[u], acc, inv);
+                store_vec<IN, OUT>(t.ad[NR], i0[u], acc, inv);
             }
         } else if (i0[u] < cnt) {
             params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(e), NR, m, inv, i0[u],
@@ -342,7 +232,7 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
             if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
             float acc[VEC];
             fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
-            if (mine) gstore_vec<IN, OUT>(a[N], i0, acc, inv);
+            if (mine) store_vec<IN, OUT>(a[N], i0, acc, inv);
         }
         if (!in_a && !in_b && i0 < cnt) params_elems<IN, OUT, RING>(a, N, m, inv, i0, VEC);
     }
@@ -398,7 +288,7 @@ params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_bl
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
             }
-            gsgd_vec<IN, OUT, MOM>(gout, param, mom, i0[u], y, pv[u], mv[u], lr, mu);
+            sgd_vec<IN, OUT, MOM>(gout, param, mom, i0[u], y, pv[u], mv[u], lr, mu);
         } else if (i0[u] < cnt) {
             params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(e), NR, m, inv,
                                                  lr, mu, i0[u], VEC);
@@ -446,7 +336,7 @@ params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t f
             if (mine) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
-                gsgd_vec<IN, OUT, MOM>(gout, param, mom, i0, y, pv, mv, lr, mu);
+                sgd_vec<IN, OUT, MOM>(gout, param, mom, i0, y, pv, mv, lr, mu);
             }
         }
         if (!in_a && !in_b && i0 < cnt)
