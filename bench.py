@@ -37,6 +37,7 @@ import os
 import re
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -141,7 +142,29 @@ def run_environment(torch):
     return env
 
 
-def main():
+def stream_ms(c, fn, reps, warm=3, settle=False):
+    """Average ms per call of fn: `warm` untimed calls, then `reps` calls
+    between one event pair on the launch stream (after a device-wide
+    synchronisation when `settle`)."""
+    torch = c.torch
+    for _ in range(warm):
+        fn()
+    if settle:
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(c.stream)
+    for _ in range(reps):
+        fn()
+    b.record(c.stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def gbps(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -162,764 +185,724 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
+    return ap.parse_args()
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
-        sys.exit(2)
 
+def setup(args):
+    """The workload's plan, its N rank buffers (seeded synthetic gradients,
+    resident in HBM) and output, and the prepared synchronisation calls."""
     import numpy as np
     import torch
 
     import gradient_allreduce_averaging_amd as ddp
     import workloads as W
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    if args.calibrate:
-        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(10):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
-        return
-    wl = W.workload(args.workload)
-    order = args.order
-    N = wl.n_ranks
+    c = types.SimpleNamespace(args=args, np=np, torch=torch, ddp=ddp, W=W)
+    c.dev = torch.device("cuda:0")
+    c.wl = wl = W.workload(args.workload)
+    c.order = args.order
+    c.N = N = wl.n_ranks
     if wl.two_bucket:
-        plan = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
+        c.plan = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
     else:
-        plan = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, wl.dtype)
-    P = plan.total
-    tin = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    tout = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
-    log(f"workload {wl.name}: N={N} P={P} buckets={plan.n_buckets} order={order} "
+        c.plan = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, wl.dtype)
+    c.P = P = c.plan.total
+    c.tin = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    c.tout = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    log(f"workload {wl.name}: N={N} P={P} buckets={c.plan.n_buckets} order={c.order} "
         f"{wl.dtype}->{wl.out_dtype}")
-
-    flats = []
+    c.flats = []
     for r in range(N):
-        t = torch.empty(P, dtype=tin, device=dev)
+        t = torch.empty(P, dtype=c.tin, device=c.dev)
         W.device_normal_(t, r, wl.stream, wl.sigma)
-        flats.append(t)
-    out = torch.empty(P, dtype=tout, device=dev)
-    plan.prepare()
-    stream = torch.cuda.current_stream()
-    sync_bytes = wl.sync_bytes()
+        c.flats.append(t)
+    c.out = torch.empty(P, dtype=c.tout, device=c.dev)
+    c.plan.prepare()
+    c.stream = torch.cuda.current_stream()
+    c.sync_bytes = wl.sync_bytes()
+    prepared = {o: ddp.make_sync(c.plan, c.flats, c.out, o, stream=c.stream) for o in ("seq", "ring")}
 
-    prepared = {o: ddp.make_sync(plan, flats, out, o, stream=stream) for o in ("seq", "ring")}
-
-    def sync(o=order):
+    def sync(o=c.order):
         prepared[o]()
 
-    # ---------------------------------------------------------------- timed
-    # K back-to-back steps, wall clock between two synchronisations; one event
-    # pair brackets the loop on the launch stream.
+    c.sync = sync
+    return c
+
+
+def timed_steps(c):
+    """K back-to-back steps, wall clock between two synchronisations; one
+    event pair brackets the loop on the launch stream.  Then the same K
+    steps with each launch between its own event pair (these add the event
+    overhead of a few microseconds to each)."""
+    torch, args = c.torch, c.args
     for _ in range(args.warmup):
-        sync()
+        c.sync()
     loop_a, loop_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    loop_a.record(stream)
+    loop_a.record(c.stream)
     for _ in range(args.steps):
-        sync()
-    loop_b.record(stream)
+        c.sync()
+    loop_b.record(c.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gpu_ms_per_step = loop_a.elapsed_time(loop_b) / args.steps
-    value = sync_bytes / (ms_per_step * 1e-3) / 1e9
-
+    c.ms_per_step = (t1 - t0) * 1e3 / args.steps
     # The reduce kernel's average launch duration: the event pair around the
     # timed loop on the launch stream, over K back-to-back launches (one
     # kernel per step, so this is the kernel plus the launch gap).
-    kern_ms = gpu_ms_per_step
-    achieved = sync_bytes / (kern_ms * 1e-3) / 1e9
-    # Spread: the same K steps again, each launch bracketed by its own event
-    # pair (these add the event overhead of a few microseconds to each).
+    c.kern_ms = loop_a.elapsed_time(loop_b) / args.steps
+    c.value = c.sync_bytes / (c.ms_per_step * 1e-3) / 1e9
+    c.achieved = c.sync_bytes / (c.kern_ms * 1e-3) / 1e9
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for a, b in ev:
-        a.record(stream)
-        sync()
-        b.record(stream)
+        a.record(c.stream)
+        c.sync()
+        b.record(c.stream)
     torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    log(f"sync: {ms_per_step * 1e3:.1f} us/step wall, {gpu_ms_per_step * 1e3:.1f} us/step on the "
-        f"stream ({achieved:.0f} GB/s); single launches between events: median "
-        f"{np.median(launch_ms) * 1e3:.1f} us, min {min(launch_ms) * 1e3:.1f} us")
+    c.launch_ms = [a.elapsed_time(b) for a, b in ev]
+    log(f"sync: {c.ms_per_step * 1e3:.1f} us/step wall, {c.kern_ms * 1e3:.1f} us/step on the "
+        f"stream ({c.achieved:.0f} GB/s); single launches between events: median "
+        f"{c.np.median(c.launch_ms) * 1e3:.1f} us, min {min(c.launch_ms) * 1e3:.1f} us")
 
-    # ---------------------------------------------------------------- one launch per bucket
-    # The same sync as DDP issues it, one all-reduce call per bucket
-    # (ddp_bucket_allreduce_avg on each bucket's sub-ranges): driven from
-    # Python, and replayed from a HIP graph that captured those launches.
-    # Against the one-launch sync this is the launch overhead it saves.
-    per_bucket = None
-    if not args.no_per_bucket and 1 < plan.n_buckets <= 4096 and P < 10 ** 9:
-        spans = [plan.bucket(b)[:2] for b in range(plan.n_buckets)]
-        ins_b = [[f[base:base + ln] for f in flats] for ln, base in spans]
-        outs_b = [out[base:base + ln] for ln, base in spans]
-        side = torch.cuda.Stream()
 
-        def per_bucket_sync():
-            for xs_b, o_b in zip(ins_b, outs_b):
-                ddp.bucket_allreduce_avg(xs_b, o_b, order, stream=side)
+def leg_per_bucket(c):
+    """The same sync as DDP issues it, one all-reduce call per bucket
+    (ddp_bucket_allreduce_avg on each bucket's sub-ranges): driven from
+    Python, and replayed from a HIP graph that captured those launches.
+    Against the one-launch sync this is the launch overhead it saves."""
+    torch, ddp, plan = c.torch, c.ddp, c.plan
+    if c.args.no_per_bucket or not 1 < plan.n_buckets <= 4096 or c.P >= 10 ** 9:
+        return None
+    spans = [plan.bucket(b)[:2] for b in range(plan.n_buckets)]
+    ins_b = [[f[base:base + ln] for f in c.flats] for ln, base in spans]
+    outs_b = [c.out[base:base + ln] for ln, base in spans]
+    side = torch.cuda.Stream()
 
-        def timed_side(fn, reps):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                fn()
-            torch.cuda.synchronize()
-            return (time.perf_counter() - t0) * 1e3 / reps
+    def per_bucket_sync():
+        for xs_b, o_b in zip(ins_b, outs_b):
+            ddp.bucket_allreduce_avg(xs_b, o_b, c.order, stream=side)
 
-        reps = 20
-        eager_ms = timed_side(per_bucket_sync, reps)
-        graph = torch.cuda.CUDAGraph()
-        per_bucket_sync()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=side):
-            per_bucket_sync()
-        graph_ms = timed_side(graph.replay, reps)
-        del graph
-        per_bucket = {"launches": plan.n_buckets, "python_loop_ms": round(eager_ms, 4),
-                      "graph_replay_ms": round(graph_ms, 4), "one_launch_ms": round(ms_per_step, 4),
-                      "one_launch_speedup_vs_graph": round(graph_ms / ms_per_step, 3)}
-        log(f"per-bucket launches: {per_bucket}")
-
-    # ---------------------------------------------------------------- MALL flushed
-    # The same sync with a 512 MiB scratch buffer overwritten before each one,
-    # so that nothing of the previous sync is left in the 256 MB MALL; each
-    # sync bracketed by its own event pair (a few microseconds of event
-    # overhead included).
-    cold = None
-    if not args.no_cold:
-        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-        reps = min(args.steps, 50)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for a, b in ev:
-            scratch.fill_(1.0)
-            a.record(stream)
-            sync()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in ev]
-        cold = {"GBps_median": round(sync_bytes / (float(np.median(ts)) * 1e-3) / 1e9, 1),
-                "GBps_best": round(sync_bytes / (min(ts) * 1e-3) / 1e9, 1),
-                "ms_median": round(float(np.median(ts)), 5), "syncs": reps,
-                "flush": "512 MiB written before every sync"}
-        log(f"MALL flushed: {cold}")
-        del scratch
-
-    # ---------------------------------------------------------------- access-pattern ceiling
-    # The same N input buffers read with the reduce's access pattern (N
-    # non-temporal 16-byte loads per lane, one-wave blocks) with and without
-    # the one store per lane, and no arithmetic: the ceiling of this pattern
-    # on this machine, taken as the best over resident-block caps per CU (the
-    # library caps its kernels the same way).  The probe's store covers the
-    # input byte count, so it runs only when input and output elements have
-    # the same size.
-    ceiling = None
-    if wl.in_bytes == wl.out_bytes and not args.no_ceiling:
-        import ctypes
-        probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
-        probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
-                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-        sink = torch.zeros(4, dtype=torch.int32, device=dev)
-        nvec = P * wl.in_bytes // 16
-        ptrs = (ctypes.c_void_p * N)(*[ctypes.c_void_p(f.data_ptr()) for f in flats])
-
-        def probe_run(write, k):
-            rc = probe.ddp_probe_stream(ptrs, N, ctypes.c_void_p(out.data_ptr()), nvec, write, k,
-                                        ctypes.c_void_p(sink.data_ptr()),
-                                        ctypes.c_void_p(stream.cuda_stream))
-            assert rc == 0, "probe launch failed"
-
-        reps = min(args.steps, 50) if P < 10 ** 8 else 5
-        res = {}
-        for write in (1, 0):
-            for k in (0, 16, 14, 12, 10, 9, 8, 7, 6):
-                for _ in range(3):
-                    probe_run(write, k)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(reps):
-                    probe_run(write, k)
-                b.record(stream)
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / reps
-                gbps = nvec * 16 * (N + write) / (ms * 1e-3) / 1e9
-                if gbps > res.get(write, (0, 0))[0]:
-                    res[write] = (gbps, k)
-        ceiling = {"pattern_GBps": round(res[1][0], 1), "pattern_blocks_per_cu": res[1][1],
-                   "read_only_GBps": round(res[0][0], 1), "read_only_blocks_per_cu": res[0][1],
-                   "kernel_frac_of_pattern": round(achieved / res[1][0], 4),
-                   "probe": f"{N} non-temporal 16-byte loads + 1 store per lane on the same "
-                            "buffers, one-wave blocks, no arithmetic (read_only: without the "
-                            "store); best over caps of 6..16 resident blocks per CU and none"}
-        log(f"ceiling: {ceiling}")
-
-    # ---------------------------------------------------------------- other order
-    other = {}
-    for o in ("seq", "ring"):
-        if o == order:
-            continue
-        for _ in range(5):
-            sync(o)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            sync(o)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / args.steps
-        other[o] = {"ms_per_sync": round(ms, 5),
-                    "GBps": round(sync_bytes / (ms * 1e-3) / 1e9, 1)}
-
-    # ---------------------------------------------------------------- parity of the timed output
-    parity = None
-    cpu = None
-    oplan, span, sampled = None, P, False
-    if not args.no_cpu_baseline:
-        import oracle
-        if wl.two_bucket:
-            oplan = oracle.plan_two_bucket(wl.numel, wl.regions)
-        else:
-            oplan = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, wl.in_bytes)
-        sampled = wl.total * N * wl.in_bytes > (4 << 30)
-        if sampled:
-            # A bounded sample for the multi-GB workloads: the leading whole
-            # buckets up to 4 GiB of inputs (a bucket's RING chunks depend on
-            # its whole length).  The rate is the figure, labelled as
-            # extrapolated; a first bucket above the budget skips it.
-            keep = 0
-            while keep < oplan.n_buckets and \
-                    (oplan.bucket_base[keep] + oplan.bucket_len[keep]) * N * wl.in_bytes <= (4 << 30):
-                keep += 1
-            if keep == 0:
-                log("cpu baseline skipped: the first bucket alone exceeds the 4 GiB sample budget")
-                oplan = None
-            else:
-                span = oplan.bucket_base[keep - 1] + oplan.bucket_len[keep - 1]
-                kept = [p for b in oplan.buckets[:keep] for p in b]
-                sub, k = [], 0
-                for b in oplan.buckets[:keep]:
-                    sub.append(list(range(k, k + len(b))))
-                    k += len(b)
-                oplan = oracle.Plan([oplan.numel[p] for p in kept], sub)
-    if oplan is not None:
-        sync()
-        torch.cuda.synchronize()
-        got = out[:span].view(torch.int32 if tout == torch.float32 else torch.int16).cpu().numpy()
-        host = [f[:span].view(torch.int32 if tin == torch.float32 else torch.int16).cpu().numpy()
-                .view(np.float32 if tin == torch.float32 else np.uint16) for f in flats]
-        sample_bytes = span * (N * wl.in_bytes + wl.out_bytes)
-        reps, t_cpu = 0, 0.0
-        want = None
-        while reps == 0 or t_cpu < args.cpu_seconds:
-            c0 = time.perf_counter()
-            want = oracle.sync_avg(oplan, host, order, wl.dtype, wl.out_dtype)
-            t_cpu += time.perf_counter() - c0
-            reps += 1
-        wv = want.view(np.int32 if tout == torch.float32 else np.int16)
-        same = got == wv
-        if tout == torch.float32:
-            both_nan = np.isnan(got.view(np.float32)) & np.isnan(want)
-        else:
-            both_nan = np.zeros_like(same)
-        parity = "bitwise equal to the CPU oracle" if bool((same | both_nan).all()) else \
-            f"MISMATCH in {int((~(same | both_nan)).sum())} elements"
-        cpu_model = "unknown"
-        try:
-            with open("/proc/cpuinfo") as f:
-                cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-        except (OSError, StopIteration):
-            pass
-        what = (f"the first {oplan.n_buckets} bucket(s), {span} of {P} elements, of the {wl.name} "
-                f"synchronisation; rate extrapolated to the whole" if sampled else
-                f"the full {wl.name} synchronisation")
-        cpu = {"value": round(sample_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "host_cpu": cpu_model, "host_threads": os.cpu_count(),
-               "sample": f"{what} ({order} order, N={N}), {reps} repetition(s), {t_cpu:.1f} s "
-                         f"single-threaded C oracle"}
-        if sampled:
-            parity = parity + " (on the sampled buckets)"
-        # context: a plain single-threaded host copy of 256 MiB (read + write bytes)
-        src_h = np.ones(1 << 26, dtype=np.float32)
-        dst_h = np.empty_like(src_h)
-        np.copyto(dst_h, src_h)
-        c0, n_cp = time.perf_counter(), 0
-        while n_cp == 0 or time.perf_counter() - c0 < 1.0:
-            np.copyto(dst_h, src_h)
-            n_cp += 1
-        cpu["host_copy_GBps"] = round(2 * src_h.nbytes * n_cp / (time.perf_counter() - c0) / 1e9, 2)
-        del src_h, dst_h
-        log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps; "
-            f"host copy {cpu['host_copy_GBps']} GB/s")
-
-        # The oracle on all of this process's host cores: SEQ order, every
-        # bucket split into disjoint element ranges, one ctypes call per range
-        # (the call releases the GIL).  SEQ has no index dependence, so the
-        # split leaves every bit as it is; its result is checked against the
-        # GPU's SEQ output of the same buffers.
-        threads = min(16, len(os.sched_getaffinity(0)))
-        pieces = []
-        for base, ln in zip(oplan.bucket_base, oplan.bucket_len):
-            step = max(1, -(-ln // threads))
-            pieces += [(base + a, min(step, ln - a)) for a in range(0, ln, step)]
-        seq_want = np.empty(span, dtype=np.float32 if tout == torch.float32 else np.uint16)
-
-        def piece(pc):
-            a, n = pc
-            seq_want[a:a + n] = oracle.bucket_avg([h[a:a + n] for h in host], "seq",
-                                                  wl.dtype, wl.out_dtype)
-
-        from concurrent.futures import ThreadPoolExecutor
-        reps_mt, t_mt = 0, 0.0
-        with ThreadPoolExecutor(threads) as ex:
-            while reps_mt == 0 or t_mt < args.cpu_seconds / 2:
-                c0 = time.perf_counter()
-                list(ex.map(piece, pieces))
-                t_mt += time.perf_counter() - c0
-                reps_mt += 1
-        sync("seq")
-        torch.cuda.synchronize()
-        got_seq = out[:span].view(torch.int32 if tout == torch.float32 else torch.int16).cpu().numpy()
-        sv = seq_want.view(got_seq.dtype)
-        ok = got_seq == sv
-        if tout == torch.float32:
-            ok |= np.isnan(got_seq.view(np.float32)) & np.isnan(seq_want)
-        cpu["all_cores"] = {
-            "value": round(sample_bytes * reps_mt / t_mt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "order": "seq", "parity_vs_gpu_seq": "bitwise equal" if bool(ok.all())
-            else f"MISMATCH in {int((~ok).sum())} elements",
-            "sample": f"{reps_mt} repetition(s) of {'the sample' if sampled else 'the full synchronisation'}"
-                      f", {len(pieces)} element ranges on {threads} threads, {t_mt:.1f} s"}
-        log(f"cpu oracle, {threads} threads (seq): {cpu['all_cores']['value']} GB/s; "
-            f"{cpu['all_cores']['parity_vs_gpu_seq']}")
-
-    # ---------------------------------------------------------------- copy layout
-    copy_path = None
-    if not args.no_copy_path and not wl.two_bucket and N * P * wl.in_bytes <= (16 << 30):
-        # per-parameter gradients of every rank, holding the same values
-        grads = [[torch.empty(n, dtype=tin, device=dev) for n in wl.numel] for _ in range(N)]
-        binds = [ddp.bind_params(plan, grads[r]) for r in range(N)]
-        for r in range(N):
-            ddp.unflatten(plan, binds[r], flats[r], stream=stream)
-        res = [torch.empty(n, dtype=tout, device=dev) for n in wl.numel]
-        rbind = ddp.bind_params(plan, res)
-
-        def full_step(st=stream):
-            for r in range(N):
-                ddp.flatten(plan, binds[r], flats[r], stream=st)
-            ddp.sync_allreduce_avg(plan, flats, out, order, stream=st)
-            ddp.unflatten(plan, rbind, out, stream=st)
-
-        for _ in range(5):
-            full_step()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        reps = max(10, args.steps // 4)
-        tf = ts = tu = 0.0
-        for _ in range(reps):
-            e[0].record(stream)
-            for r in range(N):
-                ddp.flatten(plan, binds[r], flats[r], stream=stream)
-            e[1].record(stream)
-            sync()
-            e[2].record(stream)
-            ddp.unflatten(plan, rbind, out, stream=stream)
-            e[3].record(stream)
-            torch.cuda.synchronize()
-            tf += e[0].elapsed_time(e[1])
-            ts += e[1].elapsed_time(e[2])
-            tu += e[2].elapsed_time(e[3])
-        tf, ts, tu = tf / reps, ts / reps, tu / reps
-        fb = 2 * N * P * wl.in_bytes
-        ub = 2 * P * wl.out_bytes
-        copy_path = {
-            "ms_per_step": round(tf + ts + tu, 4),
-            "flatten_ms": round(tf, 4), "flatten_GBps": round(fb / (tf * 1e-3) / 1e9, 1),
-            "sync_ms": round(ts, 4),
-            "unflatten_ms": round(tu, 4), "unflatten_GBps": round(ub / (tu * 1e-3) / 1e9, 1),
-            "metric_GBps": round(sync_bytes / ((tf + ts + tu) * 1e-3) / 1e9, 1),
-            "launches": N + 2}
-        # the same step captured once into a HIP graph and replayed
-        graph = torch.cuda.CUDAGraph()
-        cap_stream = torch.cuda.Stream()
-        cap_stream.wait_stream(stream)
-        with torch.cuda.stream(cap_stream):
-            with torch.cuda.graph(graph, stream=cap_stream):
-                full_step(cap_stream)
-        torch.cuda.synchronize()
-        loop = {}
-        for name, fn in (("eager", full_step), ("graph", graph.replay)):
-            for _ in range(3):
-                fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(reps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            loop[name] = a.elapsed_time(b) / reps
-        copy_path["eager_loop_ms_per_step"] = round(loop["eager"], 4)
-        copy_path["graph_replay_ms_per_step"] = round(loop["graph"], 4)
-
-        # the same step as one kernel over the per-parameter tensors
-        ps = ddp.param_sync(plan, binds, rbind, order)
-        for _ in range(5):
-            ps(stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            ps(stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        t_ps = a.elapsed_time(b) / reps
-        chk = [torch.empty_like(t) for t in res]
-        ddp.unflatten(plan, ddp.bind_params(plan, chk), out, stream=stream)   # out holds this sync
-        torch.cuda.synchronize()
-        same = all(torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
-                               y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
-                   for x, y in zip(res, chk))
-        copy_path["param_sync"] = {
-            "ms_per_step": round(t_ps, 4), "GBps": round(sync_bytes / (t_ps * 1e-3) / 1e9, 1),
-            "speedup_vs_three_steps": round((tf + ts + tu) / t_ps, 2),
-            "same_bits_as_three_steps": bool(same),
-            "step": "every rank's per-parameter gradients averaged into per-parameter outputs "
-                    "in one launch (ddp_param_sync_run)"}
-        log(f"copy path: {copy_path}")
-        del grads, binds, res, rbind, graph, ps, chk
-
-    # ---------------------------------------------------------------- fused optimizer step
-    # The average folded into a momentum-SGD step (ddp_sync_sgd_update) against
-    # the unfused sequence it replaces: the synchronisation, then the optimizer
-    # reading the averaged gradient back (torch's in-place ops).
-    fused = None
-    if not args.no_fused_sgd and wl.out_dtype == "f32":
-        params = torch.empty(P, dtype=torch.float32, device=dev)
-        W.device_normal_(params, 99, 7, 1.0)
-        mbuf = torch.zeros(P, dtype=torch.float32, device=dev)
-        lr, mu = 0.01, 0.9
-
-        def fused_step():
-            ddp.sync_sgd_update(plan, flats, params, lr, order, momentum_buf=mbuf, momentum=mu,
-                                stream=stream)
-
-        def unfused_step():
-            sync()
-            mbuf.mul_(mu).add_(out)
-            params.add_(mbuf, alpha=-lr)
-
-        res = {}
-        for name, fn in (("fused", fused_step), ("unfused", unfused_step)):
-            for _ in range(5):
-                fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            res[name] = a.elapsed_time(b) / args.steps
-        fb = N * P * wl.in_bytes + 4 * P * 4
-        fused = {"ms": round(res["fused"], 5), "GBps": round(fb / (res["fused"] * 1e-3) / 1e9, 1),
-                 "bytes": fb, "unfused_ms": round(res["unfused"], 5),
-                 "speedup_vs_unfused": round(res["unfused"] / res["fused"], 3),
-                 "step": "momentum SGD (mu 0.9) on f32 parameters; unfused = sync + torch mul_/add_"}
-        # the same step on per-parameter tensors (gradients, parameters and
-        # momentum buffers as autograd and the optimizer keep them)
-        if N * P * wl.in_bytes <= (16 << 30):
-            gviews = []
-            for r in range(N):
-                g = [torch.empty(n, dtype=tin, device=dev) for n in wl.numel]
-                ddp.unflatten(plan, ddp.bind_params(plan, g), flats[r], stream=stream)
-                gviews.append(g)
-            pp = [torch.empty(n, dtype=torch.float32, device=dev).normal_() for n in wl.numel]
-            pm = [torch.zeros(n, dtype=torch.float32, device=dev) for n in wl.numel]
-            step = ddp.param_sgd(plan, [ddp.bind_params(plan, g) for g in gviews],
-                                 ddp.bind_params(plan, pp), ddp.bind_params(plan, pm), None, order)
-            for _ in range(5):
-                step(lr, mu, stream)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                step(lr, mu, stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            t_p = a.elapsed_time(b) / args.steps
-            fused["per_parameter"] = {
-                "ms": round(t_p, 5), "GBps": round(fb / (t_p * 1e-3) / 1e9, 1),
-                "step": "the same step on per-parameter gradients, parameters and momentum "
-                        "(ddp_param_sgd_run)"}
-            del gviews, pp, pm, step
-        log(f"fused sgd: {fused}")
-        del params, mbuf
-
-    # ---------------------------------------------------------------- two-bucket overlap
-    # The two-bucket plan of the same tensors: DEEP_COMM averaged on an update
-    # stream while a GEMM (standing in for the first layer's backward) runs on
-    # a compute stream; exposed = overlapped time - compute time.  Steps are
-    # timed back to back with both streams joined at every step boundary.
-    overlap = None
-    if not args.no_overlap and wl.name == "resnet50":
-        tb = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
-        (dl, db, _, _), (fl_, fb_, _, _) = tb.bucket(0), tb.bucket(1)
-        mat_a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-        mat_b = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-        comp, upd, tried = side_by_side_streams(torch)
-        deep_in = [f[db:db + dl] for f in flats]
-        deep_out = out[db:db + dl]
-
-        def compute():
-            with torch.cuda.stream(comp):
-                torch.mm(mat_a, mat_b)
-
-        def deep():
-            ddp.bucket_allreduce_avg(deep_in, deep_out, order, stream=upd)
-
-        def step_barrier():
-            # a training step ends when both streams have: the next step's
-            # backward needs the averaged gradients, and the next syncs the
-            # next step's gradients
-            e_comp, e_upd = torch.cuda.Event(), torch.cuda.Event()
-            e_comp.record(comp)
-            e_upd.record(upd)
-            comp.wait_event(e_upd)
-            upd.wait_event(e_comp)
-
-        def timed(fns, reps=20):
-            for _ in range(3):
-                for f in fns:
-                    f()
-                step_barrier()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                for f in fns:
-                    f()
-                step_barrier()
-            torch.cuda.synchronize()
-            return (time.perf_counter() - t0) * 1e3 / reps
-
-        t_comp = timed([compute])
-        overlap = {"plan": "two-bucket (DEEP_COMM %d, FIRST_COMM %d elements)" % (dl, fl_),
-                   "compute_ms": round(t_comp, 4),
-                   "compute": "bf16 GEMM 4096^3 on a second stream",
-                   "streams": ("side by side (hardware queues checked; %d tried)" % tried
-                               if tried else "not found side by side: results are serial")}
-        # under both occupancy policies: the tuned cap reserves LDS that the
-        # GEMM's blocks would need, "shared" leaves it free
-        for policy in ("tuned", "shared"):
-            ddp.set_occupancy(policy)
-            t_deep = timed([deep])
-            t_both = timed([compute, deep])
-            overlap[policy] = {"deep_sync_ms": round(t_deep, 4), "overlapped_ms": round(t_both, 4),
-                               "exposed_sync_ms": round(max(t_both - t_comp, 0.0), 4),
-                               "hidden_fraction": round(1.0 - max(t_both - t_comp, 0.0) / t_deep, 3)}
-        ddp.set_occupancy("tuned")
-
-        # The bucket-by-bucket schedule of DDP ([DDP] 3.2, [TR24] 十一): bucket b
-        # (cap plan, last layers first) is averaged on the update stream as
-        # soon as a stand-in for the backward of its layers -- a bf16 GEMM
-        # with FLOPs in proportion to the bucket's share of the parameters,
-        # about 262 GFLOP in all (ResNet-50's backward at 32 images per GPU)
-        # -- has finished on the compute stream.
-        buckets = [plan.bucket(b) for b in range(plan.n_buckets)]
-        ks = [max(64, int(round(7808 * ln / P / 64)) * 64) for ln, _, _, _ in buckets]
-        lhs = [torch.randn(4096, k, device=dev, dtype=torch.bfloat16) for k in ks]
-        rhs = [torch.randn(k, 4096, device=dev, dtype=torch.bfloat16) for k in ks]
-        ready = [torch.cuda.Event() for _ in buckets]
-        ins = [[f[base:base + ln] for f in flats] for ln, base, _, _ in buckets]
-        outs_b = [out[base:base + ln] for ln, base, _, _ in buckets]
-
-        def backward():
-            with torch.cuda.stream(comp):
-                for a, b, e in zip(lhs, rhs, ready):
-                    torch.mm(a, b)
-                    e.record(comp)
-
-        def bucket_syncs(wait):
-            for b in range(len(buckets)):
-                if wait:
-                    upd.wait_event(ready[b])
-                ddp.bucket_allreduce_avg(ins[b], outs_b[b], order, stream=upd)
-
-        t_bwd = timed([backward])
-        gflop = sum(2 * 4096 * k * 4096 for k in ks) / 1e9
-        overlap["schedule"] = {"buckets": len(buckets), "backward_gflop": round(gflop, 1),
-                               "backward_ms": round(t_bwd, 4)}
-        for policy in ("tuned", "shared"):
-            ddp.set_occupancy(policy)
-            t_syncs = timed([lambda: bucket_syncs(False)])
-            t_sched = timed([backward, lambda: bucket_syncs(True)])
-            overlap["schedule"][policy] = {
-                "syncs_ms": round(t_syncs, 4), "serial_ms": round(t_bwd + t_syncs, 4),
-                "overlapped_ms": round(t_sched, 4),
-                "exposed_sync_ms": round(max(t_sched - t_bwd, 0.0), 4),
-                "hidden_fraction": round(1.0 - max(t_sched - t_bwd, 0.0) / t_syncs, 3)}
-        ddp.set_occupancy("tuned")
-
-        # the same schedule on per-parameter gradients (as autograd leaves
-        # them): bucket b of one ddp_param_sync per step, run when ready
-        pg = []
-        for r in range(N):
-            g = [torch.empty(n, dtype=tin, device=dev) for n in wl.numel]
-            ddp.unflatten(plan, ddp.bind_params(plan, g), flats[r], stream=stream)
-            pg.append(g)
-        pout = [torch.empty(n, dtype=tout, device=dev) for n in wl.numel]
-        pps = ddp.param_sync(plan, [ddp.bind_params(plan, g) for g in pg],
-                             ddp.bind_params(plan, pout), order)
-
-        def param_syncs(wait):
-            for b in range(len(buckets)):
-                if wait:
-                    upd.wait_event(ready[b])
-                pps(upd, buckets=(b, 1))
-
-        per_param = {"sync": "ddp_param_sync_run_buckets, one bucket per launch"}
-        for policy in ("tuned", "shared"):
-            ddp.set_occupancy(policy)
-            t_psyncs = timed([lambda: param_syncs(False)])
-            t_psched = timed([backward, lambda: param_syncs(True)])
-            per_param[policy] = {
-                "syncs_ms": round(t_psyncs, 4), "serial_ms": round(t_bwd + t_psyncs, 4),
-                "overlapped_ms": round(t_psched, 4),
-                "exposed_sync_ms": round(max(t_psched - t_bwd, 0.0), 4),
-                "hidden_fraction": round(1.0 - max(t_psched - t_bwd, 0.0) / t_psyncs, 3)}
-        ddp.set_occupancy("tuned")
-        overlap["schedule"]["per_parameter"] = per_param
-        del lhs, rhs, pg, pout, pps
-        log(f"overlap: {overlap}")
-        del mat_a, mat_b, tb
-
-    # ---------------------------------------------------------------- rank sweep
-    # The same plan averaged over N = 2..32 virtual ranks (N > 8 takes the
-    # looped kernel): bandwidth against the number of concurrent streams.
-    rank_sweep = None
-    if not args.no_rank_sweep and wl.name == "resnet50":
-        extra = []
-        for r in range(N, 32):
-            t = torch.empty(P, dtype=tin, device=dev)
-            W.device_normal_(t, r, wl.stream, wl.sigma)
-            extra.append(t)
-        pool = flats + extra
-        sweep_out = torch.empty(P, dtype=tout, device=dev)
-        rank_sweep = {}
-        for n in (2, 4, 6, 8, 9, 12, 16, 32):
-            row = {}
-            for o in ("ring", "seq"):
-                call = ddp.make_sync(plan, pool[:n], sweep_out, o, stream=stream)
-                for _ in range(3):
-                    call()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(50):
-                    call()
-                b.record(stream)
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / 50
-                row[o] = round((n * wl.in_bytes + wl.out_bytes) * P / (ms * 1e-3) / 1e9, 1)
-            rank_sweep[str(n)] = row
-        log(f"rank sweep (GB/s): {rank_sweep}")
-        del extra, pool, sweep_out
-
-    # ---------------------------------------------------------------- in place
-    # The all-reduce as the pages run it, in place (send buffer == receive
-    # buffer): the average overwrites rank 0's bucket buffer.  Runs after the
-    # parity leg because it rewrites rank 0's gradients.
-    in_place = {}
-    for o in (() if args.no_in_place else ("ring", "seq")):
-        call = ddp.make_sync(plan, flats, flats[0], o, stream=stream)
+    def timed_side(fn, reps):
         for _ in range(3):
-            call()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            call()
-        b.record(stream)
+            fn()
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / args.steps
-        in_place[o] = {"ms_per_sync": round(ms, 5), "GBps": round(sync_bytes / (ms * 1e-3) / 1e9, 1)}
-    log(f"in place: {in_place}")
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
 
-    # ---------------------------------------------------------------- no_sync accumulation
-    # M micro-steps: with no_sync each rank accumulates locally (M - 1
-    # accumulates) and synchronises once; without it every micro-step also
-    # synchronises.  Separate buffers keep the benchmark's inputs untouched.
-    no_sync = None
-    if not args.no_no_sync and 2 * N * P * wl.in_bytes <= (16 << 30):
-        M = 4
-        local = [f.clone() for f in flats]
-        micro = [f.clone() for f in flats]
+    eager_ms = timed_side(per_bucket_sync, 20)
+    graph = torch.cuda.CUDAGraph()
+    per_bucket_sync()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        per_bucket_sync()
+    graph_ms = timed_side(graph.replay, 20)
+    del graph
+    res = {"launches": plan.n_buckets, "python_loop_ms": round(eager_ms, 4),
+           "graph_replay_ms": round(graph_ms, 4), "one_launch_ms": round(c.ms_per_step, 4),
+           "one_launch_speedup_vs_graph": round(graph_ms / c.ms_per_step, 3)}
+    log(f"per-bucket launches: {res}")
+    return res
 
-        def acc():
-            ddp.accumulate(local, micro, stream=stream)
 
-        def sync_local():
-            ddp.sync_allreduce_avg(plan, local, out, order, stream=stream)
+def leg_cold_mall(c):
+    """The same sync with a 512 MiB scratch buffer overwritten before each
+    one, so that nothing of the previous sync is left in the 256 MB MALL;
+    each sync bracketed by its own event pair (a few microseconds of event
+    overhead included)."""
+    torch, np = c.torch, c.np
+    if c.args.no_cold:
+        return None
+    scratch = torch.empty(1 << 27, dtype=torch.float32, device=c.dev)
+    reps = min(c.args.steps, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        scratch.fill_(1.0)
+        a.record(c.stream)
+        c.sync()
+        b.record(c.stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in ev]
+    res = {"GBps_median": gbps(c.sync_bytes, float(np.median(ts))),
+           "GBps_best": gbps(c.sync_bytes, min(ts)),
+           "ms_median": round(float(np.median(ts)), 5), "syncs": reps,
+           "flush": "512 MiB written before every sync"}
+    log(f"MALL flushed: {res}")
+    return res
 
-        res = {}
-        for name, fn in (("acc", acc), ("sync", sync_local)):
-            for _ in range(3):
-                fn()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.steps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            res[name] = a.elapsed_time(b) / args.steps
-        acc_bytes = 3 * N * P * wl.in_bytes
-        no_sync = {"micro_steps": M, "accumulate_ms": round(res["acc"], 5),
-                   "accumulate_GBps": round(acc_bytes / (res["acc"] * 1e-3) / 1e9, 1),
-                   "no_sync_ms": round((M - 1) * res["acc"] + res["sync"], 5),
-                   "sync_every_step_ms": round((M - 1) * res["acc"] + M * res["sync"], 5),
-                   "syncs_saved": M - 1}
-        log(f"no_sync: {no_sync}")
-        del local, micro
 
-    traffic = measured_traffic(wl.name, order, sync_bytes)
+def leg_ceiling(c):
+    """The same N input buffers read with the reduce's access pattern (N
+    non-temporal 16-byte loads per lane, one-wave blocks) with and without
+    the one store per lane, and no arithmetic: the ceiling of this pattern on
+    this box, taken as the best over resident-block caps per CU (the library
+    caps its kernels the same way).  The probe's store covers the input byte
+    count, so it runs only when input and output elements have the same
+    size."""
+    import ctypes
+    torch, wl, N = c.torch, c.wl, c.N
+    if wl.in_bytes != wl.out_bytes or c.args.no_ceiling:
+        return None
+    probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
+    probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=c.dev)
+    nvec = c.P * wl.in_bytes // 16
+    ptrs = (ctypes.c_void_p * N)(*[ctypes.c_void_p(f.data_ptr()) for f in c.flats])
+
+    def probe_run(write, k):
+        rc = probe.ddp_probe_stream(ptrs, N, ctypes.c_void_p(c.out.data_ptr()), nvec, write, k,
+                                    ctypes.c_void_p(sink.data_ptr()),
+                                    ctypes.c_void_p(c.stream.cuda_stream))
+        assert rc == 0, "probe launch failed"
+
+    reps = min(c.args.steps, 50) if c.P < 10 ** 8 else 5
+    best = {}
+    for write in (1, 0):
+        for k in (0, 16, 14, 12, 10, 9, 8, 7, 6):
+            ms = stream_ms(c, lambda: probe_run(write, k), reps)
+            rate = nvec * 16 * (N + write) / (ms * 1e-3) / 1e9
+            if rate > best.get(write, (0, 0))[0]:
+                best[write] = (rate, k)
+    res = {"pattern_GBps": round(best[1][0], 1), "pattern_blocks_per_cu": best[1][1],
+           "read_only_GBps": round(best[0][0], 1), "read_only_blocks_per_cu": best[0][1],
+           "kernel_frac_of_pattern": round(c.achieved / best[1][0], 4),
+           "probe": f"{N} non-temporal 16-byte loads + 1 store per lane on the same "
+                    "buffers, one-wave blocks, no arithmetic (read_only: without the "
+                    "store); best over caps of 6..16 resident blocks per CU and none"}
+    log(f"ceiling: {res}")
+    return res
+
+
+def leg_other_orders(c):
+    res = {}
+    for o in ("seq", "ring"):
+        if o == c.order:
+            continue
+        ms = stream_ms(c, lambda: c.sync(o), c.args.steps, warm=5)
+        res[o] = {"ms_per_sync": round(ms, 5), "GBps": gbps(c.sync_bytes, ms)}
+    return res
+
+
+def oracle_sample(c, oracle):
+    """The oracle's plan of the workload and the element span it covers: the
+    whole plan, or for the multi-GB workloads a bounded sample, the leading
+    whole buckets up to 4 GiB of inputs (a bucket's RING chunks depend on its
+    whole length); None when the first bucket alone exceeds that."""
+    wl, N = c.wl, c.N
+    if wl.two_bucket:
+        oplan = oracle.plan_two_bucket(wl.numel, wl.regions)
+    else:
+        oplan = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, wl.in_bytes)
+    if wl.total * N * wl.in_bytes <= (4 << 30):
+        return oplan, c.P, False
+    keep = 0
+    while keep < oplan.n_buckets and \
+            (oplan.bucket_base[keep] + oplan.bucket_len[keep]) * N * wl.in_bytes <= (4 << 30):
+        keep += 1
+    if keep == 0:
+        log("cpu baseline skipped: the first bucket alone exceeds the 4 GiB sample budget")
+        return None, 0, True
+    span = oplan.bucket_base[keep - 1] + oplan.bucket_len[keep - 1]
+    kept = [p for b in oplan.buckets[:keep] for p in b]
+    sub, k = [], 0
+    for b in oplan.buckets[:keep]:
+        sub.append(list(range(k, k + len(b))))
+        k += len(b)
+    return oracle.Plan([oplan.numel[p] for p in kept], sub), span, True
+
+
+def leg_parity_and_cpu(c):
+    """Parity of the timed output against the CPU oracle, and the oracle's
+    rate on the host: one thread in the benchmark's order, then SEQ on all of
+    this process's host cores."""
+    if c.args.no_cpu_baseline:
+        return None, None
+    import oracle
+    torch, np, wl, N, order = c.torch, c.np, c.wl, c.N, c.order
+    oplan, span, sampled = oracle_sample(c, oracle)
+    if oplan is None:
+        return None, None
+    f32_out = c.tout == torch.float32
+    c.sync()
+    torch.cuda.synchronize()
+    got = c.out[:span].view(torch.int32 if f32_out else torch.int16).cpu().numpy()
+    host = [f[:span].view(torch.int32 if c.tin == torch.float32 else torch.int16).cpu().numpy()
+            .view(np.float32 if c.tin == torch.float32 else np.uint16) for f in c.flats]
+    sample_bytes = span * (N * wl.in_bytes + wl.out_bytes)
+    reps, t_cpu = 0, 0.0
+    want = None
+    while reps == 0 or t_cpu < c.args.cpu_seconds:
+        c0 = time.perf_counter()
+        want = oracle.sync_avg(oplan, host, order, wl.dtype, wl.out_dtype)
+        t_cpu += time.perf_counter() - c0
+        reps += 1
+    same = got == want.view(np.int32 if f32_out else np.int16)
+    both_nan = np.isnan(got.view(np.float32)) & np.isnan(want) if f32_out else np.zeros_like(same)
+    parity = "bitwise equal to the CPU oracle" if bool((same | both_nan).all()) else \
+        f"MISMATCH in {int((~(same | both_nan)).sum())} elements"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    what = (f"the first {oplan.n_buckets} bucket(s), {span} of {c.P} elements, of the {wl.name} "
+            f"synchronisation; rate extrapolated to the whole" if sampled else
+            f"the full {wl.name} synchronisation")
+    cpu = {"value": round(sample_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "host_cpu": cpu_model, "host_threads": os.cpu_count(),
+           "sample": f"{what} ({order} order, N={N}), {reps} repetition(s), {t_cpu:.1f} s "
+                     f"single-threaded C oracle"}
+    if sampled:
+        parity = parity + " (on the sampled buckets)"
+    # context: a plain single-threaded host copy of 256 MiB (read + write bytes)
+    src_h = np.ones(1 << 26, dtype=np.float32)
+    dst_h = np.empty_like(src_h)
+    np.copyto(dst_h, src_h)
+    c0, n_cp = time.perf_counter(), 0
+    while n_cp == 0 or time.perf_counter() - c0 < 1.0:
+        np.copyto(dst_h, src_h)
+        n_cp += 1
+    cpu["host_copy_GBps"] = round(2 * src_h.nbytes * n_cp / (time.perf_counter() - c0) / 1e9, 2)
+    del src_h, dst_h
+    log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps; "
+        f"host copy {cpu['host_copy_GBps']} GB/s")
+
+    # The oracle on all of this process's host cores: SEQ order, every bucket
+    # split into disjoint element ranges, one ctypes call per range (the call
+    # releases the GIL).  SEQ has no index dependence, so the split leaves
+    # every bit as it is; its result is checked against the GPU's SEQ output
+    # of the same buffers.
+    threads = min(16, len(os.sched_getaffinity(0)))
+    pieces = []
+    for base, ln in zip(oplan.bucket_base, oplan.bucket_len):
+        step = max(1, -(-ln // threads))
+        pieces += [(base + a, min(step, ln - a)) for a in range(0, ln, step)]
+    seq_want = np.empty(span, dtype=np.float32 if f32_out else np.uint16)
+
+    def piece(pc):
+        a, n = pc
+        seq_want[a:a + n] = oracle.bucket_avg([h[a:a + n] for h in host], "seq",
+                                              wl.dtype, wl.out_dtype)
+
+    from concurrent.futures import ThreadPoolExecutor
+    reps_mt, t_mt = 0, 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        while reps_mt == 0 or t_mt < c.args.cpu_seconds / 2:
+            c0 = time.perf_counter()
+            list(ex.map(piece, pieces))
+            t_mt += time.perf_counter() - c0
+            reps_mt += 1
+    c.sync("seq")
+    torch.cuda.synchronize()
+    got_seq = c.out[:span].view(torch.int32 if f32_out else torch.int16).cpu().numpy()
+    ok = got_seq == seq_want.view(got_seq.dtype)
+    if f32_out:
+        ok |= np.isnan(got_seq.view(np.float32)) & np.isnan(seq_want)
+    cpu["all_cores"] = {
+        "value": round(sample_bytes * reps_mt / t_mt / 1e9, 3), "unit": "GB/s", "cores": threads,
+        "order": "seq", "parity_vs_gpu_seq": "bitwise equal" if bool(ok.all())
+        else f"MISMATCH in {int((~ok).sum())} elements",
+        "sample": f"{reps_mt} repetition(s) of {'the sample' if sampled else 'the full synchronisation'}"
+                  f", {len(pieces)} element ranges on {threads} threads, {t_mt:.1f} s"}
+    log(f"cpu oracle, {threads} threads (seq): {cpu['all_cores']['value']} GB/s; "
+        f"{cpu['all_cores']['parity_vs_gpu_seq']}")
+    return parity, cpu
+
+
+def rank_grads(c):
+    """Per-parameter gradient tensors of every rank holding the values of the
+    rank buffers, as autograd would leave them."""
+    grads = []
+    for r in range(c.N):
+        g = [c.torch.empty(n, dtype=c.tin, device=c.dev) for n in c.wl.numel]
+        c.ddp.unflatten(c.plan, c.ddp.bind_params(c.plan, g), c.flats[r], stream=c.stream)
+        grads.append(g)
+    return grads
+
+
+def leg_copy_path(c):
+    """The copy layout: flatten every rank, sync, unflatten (timed step by
+    step, as an eager loop and replayed from a HIP graph), and the same step
+    as one kernel over the per-parameter tensors."""
+    torch, ddp, plan, wl, N = c.torch, c.ddp, c.plan, c.wl, c.N
+    if c.args.no_copy_path or wl.two_bucket or N * c.P * wl.in_bytes > (16 << 30):
+        return None
+    grads = rank_grads(c)
+    binds = [ddp.bind_params(plan, g) for g in grads]
+    res = [torch.empty(n, dtype=c.tout, device=c.dev) for n in wl.numel]
+    rbind = ddp.bind_params(plan, res)
+
+    def full_step(st=c.stream):
+        for r in range(N):
+            ddp.flatten(plan, binds[r], c.flats[r], stream=st)
+        ddp.sync_allreduce_avg(plan, c.flats, c.out, c.order, stream=st)
+        ddp.unflatten(plan, rbind, c.out, stream=st)
+
+    for _ in range(5):
+        full_step()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = max(10, c.args.steps // 4)
+    tf = ts = tu = 0.0
+    for _ in range(reps):
+        e[0].record(c.stream)
+        for r in range(N):
+            ddp.flatten(plan, binds[r], c.flats[r], stream=c.stream)
+        e[1].record(c.stream)
+        c.sync()
+        e[2].record(c.stream)
+        ddp.unflatten(plan, rbind, c.out, stream=c.stream)
+        e[3].record(c.stream)
+        torch.cuda.synchronize()
+        tf += e[0].elapsed_time(e[1])
+        ts += e[1].elapsed_time(e[2])
+        tu += e[2].elapsed_time(e[3])
+    tf, ts, tu = tf / reps, ts / reps, tu / reps
+    out = {"ms_per_step": round(tf + ts + tu, 4),
+           "flatten_ms": round(tf, 4), "flatten_GBps": gbps(2 * N * c.P * wl.in_bytes, tf),
+           "sync_ms": round(ts, 4),
+           "unflatten_ms": round(tu, 4), "unflatten_GBps": gbps(2 * c.P * wl.out_bytes, tu),
+           "metric_GBps": gbps(c.sync_bytes, tf + ts + tu),
+           "launches": N + 2}
+    # the same step captured once into a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(c.stream)
+    with torch.cuda.stream(cap_stream):
+        with torch.cuda.graph(graph, stream=cap_stream):
+            full_step(cap_stream)
+    torch.cuda.synchronize()
+    out["eager_loop_ms_per_step"] = round(stream_ms(c, full_step, reps, settle=True), 4)
+    out["graph_replay_ms_per_step"] = round(stream_ms(c, graph.replay, reps, settle=True), 4)
+
+    # the same step as one kernel over the per-parameter tensors
+    ps = ddp.param_sync(plan, binds, rbind, c.order)
+    t_ps = stream_ms(c, lambda: ps(c.stream), reps, warm=5, settle=True)
+    chk = [torch.empty_like(t) for t in res]
+    ddp.unflatten(plan, ddp.bind_params(plan, chk), c.out, stream=c.stream)   # out holds this sync
+    torch.cuda.synchronize()
+    same = all(torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
+                           y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
+               for x, y in zip(res, chk))
+    out["param_sync"] = {
+        "ms_per_step": round(t_ps, 4), "GBps": gbps(c.sync_bytes, t_ps),
+        "speedup_vs_three_steps": round((tf + ts + tu) / t_ps, 2),
+        "same_bits_as_three_steps": bool(same),
+        "step": "every rank's per-parameter gradients averaged into per-parameter outputs "
+                "in one launch (ddp_param_sync_run)"}
+    log(f"copy path: {out}")
+    return out
+
+
+def leg_fused_sgd(c):
+    """The average folded into a momentum-SGD step (ddp_sync_sgd_update)
+    against the unfused sequence it replaces: the synchronisation, then the
+    optimizer reading the averaged gradient back (torch's in-place ops); and
+    the same step on per-parameter tensors."""
+    torch, ddp, plan, wl, N, P = c.torch, c.ddp, c.plan, c.wl, c.N, c.P
+    if c.args.no_fused_sgd or wl.out_dtype != "f32":
+        return None
+    params = torch.empty(P, dtype=torch.float32, device=c.dev)
+    c.W.device_normal_(params, 99, 7, 1.0)
+    mbuf = torch.zeros(P, dtype=torch.float32, device=c.dev)
+    lr, mu = 0.01, 0.9
+
+    def fused_step():
+        ddp.sync_sgd_update(plan, c.flats, params, lr, c.order, momentum_buf=mbuf, momentum=mu,
+                            stream=c.stream)
+
+    def unfused_step():
+        c.sync()
+        mbuf.mul_(mu).add_(c.out)
+        params.add_(mbuf, alpha=-lr)
+
+    t_f = stream_ms(c, fused_step, c.args.steps, warm=5)
+    t_u = stream_ms(c, unfused_step, c.args.steps, warm=5)
+    fb = N * P * wl.in_bytes + 4 * P * 4
+    res = {"ms": round(t_f, 5), "GBps": gbps(fb, t_f), "bytes": fb, "unfused_ms": round(t_u, 5),
+           "speedup_vs_unfused": round(t_u / t_f, 3),
+           "step": "momentum SGD (mu 0.9) on f32 parameters; unfused = sync + torch mul_/add_"}
+    # the same step on per-parameter tensors (gradients, parameters and
+    # momentum buffers as autograd and the optimizer keep them)
+    if N * P * wl.in_bytes <= (16 << 30):
+        gviews = rank_grads(c)
+        pp = [torch.empty(n, dtype=torch.float32, device=c.dev).normal_() for n in wl.numel]
+        pm = [torch.zeros(n, dtype=torch.float32, device=c.dev) for n in wl.numel]
+        step = ddp.param_sgd(plan, [ddp.bind_params(plan, g) for g in gviews],
+                             ddp.bind_params(plan, pp), ddp.bind_params(plan, pm), None, c.order)
+        t_p = stream_ms(c, lambda: step(lr, mu, c.stream), c.args.steps, warm=5)
+        res["per_parameter"] = {
+            "ms": round(t_p, 5), "GBps": gbps(fb, t_p),
+            "step": "the same step on per-parameter gradients, parameters and momentum "
+                    "(ddp_param_sgd_run)"}
+    log(f"fused sgd: {res}")
+    return res
+
+
+def leg_overlap(c):
+    """Syncs beside compute on a second stream.  First the two-bucket plan of
+    the same tensors: DEEP_COMM averaged on an update stream while a GEMM
+    (standing in for the first layer's backward) runs on a compute stream;
+    exposed = overlapped time - compute time.  Then DDP's bucket-by-bucket
+    schedule, flat and per-parameter.  Steps are timed back to back with both
+    streams joined at every step boundary."""
+    torch, ddp, plan, wl, P = c.torch, c.ddp, c.plan, c.wl, c.P
+    if c.args.no_overlap or wl.name != "resnet50":
+        return None
+    tb = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
+    (dl, db, _, _), (fl_, _, _, _) = tb.bucket(0), tb.bucket(1)
+    mat_a = torch.randn(4096, 4096, device=c.dev, dtype=torch.bfloat16)
+    mat_b = torch.randn(4096, 4096, device=c.dev, dtype=torch.bfloat16)
+    comp, upd, tried = side_by_side_streams(torch)
+    deep_in = [f[db:db + dl] for f in c.flats]
+    deep_out = c.out[db:db + dl]
+
+    def compute():
+        with torch.cuda.stream(comp):
+            torch.mm(mat_a, mat_b)
+
+    def deep():
+        ddp.bucket_allreduce_avg(deep_in, deep_out, c.order, stream=upd)
+
+    def step_barrier():
+        # a training step ends when both streams have: the next step's
+        # backward needs the averaged gradients, and the next syncs the next
+        # step's gradients
+        e_comp, e_upd = torch.cuda.Event(), torch.cuda.Event()
+        e_comp.record(comp)
+        e_upd.record(upd)
+        comp.wait_event(e_upd)
+        upd.wait_event(e_comp)
+
+    def timed(fns, reps=20):
+        for _ in range(3):
+            for f in fns:
+                f()
+            step_barrier()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for f in fns:
+                f()
+            step_barrier()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    def hidden(t_sync, t_alone, t_both):
+        return {"exposed_sync_ms": round(max(t_both - t_alone, 0.0), 4),
+                "hidden_fraction": round(1.0 - max(t_both - t_alone, 0.0) / t_sync, 3)}
+
+    t_comp = timed([compute])
+    res = {"plan": "two-bucket (DEEP_COMM %d, FIRST_COMM %d elements)" % (dl, fl_),
+           "compute_ms": round(t_comp, 4),
+           "compute": "bf16 GEMM 4096^3 on a second stream",
+           "streams": ("side by side (hardware queues checked; %d tried)" % tried
+                       if tried else "not found side by side: results are serial")}
+    # under both occupancy policies: the tuned cap reserves LDS that the
+    # GEMM's blocks would need, "shared" leaves it free
+    for policy in ("tuned", "shared"):
+        ddp.set_occupancy(policy)
+        t_deep = timed([deep])
+        t_both = timed([compute, deep])
+        res[policy] = {"deep_sync_ms": round(t_deep, 4), "overlapped_ms": round(t_both, 4),
+                       **hidden(t_deep, t_comp, t_both)}
+    ddp.set_occupancy("tuned")
+
+    # The bucket-by-bucket schedule of DDP ([DDP] 3.2, [TR24] 十一): bucket b
+    # (cap plan, last layers first) is averaged on the update stream as soon
+    # as a stand-in for the backward of its layers -- a bf16 GEMM with FLOPs
+    # in proportion to the bucket's share of the parameters, about 262 GFLOP
+    # in all (ResNet-50's backward at 32 images per GPU) -- has finished on
+    # the compute stream.
+    buckets = [plan.bucket(b) for b in range(plan.n_buckets)]
+    ks = [max(64, int(round(7808 * ln / P / 64)) * 64) for ln, _, _, _ in buckets]
+    lhs = [torch.randn(4096, k, device=c.dev, dtype=torch.bfloat16) for k in ks]
+    rhs = [torch.randn(k, 4096, device=c.dev, dtype=torch.bfloat16) for k in ks]
+    ready = [torch.cuda.Event() for _ in buckets]
+    ins = [[f[base:base + ln] for f in c.flats] for ln, base, _, _ in buckets]
+    outs_b = [c.out[base:base + ln] for ln, base, _, _ in buckets]
+
+    def backward():
+        with torch.cuda.stream(comp):
+            for a, b, e in zip(lhs, rhs, ready):
+                torch.mm(a, b)
+                e.record(comp)
+
+    def bucket_syncs(wait):
+        for b in range(len(buckets)):
+            if wait:
+                upd.wait_event(ready[b])
+            ddp.bucket_allreduce_avg(ins[b], outs_b[b], c.order, stream=upd)
+
+    # the same schedule on per-parameter gradients (as autograd leaves them):
+    # bucket b of one ddp_param_sync per step, run when ready
+    pg = rank_grads(c)
+    pout = [torch.empty(n, dtype=c.tout, device=c.dev) for n in wl.numel]
+    pps = ddp.param_sync(plan, [ddp.bind_params(plan, g) for g in pg],
+                         ddp.bind_params(plan, pout), c.order)
+
+    def param_syncs(wait):
+        for b in range(len(buckets)):
+            if wait:
+                upd.wait_event(ready[b])
+            pps(upd, buckets=(b, 1))
+
+    t_bwd = timed([backward])
+    gflop = sum(2 * 4096 * k * 4096 for k in ks) / 1e9
+    sched = {"buckets": len(buckets), "backward_gflop": round(gflop, 1),
+             "backward_ms": round(t_bwd, 4)}
+    per_param = {"sync": "ddp_param_sync_run_buckets, one bucket per launch"}
+    for syncs, into in ((bucket_syncs, sched), (param_syncs, per_param)):
+        for policy in ("tuned", "shared"):
+            ddp.set_occupancy(policy)
+            t_syncs = timed([lambda: syncs(False)])
+            t_sched = timed([backward, lambda: syncs(True)])
+            into[policy] = {"syncs_ms": round(t_syncs, 4), "serial_ms": round(t_bwd + t_syncs, 4),
+                            "overlapped_ms": round(t_sched, 4), **hidden(t_syncs, t_bwd, t_sched)}
+        ddp.set_occupancy("tuned")
+    sched["per_parameter"] = per_param
+    res["schedule"] = sched
+    log(f"overlap: {res}")
+    return res
+
+
+def leg_rank_sweep(c):
+    """The same plan averaged over N = 2..32 virtual ranks (N > 16 takes the
+    looped kernel): bandwidth against the number of concurrent streams."""
+    torch, wl = c.torch, c.wl
+    if c.args.no_rank_sweep or wl.name != "resnet50":
+        return None
+    pool = list(c.flats)
+    for r in range(c.N, 32):
+        t = torch.empty(c.P, dtype=c.tin, device=c.dev)
+        c.W.device_normal_(t, r, wl.stream, wl.sigma)
+        pool.append(t)
+    sweep_out = torch.empty(c.P, dtype=c.tout, device=c.dev)
+    res = {}
+    for n in (2, 4, 6, 8, 9, 12, 16, 32):
+        row = {}
+        for o in ("ring", "seq"):
+            call = c.ddp.make_sync(c.plan, pool[:n], sweep_out, o, stream=c.stream)
+            ms = stream_ms(c, call, 50)
+            row[o] = gbps((n * wl.in_bytes + wl.out_bytes) * c.P, ms)
+        res[str(n)] = row
+    log(f"rank sweep (GB/s): {res}")
+    return res
+
+
+def leg_in_place(c):
+    """The all-reduce as the pages run it, in place (send buffer == receive
+    buffer): the average overwrites rank 0's bucket buffer.  Runs after the
+    parity leg because it rewrites rank 0's gradients."""
+    res = {}
+    for o in (() if c.args.no_in_place else ("ring", "seq")):
+        call = c.ddp.make_sync(c.plan, c.flats, c.flats[0], o, stream=c.stream)
+        ms = stream_ms(c, call, c.args.steps)
+        res[o] = {"ms_per_sync": round(ms, 5), "GBps": gbps(c.sync_bytes, ms)}
+    log(f"in place: {res}")
+    return res or None
+
+
+def leg_no_sync(c):
+    """M micro-steps: with no_sync each rank accumulates locally (M - 1
+    accumulates) and synchronises once; without it every micro-step also
+    synchronises.  Separate buffers keep the benchmark's inputs untouched."""
+    ddp, wl, N, P = c.ddp, c.wl, c.N, c.P
+    if c.args.no_no_sync or 2 * N * P * wl.in_bytes > (16 << 30):
+        return None
+    M = 4
+    local = [f.clone() for f in c.flats]
+    micro = [f.clone() for f in c.flats]
+    t_acc = stream_ms(c, lambda: ddp.accumulate(local, micro, stream=c.stream), c.args.steps)
+    t_sync = stream_ms(c, lambda: ddp.sync_allreduce_avg(c.plan, local, c.out, c.order,
+                                                         stream=c.stream), c.args.steps)
+    res = {"micro_steps": M, "accumulate_ms": round(t_acc, 5),
+           "accumulate_GBps": gbps(3 * N * P * wl.in_bytes, t_acc),
+           "no_sync_ms": round((M - 1) * t_acc + t_sync, 5),
+           "sync_every_step_ms": round((M - 1) * t_acc + M * t_sync, 5),
+           "syncs_saved": M - 1}
+    log(f"no_sync: {res}")
+    return res
+
+
+def calibrate(torch):
+    """A plain 1 GiB device-to-device copy, 10 times: the kernel of known size
+    that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.calibrate:
+        calibrate(torch)
+        return
+
+    c = setup(args)
+    timed_steps(c)
+    per_bucket = leg_per_bucket(c)
+    cold = leg_cold_mall(c)
+    ceiling = leg_ceiling(c)
+    other = leg_other_orders(c)
+    parity, cpu = leg_parity_and_cpu(c)
+    copy_path = leg_copy_path(c)
+    fused = leg_fused_sgd(c)
+    overlap = leg_overlap(c)
+    rank_sweep = leg_rank_sweep(c)
+    in_place = leg_in_place(c)
+    no_sync = leg_no_sync(c)
+
+    wl, P, np = c.wl, c.P, c.np
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(c.value, 1),
         "unit": "GB/s",
-        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "pct_of_peak": round(100.0 * c.value / HBM_PEAK_GBPS, 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(c.ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {len(wl.params)} gradient tensors, "
-                               f"{P} elements, {N} virtual ranks, {plan.n_buckets} buckets",
-                   "virtual_ranks": N, "elements": P, "buckets": plan.n_buckets,
+                               f"{P} elements, {c.N} virtual ranks, {c.plan.n_buckets} buckets",
+                   "virtual_ranks": c.N, "elements": P, "buckets": c.plan.n_buckets,
                    "bucket_cap_bytes": wl.bucket_cap_bytes,
                    "plan": "two-bucket" if wl.two_bucket else "cap",
-                   "order": order, "grad_dtype": wl.dtype, "out_dtype": wl.out_dtype,
+                   "order": c.order, "grad_dtype": wl.dtype, "out_dtype": wl.out_dtype,
                    "grad_layout": "bucket view (gradients live in the per-rank flat buckets)",
-                   "bytes_per_sync": sync_bytes,
+                   "bytes_per_sync": c.sync_bytes,
                    "device": torch.cuda.get_device_name(0)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic,
+        "roofline": {"bound": "hbm", "achieved": round(c.achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(c.achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(wl.name, c.order, c.sync_bytes),
                      "kernel": "reduce_fast (one launch per sync)",
-                     "kernel_ms": round(kern_ms, 5),
+                     "kernel_ms": round(c.kern_ms, 5),
                      "kernel_ms_source": "event pair around the K timed launches, / K",
-                     "single_launch_ms_median": round(float(np.median(launch_ms)), 5),
-                     "single_launch_ms_min": round(min(launch_ms), 5)},
+                     "single_launch_ms_median": round(float(np.median(c.launch_ms)), 5),
+                     "single_launch_ms_min": round(min(c.launch_ms), 5)},
         "per_bucket": per_bucket,
         "cold_mall": cold,
         "ceiling": ceiling,
@@ -928,7 +911,7 @@ def main():
         "other_orders": other,
         "copy_path": copy_path,
         "fused_sgd": fused,
-        "in_place": in_place or None,
+        "in_place": in_place,
         "rank_sweep_GBps": rank_sweep,
         "overlap": overlap,
         "no_sync": no_sync,
