@@ -21,49 +21,31 @@ __device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, 
         *reinterpret_cast<uint16_t *>(dst + j) = *reinterpret_cast<const uint16_t *>(src + j);
 }
 
-// Block-wide copy of nbytes (a multiple of 2) between 2-byte aligned addresses.
+// Block-wide copy of nbytes (a multiple of 2) between 2-byte aligned
+// addresses: 16-byte non-temporal accesses from the destination's first
+// 16-byte boundary, a thread's two loads before its stores.  The loads run
+// at whatever alignment the source has there (gfx9 and later global loads
+// take any address), so a tensor whose flat offset is not a multiple of 16
+// bytes still moves in 16-byte vectors.  A head and tail of under 16 bytes
+// move 2 bytes per thread.
 __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
 {
     const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
-    const uintptr_t s = reinterpret_cast<uintptr_t>(src);
     const int tid = threadIdx.x;
-    if (((d ^ s) & 15) == 0) {
-        const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
-        copy16b(dst, src, 0, head);
-        const int64_t nvec = (nbytes - head) >> 4;
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(src + head);
-        u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
-        int64_t j = tid;
-        for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {   // both loads before the stores
-            const u32x4 a = __builtin_nontemporal_load(sv + j);
-            const u32x4 b = __builtin_nontemporal_load(sv + j + kCopyThreads);
-            __builtin_nontemporal_store(a, dv + j);
-            __builtin_nontemporal_store(b, dv + j + kCopyThreads);
-        }
-        for (; j < nvec; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sv + j), dv + j);
-        copy16b(dst, src, head + (nvec << 4), nbytes);
-    } else if (((d ^ s) & 3) == 0) {
-        const int64_t head = min<int64_t>((4 - (d & 3)) & 3, nbytes);
-        copy16b(dst, src, 0, head);
-        const int64_t nw = (nbytes - head) >> 2;
-        const uint32_t *sw = reinterpret_cast<const uint32_t *>(src + head);
-        uint32_t *dw = reinterpret_cast<uint32_t *>(dst + head);
-        int64_t j = tid;
-        for (; j + 3 * kCopyThreads < nw; j += 4 * kCopyThreads) {
-            const uint32_t a = __builtin_nontemporal_load(sw + j);
-            const uint32_t b = __builtin_nontemporal_load(sw + j + kCopyThreads);
-            const uint32_t c = __builtin_nontemporal_load(sw + j + 2 * kCopyThreads);
-            const uint32_t e = __builtin_nontemporal_load(sw + j + 3 * kCopyThreads);
-            __builtin_nontemporal_store(a, dw + j);
-            __builtin_nontemporal_store(b, dw + j + kCopyThreads);
-            __builtin_nontemporal_store(c, dw + j + 2 * kCopyThreads);
-            __builtin_nontemporal_store(e, dw + j + 3 * kCopyThreads);
-        }
-        for (; j < nw; j += kCopyThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(sw + j), dw + j);
-        copy16b(dst, src, head + (nw << 2), nbytes);
-    } else {
-        copy16b(dst, src, 0, nbytes);
+    const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
+    copy16b(dst, src, 0, head);
+    const int64_t nvec = (nbytes - head) >> 4;
+    const char *sv = src + head;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    int64_t j = tid;
+    for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {
+        const u32x4 a = ld_stream(sv + 16 * j);
+        const u32x4 b = ld_stream(sv + 16 * (j + kCopyThreads));
+        __builtin_nontemporal_store(a, dv + j);
+        __builtin_nontemporal_store(b, dv + j + kCopyThreads);
     }
+    for (; j < nvec; j += kCopyThreads) __builtin_nontemporal_store(ld_stream(sv + 16 * j), dv + j);
+    copy16b(dst, src, head + (nvec << 4), nbytes);
 }
 
 // kCopyBlocksPerUnit blocks per copy unit, each moving up to kCopyBlockElems
