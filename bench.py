@@ -28,6 +28,7 @@ with its --no-... flag):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload resnet50|gpt1p3b|gpt1p3b_two_bucket|many_small|llama7b|tiny]
                        [--order ring|seq] [--cpu-seconds S] [--no-<section> ...]
+       (the default order is ring, or the workload's only one: seq for tiny)
        python bench.py --calibrate   (the plain-copy run that scales the HBM counters)
 """
 import argparse
@@ -170,7 +171,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="resnet50")
-    ap.add_argument("--order", default="ring", choices=["ring", "seq"])
+    ap.add_argument("--order", default=None, choices=["ring", "seq"],
+                    help="summation order of the timed sync (default: ring, or the workload's only "
+                         "order: seq for tiny)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-path", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -200,7 +203,7 @@ def setup(args):
     c = types.SimpleNamespace(args=args, np=np, torch=torch, ddp=ddp, W=W)
     c.dev = torch.device("cuda:0")
     c.wl = wl = W.workload(args.workload)
-    c.order = args.order
+    c.order = args.order or ("ring" if "ring" in wl.orders else wl.orders[0])
     c.N = N = wl.n_ranks
     if wl.two_bucket:
         c.plan = ddp.plan_two_bucket(wl.numel, wl.regions, wl.dtype)
