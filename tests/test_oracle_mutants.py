@@ -160,13 +160,20 @@ def pin_sgd(o):
     return p.tolist() == [0.125, -2.6875, 0.75] and m.tolist() == [1.25, 1.125, 0.5]
 
 
+def pin_flatten(o):
+    sizes = [3, 5, 2, 4]
+    plan = o.plan_cap(sizes, 24, 4)
+    grads = [np.array([10 * p + j for j in range(n)], np.float32) for p, n in enumerate(sizes)]
+    return o.flatten(plan, grads).tolist() == [30, 31, 32, 33, 20, 21, 10, 11, 12, 13, 14, 0, 1, 2]
+
+
 def pin_accumulate(o):
     d = np.array([1.0, 2.5, -3.0], np.float32)
     o.accumulate(d, np.array([0.5, 0.5, 1.0], np.float32))
     return d.tolist() == [1.5, 3.0, -2.0]
 
 
-BATTERY = [pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
+BATTERY = [pin_flatten, pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
            pin_p9_scale, pin_p10_single, pin_bf16_path, pin_p7_plans]
 
 
@@ -213,6 +220,11 @@ PY_MUTANTS = {
                                 "first = [p for reg in FIRST_COMM_REGIONS[::-1] for p"),
     "simulator_no_accumulate": ("b[dst][lo:hi] = data + b[dst][lo:hi]", "b[dst][lo:hi] = data"),
     "allgather_wrong_chunk": ("c = (i + 1 - s0 - t) % N", "c = (i - s0 - t) % N"),
+    "flatten_in_registration_order": (
+        "flat = np.empty(plan.total, dtype=grads[0].dtype)\n"
+        "    for b, base in zip(plan.buckets, plan.bucket_base):\n        off = base\n        for p in b:",
+        "flat = np.empty(plan.total, dtype=grads[0].dtype)\n"
+        "    for b, base in zip(plan.buckets, plan.bucket_base):\n        off = base\n        for p in sorted(b):"),
 }
 
 

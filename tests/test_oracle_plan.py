@@ -146,3 +146,21 @@ def test_flatten_unflatten_round_trip_bits():
     back = oracle.unflatten(plan, flat)
     for a, b in zip(back, grads):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_hand_worked_flatten_across_buckets():
+    """Sizes [3, 5, 2, 4], cap 24 bytes of f32 (6 elements): walking from the
+    last parameter, p3 + p2 fill bucket 0 exactly, p1 would overflow it and
+    opens bucket 1, p0 would overflow that and opens bucket 2.  Every element
+    of the flat buffer is written out by hand (value 10*p + j)."""
+    sizes = [3, 5, 2, 4]
+    plan = oracle.plan_cap(sizes, 24, 4)
+    assert plan.buckets == [[3, 2], [1], [0]]
+    assert plan.bucket_base == [0, 6, 11]
+    grads = [np.array([10 * p + j for j in range(n)], dtype=np.float32) for p, n in enumerate(sizes)]
+    flat = oracle.flatten(plan, grads)
+    assert flat.tolist() == [30, 31, 32, 33, 20, 21,
+                             10, 11, 12, 13, 14,
+                             0, 1, 2]
+    back = oracle.unflatten(plan, np.arange(14, dtype=np.float32))
+    assert [b.tolist() for b in back] == [[11, 12, 13], [6, 7, 8, 9, 10], [4, 5], [0, 1, 2, 3]]
