@@ -160,6 +160,16 @@ def pin_sgd(o):
     return p.tolist() == [0.125, -2.6875, 0.75] and m.tolist() == [1.25, 1.125, 0.5]
 
 
+def pin_sampled(o):
+    rng = np.random.default_rng(4)
+    x = [rng.standard_normal(50).astype(np.float32) for _ in range(3)]
+    whole = o.bucket_avg(x, "ring")
+    pos = np.array([0, 16, 17, 33, 34, 49])
+    vals = np.stack([np.array([x[r][i] for r in range(3)]) for i in pos])
+    got = o.sampled_avg(vals, pos, np.full(pos.size, 50), "ring")
+    return np.array_equal(got.view(np.uint32), whole[pos].view(np.uint32))
+
+
 def pin_flatten(o):
     sizes = [3, 5, 2, 4]
     plan = o.plan_cap(sizes, 24, 4)
@@ -173,7 +183,7 @@ def pin_accumulate(o):
     return d.tolist() == [1.5, 3.0, -2.0]
 
 
-BATTERY = [pin_flatten, pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
+BATTERY = [pin_sampled, pin_flatten, pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
            pin_p9_scale, pin_p10_single, pin_bf16_path, pin_p7_plans]
 
 
@@ -208,6 +218,8 @@ C_MUTANTS = {
                           "    if (N == -1) {\n        if (in_dtype != out_dtype) return -1;\n        memcpy"),
     "accumulate_subtracts": ("store_elem(dst, dtype, i, a + b);", "store_elem(dst, dtype, i, a - b);"),
     "sgd_sign_flipped": ("p[i] = p[i] - step;", "p[i] = p[i] + step;"),
+    "sampled_rows_rank_major": ("v[r] = load_elem(vals, in_dtype, s * N + r);",
+                                "v[r] = load_elem(vals, in_dtype, r * S + s);"),
     "sgd_momentum_terms_swapped": ("float v = mu * m[i];\n            v = v + gi;",
                                    "float v = mu * gi;\n            v = v + m[i];"),
 }

@@ -218,3 +218,31 @@ def test_bf16_exact_identity_on_dyadic_inputs():
             exact = Fraction(sum(int(i[j]) for i in ints), N)
             # exact mean rounded once to bf16 (8 significant bits), ties to even
             assert abs(Fraction(float(got[j])) - exact) <= abs(exact) * Fraction(1, 256)
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+@pytest.mark.parametrize("order", ["seq", "ring"])
+def test_sampled_elements_equal_the_whole_bucket_average(pair, order):
+    """sampled_avg (single elements given by value, position and bucket
+    length, as the full-size GPU tests sample them) equals the pinned
+    bucket_avg at those positions, across buckets of several lengths."""
+    in_dt, out_dt = pair
+    rng = np.random.default_rng(7)
+    for N in (1, 2, 3, 5, 8):
+        if N == 1 and in_dt != out_dt:
+            continue
+        lens = [1, 7, 64, 1001]
+        bufs = []
+        for L in lens:
+            x = [rng.standard_normal(L).astype(np.float32) for _ in range(N)]
+            if in_dt == "bf16":
+                x = [oracle.rne_bf16(v) for v in x]
+            bufs.append(x)
+        whole = [oracle.bucket_avg(x, order, in_dt, out_dt) for x in bufs]
+        pick = [(b, int(i)) for b, L in enumerate(lens) for i in rng.integers(0, L, 5)]
+        vals = np.stack([np.array([bufs[b][r][i] for r in range(N)]) for b, i in pick])
+        got = oracle.sampled_avg(vals, np.array([i for _, i in pick]),
+                                 np.array([lens[b] for b, _ in pick]), order, in_dt, out_dt)
+        want = np.array([whole[b][i] for b, i in pick], dtype=got.dtype)
+        assert np.array_equal(got.view(np.uint16 if out_dt == "bf16" else np.uint32),
+                              want.view(np.uint16 if out_dt == "bf16" else np.uint32)), (N, order)
