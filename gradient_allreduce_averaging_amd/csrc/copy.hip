@@ -48,24 +48,27 @@ __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
     copy16b(dst, src, head + (nvec << 4), nbytes);
 }
 
-// kCopyBlocksPerUnit blocks per copy unit, each moving up to kCopyBlockElems
-// elements of it (parts past a short unit's end return at once); to_flat
-// selects flatten (param -> flat) or unflatten (flat -> param).  The blocks
-// of one unit run on one XCD (workgroups are dealt to the XCDs round-robin,
-// so block b runs on XCD b % 8), where the unit's table entry is then an L2
-// hit for all but the first of them.  Units hold 4K elements: with many
-// short parameters, bigger units mostly spawn blocks that find no work.
+// BPU blocks per copy unit (copy_blocks_per_unit: 8 KiB a block), each
+// moving its share of the unit (parts past a short unit's end return at
+// once); to_flat selects flatten (param -> flat) or unflatten (flat ->
+// param).  The blocks of one unit run on one XCD (workgroups are dealt to
+// the XCDs round-robin, so block b runs on XCD b % 8), where the unit's
+// table entry is then an L2 hit for all but the first of them.  Units hold
+// 4K elements: with many short parameters, bigger units mostly spawn blocks
+// that find no work.
+template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 copy_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, char *flat, int esize,
            int to_flat)
 {
+    constexpr int64_t kBlockElems = kCopyUnitElems / BPU;
     const int64_t m = blockIdx.x / kXcds;
-    const int64_t ui = (m / kCopyBlocksPerUnit) * kXcds + blockIdx.x % kXcds;
+    const int64_t ui = (m / BPU) * kXcds + blockIdx.x % kXcds;
     if (ui >= n_units) return;
     const ddp_copy_unit u = units[first + ui];
-    const int64_t lo = (m % kCopyBlocksPerUnit) * kCopyBlockElems;
+    const int64_t lo = (m % BPU) * kBlockElems;
     if (lo >= u.count) return;
-    const int64_t n = min(u.count - lo, kCopyBlockElems);
+    const int64_t n = min(u.count - lo, kBlockElems);
     char *pp = reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize;
     char *fp = flat + (u.flat_elem + lo) * esize;
     const int64_t nbytes = n * esize;
@@ -170,17 +173,21 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     if (last <= first) return DDP_OK;
     // Every XCD gets the same number of units (the last round padded).  A
     // launch takes at most max_launch_items() work-items: a multiple of 4096,
-    // so of the kXcds * kCopyBlocksPerUnit blocks that one round of units
-    // spans.
-    const int64_t per = max_launch_items() / (kCopyThreads * kCopyBlocksPerUnit);
+    // so of the kXcds * bpu blocks that one round of units spans.
+    const int esize = dtype_size(dtype), bpu = copy_blocks_per_unit(esize);
+    const int64_t per = max_launch_items() / (kCopyThreads * bpu);
     for (int64_t u0 = first; u0 < last; u0 += per) {
         const int64_t n = std::min(per, last - u0);
-        const int64_t blocks = (n + kXcds - 1) / kXcds * kXcds * kCopyBlocksPerUnit;
-        copy_units<<<dim3((unsigned)blocks), dim3(kCopyThreads), lds_for_blocks(kCopyBlocksPerCU),
-                     static_cast<hipStream_t>(stream)>>>(bd->units, u0, n, static_cast<char *>(flat),
-                                                          dtype_size(dtype), to_flat);
-        const ddp_status_t st = launched("copy kernel launch");
-        if (st != DDP_OK) return st;
+        const dim3 g((unsigned)((n + kXcds - 1) / kXcds * kXcds * bpu)), b(kCopyThreads);
+        const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
+        char *fl = static_cast<char *>(flat);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        if (bpu == 1)
+            copy_units<1><<<g, b, lds, st>>>(bd->units, u0, n, fl, esize, to_flat);
+        else
+            copy_units<2><<<g, b, lds, st>>>(bd->units, u0, n, fl, esize, to_flat);
+        const ddp_status_t s = launched("copy kernel launch");
+        if (s != DDP_OK) return s;
     }
     return DDP_OK;
 }

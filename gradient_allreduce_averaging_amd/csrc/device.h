@@ -53,9 +53,14 @@ static_assert(kThreads * kUnroll * 8 <= 1023 && DDP_MAX_RANKS <= 64,
 
 constexpr int kCopyThreads = 256;      // flatten / unflatten blocks
 constexpr int64_t kCopyUnitElems = 4096;    // elements per copy-table entry
-constexpr int64_t kCopyBlockElems = 2048;   // elements per copy block: a unit gets
-constexpr int kCopyBlocksPerUnit = (int)(kCopyUnitElems / kCopyBlockElems);   // this many blocks
-static_assert(kCopyUnitElems % kCopyBlockElems == 0, "a copy unit splits into whole blocks");
+constexpr int64_t kCopyBlockBytes = 8192;   // bytes per copy block: an f32 unit gets two
+                                            // blocks, a bf16 unit one
+__host__ __device__ constexpr int copy_blocks_per_unit(int esize)
+{
+    return (int)(kCopyUnitElems * esize / kCopyBlockBytes);
+}
+static_assert(copy_blocks_per_unit(2) == 1 && copy_blocks_per_unit(4) == 2,
+              "a copy unit splits into whole blocks");
 
 constexpr int kF32 = 0;
 
