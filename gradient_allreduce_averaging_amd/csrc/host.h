@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "ddp.h"
 #include "device.h"
@@ -58,6 +59,25 @@ ddp_status_t launch_split(int64_t blocks, int threads, const char *what, Launch 
         if (st != DDP_OK) return st;
     }
     return DDP_OK;
+}
+
+// Calls f(std::integral_constant<int, K>()) for the K in [Lo, Hi] equal to
+// n, so that a kernel templated on the rank count can be launched for a
+// count known only at run time; false when n is outside [Lo, Hi].
+template <int Lo, int Hi, class F>
+bool with_rank_count(int n, F &&f)
+{
+    if constexpr (Lo > Hi) {
+        (void)n;
+        (void)f;
+        return false;
+    } else {
+        if (n == Lo) {
+            f(std::integral_constant<int, Lo>());
+            return true;
+        }
+        return with_rank_count<Lo + 1, Hi>(n, f);
+    }
 }
 
 // Resident blocks per CU each kernel family is capped at (0: no cap), and

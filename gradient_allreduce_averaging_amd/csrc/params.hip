@@ -362,17 +362,10 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream
                         [&](int64_t i, unsigned n) {
         const dim3 g(n);
         const int64_t b0 = tr.first + i;
-        switch (N) {
-        case 1: params_fast<1, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 2: params_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 3: params_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 4: params_fast<4, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 5: params_fast<5, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 6: params_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 7: params_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        case 8: params_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv); break;
-        default: params_many<RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, N, b0, inv); break;
-        }
+        const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
+            params_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv);
+        });
+        if (!fixed) params_many<RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, N, b0, inv);
     });
 }
 
@@ -390,17 +383,11 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, TileRange tr, float lr, 
                         [&](int64_t i, unsigned n) {
         const dim3 g(n);
         const int64_t b0 = tr.first + i;
-        switch (N) {
-        case 1: params_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 2: params_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 3: params_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 4: params_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 5: params_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 6: params_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 7: params_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        case 8: params_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv, lr, mu); break;
-        default: params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, N, b0, inv, lr, mu); break;
-        }
+        const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
+            params_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv,
+                                                                                       lr, mu);
+        });
+        if (!fixed) params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, N, b0, inv, lr, mu);
     });
 }
 

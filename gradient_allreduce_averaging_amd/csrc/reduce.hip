@@ -230,24 +230,11 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
         return launch_split(tiles, kThreads, "reduce kernel launch", [&](int64_t b0, unsigned n) {
             lb.first_block = b0;
             const dim3 g(n);
-            switch (N) {
-            case 2: reduce_fast<2, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 3: reduce_fast<3, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 4: reduce_fast<4, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 5: reduce_fast<5, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 6: reduce_fast<6, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 7: reduce_fast<7, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 8: reduce_fast<8, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 9: reduce_fast<9, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 10: reduce_fast<10, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 11: reduce_fast<11, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 12: reduce_fast<12, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 13: reduce_fast<13, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 14: reduce_fast<14, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 15: reduce_fast<15, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            case 16: reduce_fast<16, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv, out); break;
-            default: reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, lb, inv, out); break;
-            }
+            const bool fixed = with_rank_count<2, 16>(N, [&](auto nr) {
+                reduce_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(ra, total, lb, inv,
+                                                                                  out);
+            });
+            if (!fixed) reduce_many<RING, IN, OUT><<<g, b, lds, st>>>(ra, N, total, lb, inv, out);
         });
     }
     return launch_split((total + kThreads - 1) / kThreads, kThreads, "reduce kernel launch",
@@ -333,17 +320,12 @@ ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Bu
         return launch_split(tiles, kThreads, what, [&](int64_t b0, unsigned n) {
             lb.first_block = b0;
             const dim3 g(n);
-            switch (N) {
-            case 1: reduce_sgd_fast<1, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 2: reduce_sgd_fast<2, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 3: reduce_sgd_fast<3, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 4: reduce_sgd_fast<4, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 5: reduce_sgd_fast<5, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 6: reduce_sgd_fast<6, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 7: reduce_sgd_fast<7, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            case 8: reduce_sgd_fast<8, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total, lb, inv, sa); break;
-            default: reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, lb, inv, sa); break;
-            }
+            const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
+                reduce_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(
+                    ra, total, lb, inv, sa);
+            });
+            if (!fixed)
+                reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, lb, inv, sa);
         });
     }
     return launch_split((total + kThreads - 1) / kThreads, kThreads, what,
