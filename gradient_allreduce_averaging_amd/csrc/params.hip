@@ -157,6 +157,33 @@ __device__ __forceinline__ PsEntry<NA> ps_entry(const char *e)
     return t;
 }
 
+// Tiles ahead of a block whose table entry it fetches into L2 (a multiple
+// of 8, so the later block runs on the same XCD: blocks are dealt to the
+// XCDs round-robin).
+constexpr int64_t kPsPrefetch = 1024;
+
+// From eight ranks up, each block fetches the two ends of entry tile +
+// kPsPrefetch (an entry may span two 128-byte lines; lanes 0 and 1 load
+// them), so that block's scalar entry loads find it in L2 rather than HBM.
+// The value is unused; consume() keeps it live until a point where the wave
+// waits for its data loads anyway, so that the load has completed before its
+// register is reused.
+template <int NR>
+__device__ __forceinline__ uint32_t prefetch_entry(const char *table, int64_t stride, int64_t tile,
+                                                   int64_t n_entries)
+{
+    if constexpr (NR >= 8) {
+        if (tile + kPsPrefetch < n_entries) {
+            const char *f = table + (tile + kPsPrefetch) * stride +
+                            ((threadIdx.x & 1) ? stride - 4 : 0);
+            return ld_elem<uint32_t>(reinterpret_cast<uint64_t>(f), 0);
+        }
+    }
+    return 0;
+}
+
+__device__ __forceinline__ void consume(uint32_t x) { asm volatile("" ::"v"(x)); }
+
 // Sync, N known at compile time (1..8).  After the entry, all NR *
 // kPsUnroll vector loads of the lane go out before the ring chunks are
 // looked at, as in the flat reduce.  A lane's vector past the tile's end
@@ -165,11 +192,14 @@ __device__ __forceinline__ PsEntry<NA> ps_entry(const char *e)
 // are not behind a branch).
 template <int NR, bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
-params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, float inv)
+params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, int64_t n_entries,
+            float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    const char *e = table + (first_block + blockIdx.x) * stride;
+    const int64_t tile = first_block + blockIdx.x;
+    const char *e = table + tile * stride;
+    const uint32_t pf = prefetch_entry<NR>(table, stride, tile, n_entries);
     const PsEntry<NR + kSyncExtra> t = ps_entry<NR + kSyncExtra>(e);
     const PsMeta &m = t.m;
     const int64_t cnt = m.count;
@@ -198,11 +228,14 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
                     fold_seq<NR, IN>(v[u], acc);
                 else
                     fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
+                consume(pf);
                 store_vec<IN, OUT>(t.ad[NR], i0[u], acc, inv);
             }
-        } else if (i0[u] < cnt) {
-            params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(e), NR, m, inv, i0[u],
-                                        VEC);
+        } else {
+            consume(pf);
+            if (i0[u] < cnt)
+                params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(e), NR, m, inv,
+                                            i0[u], VEC);
         }
     }
 }
@@ -245,13 +278,15 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
 // elements) moves two.
 template <int NR, bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
-params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, float inv,
-                float lr, float mu)
+params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
+                int64_t n_entries, float inv, float lr, float mu)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
-    const char *e = table + (first_block + blockIdx.x) * stride;
+    const int64_t tile = first_block + blockIdx.x;
+    const char *e = table + tile * stride;
+    const uint32_t pf = prefetch_entry<NR>(table, stride, tile, n_entries);
     const PsEntry<NR + kSgdExtra> t = ps_entry<NR + kSgdExtra>(e);
     const PsMeta &m = t.m;
     const uint64_t gout = t.ad[NR], param = t.ad[NR + 1], mom = t.ad[NR + 2];
@@ -288,10 +323,13 @@ params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_bl
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
             }
+            consume(pf);
             sgd_vec<IN, OUT, MOM>(gout, param, mom, i0[u], y, pv[u], mv[u], lr, mu);
-        } else if (i0[u] < cnt) {
-            params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(e), NR, m, inv,
-                                                 lr, mu, i0[u], VEC);
+        } else {
+            consume(pf);
+            if (i0[u] < cnt)
+                params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(e), NR, m,
+                                                     inv, lr, mu, i0[u], VEC);
         }
     }
 }
@@ -363,7 +401,8 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream
         const dim3 g(n);
         const int64_t b0 = tr.first + i;
         const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
-            params_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0, inv);
+            params_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0,
+                                                                            ps->n_tiles, inv);
         });
         if (!fixed) params_many<RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, N, b0, inv);
     });
@@ -384,8 +423,8 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, TileRange tr, float lr, 
         const dim3 g(n);
         const int64_t b0 = tr.first + i;
         const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
-            params_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, b0, inv,
-                                                                                       lr, mu);
+            params_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(
+                tb, sd, b0, ps->n_tiles, inv, lr, mu);
         });
         if (!fixed) params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, N, b0, inv, lr, mu);
     });
