@@ -75,12 +75,12 @@ int sgd_blocks_per_cu(int N, bool mom)
 // The per-parameter sync (params.hip): the reduce's pattern behind one
 // table entry per block, whose scalar-load latency more resident blocks
 // hide.  Measured at N = 4 (many-small: 16) and N = 8 (ResNet-50 and
-// GPT-1.3B in f32: 10; Llama-7B in bf16: 12); other N take the cap of the
-// flat kernel of the same shape (unrolled up to 8, looped above) plus two.
-int params_blocks_per_cu(int N, bool ring, bool bf16)
+// GPT-1.3B in f32, Llama-7B in bf16: 10); other N take the cap of the flat
+// kernel of the same shape (unrolled up to 8, looped above) plus two.
+int params_blocks_per_cu(int N, bool ring)
 {
     if (N == 4) return 16;
-    if (N == 8) return bf16 ? 12 : 10;
+    if (N == 8) return 10;
     if (N > 8) return N <= 11 ? (ring ? 14 : 12) : 10;   // the looped kernel's caps + 2
     const int k = reduce_blocks_per_cu(N, ring);
     return k > 0 ? std::min(k + 2, 16) : 0;

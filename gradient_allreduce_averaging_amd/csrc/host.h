@@ -84,7 +84,7 @@ bool with_rank_count(int n, F &&f)
 // the dynamic-LDS request that imposes a cap of k (see common.hip).
 int reduce_blocks_per_cu(int N, bool ring);
 int sgd_blocks_per_cu(int N, bool mom);
-int params_blocks_per_cu(int N, bool ring, bool bf16);
+int params_blocks_per_cu(int N, bool ring);
 int params_sgd_blocks_per_cu(int N, bool mom);
 constexpr int kCopyBlocksPerCU = 7;   // flatten / unflatten (256-thread blocks)
 unsigned lds_for_blocks(int k);

@@ -394,7 +394,7 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream
     const float inv = 1.0f / (float)N;
     const char *tb = ps->table;
     const int64_t sd = ps->stride;
-    const unsigned lds = lds_for_blocks(params_blocks_per_cu(N, RING, IN == kBF16));
+    const unsigned lds = lds_for_blocks(params_blocks_per_cu(N, RING));
     const dim3 b(kThreads);
     return launch_split(tr.count, kThreads, "parameter sync kernel launch",
                         [&](int64_t i, unsigned n) {
