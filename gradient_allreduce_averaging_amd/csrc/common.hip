@@ -86,12 +86,14 @@ int params_blocks_per_cu(int N, bool ring)
     return k > 0 ? std::min(k + 2, 16) : 0;
 }
 
-// The per-parameter fused SGD step: the flat step's caps, except N = 4 with
-// momentum (many-small: 10 gave 6.50 TB/s against 6.33 at the flat step's 8;
-// at N = 8, ResNet-50, 6 and 7 were within 0.3 %).
+// The per-parameter fused SGD step: the flat step's caps, except with
+// momentum at N = 4 (many-small: 10 gave 6.50 TB/s against 6.33 at the flat
+// step's 8) and N = 8 (ResNet-50: 7 gave 6.36 against 6.31 at 6, GPT-1.3B
+// level; fresh processes, two rounds).
 int params_sgd_blocks_per_cu(int N, bool mom)
 {
     if (N == 4 && mom) return 10;
+    if (N == 8 && mom) return 7;
     return sgd_blocks_per_cu(N, mom);
 }
 
