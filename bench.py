@@ -29,6 +29,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload resnet50|gpt1p3b|gpt1p3b_two_bucket|many_small|llama7b|tiny]
                        [--order ring|seq] [--cpu-seconds S] [--no-<section> ...]
        (the default order is ring, or the workload's only one: seq for tiny)
+       python bench.py --layout per-parameter [...]   (the one-kernel sync over per-parameter
+                                                        tensors as the timed step)
        python bench.py --calibrate   (the plain-copy run that scales the HBM counters)
 """
 import argparse
@@ -184,6 +186,11 @@ def parse_args():
     ap.add_argument("--no-rank-sweep", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-per-bucket", action="store_true")
+    ap.add_argument("--layout", default="bucket-view", choices=["bucket-view", "per-parameter"],
+                    help="bucket-view: the timed step reads the per-rank flat buckets "
+                         "(ddp_sync_allreduce_avg); per-parameter: it reads every rank's "
+                         "per-parameter tensors in one kernel (ddp_param_sync_run), and only the "
+                         "timed step, the flushed-MALL leg, the other order and parity run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -214,15 +221,18 @@ def setup(args):
     c.tout = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
     log(f"workload {wl.name}: N={N} P={P} buckets={c.plan.n_buckets} order={c.order} "
         f"{wl.dtype}->{wl.out_dtype}")
+    c.plan.prepare()
+    c.stream = torch.cuda.current_stream()
+    c.sync_bytes = wl.sync_bytes()
+    if args.layout == "per-parameter":
+        setup_per_parameter(c)
+        return c
     c.flats = []
     for r in range(N):
         t = torch.empty(P, dtype=c.tin, device=c.dev)
         W.device_normal_(t, r, wl.stream, wl.sigma)
         c.flats.append(t)
     c.out = torch.empty(P, dtype=c.tout, device=c.dev)
-    c.plan.prepare()
-    c.stream = torch.cuda.current_stream()
-    c.sync_bytes = wl.sync_bytes()
     prepared = {o: ddp.make_sync(c.plan, c.flats, c.out, o, stream=c.stream) for o in ("seq", "ring")}
 
     def sync(o=c.order):
@@ -230,6 +240,52 @@ def setup(args):
 
     c.sync = sync
     return c
+
+
+def setup_per_parameter(c):
+    """Per-parameter gradient tensors of every rank, as autograd leaves them
+    (the same distribution, seeded per rank and tensor), per-parameter
+    outputs, and the one-kernel sync (ddp_param_sync_run).  Nothing large is
+    allocated and freed before the timed steps."""
+    torch, ddp, plan, wl = c.torch, c.ddp, c.plan, c.wl
+    c.grads = []
+    for r in range(c.N):
+        g = [torch.empty(n, dtype=c.tin, device=c.dev) for n in wl.numel]
+        for p, t in enumerate(g):
+            c.W.device_normal_(t, r * 100_003 + p, wl.stream, wl.sigma)
+        c.grads.append(g)
+    c.pout = [torch.empty(n, dtype=c.tout, device=c.dev) for n in wl.numel]
+    binds = [ddp.bind_params(plan, g) for g in c.grads]
+    obind = ddp.bind_params(plan, c.pout)
+    prepared = {o: ddp.param_sync(plan, binds, obind, o) for o in ("seq", "ring")}
+
+    def sync(o=c.order):
+        prepared[o](c.stream)
+
+    c.sync = sync
+
+
+def leg_parity_per_parameter(c):
+    """Per-parameter layout: the timed outputs against the flat sync of the
+    same values (flatten every rank, ddp_sync_allreduce_avg, unflatten), bit
+    for bit, where the flat copies fit beside the tensors (inputs up to
+    16 GB); the GPU tests check the rest against the oracle on samples."""
+    torch, ddp, plan, wl = c.torch, c.ddp, c.plan, c.wl
+    if c.N * c.P * wl.in_bytes > (16 << 30):
+        return "not checked here (inputs above 16 GB); the GPU tests compare sampled elements"
+    c.sync()
+    flats = [torch.empty(c.P, dtype=c.tin, device=c.dev) for _ in range(c.N)]
+    for g, f in zip(c.grads, flats):
+        ddp.flatten(plan, ddp.bind_params(plan, g), f, stream=c.stream)
+    out = torch.empty(c.P, dtype=c.tout, device=c.dev)
+    ddp.sync_allreduce_avg(plan, flats, out, c.order, stream=c.stream)
+    want = [torch.empty_like(t) for t in c.pout]
+    ddp.unflatten(plan, ddp.bind_params(plan, want), out, stream=c.stream)
+    torch.cuda.synchronize()
+    bits = torch.int16 if c.tout == torch.bfloat16 else torch.int32
+    same = all(torch.equal(x.view(bits), y.view(bits)) for x, y in zip(c.pout, want))
+    return ("bitwise equal to flatten + sync + unflatten of the same values" if same
+            else "MISMATCH against flatten + sync + unflatten")
 
 
 def timed_steps(c):
@@ -862,17 +918,22 @@ def main():
 
     c = setup(args)
     timed_steps(c)
-    per_bucket = leg_per_bucket(c)
+    per_param = args.layout == "per-parameter"
+    per_bucket = None if per_param else leg_per_bucket(c)
     cold = leg_cold_mall(c)
-    ceiling = leg_ceiling(c)
+    ceiling = None if per_param else leg_ceiling(c)
     other = leg_other_orders(c)
-    parity, cpu = leg_parity_and_cpu(c)
-    copy_path = leg_copy_path(c)
-    fused = leg_fused_sgd(c)
-    overlap = leg_overlap(c)
-    rank_sweep = leg_rank_sweep(c)
-    in_place = leg_in_place(c)
-    no_sync = leg_no_sync(c)
+    if per_param:
+        parity, cpu = leg_parity_per_parameter(c), None
+        copy_path = fused = overlap = rank_sweep = in_place = no_sync = None
+    else:
+        parity, cpu = leg_parity_and_cpu(c)
+        copy_path = leg_copy_path(c)
+        fused = leg_fused_sgd(c)
+        overlap = leg_overlap(c)
+        rank_sweep = leg_rank_sweep(c)
+        in_place = leg_in_place(c)
+        no_sync = leg_no_sync(c)
 
     wl, P, np = c.wl, c.P, c.np
     line = {
@@ -895,13 +956,17 @@ def main():
                    "bucket_cap_bytes": wl.bucket_cap_bytes,
                    "plan": "two-bucket" if wl.two_bucket else "cap",
                    "order": c.order, "grad_dtype": wl.dtype, "out_dtype": wl.out_dtype,
-                   "grad_layout": "bucket view (gradients live in the per-rank flat buckets)",
+                   "grad_layout": ("per-parameter tensors of every rank, read where they lie by one "
+                                   "kernel (ddp_param_sync_run)" if per_param else
+                                   "bucket view (gradients live in the per-rank flat buckets)"),
                    "bytes_per_sync": c.sync_bytes,
                    "device": torch.cuda.get_device_name(0)},
         "roofline": {"bound": "hbm", "achieved": round(c.achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(c.achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(wl.name, c.order, c.sync_bytes),
-                     "kernel": "reduce_fast (one launch per sync)",
+                     "traffic": None if per_param else measured_traffic(wl.name, c.order,
+                                                                        c.sync_bytes),
+                     "kernel": ("params_fast" if per_param else "reduce_fast") +
+                               " (one launch per sync)",
                      "kernel_ms": round(c.kern_ms, 5),
                      "kernel_ms_source": "event pair around the K timed launches, / K",
                      "single_launch_ms_median": round(float(np.median(c.launch_ms)), 5),
