@@ -11,6 +11,9 @@ the step; the same run also times the copy layout (flatten every rank, sync,
 unflatten) and reports it under "copy_path".
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
+The process idles --settle-seconds (20) before its first GPU call: buffers
+allocated within about 20 s of another process releasing tens of GB of
+device memory were measured to stream 4-5 % slower for as long as they live.
 Besides the metric and its roofline, the line carries (each can be skipped
 with its --no-... flag):
   other_orders   the other summation order
@@ -118,6 +121,26 @@ def side_by_side_streams(torch, tries=32):
     return first, second, None
 
 
+def hwmon_readings(torch):
+    """Junction and memory (HBM) temperature in degrees C and board power in
+    W of device 0, from its hwmon node in sysfs (empty when unreadable)."""
+    import glob
+    try:
+        p = torch.cuda.get_device_properties(0)
+        base = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                f"{p.pci_device_id:02x}.0/hwmon/hwmon*")
+        out = {}
+        for d in glob.glob(base):
+            for f in glob.glob(d + "/temp*_label"):
+                label = open(f).read().strip()
+                out[f"{label}_C"] = int(open(f.replace("_label", "_input")).read()) / 1000
+            if os.path.exists(d + "/power1_input"):
+                out["power_W"] = int(open(d + "/power1_input").read()) / 1e6
+        return out
+    except (OSError, AttributeError, ValueError):
+        return {}
+
+
 def run_environment(torch):
     """ROCm release, HIP runtime and the device's peak clocks, for the record."""
     env = {"hip_runtime": torch.version.hip, "torch": torch.__version__,
@@ -191,6 +214,10 @@ def parse_args():
                          "(ddp_sync_allreduce_avg); per-parameter: it reads every rank's "
                          "per-parameter tensors in one kernel (ddp_param_sync_run), and only the "
                          "timed step, the flushed-MALL leg, the other order and parity run")
+    ap.add_argument("--settle-seconds", type=float, default=20.0,
+                    help="idle pause before the first GPU call: buffers allocated within about 20 s "
+                         "of another process releasing tens of GB of device memory stream 4-5 %% "
+                         "slower for as long as they live (0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
@@ -909,6 +936,9 @@ def main():
               "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
         sys.exit(2)
 
+    if args.settle_seconds > 0 and not args.calibrate:
+        log(f"idle {args.settle_seconds:.0f} s before the first GPU call")
+        time.sleep(args.settle_seconds)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -917,7 +947,9 @@ def main():
         return
 
     c = setup(args)
+    sensors_before = hwmon_readings(torch)
     timed_steps(c)
+    sensors_after = hwmon_readings(torch)
     per_param = args.layout == "per-parameter"
     per_bucket = None if per_param else leg_per_bucket(c)
     cold = leg_cold_mall(c)
@@ -983,7 +1015,9 @@ def main():
         "rank_sweep_GBps": rank_sweep,
         "overlap": overlap,
         "no_sync": no_sync,
-        "env": run_environment(torch),
+        "env": dict(run_environment(torch),
+                    sensors={"before_timed_steps": sensors_before,
+                             "after_timed_steps": sensors_after}),
     }
     print(json.dumps(line), flush=True)
 
