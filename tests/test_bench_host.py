@@ -56,3 +56,15 @@ def test_traffic_is_reported_only_for_the_hashed_code(tmp_path):
     rec["resnet50/ring"]["kernel_source_sha"] = "0" * 16
     f.write_text(json.dumps(rec))
     assert b.measured_traffic("resnet50", "ring", 1) is None
+
+
+def test_parser_defaults_and_layouts(monkeypatch):
+    b = _bench()
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = b.parse_args()
+    assert (a.gpus, a.steps, a.warmup, a.workload, a.layout) == (1, 200, 20, "resnet50", "bucket-view")
+    assert a.order is None and a.settle_seconds == 20.0
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--layout", "per-parameter", "--settle-seconds", "0",
+                                      "--workload", "tiny", "--order", "seq"])
+    a = b.parse_args()
+    assert (a.layout, a.settle_seconds, a.workload, a.order) == ("per-parameter", 0.0, "tiny", "seq")
