@@ -129,13 +129,16 @@ def hwmon_readings(torch):
         p = torch.cuda.get_device_properties(0)
         base = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
                 f"{p.pci_device_id:02x}.0/hwmon/hwmon*")
+        def read(path):
+            with open(path) as fh:
+                return fh.read().strip()
+
         out = {}
         for d in glob.glob(base):
             for f in glob.glob(d + "/temp*_label"):
-                label = open(f).read().strip()
-                out[f"{label}_C"] = int(open(f.replace("_label", "_input")).read()) / 1000
+                out[f"{read(f)}_C"] = int(read(f.replace("_label", "_input"))) / 1000
             if os.path.exists(d + "/power1_input"):
-                out["power_W"] = int(open(d + "/power1_input").read()) / 1e6
+                out["power_W"] = int(read(d + "/power1_input")) / 1e6
         return out
     except (OSError, AttributeError, ValueError):
         return {}
