@@ -83,6 +83,11 @@ def load_core(path: str):
     lib.oracle_bucket_avg.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_void_p]
+    lib.oracle_bucket_range_avg.restype = ctypes.c_int
+    lib.oracle_bucket_range_avg.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p]
     lib.oracle_sampled_avg.restype = ctypes.c_int
     lib.oracle_sampled_avg.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -200,6 +205,30 @@ def bucket_avg(xs: Sequence[np.ndarray], order: str, in_dtype: str = "f32",
     rc = _core().oracle_bucket_avg(_ptrs(xs), len(xs), L, _ORDER_CODE[order],
                                    _DTYPE_CODE[in_dtype], _DTYPE_CODE[out_dtype],
                                    out.ctypes.data)
+    if rc:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def bucket_range_avg(xs: Sequence[np.ndarray], bucket_len: int, lo: int, order: str,
+                     in_dtype: str = "f32", out_dtype: str = None,
+                     out: np.ndarray = None) -> np.ndarray:
+    """Elements [lo, lo + n) of one bucket's average, n = xs[r].size: xs[r]
+    holds rank r's elements lo..lo+n-1 of a bucket of bucket_len elements.
+    Each element is folded as by bucket_avg at its position in the whole
+    bucket.  The C call releases the GIL, so pieces can run on threads."""
+    out_dtype = out_dtype or in_dtype
+    xs = [np.ascontiguousarray(x, dtype=_NP_DTYPE[in_dtype]) for x in xs]
+    n = xs[0].size
+    if any(x.size != n for x in xs):
+        raise ValueError("rank pieces differ in length")
+    if out is None:
+        out = np.empty(n, dtype=_NP_DTYPE[out_dtype])
+    elif out.dtype != _NP_DTYPE[out_dtype] or out.size != n or not out.flags.c_contiguous:
+        raise ValueError("out does not match the piece")
+    rc = _core().oracle_bucket_range_avg(_ptrs(xs), len(xs), bucket_len, lo, n,
+                                         _ORDER_CODE[order], _DTYPE_CODE[in_dtype],
+                                         _DTYPE_CODE[out_dtype], out.ctypes.data)
     if rc:
         raise ValueError("oracle rejected the arguments")
     return out

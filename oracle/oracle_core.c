@@ -140,6 +140,32 @@ int oracle_bucket_avg(const void *const *x, int N, int64_t len, int order,
     return 0;
 }
 
+/* Average the piece [lo, lo + n) of a bucket of length len, for checking a
+ * bucket too large to hold on the host in one piece.  x[r] points at rank
+ * r's element lo (n elements of in_dtype); out receives n elements of
+ * out_dtype.  Every element is folded exactly as in oracle_bucket_avg, with
+ * its position lo + k in the whole bucket choosing its ring start, so the
+ * pieces of a bucket together give oracle_bucket_avg's result. */
+int oracle_bucket_range_avg(const void *const *x, int N, int64_t len, int64_t lo, int64_t n,
+                            int order, int in_dtype, int out_dtype, void *out)
+{
+    if (check_args(N, order, in_dtype, out_dtype)) return -1;
+    if (len < 0 || lo < 0 || n < 0 || lo > len || n > len - lo) return -1;
+    if (N == 1) {   /* the input, bit for bit */
+        if (in_dtype != out_dtype) return -1;
+        memcpy(out, x[0], (size_t)n * (in_dtype == ORACLE_BF16 ? 2u : 4u));
+        return 0;
+    }
+    const float scale = 1.0f / (float)N;
+    float v[1024];
+    for (int64_t k = 0; k < n; ++k) {
+        for (int r = 0; r < N; ++r) v[r] = load_elem(x[r], in_dtype, k);
+        float acc = fold(v, N, order, lo + k, len);
+        store_elem(out, out_dtype, k, acc * scale);
+    }
+    return 0;
+}
+
 /* Average S sampled elements.  vals holds S rows of N input values (row s is
  * the N ranks' values of one element), pos[s] is that element's position in
  * its bucket and len[s] the bucket's length. */

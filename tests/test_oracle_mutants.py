@@ -6,7 +6,8 @@ Mistakes planted in the C core: ring start rank off by one, ring walked
 backwards, floor instead of ceil chunking, a rank dropped from the sum, the
 scale by 1/(N-1), a -0 start for the sequential sum, round-half-up instead of
 ties-to-even, the NaN quiet bit lost, a wrong bf16 widening, the N == 1
-identity replaced by the fold.  In the Python layer: forward instead of
+identity replaced by the fold, a bucket piece folded as if it began
+the bucket.  In the Python layer: forward instead of
 reverse packing, closing a bucket when it is exactly full, FIRST_COMM regions
 in the wrong order, the simulator forgetting to accumulate, the all-gather
 forwarding the wrong chunk.
@@ -170,6 +171,15 @@ def pin_sampled(o):
     return np.array_equal(got.view(np.uint32), whole[pos].view(np.uint32))
 
 
+def pin_bucket_pieces(o):
+    rng = np.random.default_rng(5)
+    x = [rng.standard_normal(50).astype(np.float32) for _ in range(3)]
+    whole = o.bucket_avg(x, "ring")
+    got = np.concatenate([o.bucket_range_avg([v[a:b] for v in x], 50, a, "ring")
+                          for a, b in ((0, 10), (10, 30), (30, 50))])
+    return np.array_equal(got.view(np.uint32), whole.view(np.uint32))
+
+
 def pin_flatten(o):
     sizes = [3, 5, 2, 4]
     plan = o.plan_cap(sizes, 24, 4)
@@ -183,7 +193,7 @@ def pin_accumulate(o):
     return d.tolist() == [1.5, 3.0, -2.0]
 
 
-BATTERY = [pin_sampled, pin_flatten, pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
+BATTERY = [pin_sampled, pin_bucket_pieces, pin_flatten, pin_accumulate, pin_sgd, pin_p1_tables, pin_p2_zero_start, pin_p3_identity, pin_p5_simulator, pin_p8_rne,
            pin_p9_scale, pin_p10_single, pin_bf16_path, pin_p7_plans]
 
 
@@ -220,6 +230,8 @@ C_MUTANTS = {
     "sgd_sign_flipped": ("p[i] = p[i] - step;", "p[i] = p[i] + step;"),
     "sampled_rows_rank_major": ("v[r] = load_elem(vals, in_dtype, s * N + r);",
                                 "v[r] = load_elem(vals, in_dtype, r * S + s);"),
+    "piece_positions_from_zero": ("float acc = fold(v, N, order, lo + k, len);",
+                                  "float acc = fold(v, N, order, k, len);"),
     "sgd_momentum_terms_swapped": ("float v = mu * m[i];\n            v = v + gi;",
                                    "float v = mu * gi;\n            v = v + m[i];"),
 }

@@ -246,3 +246,40 @@ def test_sampled_elements_equal_the_whole_bucket_average(pair, order):
         want = np.array([whole[b][i] for b, i in pick], dtype=got.dtype)
         assert np.array_equal(got.view(np.uint16 if out_dt == "bf16" else np.uint32),
                               want.view(np.uint16 if out_dt == "bf16" else np.uint32)), (N, order)
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+@pytest.mark.parametrize("order", ["seq", "ring"])
+def test_bucket_pieces_equal_the_whole_bucket_average(pair, order):
+    """bucket_range_avg (a bucket checked piece by piece, as the full-size
+    GPU tests stream it) equals the pinned bucket_avg on every piece, for
+    pieces that start and end inside ring chunks, on chunk edges, empty
+    pieces and the whole bucket; the pieces of a cut concatenate to it."""
+    in_dt, out_dt = pair
+    view = np.uint16 if out_dt == "bf16" else np.uint32
+    rng = np.random.default_rng(11)
+    for N in (1, 2, 3, 5, 8, 9):
+        if N == 1 and in_dt != out_dt:
+            continue
+        for L in (1, 7, 64, 1001):
+            x = [rng.standard_normal(L).astype(np.float32) for _ in range(N)]
+            if in_dt == "bf16":
+                x = [oracle.rne_bf16(v) for v in x]
+            whole = oracle.bucket_avg(x, order, in_dt, out_dt)
+            cuts = sorted({0, L, *(int(c) for c in rng.integers(0, L + 1, 4)),
+                           min(L, -(-L // N)), min(L, 2 * -(-L // N))})
+            pieces = [oracle.bucket_range_avg([v[a:b] for v in x], L, a, order, in_dt, out_dt)
+                      for a, b in zip(cuts[:-1], cuts[1:])]
+            assert np.array_equal(np.concatenate(pieces).view(view), whole.view(view)), (N, L)
+            for _ in range(6):
+                a = int(rng.integers(0, L + 1))
+                b = int(rng.integers(a, L + 1))
+                got = oracle.bucket_range_avg([v[a:b] for v in x], L, a, order, in_dt, out_dt)
+                assert np.array_equal(got.view(view), whole[a:b].view(view)), (N, L, a, b)
+
+
+def test_bucket_piece_rejects_a_range_outside_the_bucket():
+    x = [np.zeros(5, np.float32)] * 2
+    for lo, L in ((-1, 10), (6, 10), (3, 7)):
+        with pytest.raises(ValueError):
+            oracle.bucket_range_avg(x, L, lo, "ring")
