@@ -29,7 +29,14 @@
 // precomputed word naming the chunk segment holding its first element and
 // the segment after it (start ranks and in-tile ends); a lane whose vector
 // lies wholly inside either folds from registers in that segment's rotated
-// order, and a vector straddling a chunk or bucket boundary (at most a few
+// order.  Every other vector -- one straddling a chunk or bucket boundary,
+// or one lying past the second segment (a tile meeting three or more
+// chunks, which needs a chunk shorter than a tile: a bucket of fewer than
+// about N tiles) -- takes the
+// per-element path (reduce_elems): each of its elements finds its own bucket
+// and start rank (ring_start) and is folded on its own.  Either way each
+// element gets the same additions in the same order, so the result is the
+// same bits whichever path a vector takes.
 #pragma once
 
 #include <hip/hip_runtime.h>
