@@ -40,20 +40,26 @@ def _build_probe(verbose: bool) -> str:
     return PROBE_LIB
 
 
+def _compile(src: str, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
+    # hidden visibility: only the DDP_API declarations of ddp.h are exported
+    cmd = [HIPCC] + COMMON + ["-fvisibility=hidden", "-c", path, "-o", obj]
+    if src.endswith(".hip"):
+        cmd[1:1] = ["-x", "hip"] + DEVICE
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libddp.so (and libddp_probe.so) next to this file."""
-    objs = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(CSRC, src.rsplit(".", 1)[0] + ".o")
-        # hidden visibility: only the DDP_API declarations of ddp.h are exported
-        cmd = [HIPCC] + COMMON + ["-fvisibility=hidden", "-c", path, "-o", obj]
-        if src.endswith(".hip"):
-            cmd[1:1] = ["-x", "hip"] + DEVICE
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-        objs.append(obj)
+    """Compile every source (in parallel, one hipcc per source) and link
+    libddp.so (and libddp_probe.so) next to this file."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, verbose), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:

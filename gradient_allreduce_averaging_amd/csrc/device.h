@@ -107,6 +107,67 @@ __host__ __device__ inline Buckets single_bucket(int64_t lo, int64_t hi)
 // Workgroups are dealt to the XCDs round-robin, so tile t runs on XCD t % 8.
 constexpr int kXcds = 8;
 
+// Tables of a plan's RING synchronisation, computed by the same code on the
+// host (the tables a plan uploads once) and on the device (the tables
+// ddp_sync_allreduce_avg_noalloc rebuilds in its static buffer).
+//
+// The bucket holding flat element i, 0 <= i < base[nb]: the smallest b with
+// base[b + 1] > i, so empty buckets (base[b] == base[b + 1]) are skipped.
+__host__ __device__ inline int32_t bucket_holding(const int64_t *base, int32_t nb, int64_t i)
+{
+    int32_t lo = 0, hi = nb - 1;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo) / 2;
+        if (base[mid + 1] > i)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+__host__ __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Ring-segment word of tile t (tiles of `tile` elements over a flat layout of
+// nb buckets, n_ranks >= 2), as tile_segs decodes it.  Segments are the
+// non-empty ring chunks of every bucket in flat order: chunk c of a bucket
+// of length L is [c*C, min((c+1)*C, L)) with C = ceil(L/N), started by rank
+// (c+1) mod N.  Segment a holds the tile's first element; segment b is the
+// next one when a ends inside the tile (the next chunk of the bucket, or
+// chunk 0 of the next non-empty bucket).  Ends are relative to the tile.
+__host__ __device__ inline uint32_t ring_tile_word(const int64_t *base, int32_t nb, int64_t tile,
+                                                   int n_ranks, int64_t t)
+{
+    const int64_t total = base[nb];
+    const int64_t t0 = t * tile, t1 = min64(t0 + tile, total);
+    const int32_t b = bucket_holding(base, nb, t0);
+    const int64_t bb = base[b], be = base[b + 1];
+    const int64_t C = (be - bb + n_ranks - 1) / n_ranks;
+    const int64_t c = (t0 - bb) / C;
+    const int64_t a_hi = min64(bb + (c + 1) * C, be);
+    const uint32_t sa = (uint32_t)((c + 1) % n_ranks);
+    const uint32_t cut_a = (uint32_t)(min64(a_hi, t1) - t0);
+    uint32_t sb = 0, cut_b = cut_a;
+    if (a_hi < t1) {
+        int64_t b_hi;
+        if (a_hi < be) {   // the bucket's next chunk
+            b_hi = min64(a_hi + C, be);
+            sb = (uint32_t)((c + 2) % n_ranks);
+        } else {           // chunk 0 of the next non-empty bucket
+            const int32_t b2 = bucket_holding(base, nb, a_hi);
+            const int64_t C2 = (base[b2 + 1] - base[b2] + n_ranks - 1) / n_ranks;
+            b_hi = min64(base[b2] + C2, base[b2 + 1]);
+            sb = (uint32_t)(1 % n_ranks);
+        }
+        cut_b = (uint32_t)(min64(b_hi, t1) - t0);
+    }
+    return sa | sb << 6 | cut_a << 12 | cut_b << 22;
+}
+
+// Tiles per XCD stripe of the word table: tile t's word sits at
+// (t % kXcds) * stride + t / kXcds.
+__host__ __device__ inline int64_t word_stride(int64_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds; }
+
 // The chunk segments a tile may meet on the vector path.
 struct Segs {
     int64_t a_lo, a_hi, b_lo, b_hi;

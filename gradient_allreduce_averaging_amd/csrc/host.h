@@ -80,6 +80,16 @@ bool with_rank_count(int n, F &&f)
     }
 }
 
+// reduce.hip: the validation every reduce entry point shares (the output
+// may be null only when out_optional is set), the N == 1 copy, and the
+// reduce launch over the buckets bk (vec_ok: every written buffer on a
+// 16-byte boundary).
+ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int order, int in,
+                          int out_dt, const void *out, bool out_optional = false);
+ddp_status_t copy_single(const void *in, int64_t len, int esize, void *out, hipStream_t st);
+ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
+                           const Buckets &bk, void *out, hipStream_t st, bool vec_ok);
+
 // Resident blocks per CU each kernel family is capped at (0: no cap), and
 // the dynamic-LDS request that imposes a cap of k (see common.hip).
 int reduce_blocks_per_cu(int N, bool ring);

@@ -245,6 +245,10 @@ ddp_status_t launch_typed(const RankArgs &ra, int N, int64_t total, const Bucket
                         });
 }
 
+}  // namespace
+
+namespace ddp_detail {
+
 ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
                            const Buckets &bk, void *out, hipStream_t st, bool vec_ok)
 {
@@ -259,6 +263,10 @@ ddp_status_t launch_reduce(const RankArgs &ra, int N, int64_t total, int order, 
     return ring ? launch_typed<true, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok)
                 : launch_typed<false, kF32, kBF16>(ra, N, total, bk, inv, out, st, vec_ok);
 }
+
+}  // namespace ddp_detail
+
+namespace {
 
 // One bucket of len elements.  The vector kernel streams best from 128-byte
 // aligned tiles (an L2 line: a misaligned 1 KiB wave load touches 9 lines
@@ -360,10 +368,14 @@ ddp_status_t launch_sgd(const RankArgs &ra, int N, int64_t total, int order, int
                : launch_sgd_pair<false, false>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok);
 }
 
+}  // namespace
+
+namespace ddp_detail {
+
 // Common validation of a reduce call.  Returns OK or an error code.  The
 // output may be null only when out_optional is set.
 ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int order, int in,
-                          int out_dt, const void *out, bool out_optional = false)
+                          int out_dt, const void *out, bool out_optional)
 {
     if (n < 1 || len < 0) return DDP_ERR_INVALID_ARG;
     if (order != DDP_ORDER_SEQUENTIAL && order != DDP_ORDER_RING) return DDP_ERR_INVALID_ARG;
@@ -393,6 +405,10 @@ ddp_status_t copy_single(const void *in, int64_t len, int esize, void *out, hipS
     return e == hipSuccess ? DDP_OK : hip_fail("hipMemcpyAsync (N == 1)", e);
 }
 
+}  // namespace ddp_detail
+
+namespace {
+
 // Device tables of `plan` for tiles of `tile` elements on the current device.
 ddp_status_t plan_tables(ddp_plan *plan, int64_t tile, const ddp_dev_tables **out)
 {
@@ -417,12 +433,8 @@ ddp_status_t plan_tables(ddp_plan *plan, int64_t tile, const ddp_dev_tables **ou
     } catch (...) {
         return DDP_ERR_NOMEM;
     }
-    int32_t b = 0;
-    for (int64_t k = 0; k < entries; ++k) {
-        const int64_t first = k * stride;
-        while (plan->bucket_base[b + 1] <= first) ++b;   // skips empty buckets
-        tb[k] = b;
-    }
+    for (int64_t k = 0; k < entries; ++k)
+        tb[k] = bucket_holding(plan->bucket_base.data(), nb, k * stride);
     const size_t base_bytes = sizeof(int64_t) * (size_t)(nb + 1);
     const size_t tb_bytes = sizeof(int32_t) * tb.size();
     if ((e = hipMalloc(&t.bucket_base, base_bytes)) != hipSuccess)
@@ -443,17 +455,10 @@ ddp_status_t plan_tables(ddp_plan *plan, int64_t tile, const ddp_dev_tables **ou
     return DDP_OK;
 }
 
-// Ring segments of every tile of a plan for n_ranks ranks, the word tile_segs
-// reads: start ranks of the segment holding the tile's first element and of
-// the next one, and where each ends inside the tile.  Segments are the
-// non-empty ring chunks of every bucket in flat order (chunk c of a bucket of
-// length L is [c*C, min((c+1)*C, L)) with C = ceil(L/N), started by rank
-// (c+1) mod N).  The words are striped by XCD -- tile t at
-// (t % 8) * stride + t / 8 -- so that each XCD's L2 fetches only lines of
-// its own tiles.  Built on the host and uploaded once per device, tile size
-// and rank count.
-int64_t desc_stride(int64_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds; }
-
+// Ring segments of every tile of a plan for n_ranks ranks: one word per tile
+// (ring_tile_word), striped by XCD -- tile t at (t % 8) * stride + t / 8 --
+// so that each XCD's L2 fetches only lines of its own tiles.  Built on the
+// host and uploaded once per device, tile size and rank count.
 ddp_status_t ring_tile_desc(ddp_plan *plan, int64_t tile, int n_ranks, const uint32_t **out)
 {
     int dev = -1;
@@ -466,39 +471,18 @@ ddp_status_t ring_tile_desc(ddp_plan *plan, int64_t tile, int n_ranks, const uin
         *out = it->second;
         return DDP_OK;
     }
-    struct Seg {
-        int64_t lo, hi;
-        uint32_t start;
-    };
-    const int64_t total = plan->total, n_tiles = (total + tile - 1) / tile;
-    std::vector<Seg> segs;
+    const int64_t n_tiles = (plan->total + tile - 1) / tile;
+    const int64_t stride = word_stride(n_tiles);
     std::vector<uint32_t> w;
     try {
-        for (int32_t b = 0; b < plan->n_buckets(); ++b) {
-            const int64_t base = plan->bucket_base[b], end = plan->bucket_base[b + 1];
-            const int64_t C = (end - base + n_ranks - 1) / n_ranks;
-            for (int c = 0; c < n_ranks && base + c * C < end; ++c)
-                segs.push_back({base + c * C, std::min(base + (c + 1) * C, end),
-                                (uint32_t)((c + 1) % n_ranks)});
-        }
-        w.assign((size_t)std::max<int64_t>(kXcds * desc_stride(n_tiles), 1), 0u);
+        w.assign((size_t)std::max<int64_t>(kXcds * stride, 1), 0u);
     } catch (...) {
         return DDP_ERR_NOMEM;
     }
-    // the segments cover [0, total) in order, so one forward pass finds them
-    size_t j = 0;
-    for (int64_t t = 0; t < n_tiles; ++t) {
-        const int64_t t0 = t * tile, t1 = std::min(t0 + tile, total);
-        while (segs[j].hi <= t0) ++j;
-        const uint32_t cut_a = (uint32_t)(std::min(segs[j].hi, t1) - t0);
-        uint32_t cut_b = cut_a, sb = 0;
-        if (segs[j].hi < t1) {
-            cut_b = (uint32_t)(std::min(segs[j + 1].hi, t1) - t0);
-            sb = segs[j + 1].start;
-        }
-        w[(size_t)((t % kXcds) * desc_stride(n_tiles) + t / kXcds)] =
-            segs[j].start | sb << 6 | cut_a << 12 | cut_b << 22;
-    }
+    const int64_t *base = plan->bucket_base.data();
+    const int32_t nb = plan->n_buckets();
+    for (int64_t t = 0; t < n_tiles; ++t)
+        w[(size_t)((t % kXcds) * stride + t / kXcds)] = ring_tile_word(base, nb, tile, n_ranks, t);
     uint32_t *d = nullptr;
     const size_t bytes = sizeof(uint32_t) * w.size();
     if ((e = hipMalloc(&d, bytes)) != hipSuccess)
@@ -520,7 +504,7 @@ ddp_status_t ring_buckets(ddp_plan *plan, int in, int n_ranks, Buckets *bk)
     if (st != DDP_OK) return st;
     const uint32_t *desc = nullptr;
     if ((st = ring_tile_desc(plan, tile_elems(in), n_ranks, &desc)) != DDP_OK) return st;
-    *bk = {t->bucket_base, t->tile_bucket, desc, desc_stride(t->n_tiles), 0, plan->total,
+    *bk = {t->bucket_base, t->tile_bucket, desc, word_stride(t->n_tiles), 0, plan->total,
            plan->n_buckets(), 0};
     return DDP_OK;
 }
