@@ -31,7 +31,7 @@ _DTYPES = {"f32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16, F32: F32,
 REGION_BN_BIAS, REGION_BN_WEIGHT, REGION_FC_BIAS, REGION_FC_WEIGHT, REGION_FIRST, REGION_DEEP = range(6)
 
 STATUS = {0: "DDP_OK", 1: "DDP_ERR_INVALID_ARG", 2: "DDP_ERR_UNSUPPORTED", 3: "DDP_ERR_OVERFLOW",
-          4: "DDP_ERR_ALIAS", 5: "DDP_ERR_HIP", 6: "DDP_ERR_NOMEM"}
+          4: "DDP_ERR_ALIAS", 5: "DDP_ERR_HIP", 6: "DDP_ERR_NOMEM", 7: "DDP_ERR_CAPACITY"}
 
 
 class DDPError(RuntimeError):
@@ -90,6 +90,8 @@ def _load():
                                      ctypes.c_int),
         "ddp_sync_allreduce_avg": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_int, vp, vp], ctypes.c_int),
+        "ddp_sync_allreduce_avg_noalloc": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int,
+                                            ctypes.c_int, vp, vp], ctypes.c_int),
         "ddp_sync_sgd_update": ([vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                  vp, vp, vp, ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
         "ddp_param_sync_create": ([vp, ctypes.POINTER(vp), ctypes.c_int32, vp, ctypes.c_int,
@@ -426,6 +428,25 @@ def sync_allreduce_avg(plan: Plan, rank_flats: Sequence, out_flat, order="ring",
     _check(lib.ddp_sync_allreduce_avg(plan.handle, ptrs, len(rank_flats), _ORDERS[order],
                                       _dtype_code(out_flat), _dev_ptr(out_flat),
                                       _stream_handle(stream)), "ddp_sync_allreduce_avg")
+
+
+def sync_allreduce_avg_noalloc(plan: Plan, rank_flats: Sequence, out_flat, order="ring",
+                               stream=None):
+    """sync_allreduce_avg that allocates no device memory: the plan's tables
+    are rebuilt on every call in the library's static device buffer
+    (``ddp_sync_allreduce_avg_noalloc``; calls that overlap on one device race
+    on it)."""
+    total = plan.total
+    for t in rank_flats:
+        if _dtype_code(t) != plan.dtype or t.numel() < total:
+            raise ValueError("rank flat buffers differ from the plan's dtype or size")
+    if out_flat.numel() < total:
+        raise ValueError("output too short")
+    ptrs = _ptr_array([_dev_ptr(t) for t in rank_flats])
+    _check(lib.ddp_sync_allreduce_avg_noalloc(plan.handle, ptrs, len(rank_flats), _ORDERS[order],
+                                              _dtype_code(out_flat), _dev_ptr(out_flat),
+                                              _stream_handle(stream)),
+           "ddp_sync_allreduce_avg_noalloc")
 
 
 class _PreparedSync:

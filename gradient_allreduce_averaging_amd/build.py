@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libddp.so")
-SOURCES = ["plan.cpp", "common.hip", "reduce.hip", "accumulate.hip", "copy.hip", "params.hip"]
+SOURCES = ["plan.cpp", "common.hip", "reduce.hip", "accumulate.hip", "copy.hip", "params.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

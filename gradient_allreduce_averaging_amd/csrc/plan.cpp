@@ -205,6 +205,7 @@ const char *ddp_status_string(ddp_status_t status)
     case DDP_ERR_ALIAS: return "output partially overlaps an input";
     case DDP_ERR_HIP: return "HIP runtime error";
     case DDP_ERR_NOMEM: return "out of memory";
+    case DDP_ERR_CAPACITY: return "exceeds the static buffer of the no-allocation entry point";
     }
     return "unknown status";
 }

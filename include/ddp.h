@@ -72,7 +72,9 @@ typedef enum {
     DDP_ERR_OVERFLOW = 3,      /* a size that does not fit the int64 layout */
     DDP_ERR_ALIAS = 4,         /* output overlaps an input other than exactly */
     DDP_ERR_HIP = 5,           /* a HIP runtime call failed */
-    DDP_ERR_NOMEM = 6          /* host or device allocation failed */
+    DDP_ERR_NOMEM = 6,         /* host or device allocation failed */
+    DDP_ERR_CAPACITY = 7       /* beyond a fixed capacity (the no-allocation
+                                  entry point's static buffer) */
 } ddp_status_t;
 
 typedef enum { DDP_F32 = 0, DDP_BF16 = 1 } ddp_dtype_t;
@@ -385,6 +387,36 @@ DDP_API void ddp_param_sync_free(ddp_param_sync_t *sync);
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, ALIAS, HIP. */
 DDP_API ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
                             ddp_dtype_t dtype, void *stream);
+
+/* ------------------------------------------------------------ no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * ddp_sync_allreduce_avg with the same arguments and the same result, bit
+ * for bit, that never allocates device memory and calls no allocating HIP
+ * routine.  Where ddp_sync_allreduce_avg reads the plan's device tables
+ * (RING order with out_flat on a 16-byte boundary), this call rebuilds them
+ * on `stream`, before the reduce, in a static device buffer of
+ * DDP_NOALLOC_SCRATCH_BYTES that each device holds from its first such call
+ * until the process ends: the bucket bases ((n_buckets + 1) * 8 bytes), a
+ * bucket index per 64 tiles and a 4-byte ring word per tile (tiles of 256
+ * f32 or 512 bf16 elements), each part rounded up to 256 bytes.  That fits
+ * about 16 M tiles: 4.2 G f32 or 8.4 G bf16 elements.  Every other case is
+ * ddp_sync_allreduce_avg's own path, which allocates nothing there.
+ *
+ * Every call on a device shares that device's buffer and leaves its
+ * contents behind; calls that overlap on one device (on different streams
+ * without an ordering between them) race on it and may give wrong results.
+ * Calls on one stream, or ordered by events, are safe.
+ * Errors: as ddp_sync_allreduce_avg, plus DDP_ERR_CAPACITY when the plan's
+ * tables exceed the buffer (nothing is enqueued), DDP_ERR_UNSUPPORTED for a
+ * device index of 64 or more. */
+#define DDP_NOALLOC_SCRATCH_BYTES (64ll << 20)
+DDP_API ddp_status_t ddp_sync_allreduce_avg_noalloc(ddp_plan_t *plan,
+                                                    const void *const *rank_flat,
+                                                    int32_t n_ranks, ddp_order_t order,
+                                                    ddp_dtype_t out_dtype, void *out_flat,
+                                                    void *stream);
 
 /* ------------------------------------------------------------------ occupancy
  * How many blocks of the streaming kernels (reduce, fused SGD step, flatten /

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     assert ddp.abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         assert ddp.status_string(code)
 
 
@@ -152,6 +152,30 @@ def test_reduce_argument_errors_are_host_side():
     assert L.ddp_sync_allreduce_avg(p.handle, two, 2, 0, 0, ctypes.c_void_p(0x200004), None) == 4
     pb = ddp.plan_buckets([3, 4], 1 << 20, "bf16")
     assert L.ddp_sync_allreduce_avg(pb.handle, two, 2, 0, 0, out, None) == 2   # bf16 -> f32
+
+
+def test_noalloc_sync_argument_errors_are_host_side():
+    """The no-allocation sync validates like ddp_sync_allreduce_avg, and a
+    plan whose RING tables exceed its static buffer (DDP_NOALLOC_SCRATCH_BYTES
+    = 64 MiB: about 16 M tiles) is refused before any GPU call."""
+    L = ddp.lib
+    P = lambda *a: (ctypes.c_void_p * len(a))(*[ctypes.c_void_p(x) for x in a])   # noqa: E731
+    f = L.ddp_sync_allreduce_avg_noalloc
+    two = P(0x200000, 0x300000)
+    out = ctypes.c_void_p(0x400000)
+    assert f(None, two, 2, 1, 0, out, None) == 1
+    p = ddp.plan_buckets([3, 4], 1 << 20)
+    assert f(p.handle, two, 0, 1, 0, out, None) == 1
+    assert f(p.handle, two, 2, 2, 0, out, None) == 1                           # bad order
+    assert f(p.handle, P(0x200000), 1, 1, 1, out, None) == 2
+    assert f(p.handle, two, 2, 1, 0, ctypes.c_void_p(0x200004), None) == 4
+    pb = ddp.plan_buckets([3, 4], 1 << 20, "bf16")
+    assert f(pb.handle, two, 2, 1, 0, out, None) == 2                          # bf16 -> f32
+    # 2^32 + 1 f32 elements: 16 M + 1 tiles of 256, more words than the buffer holds
+    big = ddp.plan_buckets([1 << 31, (1 << 31) + 1], 1 << 40)
+    far = P(0x100000000000, 0x200000000000)
+    assert f(big.handle, far, 2, 1, 0, ctypes.c_void_p(0x300000000000), None) == 7
+    assert ddp.status_string(7) != ddp.status_string(6)
 
 
 def test_flatten_argument_errors():
