@@ -7,33 +7,35 @@ synchronisation of the workload: every bucket of the plan reduced over the N
 virtual ranks in the fixed order, scaled by 1/N and written -- one launch of
 ddp_sync_allreduce_avg.  Gradients sit in their bucket buffers (the
 gradient-as-bucket-view layout), so flatten and unflatten are not needed in
-the step; the same run also times the copy layout (flatten every rank, sync,
-unflatten) and reports it under "copy_path".
+the step; the ResNet-50 record also times the copy layout (flatten every
+rank, sync, unflatten) under "copy_path".
 
-Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
-The process idles --settle-seconds (20) before its first GPU call: buffers
-allocated within about 20 s of another process releasing tens of GB of
-device memory were measured to stream 4-5 % slower for as long as they live.
-Besides the metric and its roofline, the line carries (each can be skipped
-with its --no-... flag):
-  other_orders   the other summation order
-  per_bucket     the same sync as one launch per bucket (loop and graph)
+The headline is GPT-1.3B (1.3 G f32 gradients, 8 virtual ranks, 146 buckets
+of 25 MiB, ring order).  Every workload runs in a fresh child process of its
+own; the parent never touches the GPU, idles --settle-seconds (20) before the
+first child and --config-settle-seconds (10) before each further one
+(buffers allocated within about 20 s of another process releasing tens of GB
+of device memory were measured to stream 1-5 % slower).  The headline's
+record is the line; the other workloads' records go under "configs".
+
+Per workload: a declared clock ramp (back-to-back syncs for --ramp-ms, the
+first K of them timed as "without_ramp"), W warm-up syncs, K timed syncs
+(value, ms_per_step and the roofline), then
   cold_mall      the sync with the MALL flushed before each one
   ceiling        a probe of the reduce's bare access pattern
-  cpu_baseline   the CPU oracle (one thread, and SEQ on all host cores)
-  copy_path      flatten + sync + unflatten (eager and graph-replayed), and
-                 the same step as one kernel over per-parameter tensors
-  fused_sgd      the average fused into a momentum-SGD step (flat and
-                 per-parameter tensors)
-  overlap        syncs beside compute on a second stream
-  rank_sweep_GBps, in_place, no_sync, env
+  other_orders   the other summation order
+  cpu_baseline   the CPU oracle on all host cores and on one, with parity
+and for ResNet-50 only (--extras): per_bucket, copy_path, fused_sgd,
+overlap, rank_sweep_GBps, in_place, no_sync, small_means; for tiny the
+latency of a sync (Python call, prepared call, graph replay).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload resnet50|gpt1p3b|gpt1p3b_two_bucket|many_small|llama7b|tiny]
-                       [--order ring|seq] [--cpu-seconds S] [--no-<section> ...]
-       (the default order is ring, or the workload's only one: seq for tiny)
-       python bench.py --layout per-parameter [...]   (the one-kernel sync over per-parameter
-                                                        tensors as the timed step)
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--configs a,b,...|none] [--order ring|seq] [--no-<section> ...]
+       python bench.py --child --workload NAME [...]   (one workload, this process)
+       python bench.py --child --layout per-parameter --workload NAME [...]
+                       (the one-kernel sync over per-parameter tensors as the timed step)
        python bench.py --calibrate   (the plain-copy run that scales the HBM counters)
 """
 import argparse
@@ -41,6 +43,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 import types
@@ -75,18 +78,28 @@ def kernel_source_sha():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload, order, algorithmic_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when they were taken on another version of the kernel source."""
+def measured_traffic(workload, order):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (profiles/traffic.json) and where they come from, or None and the reason
+    when there are none for this kernel source.  The counters are not taken
+    in this run."""
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, "no counter file"
     rec = table.get(f"{workload}/{order}")
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    if not rec:
+        return None, f"no counter run for {workload}/{order}"
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None, (f"counters taken on kernel source {rec.get('kernel_source_sha')}, not "
+                      f"this one ({kernel_source_sha()})")
+    return rec.get("hbm_bytes_per_launch"), {
+        "profile": rec.get("profile"), "kernel_source_sha": rec.get("kernel_source_sha"),
+        "taken": rec.get("taken"), "read_bytes": rec.get("read_bytes"),
+        "write_bytes": rec.get("write_bytes"),
+        "how": "rocprofv3 FETCH_SIZE and WRITE_SIZE of the same kernel in committed runs, "
+               "scaled as the profile states; not measured in this run"}
 
 
 def side_by_side_streams(torch, tries=32):
@@ -193,15 +206,33 @@ def gbps(nbytes, ms):
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+DEFAULT_CONFIGS = "resnet50,many_small,tiny,gpt1p3b_two_bucket,llama7b"
+
+
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="resnet50")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt1p3b",
+                    help="the headline workload (default gpt1p3b: GPT-1.3B, 146 buckets, N=8)")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="the other workloads measured after the headline, each in a fresh child "
+                         "process, comma-separated ('none' for the headline alone)")
+    ap.add_argument("--child", action="store_true",
+                    help="measure --workload in this process and print its JSON line (what the "
+                         "parent runs per workload; the parent itself never touches the GPU)")
+    ap.add_argument("--extras", default=None, choices=["on", "off"],
+                    help="the legs beyond the metric (per-bucket launches, copy path, fused SGD, "
+                         "overlap, rank sweep, in place, no_sync, small means); default: on for "
+                         "resnet50 only")
     ap.add_argument("--order", default=None, choices=["ring", "seq"],
                     help="summation order of the timed sync (default: ring, or the workload's only "
                          "order: seq for tiny)")
+    ap.add_argument("--ramp-ms", type=float, default=300.0,
+                    help="time-based clock ramp: syncs run back to back for at least this long "
+                         "before the counted warm-up (declared in the line with the rate of the "
+                         "first K syncs, i.e. the result without it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-path", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
@@ -218,10 +249,16 @@ def parse_args():
                          "per-parameter tensors in one kernel (ddp_param_sync_run), and only the "
                          "timed step, the flushed-MALL leg, the other order and parity run")
     ap.add_argument("--settle-seconds", type=float, default=20.0,
-                    help="idle pause before the first GPU call: buffers allocated within about 20 s "
-                         "of another process releasing tens of GB of device memory stream 4-5 %% "
-                         "slower for as long as they live (0 to skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+                    help="idle pause before the first child starts (0 to skip): buffers allocated "
+                         "within about 20 s of another process releasing tens of GB of device "
+                         "memory were measured to stream 1-5 %% slower for as long as they live")
+    ap.add_argument("--config-settle-seconds", type=float, default=10.0,
+                    help="idle pause before each further child (after the previous one released "
+                         "its buffers)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle time of the headline (half on one thread, half on all cores)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="CPU oracle time of each further workload")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 10 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -319,38 +356,63 @@ def leg_parity_per_parameter(c):
 
 
 def timed_steps(c):
-    """K back-to-back steps, wall clock between two synchronisations; one
-    event pair brackets the loop on the launch stream.  Then the same K
+    """The metric.  First a declared, time-based clock ramp: syncs back to
+    back for at least --ramp-ms, of which the first K are timed between one
+    event pair (the result without a ramp).  Then W untimed warm-up syncs and
+    K timed back-to-back syncs, wall clock between two synchronisations, with
+    one event pair around the loop on the launch stream.  Then the same K
     steps with each launch between its own event pair (these add the event
     overhead of a few microseconds to each)."""
     torch, args = c.torch, c.args
+    K = args.steps
+    torch.cuda.synchronize()
+    first_a, first_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_ramp0 = time.perf_counter()
+    first_a.record(c.stream)
+    for _ in range(K):
+        c.sync()
+    first_b.record(c.stream)
+    n_ramp = K
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t_ramp0) * 1e3 < args.ramp_ms:
+        for _ in range(4):
+            c.sync()
+        n_ramp += 4
+        torch.cuda.synchronize()
+    ramp_ms = (time.perf_counter() - t_ramp0) * 1e3
+    first_ms = first_a.elapsed_time(first_b) / K
+    c.ramp = {"min_ms": args.ramp_ms, "ms": round(ramp_ms, 2), "syncs": n_ramp,
+              "without_ramp": {"syncs": K, "kernel_ms": round(first_ms, 5),
+                               "GBps": gbps(c.sync_bytes, first_ms),
+                               "how": "the first K syncs of the process, one event pair"}}
     for _ in range(args.warmup):
         c.sync()
     loop_a, loop_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     loop_a.record(c.stream)
-    for _ in range(args.steps):
+    for _ in range(K):
         c.sync()
     loop_b.record(c.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    c.ms_per_step = (t1 - t0) * 1e3 / args.steps
+    c.ms_per_step = (t1 - t0) * 1e3 / K
     # The reduce kernel's average launch duration: the event pair around the
     # timed loop on the launch stream, over K back-to-back launches (one
     # kernel per step, so this is the kernel plus the launch gap).
-    c.kern_ms = loop_a.elapsed_time(loop_b) / args.steps
+    c.kern_ms = loop_a.elapsed_time(loop_b) / K
     c.value = c.sync_bytes / (c.ms_per_step * 1e-3) / 1e9
     c.achieved = c.sync_bytes / (c.kern_ms * 1e-3) / 1e9
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(K)]
     for a, b in ev:
         a.record(c.stream)
         c.sync()
         b.record(c.stream)
     torch.cuda.synchronize()
     c.launch_ms = [a.elapsed_time(b) for a, b in ev]
-    log(f"sync: {c.ms_per_step * 1e3:.1f} us/step wall, {c.kern_ms * 1e3:.1f} us/step on the "
+    log(f"{c.wl.name}: ramp {ramp_ms:.0f} ms ({n_ramp} syncs; first {K}: {first_ms * 1e3:.1f} us "
+        f"each); {c.ms_per_step * 1e3:.1f} us/step wall, {c.kern_ms * 1e3:.1f} us/step on the "
         f"stream ({c.achieved:.0f} GB/s); single launches between events: median "
         f"{c.np.median(c.launch_ms) * 1e3:.1f} us, min {min(c.launch_ms) * 1e3:.1f} us")
 
@@ -398,28 +460,43 @@ def leg_per_bucket(c):
 
 
 def leg_cold_mall(c):
-    """The same sync with a 512 MiB scratch buffer overwritten before each
-    one, so that nothing of the previous sync is left in the 256 MB MALL;
-    each sync bracketed by its own event pair (a few microseconds of event
-    overhead included)."""
+    """The sync with nothing of the previous one left in the 256 MB MALL:
+    K times (overwrite a 512 MiB scratch buffer, sync) between one event
+    pair, minus K overwrites alone between another, divided by K -- the same
+    back-to-back form as the headline, so the two differ only by MALL reuse.
+    Three trials; the median is reported."""
     torch, np = c.torch, c.np
-    if c.args.no_cold:
-        return None
+    if c.args.no_cold or c.sync_bytes < (64 << 20):
+        return None   # a sync of a few KB lives in the caches whatever is flushed
     scratch = torch.empty(1 << 27, dtype=torch.float32, device=c.dev)
-    reps = min(c.args.steps, 50)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for a, b in ev:
-        scratch.fill_(1.0)
+    reps = max(5, min(c.args.steps, 50))
+
+    def pair(with_sync):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(c.stream)
-        c.sync()
+        for _ in range(reps):
+            scratch.fill_(1.0)
+            if with_sync:
+                c.sync()
         b.record(c.stream)
-    torch.cuda.synchronize()
-    ts = [a.elapsed_time(b) for a, b in ev]
-    res = {"GBps_median": gbps(c.sync_bytes, float(np.median(ts))),
-           "GBps_best": gbps(c.sync_bytes, min(ts)),
-           "ms_median": round(float(np.median(ts)), 5), "syncs": reps,
-           "flush": "512 MiB written before every sync"}
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    pair(True)
+    per_sync, flush = [], []
+    for _ in range(3):
+        both, alone = pair(True), pair(False)
+        per_sync.append((both - alone) / reps)
+        flush.append(alone / reps)
+    ms = float(np.median(per_sync))
+    res = {"GBps": gbps(c.sync_bytes, ms), "ms_per_sync": round(ms, 5),
+           "frac_of_peak": round(c.sync_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "vs_back_to_back": round(c.kern_ms / ms, 4),
+           "flush_ms": round(float(np.median(flush)), 5), "syncs": reps, "trials": 3,
+           "how": "event pair around K x (512 MiB overwrite + sync) minus one around K "
+                  "overwrites alone, / K; median of 3 trials"}
+    del scratch
     log(f"MALL flushed: {res}")
     return res
 
@@ -434,8 +511,8 @@ def leg_ceiling(c):
     size."""
     import ctypes
     torch, wl, N = c.torch, c.wl, c.N
-    if wl.in_bytes != wl.out_bytes or c.args.no_ceiling:
-        return None
+    if wl.in_bytes != wl.out_bytes or c.args.no_ceiling or c.sync_bytes < (64 << 20):
+        return None   # (a sync of a few KB is latency-bound: no bandwidth ceiling to compare)
     probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
     probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
@@ -478,78 +555,120 @@ def leg_other_orders(c):
     return res
 
 
+SAMPLE_INPUT_BYTES = 4 << 30
+
+
 def oracle_sample(c, oracle):
-    """The oracle's plan of the workload and the element span it covers: the
-    whole plan, or for the multi-GB workloads a bounded sample, the leading
-    whole buckets up to 4 GiB of inputs (a bucket's RING chunks depend on its
-    whole length); None when the first bucket alone exceeds that."""
+    """The runs of elements the CPU oracle computes: the whole plan, or for
+    the multi-GB workloads a bounded sample -- the leading buckets up to
+    4 GiB of inputs, the last one cut short where the budget ends (a piece
+    keeps its position in its bucket, so its ring chunks are the whole
+    bucket's).  Returns [(flat start, bucket length, position in bucket,
+    count)] and whether it is a sample."""
     wl, N = c.wl, c.N
     if wl.two_bucket:
         oplan = oracle.plan_two_bucket(wl.numel, wl.regions)
     else:
         oplan = oracle.plan_cap(wl.numel, wl.bucket_cap_bytes, wl.in_bytes)
-    if wl.total * N * wl.in_bytes <= (4 << 30):
-        return oplan, c.P, False
-    keep = 0
-    while keep < oplan.n_buckets and \
-            (oplan.bucket_base[keep] + oplan.bucket_len[keep]) * N * wl.in_bytes <= (4 << 30):
-        keep += 1
-    if keep == 0:
-        log("cpu baseline skipped: the first bucket alone exceeds the 4 GiB sample budget")
-        return None, 0, True
-    span = oplan.bucket_base[keep - 1] + oplan.bucket_len[keep - 1]
-    kept = [p for b in oplan.buckets[:keep] for p in b]
-    sub, k = [], 0
-    for b in oplan.buckets[:keep]:
-        sub.append(list(range(k, k + len(b))))
-        k += len(b)
-    return oracle.Plan([oplan.numel[p] for p in kept], sub), span, True
+    budget = SAMPLE_INPUT_BYTES // (N * wl.in_bytes)   # elements
+    runs, left = [], budget
+    for base, ln in zip(oplan.bucket_base, oplan.bucket_len):
+        if ln == 0:
+            continue
+        n = min(ln, left)
+        if n <= 0:
+            break
+        runs.append((base, ln, 0, n))
+        left -= n
+    return runs, sum(r[3] for r in runs) < c.P
 
 
-def leg_parity_and_cpu(c):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        return "unknown"
+
+
+def leg_parity_and_cpu(c, cpu_seconds):
     """Parity of the timed output against the CPU oracle, and the oracle's
-    rate on the host: one thread in the benchmark's order, then SEQ on all of
-    this process's host cores."""
+    rate on the host: the oracle's piece form (each element folded at its
+    position in its bucket) over the same runs of elements, split into
+    disjoint ranges on all of this process's host cores (the C call releases
+    the GIL, and the split leaves every bit as it is), then on one thread.
+    Half of cpu_seconds each."""
     if c.args.no_cpu_baseline:
         return None, None
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     torch, np, wl, N, order = c.torch, c.np, c.wl, c.N, c.order
-    oplan, span, sampled = oracle_sample(c, oracle)
-    if oplan is None:
-        return None, None
-    f32_out = c.tout == torch.float32
+    runs, sampled = oracle_sample(c, oracle)
+    span = sum(n for _, _, _, n in runs)
+    f32_in, f32_out = c.tin == torch.float32, c.tout == torch.float32
+    in_np, out_np = (np.float32 if f32_in else np.uint16), (np.float32 if f32_out else np.uint16)
     c.sync()
     torch.cuda.synchronize()
-    got = c.out[:span].view(torch.int32 if f32_out else torch.int16).cpu().numpy()
-    host = [f[:span].view(torch.int32 if c.tin == torch.float32 else torch.int16).cpu().numpy()
-            .view(np.float32 if c.tin == torch.float32 else np.uint16) for f in c.flats]
+
+    def host(t, a, n):
+        return t[a:a + n].view(torch.int32 if t.dtype == torch.float32 else torch.int16) \
+            .cpu().numpy().view(np.float32 if t.dtype == torch.float32 else np.uint16)
+
+    xs = [np.concatenate([host(f, a, n) for a, _, _, n in runs]) for f in c.flats]
+    got = np.concatenate([host(c.out, a, n) for a, _, _, n in runs])
+    # threads: the CPUs this process may use (at most 16, the box's share),
+    # one per million elements at least
+    threads = max(1, min(16, len(os.sched_getaffinity(0)), span >> 20))
+    pieces, k = [], 0          # (offset in the sample, bucket length, position, count)
+    for _, ln, pos, n in runs:
+        step = max(1, -(-n // threads))
+        pieces += [(k + s, ln, pos + s, min(step, n - s)) for s in range(0, n, step)]
+        k += n
+    want = np.empty(span, dtype=out_np)
+
+    def piece(pc):
+        k0, ln, pos, n = pc
+        oracle.bucket_range_avg([x[k0:k0 + n] for x in xs], ln, pos, order, wl.dtype,
+                                wl.out_dtype, out=want[k0:k0 + n])
+
     sample_bytes = span * (N * wl.in_bytes + wl.out_bytes)
-    reps, t_cpu = 0, 0.0
-    want = None
-    while reps == 0 or t_cpu < c.args.cpu_seconds:
-        c0 = time.perf_counter()
-        want = oracle.sync_avg(oplan, host, order, wl.dtype, wl.out_dtype)
-        t_cpu += time.perf_counter() - c0
-        reps += 1
-    same = got == want.view(np.int32 if f32_out else np.int16)
-    both_nan = np.isnan(got.view(np.float32)) & np.isnan(want) if f32_out else np.zeros_like(same)
-    parity = "bitwise equal to the CPU oracle" if bool((same | both_nan).all()) else \
-        f"MISMATCH in {int((~(same | both_nan)).sum())} elements"
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
-    what = (f"the first {oplan.n_buckets} bucket(s), {span} of {c.P} elements, of the {wl.name} "
-            f"synchronisation; rate extrapolated to the whole" if sampled else
-            f"the full {wl.name} synchronisation")
-    cpu = {"value": round(sample_bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
-           "kind": "oracle", "host_cpu": cpu_model, "host_threads": os.cpu_count(),
-           "sample": f"{what} ({order} order, N={N}), {reps} repetition(s), {t_cpu:.1f} s "
-                     f"single-threaded C oracle"}
+
+    def timed_runs(ex, budget):
+        reps, t = 0, 0.0
+        while reps == 0 or t < budget:
+            t0 = time.perf_counter()
+            if ex is None:
+                for pc in pieces:
+                    piece(pc)
+            else:
+                list(ex.map(piece, pieces))
+            t += time.perf_counter() - t0
+            reps += 1
+        return reps, t
+
+    with ThreadPoolExecutor(threads) as ex:
+        reps_mt, t_mt = timed_runs(ex, cpu_seconds / 2)
+    same = got.view(np.uint32 if f32_out else np.uint16) == want.view(np.uint32 if f32_out
+                                                                       else np.uint16)
+    if f32_out:
+        same |= np.isnan(got) & np.isnan(want)
+    parity = "bitwise equal to the CPU oracle" if bool(same.all()) else \
+        f"MISMATCH in {int((~same).sum())} elements"
+    reps_1, t_1 = timed_runs(None, cpu_seconds / 2)
+    what = (f"the leading {span} of {c.P} elements ({len(runs)} bucket(s), the last one cut at "
+            f"4 GiB of inputs) of the {wl.name} synchronisation; rate extrapolated to the whole"
+            if sampled else f"the full {wl.name} synchronisation")
+    cpu = {"value": round(sample_bytes * reps_mt / t_mt / 1e9, 3), "unit": "GB/s",
+           "cores": threads, "kind": "oracle", "order": order,
+           "host_cpu": _cpu_model(), "host_threads": os.cpu_count(),
+           "sample": f"{what} ({order} order, N={N}): {reps_mt} repetition(s) in "
+                     f"{t_mt:.1f} s, {len(pieces)} element ranges on {threads} threads "
+                     f"(oracle.bucket_range_avg)",
+           "single_thread": {"value": round(sample_bytes * reps_1 / t_1 / 1e9, 3),
+                             "unit": "GB/s", "cores": 1,
+                             "sample": f"the same, {reps_1} repetition(s) in {t_1:.1f} s"}}
     if sampled:
-        parity = parity + " (on the sampled buckets)"
+        parity = parity + f" (on the sampled {span} elements)"
     # context: a plain single-threaded host copy of 256 MiB (read + write bytes)
     src_h = np.ones(1 << 26, dtype=np.float32)
     dst_h = np.empty_like(src_h)
@@ -559,49 +678,8 @@ def leg_parity_and_cpu(c):
         np.copyto(dst_h, src_h)
         n_cp += 1
     cpu["host_copy_GBps"] = round(2 * src_h.nbytes * n_cp / (time.perf_counter() - c0) / 1e9, 2)
-    del src_h, dst_h
-    log(f"parity: {parity}; cpu oracle {cpu['value']} GB/s over {reps} reps; "
-        f"host copy {cpu['host_copy_GBps']} GB/s")
-
-    # The oracle on all of this process's host cores: SEQ order, every bucket
-    # split into disjoint element ranges, one ctypes call per range (the call
-    # releases the GIL).  SEQ has no index dependence, so the split leaves
-    # every bit as it is; its result is checked against the GPU's SEQ output
-    # of the same buffers.
-    threads = min(16, len(os.sched_getaffinity(0)))
-    pieces = []
-    for base, ln in zip(oplan.bucket_base, oplan.bucket_len):
-        step = max(1, -(-ln // threads))
-        pieces += [(base + a, min(step, ln - a)) for a in range(0, ln, step)]
-    seq_want = np.empty(span, dtype=np.float32 if f32_out else np.uint16)
-
-    def piece(pc):
-        a, n = pc
-        seq_want[a:a + n] = oracle.bucket_avg([h[a:a + n] for h in host], "seq",
-                                              wl.dtype, wl.out_dtype)
-
-    from concurrent.futures import ThreadPoolExecutor
-    reps_mt, t_mt = 0, 0.0
-    with ThreadPoolExecutor(threads) as ex:
-        while reps_mt == 0 or t_mt < c.args.cpu_seconds / 2:
-            c0 = time.perf_counter()
-            list(ex.map(piece, pieces))
-            t_mt += time.perf_counter() - c0
-            reps_mt += 1
-    c.sync("seq")
-    torch.cuda.synchronize()
-    got_seq = c.out[:span].view(torch.int32 if f32_out else torch.int16).cpu().numpy()
-    ok = got_seq == seq_want.view(got_seq.dtype)
-    if f32_out:
-        ok |= np.isnan(got_seq.view(np.float32)) & np.isnan(seq_want)
-    cpu["all_cores"] = {
-        "value": round(sample_bytes * reps_mt / t_mt / 1e9, 3), "unit": "GB/s", "cores": threads,
-        "order": "seq", "parity_vs_gpu_seq": "bitwise equal" if bool(ok.all())
-        else f"MISMATCH in {int((~ok).sum())} elements",
-        "sample": f"{reps_mt} repetition(s) of {'the sample' if sampled else 'the full synchronisation'}"
-                  f", {len(pieces)} element ranges on {threads} threads, {t_mt:.1f} s"}
-    log(f"cpu oracle, {threads} threads (seq): {cpu['all_cores']['value']} GB/s; "
-        f"{cpu['all_cores']['parity_vs_gpu_seq']}")
+    log(f"{wl.name} parity: {parity}; cpu oracle {cpu['value']} GB/s on {threads} threads, "
+        f"{cpu['single_thread']['value']} GB/s on one; host copy {cpu['host_copy_GBps']} GB/s")
     return parity, cpu
 
 
@@ -920,6 +998,100 @@ def leg_no_sync(c):
     return res
 
 
+def latency(c, make_call, reps=2000):
+    """Latency of a short synchronisation, in microseconds per call, three
+    ways: `make_call(stream, prepared)` returns a zero-argument call that
+    enqueues it on `stream` -- marshalling every argument per call
+    (prepared=False) or once (prepared=True, one C call per step) -- and the
+    prepared call captured into a HIP graph: one call per replay (the wall
+    time of a replay), and 100 calls in one graph (device time per call)."""
+    torch = c.torch
+
+    def wall(fn, n):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / n
+
+    res = {"python_call_us": round(wall(make_call(c.stream, False), reps), 2),
+           "prepared_call_us": round(wall(make_call(c.stream, True), reps), 2)}
+    side = torch.cuda.Stream()
+    side.wait_stream(c.stream)
+    call = make_call(side, True)
+    call()
+    torch.cuda.synchronize()
+    g1, g100 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1, stream=side):
+        call()
+    with torch.cuda.graph(g100, stream=side):
+        for _ in range(100):
+            call()
+    torch.cuda.synchronize()
+    res["graph_replay_us"] = round(wall(g1.replay, reps), 2)
+    res["graph_of_100_us_per_call"] = round(wall(g100.replay, 20) / 100, 3)
+    del g1, g100
+    return res
+
+
+def leg_tiny_latency(c):
+    """The latency-bound workload (tiny: 15 KB per sync): its sync through
+    the plain Python call, the prepared call and graph replay."""
+    ddp = c.ddp
+    if c.wl.name != "tiny":
+        return None
+
+    def make_call(st, prepared):
+        if prepared:
+            return ddp.make_sync(c.plan, c.flats, c.out, c.order, stream=st)
+        return lambda: ddp.sync_allreduce_avg(c.plan, c.flats, c.out, c.order, stream=st)
+
+    res = latency(c, make_call)
+    log(f"tiny latency: {res}")
+    return res
+
+
+def leg_small_means(c):
+    """The same mean all-reduce at its other call sites ([TR24] 十二, 十三):
+    the BN running statistics -- every BN layer's running mean and running
+    variance, one contiguous range of 2 x (BN channels) f32 values -- and a
+    validation record of 3 scalars (loss, top-1, top-5), over the N virtual
+    ranks, ring order; checked against the oracle and timed as latency."""
+    import oracle
+    torch, ddp, wl, N, np = c.torch, c.ddp, c.wl, c.N, c.np
+    if wl.name != "resnet50":
+        return None
+    bn_channels = sum(p.numel for p in wl.params if p.region == c.W.REGION_BN_WEIGHT)
+    res = {}
+    rng = np.random.default_rng(12)
+    for name, length in (("bn_running_stats", 2 * bn_channels), ("metric_record", 3)):
+        xs = [(rng.standard_normal(length) * 0.5 + 1.0).astype(np.float32) for _ in range(N)]
+        ins = [torch.from_numpy(x).to(c.dev) for x in xs]
+        out = torch.empty(length, device=c.dev)
+        plan = ddp.plan_buckets([length], 1 << 40, "f32")
+
+        def make_call(st, prepared, plan=plan, ins=ins, out=out):
+            if prepared:
+                return ddp.make_sync(plan, ins, out, c.order, stream=st)
+            return lambda: ddp.bucket_allreduce_avg(ins, out, c.order, stream=st)
+
+        lat = latency(c, make_call, reps=1000)
+        ddp.bucket_allreduce_avg(ins, out, c.order, stream=c.stream)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = oracle.bucket_avg(xs, c.order)
+        lat["elements"] = length
+        lat["parity"] = ("bitwise equal to the CPU oracle"
+                         if np.array_equal(got.view(np.uint32), want.view(np.uint32)) else
+                         "MISMATCH against the CPU oracle")
+        res[name] = lat
+    log(f"small means: {res}")
+    return res
+
+
 def calibrate(torch):
     """A plain 1 GiB device-to-device copy, 10 times: the kernel of known size
     that scales the FETCH_SIZE / WRITE_SIZE counters."""
@@ -931,47 +1103,46 @@ def calibrate(torch):
     print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
 
 
-def main():
-    args = parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
-        sys.exit(2)
+def dtype_label(wl):
+    """The arithmetic the path computes in: the FP32 fold, with the input and
+    output element types when they are not f32."""
+    if wl.dtype == wl.out_dtype == "f32":
+        return "f32"
+    return f"{wl.dtype}->{wl.out_dtype} (f32 accumulate)"
 
-    if args.settle_seconds > 0 and not args.calibrate:
-        log(f"idle {args.settle_seconds:.0f} s before the first GPU call")
-        time.sleep(args.settle_seconds)
+
+def measure(args, cpu_seconds):
+    """One workload measured in this process: its JSON record (the line a
+    child prints)."""
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    if args.calibrate:
-        calibrate(torch)
-        return
-
     c = setup(args)
     sensors_before = hwmon_readings(torch)
     timed_steps(c)
     sensors_after = hwmon_readings(torch)
     per_param = args.layout == "per-parameter"
-    per_bucket = None if per_param else leg_per_bucket(c)
+    extras = (args.extras == "on") if args.extras else c.wl.name == "resnet50"
     cold = leg_cold_mall(c)
     ceiling = None if per_param else leg_ceiling(c)
     other = leg_other_orders(c)
     if per_param:
         parity, cpu = leg_parity_per_parameter(c), None
-        copy_path = fused = overlap = rank_sweep = in_place = no_sync = None
     else:
-        parity, cpu = leg_parity_and_cpu(c)
-        copy_path = leg_copy_path(c)
-        fused = leg_fused_sgd(c)
-        overlap = leg_overlap(c)
-        rank_sweep = leg_rank_sweep(c)
-        in_place = leg_in_place(c)
-        no_sync = leg_no_sync(c)
+        parity, cpu = leg_parity_and_cpu(c, cpu_seconds)
+    more = {}
+    if extras and not per_param:
+        more = {"per_bucket": leg_per_bucket(c), "copy_path": leg_copy_path(c),
+                "fused_sgd": leg_fused_sgd(c), "overlap": leg_overlap(c),
+                "rank_sweep_GBps": leg_rank_sweep(c), "in_place": leg_in_place(c),
+                "no_sync": leg_no_sync(c), "small_means": leg_small_means(c)}
+    tiny = leg_tiny_latency(c)
 
     wl, P, np = c.wl, c.P, c.np
-    line = {
+    kernel = "params_fast" if per_param else "reduce_fast"
+    traffic, traffic_source = (None, "not taken for the per-parameter layout") if per_param else \
+        measured_traffic(wl.name, c.order)
+    record = {
         "metric": METRIC,
         "value": round(c.value, 1),
         "unit": "GB/s",
@@ -983,7 +1154,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dtype_label(wl),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {len(wl.params)} gradient tensors, "
                                f"{P} elements, {c.N} virtual ranks, {c.plan.n_buckets} buckets",
@@ -998,30 +1169,99 @@ def main():
                    "device": torch.cuda.get_device_name(0)},
         "roofline": {"bound": "hbm", "achieved": round(c.achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(c.achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if per_param else measured_traffic(wl.name, c.order,
-                                                                        c.sync_bytes),
-                     "kernel": ("params_fast" if per_param else "reduce_fast") +
-                               " (one launch per sync)",
+                     "traffic": traffic, "traffic_source": traffic_source,
+                     "kernel": kernel + " (one launch per sync)",
                      "kernel_ms": round(c.kern_ms, 5),
-                     "kernel_ms_source": "event pair around the K timed launches, / K",
+                     "kernel_ms_source": "event pair around the K timed launches on the launch "
+                                         "stream, / K",
                      "single_launch_ms_median": round(float(np.median(c.launch_ms)), 5),
                      "single_launch_ms_min": round(min(c.launch_ms), 5)},
-        "per_bucket": per_bucket,
+        "ramp": c.ramp,
         "cold_mall": cold,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity": parity,
         "other_orders": other,
-        "copy_path": copy_path,
-        "fused_sgd": fused,
-        "in_place": in_place,
-        "rank_sweep_GBps": rank_sweep,
-        "overlap": overlap,
-        "no_sync": no_sync,
+        **({"latency": tiny} if tiny else {}),
+        **{k: v for k, v in more.items() if v is not None},
         "env": dict(run_environment(torch),
                     sensors={"before_timed_steps": sensors_before,
                              "after_timed_steps": sensors_after}),
     }
+    return record
+
+
+# keys every record repeats; a workload under "configs" drops them
+_SHARED_KEYS = ("metric", "unit", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
+                "vs_baseline", "data")
+
+
+def run_child(args, workload, cpu_seconds, headline):
+    """Measures one workload in a fresh child process (started by this
+    process, which has not touched the GPU) and returns its record."""
+    cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", "--workload", workload,
+           "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--ramp-ms", str(args.ramp_ms), "--cpu-seconds", str(cpu_seconds)]
+    for flag in ("cpu_baseline", "copy_path", "ceiling", "fused_sgd", "overlap", "no_sync",
+                 "in_place", "rank_sweep", "cold", "per_bucket"):
+        if getattr(args, "no_" + flag):
+            cmd.append("--no-" + flag.replace("_", "-"))
+    if args.extras:
+        cmd += ["--extras", args.extras]
+    if headline:
+        cmd += ["--layout", args.layout] + (["--order", args.order] if args.order else [])
+    log(f"bench: {workload} in a child process")
+    t0 = time.perf_counter()
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    lines = [l for l in proc.stdout.splitlines() if l.startswith("{")]
+    if proc.returncode != 0 or not lines:
+        return {"error": f"child exited with status {proc.returncode}"}
+    rec = json.loads(lines[-1])
+    rec["child_wall_s"] = round(time.perf_counter() - t0, 1)
+    return rec
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the N virtual ranks of a synchronisation live in that GPU's HBM", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate:
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        calibrate(torch)
+        return
+    if args.child:
+        print(json.dumps(measure(args, args.cpu_seconds)), flush=True)
+        return
+
+    # Parent: never touches the GPU; every workload runs in a child of its own.
+    if args.settle_seconds > 0:
+        log(f"bench: idle {args.settle_seconds:.0f} s before the first GPU call")
+        time.sleep(args.settle_seconds)
+    line = run_child(args, args.workload, args.cpu_seconds, headline=True)
+    if "error" in line:
+        log(f"bench: the headline workload {args.workload} failed: {line['error']}")
+        sys.exit(1)
+    names = [w for w in args.configs.split(",") if w and w != "none" and w != args.workload]
+    configs = {}
+    for w in names:
+        if args.config_settle_seconds > 0:
+            time.sleep(args.config_settle_seconds)
+        rec = run_child(args, w, args.config_cpu_seconds, headline=False)
+        configs[w] = {k: v for k, v in rec.items() if k not in _SHARED_KEYS}
+    line["configs"] = configs
+    line["protocol"] = {
+        "processes": "each workload in a fresh child process; the parent never touches the GPU",
+        "settle_seconds_before_first": args.settle_seconds,
+        "settle_seconds_between": args.config_settle_seconds,
+        "order": [args.workload] + names,
+        "per_workload": f"ramp >= {args.ramp_ms:.0f} ms of back-to-back syncs (the first "
+                        f"{args.steps} timed: ramp.without_ramp), {args.warmup} warm-up syncs, "
+                        f"{args.steps} timed syncs; then the flushed-MALL leg, the probe, the "
+                        f"other order, parity and the CPU oracle"}
     print(json.dumps(line), flush=True)
 
 

@@ -47,24 +47,57 @@ def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
 def test_traffic_is_reported_only_for_the_hashed_code(tmp_path):
     b = _bench()
     import json
-    rec = {"resnet50/ring": {"kernel_source_sha": b.kernel_source_sha(), "hbm_bytes_per_launch": 123}}
+    rec = {"resnet50/ring": {"kernel_source_sha": b.kernel_source_sha(), "hbm_bytes_per_launch": 123,
+                             "profile": "profiles/x.md", "taken": "2026-12-02"}}
     f = tmp_path / "t.json"
     f.write_text(json.dumps(rec))
     b.TRAFFIC_FILE = str(f)
-    assert b.measured_traffic("resnet50", "ring", 1) == 123
-    assert b.measured_traffic("resnet50", "seq", 1) is None
+    nbytes, src = b.measured_traffic("resnet50", "ring")
+    assert nbytes == 123 and src["profile"] == "profiles/x.md" and src["taken"] == "2026-12-02"
+    nbytes, why = b.measured_traffic("resnet50", "seq")
+    assert nbytes is None and "no counter run" in why
     rec["resnet50/ring"]["kernel_source_sha"] = "0" * 16
     f.write_text(json.dumps(rec))
-    assert b.measured_traffic("resnet50", "ring", 1) is None
+    nbytes, why = b.measured_traffic("resnet50", "ring")
+    assert nbytes is None and "0" * 16 in why
 
 
 def test_parser_defaults_and_layouts(monkeypatch):
     b = _bench()
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = b.parse_args()
-    assert (a.gpus, a.steps, a.warmup, a.workload, a.layout) == (1, 200, 20, "resnet50", "bucket-view")
-    assert a.order is None and a.settle_seconds == 20.0
+    assert (a.gpus, a.steps, a.warmup, a.workload, a.layout) == (1, 50, 10, "gpt1p3b", "bucket-view")
+    assert a.order is None and a.settle_seconds == 20.0 and not a.child
+    assert a.configs.split(",") == ["resnet50", "many_small", "tiny", "gpt1p3b_two_bucket", "llama7b"]
     monkeypatch.setattr(sys, "argv", ["bench.py", "--layout", "per-parameter", "--settle-seconds", "0",
-                                      "--workload", "tiny", "--order", "seq"])
+                                      "--workload", "tiny", "--order", "seq", "--child"])
     a = b.parse_args()
-    assert (a.layout, a.settle_seconds, a.workload, a.order) == ("per-parameter", 0.0, "tiny", "seq")
+    assert (a.layout, a.settle_seconds, a.workload, a.order, a.child) == \
+        ("per-parameter", 0.0, "tiny", "seq", True)
+
+
+def test_dtype_label_follows_the_workload():
+    b = _bench()
+    import workloads as W
+    assert b.dtype_label(W.workload("gpt1p3b")) == "f32"
+    assert b.dtype_label(W.workload("llama7b")) == "bf16->bf16 (f32 accumulate)"
+
+
+def test_cpu_sample_is_bounded_and_keeps_bucket_positions():
+    """The CPU oracle's sample of a multi-GB workload: leading buckets up to
+    4 GiB of inputs, the last one cut short at its own position 0."""
+    b = _bench()
+    import types
+    import workloads as W
+    import oracle
+    for name in ("gpt1p3b", "gpt1p3b_two_bucket", "resnet50"):
+        wl = W.workload(name)
+        c = types.SimpleNamespace(wl=wl, N=wl.n_ranks, P=wl.total)
+        runs, sampled = b.oracle_sample(c, oracle)
+        n = sum(r[3] for r in runs)
+        assert n * wl.n_ranks * wl.in_bytes <= b.SAMPLE_INPUT_BYTES
+        assert sampled == (n < wl.total)
+        assert all(pos == 0 and 0 < cnt <= ln for _, ln, pos, cnt in runs)
+        starts = [a for a, _, _, _ in runs]
+        assert starts == sorted(starts)
+    assert not sampled           # resnet50: the whole synchronisation
