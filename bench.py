@@ -54,10 +54,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "effective HBM GB/s (N·P·bytes read + P written) and % of peak per sync"
 CSRC = os.path.join(ROOT, "gradient_allreduce_averaging_amd", "csrc")
-# the library's device and launch code: every kernel source and header but the
-# benchmark's own probe
-KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                        if f.endswith((".hip", ".h")) and f != "probe.hip")
+# the sources the flat reduce kernel (the one whose HBM counters are recorded)
+# is built and launched from: its kernels and launches, the shared device
+# code, the host helpers and the occupancy caps
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("common.hip", "device.h", "host.h", "reduce.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

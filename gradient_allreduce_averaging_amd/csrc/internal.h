@@ -57,9 +57,9 @@ struct ddp_binding {
     std::vector<uint64_t> param_addr;         // [n_params] the bound gradient pointers
 };
 
-// A synchronisation over per-parameter tensors (params.hip): one table entry
-// per tile of each parameter, with every rank's address and those of the
-// tensors it writes.
+// A synchronisation over per-parameter tensors (params.hip): an 8-byte record
+// per tile of each parameter (its parameter and ring chunks), then an entry
+// per parameter with every rank's address and those of the tensors it writes.
 struct ddp_param_sync {
     int device = -1;
     int n_ranks = 0;
@@ -67,9 +67,11 @@ struct ddp_param_sync {
     int in = 0, out = 0;                      // ddp_dtype_t of inputs and outputs
     bool sgd = false;                         // built by ddp_param_sgd_create
     bool momentum = false;                    // sgd: with a momentum buffer
-    char *table = nullptr;                    // device array, n_tiles * stride bytes
+    char *table = nullptr;                    // device array: tile records, then parameter entries
     int64_t n_tiles = 0;
-    int64_t stride = 0;                       // bytes per entry
+    int64_t rstride = 0;                      // tile records per XCD stripe
+    int64_t pstride = 0;                      // bytes per parameter entry
+    int64_t params_offset = 0;                // byte offset of the parameter entries
     std::vector<int64_t> bucket_tile;         // [n_buckets + 1] first entry of each bucket
 };
 

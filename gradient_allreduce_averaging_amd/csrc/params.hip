@@ -40,36 +40,71 @@ inline int64_t ps_tile_elems(int in) { return (int64_t)kThreads * kPsUnroll * ve
 
 // A parameter is cut into tiles of ps_tile_elems elements from its own start
 // (the last one shorter), so every address inside a tile has the alignment
-// of the parameter's address.  One table entry per tile, `stride` bytes
-// (16-byte aligned):
-//   uint64_t addr[N + X]   ranks 0..N-1, then the X tensors written, at the
-//                          tile's first element:
-//                            sync: the output (X = 1)
-//                            SGD:  the averaged gradient (0 if not stored),
-//                                  the parameters, the momentum (0 if none)
-//                                  (X = 3)
-//   PsMeta                 below
+// of the parameter's address.  The table has two parts:
+//
+//   tile records, 8 bytes each, striped by XCD (tile t at
+//   (t % kXcds) * rstride + t / kXcds, so that each XCD's L2 fetches lines
+//   of its own tiles only): the tile's parameter entry and its ring word;
+//
+//   parameter entries, `pstride` bytes each (16-byte aligned), one per
+//   parameter with elements, in flat order:
+//     uint64_t addr[N + X]   ranks 0..N-1, then the X tensors written, at the
+//                            parameter's first element:
+//                              sync: the output (X = 1)
+//                              SGD:  the averaged gradient (0 if not stored),
+//                                    the parameters, the momentum (0 if none)
+//                                    (X = 3)
+//     PsParamMeta            below
+//
+// A tile's addresses are its parameter's plus the tile's first element j0 =
+// (tile - first_tile) * ps_tile_elems, so the table costs 8 bytes per tile
+// (0.09 % of the 9 KiB an f32 tile of 8 ranks moves) and a few dozen bytes
+// per parameter.
+struct PsTile {
+    uint32_t param;   // parameter entry index
+    uint32_t ring;    // the ring chunks the tile meets: start rank of chunk a
+                      // (bits 0-5) and of chunk b (bits 6-11), where a (bits
+                      // 12-21) and b (bits 22-31) end, relative to the tile's
+                      // first element
+};
+
+struct PsParamMeta {
+    int64_t pos0;         // position of the parameter's first element in its bucket
+    int64_t blen;         // length of that bucket
+    int64_t first_tile;   // the parameter's first tile
+    int64_t numel;        // its elements
+    uint32_t vec;         // 1: every written tensor of the parameter 16-byte aligned
+    uint32_t pad;
+};
+
+// One tile's view of its entry, in registers.
 struct PsMeta {
     int64_t pos;      // position of the tile's first element inside its bucket
     int64_t blen;     // length of that bucket
+    int64_t j0;       // the tile's first element inside its parameter
     uint32_t count;   // elements in the tile, 1..tile
-    uint32_t vec;     // 1: every written tensor of the parameter 16-byte aligned
-    uint32_t starts;  // the ring chunks the tile meets: start rank of chunk a
-                      // (bits 0-5) and of chunk b (bits 6-11) ...
-    uint32_t cuts;    // ... and where a (bits 0-15) and b (bits 16-31) end,
-                      // relative to the tile's first element
+    uint32_t vec;
+    uint32_t ring;
 };
 
 constexpr int kSyncExtra = 1, kSgdExtra = 3;
 
-int64_t ps_stride(int N, int extra)
+int64_t ps_pstride(int N, int extra)
 {
-    return (8 * (int64_t)(N + extra) + (int64_t)sizeof(PsMeta) + 15) / 16 * 16;
+    return (8 * (int64_t)(N + extra) + (int64_t)sizeof(PsParamMeta) + 15) / 16 * 16;
+}
+
+// Where tile t's record sits: XCD-striped.
+__host__ __device__ inline int64_t ps_record(int64_t t, int64_t rstride)
+{
+    const uint64_t u = (uint64_t)t;   // t >= 0: unsigned division is a shift and a mask
+    return (int64_t)((u % kXcds) * (uint64_t)rstride + u / kXcds);
 }
 
 __device__ __forceinline__ u32x4 gld_stream(uint64_t addr) { return ld_at(addr, 0); }
 
-// The scaled average of tile element i, one element at a time (N >= 2).
+// The scaled average of tile element i, one element at a time (N >= 2); a
+// holds the parameter's base addresses.
 template <int IN, bool RING>
 __device__ __forceinline__ float ps_avg_elem(const uint64_t *a, int N, const PsMeta &m, float inv,
                                              int64_t i)
@@ -79,10 +114,11 @@ __device__ __forceinline__ float ps_avg_elem(const uint64_t *a, int N, const PsM
         const int64_t C = (m.blen + N - 1) / N;
         r = (int)(((m.pos + i) / C + 1) % N);
     }
-    return avg_at<IN, RING>(a, N, r, inv, i);
+    return avg_at<IN, RING>(a, N, r, inv, m.j0 + i);
 }
 
-// Per-element path of the sync: tile elements [i0, i0 + cnt) clipped to the tile.
+// Per-element path of the sync: tile elements [i0, i0 + cnt) clipped to the
+// tile; a: the parameter entry's addresses (in memory).
 template <int IN, int OUT, bool RING>
 __device__ void params_elems(const uint64_t *a, int N, const PsMeta &m, float inv, int64_t i0,
                              int cnt)
@@ -93,12 +129,12 @@ __device__ void params_elems(const uint64_t *a, int N, const PsMeta &m, float in
         if (i >= (int64_t)m.count) break;
         if (N == 1) {   // the input, bit for bit (inputs and outputs share a dtype)
             if (IN == kF32)
-                st_elem<uint32_t>(out, i, ld_elem<uint32_t>(a[0], i));
+                st_elem<uint32_t>(out, m.j0 + i, ld_elem<uint32_t>(a[0], m.j0 + i));
             else
-                st_elem<uint16_t>(out, i, ld_elem<uint16_t>(a[0], i));
+                st_elem<uint16_t>(out, m.j0 + i, ld_elem<uint16_t>(a[0], m.j0 + i));
             continue;
         }
-        store_elem<OUT>(out, i, ps_avg_elem<IN, RING>(a, N, m, inv, i));
+        store_elem<OUT>(out, m.j0 + i, ps_avg_elem<IN, RING>(a, N, m, inv, i));
     }
 }
 
@@ -110,8 +146,9 @@ __device__ void params_sgd_elems(const uint64_t *a, int N, const PsMeta &m, floa
     for (int e = 0; e < cnt; ++e) {
         const int64_t i = i0 + e;
         if (i >= (int64_t)m.count) break;
-        const float y = N == 1 ? load_elem<IN>(a[0], i) : ps_avg_elem<IN, RING>(a, N, m, inv, i);
-        sgd_at<OUT, MOM>(a[N], a[N + 1], a[N + 2], i, y, lr, mu);
+        const float y = N == 1 ? load_elem<IN>(a[0], m.j0 + i)
+                               : ps_avg_elem<IN, RING>(a, N, m, inv, i);
+        sgd_at<OUT, MOM>(a[N], a[N + 1], a[N + 2], m.j0 + i, y, lr, mu);
     }
 }
 
@@ -127,56 +164,78 @@ __device__ __forceinline__ PsSegs ps_segs(const PsMeta &m)
     s.a_hi = s.b_lo = s.b_hi = m.count;
     s.sa = s.sb = 0;
     if (RING) {
-        s.sa = __builtin_amdgcn_readfirstlane((int)(m.starts & 63u));
-        s.sb = __builtin_amdgcn_readfirstlane((int)((m.starts >> 6) & 63u));
-        s.a_hi = s.b_lo = (int64_t)(m.cuts & 0xffffu);
-        s.b_hi = (int64_t)(m.cuts >> 16);
+        s.sa = __builtin_amdgcn_readfirstlane((int)(m.ring & 63u));
+        s.sb = __builtin_amdgcn_readfirstlane((int)((m.ring >> 6) & 63u));
+        s.a_hi = s.b_lo = (int64_t)((m.ring >> 12) & 1023u);
+        s.b_hi = (int64_t)(m.ring >> 22);
     }
     return s;
 }
 
-// The tile's entry: every address and the metadata, fetched in one batch of
-// scalar loads before any of them is used (a use behind a branch would
-// otherwise wait for the flags before fetching its address).
+// The table of one sync, as the kernels get it.
+struct PsTable {
+    const PsTile *tiles;   // XCD-striped records
+    const char *params;    // parameter entries
+    int64_t rstride;       // records per XCD stripe
+    int64_t pstride;       // bytes per parameter entry
+    int64_t n_tiles;
+    int64_t tile_elems;
+};
+
+// The tile's entry: its record, then every address and the metadata of its
+// parameter, fetched in one batch of scalar loads before any of them is used
+// (a use behind a branch would otherwise wait for the flags before fetching
+// its address).
 template <int NA>
 struct PsEntry {
     uint64_t ad[NA];
     PsMeta m;
+    const char *pe;   // the parameter entry (per-element paths read addresses there)
 };
 
 template <int NA>
-__device__ __forceinline__ PsEntry<NA> ps_entry(const char *e)
+__device__ __forceinline__ PsEntry<NA> ps_entry(const PsTable &tb, int64_t tile)
 {
     PsEntry<NA> t;
-    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
+    const PsTile rec = tb.tiles[ps_record(tile, tb.rstride)];
+    t.pe = tb.params + (int64_t)rec.param * tb.pstride;
+    const uint64_t *a = reinterpret_cast<const uint64_t *>(t.pe);
 #pragma unroll
     for (int k = 0; k < NA; ++k) t.ad[k] = a[k];
-    t.m = *reinterpret_cast<const PsMeta *>(e + 8 * NA);
+    const PsParamMeta pm = *reinterpret_cast<const PsParamMeta *>(t.pe + 8 * NA);
 #pragma unroll
     for (int k = 0; k < NA; ++k) asm volatile("" : "+s"(t.ad[k]));
+    t.m.j0 = (tile - pm.first_tile) * tb.tile_elems;
+    t.m.pos = pm.pos0 + t.m.j0;
+    t.m.blen = pm.blen;
+    const int64_t left = pm.numel - t.m.j0;
+    t.m.count = (uint32_t)(left < tb.tile_elems ? left : tb.tile_elems);
+    t.m.vec = pm.vec;
+    t.m.ring = rec.ring;
     return t;
 }
 
-// Tiles ahead of a block whose table entry it fetches into L2 (a multiple
-// of 8, so the later block runs on the same XCD: blocks are dealt to the
-// XCDs round-robin).
+// Tiles ahead of a block whose record it fetches into L2 (a multiple of 8,
+// so the later block runs on the same XCD: blocks are dealt to the XCDs
+// round-robin).
 constexpr int64_t kPsPrefetch = 1024;
 
-// From eight ranks up, each block fetches the two ends of entry tile +
-// kPsPrefetch (an entry may span two 128-byte lines; lanes 0 and 1 load
-// them), so that block's scalar entry loads find it in L2 rather than HBM.
-// The value is unused; consume() keeps it live until a point where the wave
-// waits for its data loads anyway, so that the load has completed before its
-// register is reused.
+// From eight ranks up, each block fetches the record of tile +
+// kPsPrefetch, so that block's scalar record load finds it in L2 rather than
+// HBM (parameter entries are few and stay in L2).  Every lane loads one of
+// its two words (lane & 1), with no branch on the lane: a lane-dependent
+// address makes it one vector load, which the wave does not wait for here (a
+// uniform one would become a scalar load waited for at once).  The value is
+// unused; consume() keeps it live until a point where the wave waits for its
+// data loads anyway, so that the load has completed before its register is
+// reused.
 template <int NR>
-__device__ __forceinline__ uint32_t prefetch_entry(const char *table, int64_t stride, int64_t tile,
-                                                   int64_t n_entries)
+__device__ __forceinline__ uint32_t prefetch_record(const PsTable &tb, int64_t tile)
 {
     if constexpr (NR >= 8) {
-        if (tile + kPsPrefetch < n_entries) {
-            const char *f = table + (tile + kPsPrefetch) * stride +
-                            ((threadIdx.x & 1) ? stride - 4 : 0);
-            return ld_elem<uint32_t>(reinterpret_cast<uint64_t>(f), 0);
+        if (tile + kPsPrefetch < tb.n_tiles) {
+            const PsTile *f = tb.tiles + ps_record(tile + kPsPrefetch, tb.rstride);
+            return ld_elem<uint32_t>(reinterpret_cast<uint64_t>(f), threadIdx.x & 1);
         }
     }
     return 0;
@@ -188,19 +247,17 @@ __device__ __forceinline__ void consume(uint32_t x) { asm volatile("" ::"v"(x));
 // kPsUnroll vector loads of the lane go out before the ring chunks are
 // looked at, as in the flat reduce.  A lane's vector past the tile's end
 // reads the tile's first vector and drops it; a tile without the vector
-// path reads 16 bytes of its own entry instead, and drops them (the loads
-// are not behind a branch).
+// path reads 16 bytes of its parameter entry instead, and drops them (the
+// loads are not behind a branch).
 template <int NR, bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
-params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block, int64_t n_entries,
-            float inv)
+params_fast(PsTable tb, int64_t first_block, float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     const int64_t tile = first_block + blockIdx.x;
-    const char *e = table + tile * stride;
-    const uint32_t pf = prefetch_entry<NR>(table, stride, tile, n_entries);
-    const PsEntry<NR + kSyncExtra> t = ps_entry<NR + kSyncExtra>(e);
+    const uint32_t pf = prefetch_record<NR>(tb, tile);
+    const PsEntry<NR + kSyncExtra> t = ps_entry<NR + kSyncExtra>(tb, tile);
     const PsMeta &m = t.m;
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
@@ -209,10 +266,10 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
 #pragma unroll
     for (int u = 0; u < kPsUnroll; ++u) {
         i0[u] = ((int64_t)u * kThreads + threadIdx.x) * VEC;
-        const int64_t off = i0[u] + VEC <= cnt ? i0[u] * ISZ : 0;
+        const int64_t off = (m.j0 + (i0[u] + VEC <= cnt ? i0[u] : 0)) * ISZ;
 #pragma unroll
         for (int k = 0; k < NR; ++k)
-            v[u][k] = gld_stream(vec ? t.ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(e));
+            v[u][k] = gld_stream(vec ? t.ad[k] + (uint64_t)off : reinterpret_cast<uint64_t>(t.pe));
     }
     const PsSegs sg = ps_segs<RING>(m);
 #pragma unroll
@@ -221,7 +278,8 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
         const bool in_b = RING && vec && i0[u] >= sg.b_lo && i0[u] + VEC <= sg.b_hi;
         if (in_a || in_b) {
             if constexpr (NR == 1 && IN == OUT) {
-                st_at<std::conditional_t<IN == kF32, float, uint16_t>>(t.ad[1], i0[u], v[u][0]);
+                st_at<std::conditional_t<IN == kF32, float, uint16_t>>(t.ad[1], m.j0 + i0[u],
+                                                                       v[u][0]);
             } else {
                 float acc[VEC];
                 if (!RING)
@@ -229,28 +287,37 @@ params_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
                 else
                     fold_ring<NR, IN>(v[u], in_a ? sg.sa : sg.sb, acc);
                 consume(pf);
-                store_vec<IN, OUT>(t.ad[NR], i0[u], acc, inv);
+                store_vec<IN, OUT>(t.ad[NR], m.j0 + i0[u], acc, inv);
             }
         } else {
             consume(pf);
             if (i0[u] < cnt)
-                params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(e), NR, m, inv,
+                params_elems<IN, OUT, RING>(reinterpret_cast<const uint64_t *>(t.pe), NR, m, inv,
                                             i0[u], VEC);
         }
     }
 }
 
 // Sync, any N up to DDP_MAX_RANKS: one pass per ring chunk the wave's lanes
-// meet, folded with fold_looped from the entry's addresses.
+// meet, folded with fold_looped from the parameter entry's addresses.
 template <bool RING, int IN, int OUT>
 __global__ void __launch_bounds__(kThreads)
-params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first_block, float inv)
+params_many(PsTable tb, int N, int64_t first_block, float inv)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
-    const char *e = table + (first_block + blockIdx.x) * stride;
-    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
-    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + kSyncExtra));
+    const int64_t tile = first_block + blockIdx.x;
+    const PsTile rec = tb.tiles[ps_record(tile, tb.rstride)];
+    const char *pe = tb.params + (int64_t)rec.param * tb.pstride;
+    const uint64_t *a = reinterpret_cast<const uint64_t *>(pe);
+    const PsParamMeta pm = *reinterpret_cast<const PsParamMeta *>(pe + 8 * (N + kSyncExtra));
+    PsMeta m;
+    m.j0 = (tile - pm.first_tile) * tb.tile_elems;
+    m.pos = pm.pos0 + m.j0;
+    m.blen = pm.blen;
+    m.count = (uint32_t)min(pm.numel - m.j0, tb.tile_elems);
+    m.vec = pm.vec;
+    m.ring = rec.ring;
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     const PsSegs sg = ps_segs<RING>(m);
@@ -264,8 +331,10 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
             const bool mine = pass == 0 ? in_a : in_b;
             if (!__builtin_amdgcn_ballot_w64(mine)) continue;   // no lane of the wave here
             float acc[VEC];
-            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, acc);
-            if (mine) store_vec<IN, OUT>(a[N], i0, acc, inv);
+            // lanes not taking part re-read the tile's first vector
+            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, (m.j0 + (mine ? i0 : 0)) * ISZ,
+                                  acc);
+            if (mine) store_vec<IN, OUT>(a[N], m.j0 + i0, acc, inv);
         }
         if (!in_a && !in_b && i0 < cnt) params_elems<IN, OUT, RING>(a, N, m, inv, i0, VEC);
     }
@@ -278,19 +347,17 @@ params_many(const char *__restrict__ table, int64_t stride, int N, int64_t first
 // elements) moves two.
 template <int NR, bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
-params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_block,
-                int64_t n_entries, float inv, float lr, float mu)
+params_sgd_fast(PsTable tb, int64_t first_block, float inv, float lr, float mu)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
     const int64_t tile = first_block + blockIdx.x;
-    const char *e = table + tile * stride;
-    const uint32_t pf = prefetch_entry<NR>(table, stride, tile, n_entries);
-    const PsEntry<NR + kSgdExtra> t = ps_entry<NR + kSgdExtra>(e);
+    const uint32_t pf = prefetch_record<NR>(tb, tile);
+    const PsEntry<NR + kSgdExtra> t = ps_entry<NR + kSgdExtra>(tb, tile);
     const PsMeta &m = t.m;
     const uint64_t gout = t.ad[NR], param = t.ad[NR + 1], mom = t.ad[NR + 2];
-    const uint64_t dummy = reinterpret_cast<uint64_t>(e);
+    const uint64_t dummy = reinterpret_cast<uint64_t>(t.pe);
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     int64_t i0[kPsUnroll];
@@ -298,14 +365,14 @@ params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_bl
 #pragma unroll
     for (int u = 0; u < kPsUnroll; ++u) {
         i0[u] = ((int64_t)u * kThreads + threadIdx.x) * VEC;
-        const bool whole = i0[u] + VEC <= cnt;
-        const int64_t go = whole ? i0[u] * ISZ : 0, po = whole ? i0[u] * 4 : 0;
+        const int64_t j = m.j0 + (i0[u] + VEC <= cnt ? i0[u] : 0);
+        const int64_t go = j * ISZ, po = j * 4;
 #pragma unroll
         for (int k = 0; k < NR; ++k) v[u][k] = gld_stream(vec ? t.ad[k] + (uint64_t)go : dummy);
 #pragma unroll
-        for (int j = 0; j < PV; ++j) {
-            pv[u][j] = gld_stream(vec ? param + (uint64_t)(po + 16 * j) : dummy);
-            if (MOM) mv[u][j] = gld_stream(vec ? mom + (uint64_t)(po + 16 * j) : dummy);
+        for (int q = 0; q < PV; ++q) {
+            pv[u][q] = gld_stream(vec ? param + (uint64_t)(po + 16 * q) : dummy);
+            if (MOM) mv[u][q] = gld_stream(vec ? mom + (uint64_t)(po + 16 * q) : dummy);
         }
     }
     const PsSegs sg = ps_segs<RING>(m);
@@ -324,12 +391,12 @@ params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_bl
                 for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
             }
             consume(pf);
-            sgd_vec<IN, OUT, MOM>(gout, param, mom, i0[u], y, pv[u], mv[u], lr, mu);
+            sgd_vec<IN, OUT, MOM>(gout, param, mom, m.j0 + i0[u], y, pv[u], mv[u], lr, mu);
         } else {
             consume(pf);
             if (i0[u] < cnt)
-                params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(e), NR, m,
-                                                     inv, lr, mu, i0[u], VEC);
+                params_sgd_elems<IN, OUT, RING, MOM>(reinterpret_cast<const uint64_t *>(t.pe), NR,
+                                                     m, inv, lr, mu, i0[u], VEC);
         }
     }
 }
@@ -338,15 +405,23 @@ params_sgd_fast(const char *__restrict__ table, int64_t stride, int64_t first_bl
 // vectors first, then the ranks folded as in params_many.
 template <bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
-params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t first_block,
-                float inv, float lr, float mu)
+params_sgd_many(PsTable tb, int N, int64_t first_block, float inv, float lr, float mu)
 {
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
-    const char *e = table + (first_block + blockIdx.x) * stride;
-    const uint64_t *a = reinterpret_cast<const uint64_t *>(e);
-    const PsMeta m = *reinterpret_cast<const PsMeta *>(e + 8 * (N + kSgdExtra));
+    const int64_t tile = first_block + blockIdx.x;
+    const PsTile rec = tb.tiles[ps_record(tile, tb.rstride)];
+    const char *pe = tb.params + (int64_t)rec.param * tb.pstride;
+    const uint64_t *a = reinterpret_cast<const uint64_t *>(pe);
+    const PsParamMeta pm = *reinterpret_cast<const PsParamMeta *>(pe + 8 * (N + kSgdExtra));
+    PsMeta m;
+    m.j0 = (tile - pm.first_tile) * tb.tile_elems;
+    m.pos = pm.pos0 + m.j0;
+    m.blen = pm.blen;
+    m.count = (uint32_t)min(pm.numel - m.j0, tb.tile_elems);
+    m.vec = pm.vec;
+    m.ring = rec.ring;
     const uint64_t gout = a[N], param = a[N + 1], mom = a[N + 2];
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
@@ -358,11 +433,11 @@ params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t f
         const bool in_b = RING && vec && i0 >= sg.b_lo && i0 + VEC <= sg.b_hi;
         u32x4 pv[PV], mv[PV];
         if (vec) {   // a lane past the end reads the tile's first vectors and drops them
-            const int64_t po = i0 + VEC <= cnt ? i0 * 4 : 0;
+            const int64_t po = (m.j0 + (i0 + VEC <= cnt ? i0 : 0)) * 4;
 #pragma unroll
-            for (int j = 0; j < PV; ++j) {
-                pv[j] = gld_stream(param + (uint64_t)(po + 16 * j));
-                if (MOM) mv[j] = gld_stream(mom + (uint64_t)(po + 16 * j));
+            for (int q = 0; q < PV; ++q) {
+                pv[q] = gld_stream(param + (uint64_t)(po + 16 * q));
+                if (MOM) mv[q] = gld_stream(mom + (uint64_t)(po + 16 * q));
             }
         }
 #pragma unroll 1
@@ -370,11 +445,12 @@ params_sgd_many(const char *__restrict__ table, int64_t stride, int N, int64_t f
             const bool mine = pass == 0 ? in_a : in_b;
             if (!__builtin_amdgcn_ballot_w64(mine)) continue;
             float y[VEC];
-            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, mine ? i0 * ISZ : 0, y);
+            fold_looped<IN, RING>(a, N, pass == 0 ? sg.sa : sg.sb, (m.j0 + (mine ? i0 : 0)) * ISZ,
+                                  y);
             if (mine) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) y[k] = y[k] * inv;
-                sgd_vec<IN, OUT, MOM>(gout, param, mom, i0, y, pv, mv, lr, mu);
+                sgd_vec<IN, OUT, MOM>(gout, param, mom, m.j0 + i0, y, pv, mv, lr, mu);
             }
         }
         if (!in_a && !in_b && i0 < cnt)
@@ -387,13 +463,25 @@ struct TileRange {
     int64_t first, count;
 };
 
+// The table of a sync as the kernels take it.
+PsTable ps_table(const ddp_param_sync *ps)
+{
+    PsTable tb;
+    tb.tiles = reinterpret_cast<const PsTile *>(ps->table);
+    tb.params = ps->table + ps->params_offset;
+    tb.rstride = ps->rstride;
+    tb.pstride = ps->pstride;
+    tb.n_tiles = ps->n_tiles;
+    tb.tile_elems = ps_tile_elems(ps->in);
+    return tb;
+}
+
 template <bool RING, int IN, int OUT>
 ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream_t st)
 {
     const int N = ps->n_ranks;
     const float inv = 1.0f / (float)N;
-    const char *tb = ps->table;
-    const int64_t sd = ps->stride;
+    const PsTable tb = ps_table(ps);
     const unsigned lds = lds_for_blocks(params_blocks_per_cu(N, RING));
     const dim3 b(kThreads);
     return launch_split(tr.count, kThreads, "parameter sync kernel launch",
@@ -401,10 +489,9 @@ ddp_status_t launch_sync_typed(const ddp_param_sync *ps, TileRange tr, hipStream
         const dim3 g(n);
         const int64_t b0 = tr.first + i;
         const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
-            params_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, b0,
-                                                                            ps->n_tiles, inv);
+            params_fast<decltype(nr)::value, RING, IN, OUT><<<g, b, lds, st>>>(tb, b0, inv);
         });
-        if (!fixed) params_many<RING, IN, OUT><<<g, b, lds, st>>>(tb, sd, N, b0, inv);
+        if (!fixed) params_many<RING, IN, OUT><<<g, b, lds, st>>>(tb, N, b0, inv);
     });
 }
 
@@ -414,8 +501,7 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, TileRange tr, float lr, 
 {
     const int N = ps->n_ranks;
     const float inv = 1.0f / (float)N;
-    const char *tb = ps->table;
-    const int64_t sd = ps->stride;
+    const PsTable tb = ps_table(ps);
     const unsigned lds = lds_for_blocks(params_sgd_blocks_per_cu(N, MOM));
     const dim3 b(kThreads);
     return launch_split(tr.count, kThreads, "parameter SGD kernel launch",
@@ -424,9 +510,9 @@ ddp_status_t launch_sgd_typed(const ddp_param_sync *ps, TileRange tr, float lr, 
         const int64_t b0 = tr.first + i;
         const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
             params_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(
-                tb, sd, b0, ps->n_tiles, inv, lr, mu);
+                tb, b0, inv, lr, mu);
         });
-        if (!fixed) params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, sd, N, b0, inv, lr, mu);
+        if (!fixed) params_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(tb, N, b0, inv, lr, mu);
     });
 }
 
@@ -501,8 +587,8 @@ ddp_status_t check_param_alias(const ddp_plan *plan, const ddp_binding_t *const 
 }
 
 // The ring chunks met by bucket positions [t0, t0 + count) of a bucket of
-// blen elements over N ranks: the entry's starts and cuts words.
-void ring_words(int64_t t0, int64_t count, int64_t blen, int N, uint32_t *starts, uint32_t *cuts)
+// blen elements over N ranks, as a record's ring word.
+uint32_t ring_word(int64_t t0, int64_t count, int64_t blen, int N)
 {
     const int64_t C = (blen + N - 1) / N, t1 = t0 + count;
     const int64_t ca = t0 / C, a_end = std::min((ca + 1) * C, blen);
@@ -512,8 +598,7 @@ void ring_words(int64_t t0, int64_t count, int64_t blen, int N, uint32_t *starts
         cut_b = (uint32_t)(std::min(std::min((ca + 2) * C, blen), t1) - t0);
         sb = (uint32_t)((ca + 2) % N);
     }
-    *starts = (uint32_t)((ca + 1) % N) | sb << 6;
-    *cuts = cut_a | cut_b << 16;
+    return (uint32_t)((ca + 1) % N) | sb << 6 | cut_a << 12 | cut_b << 22;
 }
 
 // Validates the bindings and builds the device table of a per-parameter
@@ -544,10 +629,15 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
     ddp_status_t st = check_param_alias(plan, R, n_ranks, isz, w, nw);
     if (st != DDP_OK) return st;
 
-    const int64_t T = ps_tile_elems(in), stride = ps_stride(n_ranks, nw);
-    int64_t n_tiles = 0;
-    for (int32_t p = 0; p < plan->n_params; ++p) n_tiles += (plan->numel[p] + T - 1) / T;
-    if (n_tiles > INT64_MAX / stride) return DDP_ERR_OVERFLOW;
+    const int64_t T = ps_tile_elems(in), pstride = ps_pstride(n_ranks, nw);
+    int64_t n_tiles = 0, n_entries = 0;
+    for (int32_t p = 0; p < plan->n_params; ++p) {
+        n_tiles += (plan->numel[p] + T - 1) / T;
+        n_entries += plan->numel[p] > 0 ? 1 : 0;
+    }
+    if (n_tiles > (int64_t)UINT32_MAX * kXcds) return DDP_ERR_OVERFLOW;
+    const int64_t rstride = word_stride(n_tiles);
+    const int64_t rec_bytes = (kXcds * rstride * (int64_t)sizeof(PsTile) + 255) / 256 * 256;
     ddp_param_sync *ps = new (std::nothrow) ddp_param_sync();
     if (!ps) return DDP_ERR_NOMEM;
     ps->device = dev;
@@ -558,82 +648,69 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
     ps->sgd = sgd;
     ps->momentum = sgd && w[2].bd != nullptr;
     ps->n_tiles = n_tiles;
-    ps->stride = stride;
+    ps->rstride = rstride;
+    ps->pstride = pstride;
+    ps->params_offset = rec_bytes;
+    std::vector<PsTile> recs;
+    std::vector<char> ents;
     try {
         ps->bucket_tile.assign((size_t)plan->n_buckets() + 1, 0);
+        recs.assign((size_t)(kXcds * rstride), PsTile{0u, 0u});
+        ents.assign((size_t)(n_entries * pstride), 0);
     } catch (...) {
         delete ps;
         return DDP_ERR_NOMEM;
     }
-    for (int32_t b = 0; b < plan->n_buckets(); ++b) {
-        int64_t t = 0;
-        for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s)
-            t += (plan->numel[plan->slot_param[s]] + T - 1) / T;
-        ps->bucket_tile[b + 1] = ps->bucket_tile[b] + t;
-    }
-    if (n_tiles == 0) {
-        *out = ps;
-        return DDP_OK;
-    }
-    if ((he = hipMalloc(&ps->table, (size_t)(n_tiles * stride))) != hipSuccess) {
-        delete ps;
-        return hip_fail("hipMalloc (parameter tiles)", he, DDP_ERR_NOMEM);
-    }
-    // Entries in flat order, built and uploaded in pieces of at most 64 MiB.
-    const int64_t per_chunk = std::max<int64_t>(1, (64 << 20) / stride);
-    std::vector<char> host;
-    try {
-        host.assign((size_t)(std::min(per_chunk, n_tiles) * stride), 0);
-    } catch (...) {
-        ddp_param_sync_free(ps);
-        return DDP_ERR_NOMEM;
-    }
-    int64_t done = 0, fill = 0;
-    auto flush = [&]() -> ddp_status_t {
-        const hipError_t e = hipMemcpy(ps->table + done * stride, host.data(),
-                                       (size_t)(fill * stride), hipMemcpyHostToDevice);
-        if (e != hipSuccess) return hip_fail("hipMemcpy (parameter tiles)", e);
-        done += fill;
-        fill = 0;
-        std::memset(host.data(), 0, host.size());
-        return DDP_OK;
-    };
+    // Parameter entries in flat order; each parameter's tiles are consecutive.
     const bool ring = order == DDP_ORDER_RING && n_ranks > 1;
+    int64_t t = 0, q = 0;
     for (int32_t b = 0; b < plan->n_buckets(); ++b) {
         const int64_t blen = plan->bucket_base[b + 1] - plan->bucket_base[b];
         for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
             const int32_t p = plan->slot_param[s];
             const int64_t n = plan->numel[p];
+            if (n == 0) continue;
+            char *ent = ents.data() + q * pstride;
+            uint64_t *addr = reinterpret_cast<uint64_t *>(ent);
+            for (int r = 0; r < n_ranks; ++r) addr[r] = R[r]->param_addr[p];
             // the vector path stores 16-byte vectors to the written tensors;
             // the gradients are read at whatever element alignment they have
             bool vec = true;
-            for (int k = 0; k < nw; ++k) vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 16 == 0);
-            for (int64_t j0 = 0; j0 < n; j0 += T) {
-                char *ent = host.data() + fill * stride;
-                uint64_t *addr = reinterpret_cast<uint64_t *>(ent);
-                for (int r = 0; r < n_ranks; ++r)
-                    addr[r] = R[r]->param_addr[p] + (uint64_t)(j0 * isz);
-                for (int k = 0; k < nw; ++k)
-                    addr[n_ranks + k] =
-                        w[k].bd ? w[k].bd->param_addr[p] + (uint64_t)(j0 * w[k].esz) : 0;
-                PsMeta m;
-                std::memset(&m, 0, sizeof(m));
-                m.pos = plan->param_offset[p] + j0;
-                m.blen = blen;
-                m.count = (uint32_t)std::min(T, n - j0);
-                m.vec = vec ? 1u : 0u;
-                if (ring) ring_words(m.pos, m.count, blen, n_ranks, &m.starts, &m.cuts);
-                std::memcpy(ent + 8 * (n_ranks + nw), &m, sizeof(m));
-                if (++fill == per_chunk && (st = flush()) != DDP_OK) {
-                    ddp_param_sync_free(ps);
-                    return st;
-                }
+            for (int k = 0; k < nw; ++k) {
+                addr[n_ranks + k] = w[k].bd ? w[k].bd->param_addr[p] : 0;
+                vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 16 == 0);
             }
+            PsParamMeta pm;
+            std::memset(&pm, 0, sizeof(pm));
+            pm.pos0 = plan->param_offset[p];
+            pm.blen = blen;
+            pm.first_tile = t;
+            pm.numel = n;
+            pm.vec = vec ? 1u : 0u;
+            std::memcpy(ent + 8 * (n_ranks + nw), &pm, sizeof(pm));
+            for (int64_t j0 = 0; j0 < n; j0 += T, ++t)
+                recs[(size_t)ps_record(t, rstride)] =
+                    PsTile{(uint32_t)q, ring ? ring_word(pm.pos0 + j0, std::min(T, n - j0), blen,
+                                                         n_ranks)
+                                             : 0u};
+            ++q;
         }
+        ps->bucket_tile[b + 1] = t;
     }
-    if (fill > 0 && (st = flush()) != DDP_OK) {
+    if (n_tiles == 0) {
+        *out = ps;
+        return DDP_OK;
+    }
+    if ((he = hipMalloc(&ps->table, (size_t)(rec_bytes + n_entries * pstride))) != hipSuccess) {
+        delete ps;
+        return hip_fail("hipMalloc (parameter tiles)", he, DDP_ERR_NOMEM);
+    }
+    if ((he = hipMemcpy(ps->table, recs.data(), recs.size() * sizeof(PsTile),
+                        hipMemcpyHostToDevice)) != hipSuccess ||
+        (he = hipMemcpy(ps->table + rec_bytes, ents.data(), ents.size(),
+                        hipMemcpyHostToDevice)) != hipSuccess) {
         ddp_param_sync_free(ps);
-        return st;
+        return hip_fail("hipMemcpy (parameter tiles)", he);
     }
     *out = ps;
     return DDP_OK;

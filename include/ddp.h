@@ -308,10 +308,11 @@ DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *ra
  *                      outputs may not overlap each other
  *   order, out_dtype   as ddp_sync_allreduce_avg (N == 1: the input, bit
  *                      for bit, and out_dtype must equal the plan's dtype)
- * It uploads a table with one entry per tile of each parameter (256 f32 or
- * 512 bf16 elements): 8 * (n_ranks + 1) + 32 bytes rounded up to 16 (112
- * for 8 ranks, 1.2 % of the 9 KiB such a tile reads and writes), held until
- * ddp_param_sync_free.  The bindings' addresses are copied into it: bind
+ * It uploads a table, held until ddp_param_sync_free: an 8-byte record per
+ * tile of each parameter (256 f32 or 512 bf16 elements; 0.09 % of the 9 KiB
+ * an f32 tile of 8 ranks reads and writes) and, per parameter with elements,
+ * its n_ranks + 1 addresses and 40 bytes of position, rounded up to 16
+ * bytes (Llama-7B, 8 ranks: 105 MB in all).  The bindings' addresses are copied into it: bind
  * again if a gradient moves.  Parameters whose written tensors (outputs;
  * parameters, momentum and stored average of the SGD step) sit on 16-byte
  * boundaries take the vector path, reading the gradients at any element
@@ -352,7 +353,8 @@ DDP_API ddp_status_t ddp_param_sync_run_buckets(const ddp_param_sync_t *sync, in
  *   momentum   binding of f32 momentum buffers (start from zeros), updated
  *              in place, or NULL for plain SGD
  * params and momentum may overlap no other tensor (DDP_ERR_ALIAS).  The
- * table holds 8 * (n_ranks + 3) + 32 bytes per tile, rounded up to 16.
+ * table holds 8 bytes per tile and 8 * (n_ranks + 3) + 40 bytes per
+ * parameter, rounded up to 16.
  * ddp_param_sgd_run enqueues one step with learning rate lr and momentum
  * factor mu; it allocates nothing.  A sync made by one create function is
  * refused by the other's run function (DDP_ERR_INVALID_ARG).
