@@ -220,7 +220,7 @@ __device__ __forceinline__ PsEntry<NA> ps_entry(const PsTable &tb, int64_t tile)
 // round-robin).
 constexpr int64_t kPsPrefetch = 1024;
 
-// From eight ranks up, each block fetches the record of tile +
+// From four ranks up, each block fetches the record of tile +
 // kPsPrefetch, so that block's scalar record load finds it in L2 rather than
 // HBM (parameter entries are few and stay in L2).  Every lane loads one of
 // its two words (lane & 1), with no branch on the lane: a lane-dependent
@@ -232,7 +232,7 @@ constexpr int64_t kPsPrefetch = 1024;
 template <int NR>
 __device__ __forceinline__ uint32_t prefetch_record(const PsTable &tb, int64_t tile)
 {
-    if constexpr (NR >= 8) {
+    if constexpr (NR >= 4) {
         if (tile + kPsPrefetch < tb.n_tiles) {
             const PsTile *f = tb.tiles + ps_record(tile + kPsPrefetch, tb.rstride);
             return ld_elem<uint32_t>(reinterpret_cast<uint64_t>(f), threadIdx.x & 1);
