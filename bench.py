@@ -26,8 +26,9 @@ first K of them timed as "without_ramp"), W warm-up syncs, K timed syncs
   other_orders   the other summation order
   cpu_baseline   the CPU oracle on all host cores and on one, with parity
 and for ResNet-50 only (--extras): per_bucket, copy_path, fused_sgd,
-overlap, rank_sweep_GBps, in_place, no_sync, small_means; for tiny the
-latency of a sync (Python call, prepared call, graph replay).
+overlap, rank_sweep_GBps, in_place, no_sync, small_means; for many-small
+copy_path; for tiny the latency of a sync (Python call, prepared call, graph
+replay).
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
 
@@ -694,6 +695,42 @@ def rank_grads(c):
     return grads
 
 
+def copy_ceiling(c):
+    """A plain copy of one rank buffer (the bytes one flatten or unflatten
+    launch moves), one launch per rank back to back, through the probe's
+    one-load-one-store pattern (non-temporal 16-byte accesses, one-wave
+    blocks): the ceiling of a copy of this size on this machine, best over
+    resident-block caps."""
+    import ctypes
+    torch, N, wl = c.torch, c.N, c.wl
+    if wl.in_bytes != wl.out_bytes:
+        return None
+    probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
+    probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=c.dev)
+    nvec = c.P * wl.in_bytes // 16
+    srcs = [(ctypes.c_void_p * 1)(ctypes.c_void_p(f.data_ptr())) for f in c.flats]
+
+    def copies(k):
+        for src in srcs:
+            rc = probe.ddp_probe_stream(src, 1, ctypes.c_void_p(c.out.data_ptr()), nvec, 1, k,
+                                        ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(c.stream.cuda_stream))
+            assert rc == 0, "probe launch failed"
+
+    best = (0.0, 0)
+    for k in (0, 4, 5, 6, 7, 8):
+        ms = stream_ms(c, lambda: copies(k), 10, settle=True)
+        rate = 2 * N * nvec * 16 / (ms * 1e-3) / 1e9
+        best = max(best, (rate, k))
+    return {"GBps": round(best[0], 1), "blocks_per_cu": best[1],
+            "probe": f"{N} launches, each a plain copy of one rank buffer ({nvec * 16} B) with the "
+                     "one-load-one-store pattern, back to back; best over caps of 4..8 resident "
+                     "blocks per CU and none"}
+
+
 def leg_copy_path(c):
     """The copy layout: flatten every rank, sync, unflatten (timed step by
     step, as an eager loop and replayed from a HIP graph), and the same step
@@ -714,29 +751,32 @@ def leg_copy_path(c):
 
     for _ in range(5):
         full_step()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     reps = max(10, c.args.steps // 4)
-    tf = ts = tu = 0.0
-    for _ in range(reps):
-        e[0].record(c.stream)
+
+    def flatten_all():
         for r in range(N):
             ddp.flatten(plan, binds[r], c.flats[r], stream=c.stream)
-        e[1].record(c.stream)
-        c.sync()
-        e[2].record(c.stream)
+
+    def unflatten_one():
         ddp.unflatten(plan, rbind, c.out, stream=c.stream)
-        e[3].record(c.stream)
-        torch.cuda.synchronize()
-        tf += e[0].elapsed_time(e[1])
-        ts += e[1].elapsed_time(e[2])
-        tu += e[2].elapsed_time(e[3])
-    tf, ts, tu = tf / reps, ts / reps, tu / reps
+
+    # each step back to back, K times between one event pair, as the
+    # headline times the sync
+    tf = stream_ms(c, flatten_all, reps, settle=True)
+    ts = stream_ms(c, c.sync, reps, settle=True)
+    tu = stream_ms(c, unflatten_one, reps, settle=True)
     out = {"ms_per_step": round(tf + ts + tu, 4),
            "flatten_ms": round(tf, 4), "flatten_GBps": gbps(2 * N * c.P * wl.in_bytes, tf),
            "sync_ms": round(ts, 4),
            "unflatten_ms": round(tu, 4), "unflatten_GBps": gbps(2 * c.P * wl.out_bytes, tu),
            "metric_GBps": gbps(c.sync_bytes, tf + ts + tu),
-           "launches": N + 2}
+           "launches": N + 2,
+           "timing": "each step K times back to back between one event pair"}
+    ceil = copy_ceiling(c)
+    if ceil:
+        out["copy_ceiling"] = ceil
+        out["flatten_frac_of_copy_ceiling"] = round(out["flatten_GBps"] / ceil["GBps"], 4)
+        out["unflatten_frac_of_copy_ceiling"] = round(out["unflatten_GBps"] / ceil["GBps"], 4)
     # the same step captured once into a HIP graph and replayed
     graph = torch.cuda.CUDAGraph()
     cap_stream = torch.cuda.Stream()
@@ -827,15 +867,15 @@ def leg_overlap(c):
     mat_a = torch.randn(4096, 4096, device=c.dev, dtype=torch.bfloat16)
     mat_b = torch.randn(4096, 4096, device=c.dev, dtype=torch.bfloat16)
     comp, upd, tried = side_by_side_streams(torch)
-    deep_in = [f[db:db + dl] for f in c.flats]
-    deep_out = c.out[db:db + dl]
 
     def compute():
         with torch.cuda.stream(comp):
             torch.mm(mat_a, mat_b)
 
     def deep():
-        ddp.bucket_allreduce_avg(deep_in, deep_out, c.order, stream=upd)
+        # DEEP_COMM of the two-bucket plan (timing only: the cap plan's buffers
+        # are read at the bucket's place), with that plan's occupancy policy
+        ddp.sync_allreduce_avg_bucket(tb, 0, c.flats, c.out, c.order, stream=upd)
 
     def step_barrier():
         # a training step ends when both streams have: the next step's
@@ -871,15 +911,15 @@ def leg_overlap(c):
            "compute": "bf16 GEMM 4096^3 on a second stream",
            "streams": ("side by side (hardware queues checked; %d tried)" % tried
                        if tried else "not found side by side: results are serial")}
-    # under both occupancy policies: the tuned cap reserves LDS that the
-    # GEMM's blocks would need, "shared" leaves it free
+    # under both occupancy policies, set on the plan (the process-wide policy
+    # is not touched): the tuned cap reserves LDS that the GEMM's blocks would
+    # need, "shared" leaves it free
     for policy in ("tuned", "shared"):
-        ddp.set_occupancy(policy)
+        tb.set_occupancy(policy)
         t_deep = timed([deep])
         t_both = timed([compute, deep])
         res[policy] = {"deep_sync_ms": round(t_deep, 4), "overlapped_ms": round(t_both, 4),
                        **hidden(t_deep, t_comp, t_both)}
-    ddp.set_occupancy("tuned")
 
     # The bucket-by-bucket schedule of DDP ([DDP] 3.2, [TR24] 十一): bucket b
     # (cap plan, last layers first) is averaged on the update stream as soon
@@ -892,8 +932,9 @@ def leg_overlap(c):
     lhs = [torch.randn(4096, k, device=c.dev, dtype=torch.bfloat16) for k in ks]
     rhs = [torch.randn(k, 4096, device=c.dev, dtype=torch.bfloat16) for k in ks]
     ready = [torch.cuda.Event() for _ in buckets]
-    ins = [[f[base:base + ln] for f in c.flats] for ln, base, _, _ in buckets]
-    outs_b = [c.out[base:base + ln] for ln, base, _, _ in buckets]
+    # a plan object of its own for the overlapped syncs, so that its policy
+    # is theirs alone
+    sched_plan = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, wl.dtype)
 
     def backward():
         with torch.cuda.stream(comp):
@@ -905,7 +946,7 @@ def leg_overlap(c):
         for b in range(len(buckets)):
             if wait:
                 upd.wait_event(ready[b])
-            ddp.bucket_allreduce_avg(ins[b], outs_b[b], c.order, stream=upd)
+            ddp.sync_allreduce_avg_bucket(sched_plan, b, c.flats, c.out, c.order, stream=upd)
 
     # the same schedule on per-parameter gradients (as autograd leaves them):
     # bucket b of one ddp_param_sync per step, run when ready
@@ -925,14 +966,15 @@ def leg_overlap(c):
     sched = {"buckets": len(buckets), "backward_gflop": round(gflop, 1),
              "backward_ms": round(t_bwd, 4)}
     per_param = {"sync": "ddp_param_sync_run_buckets, one bucket per launch"}
-    for syncs, into in ((bucket_syncs, sched), (param_syncs, per_param)):
+    sched["sync"] = "ddp_sync_allreduce_avg_bucket, one bucket per launch"
+    for syncs, into, obj in ((bucket_syncs, sched, sched_plan), (param_syncs, per_param, pps)):
         for policy in ("tuned", "shared"):
-            ddp.set_occupancy(policy)
+            obj.set_occupancy(policy)
             t_syncs = timed([lambda: syncs(False)])
             t_sched = timed([backward, lambda: syncs(True)])
             into[policy] = {"syncs_ms": round(t_syncs, 4), "serial_ms": round(t_bwd + t_syncs, 4),
                             "overlapped_ms": round(t_sched, 4), **hidden(t_syncs, t_bwd, t_sched)}
-        ddp.set_occupancy("tuned")
+    assert ddp.get_occupancy() == "tuned"
     sched["per_parameter"] = per_param
     res["schedule"] = sched
     log(f"overlap: {res}")
@@ -1123,6 +1165,7 @@ def measure(args, cpu_seconds):
     sensors_after = hwmon_readings(torch)
     per_param = args.layout == "per-parameter"
     extras = (args.extras == "on") if args.extras else c.wl.name == "resnet50"
+    copy_only = args.extras is None and c.wl.name == "many_small"   # the copies of many tensors
     cold = leg_cold_mall(c)
     ceiling = None if per_param else leg_ceiling(c)
     other = leg_other_orders(c)
@@ -1136,6 +1179,8 @@ def measure(args, cpu_seconds):
                 "fused_sgd": leg_fused_sgd(c), "overlap": leg_overlap(c),
                 "rank_sweep_GBps": leg_rank_sweep(c), "in_place": leg_in_place(c),
                 "no_sync": leg_no_sync(c), "small_means": leg_small_means(c)}
+    elif copy_only and not per_param:
+        more = {"copy_path": leg_copy_path(c)}
     tiny = leg_tiny_latency(c)
 
     wl, P, np = c.wl, c.P, c.np

@@ -81,6 +81,12 @@ def _load():
         "ddp_plan_prepare_ranks": ([vp, ctypes.c_int32], ctypes.c_int),
         "ddp_set_occupancy": ([ctypes.c_int], ctypes.c_int),
         "ddp_get_occupancy": ([], ctypes.c_int),
+        "ddp_plan_set_occupancy": ([vp, ctypes.c_int], ctypes.c_int),
+        "ddp_plan_get_occupancy": ([vp], ctypes.c_int),
+        "ddp_param_sync_set_occupancy": ([vp, ctypes.c_int], ctypes.c_int),
+        "ddp_param_sync_get_occupancy": ([vp], ctypes.c_int),
+        "ddp_sync_allreduce_avg_bucket": ([vp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.c_int32,
+                                           ctypes.c_int, ctypes.c_int, vp, vp], ctypes.c_int),
         "ddp_bind_params": ([vp, ctypes.POINTER(vp), vp, ctypes.POINTER(vp)], ctypes.c_int),
         "ddp_binding_free": ([vp], None),
         "ddp_flatten": ([vp, vp, ctypes.c_int32, vp, ctypes.c_int, vp], ctypes.c_int),
@@ -209,6 +215,14 @@ class Plan:
             out.append([self.slot_param(s) for s in range(fs, fs + ns)])
         return out
 
+    def set_occupancy(self, policy):
+        """This plan's occupancy policy for the calls that take it:
+        "tuned", "shared" or "default" (follow the process-wide one)."""
+        _check(lib.ddp_plan_set_occupancy(self._h, _OCCUPANCY[policy]), "ddp_plan_set_occupancy")
+
+    def get_occupancy(self) -> str:
+        return _OCCUPANCY_NAME[lib.ddp_plan_get_occupancy(self._h)]
+
     def prepare(self, n_ranks: Optional[int] = None):
         """Upload the plan's device tables now (``ddp_plan_prepare``), and with
         ``n_ranks`` also the RING table for that rank count
@@ -307,6 +321,14 @@ class ParamSync:
                                                   _stream_handle(stream)),
                    "ddp_param_sync_run_buckets")
 
+    def set_occupancy(self, policy):
+        """This sync's occupancy policy: "tuned", "shared" or "default"."""
+        _check(lib.ddp_param_sync_set_occupancy(self._h, _OCCUPANCY[policy]),
+               "ddp_param_sync_set_occupancy")
+
+    def get_occupancy(self) -> str:
+        return _OCCUPANCY_NAME[lib.ddp_param_sync_get_occupancy(self._h)]
+
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None
         if h and lib is not None:
@@ -366,6 +388,14 @@ class ParamSGD:
             _check(lib.ddp_param_sgd_run_buckets(self._h, int(buckets[0]), int(buckets[1]), lr,
                                                  momentum, _stream_handle(stream)),
                    "ddp_param_sgd_run_buckets")
+
+    def set_occupancy(self, policy):
+        """This sync's occupancy policy: "tuned", "shared" or "default"."""
+        _check(lib.ddp_param_sync_set_occupancy(self._h, _OCCUPANCY[policy]),
+               "ddp_param_sync_set_occupancy")
+
+    def get_occupancy(self) -> str:
+        return _OCCUPANCY_NAME[lib.ddp_param_sync_get_occupancy(self._h)]
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None
@@ -447,6 +477,23 @@ def sync_allreduce_avg_noalloc(plan: Plan, rank_flats: Sequence, out_flat, order
                                               _dtype_code(out_flat), _dev_ptr(out_flat),
                                               _stream_handle(stream)),
            "ddp_sync_allreduce_avg_noalloc")
+
+
+def sync_allreduce_avg_bucket(plan: Plan, bucket: int, rank_flats: Sequence, out_flat,
+                              order="ring", stream=None):
+    """Average bucket ``bucket`` of the plan's flat buffers on its own, with the
+    plan's occupancy policy (``ddp_sync_allreduce_avg_bucket``)."""
+    total = plan.total
+    for t in rank_flats:
+        if _dtype_code(t) != plan.dtype or t.numel() < total:
+            raise ValueError("rank flat buffers differ from the plan's dtype or size")
+    if out_flat.numel() < total:
+        raise ValueError("output too short")
+    ptrs = _ptr_array([_dev_ptr(t) for t in rank_flats])
+    _check(lib.ddp_sync_allreduce_avg_bucket(plan.handle, int(bucket), ptrs, len(rank_flats),
+                                             _ORDERS[order], _dtype_code(out_flat),
+                                             _dev_ptr(out_flat), _stream_handle(stream)),
+           "ddp_sync_allreduce_avg_bucket")
 
 
 class _PreparedSync:
@@ -534,15 +581,21 @@ def abi_version() -> int:
 
 OCCUPANCY_TUNED = 0
 OCCUPANCY_SHARED = 1
-_OCCUPANCY = {"tuned": OCCUPANCY_TUNED, "shared": OCCUPANCY_SHARED,
-              OCCUPANCY_TUNED: OCCUPANCY_TUNED, OCCUPANCY_SHARED: OCCUPANCY_SHARED}
+OCCUPANCY_DEFAULT = 2
+_OCCUPANCY = {"tuned": OCCUPANCY_TUNED, "shared": OCCUPANCY_SHARED, "default": OCCUPANCY_DEFAULT,
+              OCCUPANCY_TUNED: OCCUPANCY_TUNED, OCCUPANCY_SHARED: OCCUPANCY_SHARED,
+              OCCUPANCY_DEFAULT: OCCUPANCY_DEFAULT}
+_OCCUPANCY_NAME = {OCCUPANCY_TUNED: "tuned", OCCUPANCY_SHARED: "shared",
+                   OCCUPANCY_DEFAULT: "default"}
 
 
 def set_occupancy(policy) -> None:
     """``"tuned"`` (default): the streaming kernels run at their measured best
     number of resident blocks per CU; ``"shared"``: no cap, for syncs that
-    overlap compute on other streams (``ddp_set_occupancy``).  Process-wide."""
-    if policy not in _OCCUPANCY:
+    overlap compute on other streams (``ddp_set_occupancy``).  Process-wide:
+    the policy of calls without an object and of objects left at "default"
+    (see Plan.set_occupancy, ParamSync.set_occupancy)."""
+    if policy not in ("tuned", "shared", OCCUPANCY_TUNED, OCCUPANCY_SHARED):
         raise ValueError(f"unknown occupancy policy {policy!r}")
     _check(lib.ddp_set_occupancy(_OCCUPANCY[policy]), "ddp_set_occupancy")
 

@@ -99,15 +99,32 @@ int params_sgd_blocks_per_cu(int N, bool mom)
 
 constexpr int kMaxDevices = 64;
 
-// DDP_OCCUPANCY_TUNED or DDP_OCCUPANCY_SHARED, process-wide.
+// DDP_OCCUPANCY_TUNED or DDP_OCCUPANCY_SHARED, process-wide: the policy of
+// calls made without an object that has its own.
 std::atomic<int> g_occupancy{DDP_OCCUPANCY_TUNED};
+
+// The policy of the object (plan or per-parameter sync) whose entry point
+// this thread is in, or -1.
+thread_local int tl_occupancy = -1;
+
+OccupancyScope::OccupancyScope(int policy) : prev_(tl_occupancy)
+{
+    if (policy == DDP_OCCUPANCY_TUNED || policy == DDP_OCCUPANCY_SHARED) tl_occupancy = policy;
+}
+
+OccupancyScope::~OccupancyScope() { tl_occupancy = prev_; }
+
+int current_occupancy()
+{
+    return tl_occupancy >= 0 ? tl_occupancy : g_occupancy.load(std::memory_order_relaxed);
+}
 
 // Dynamic LDS bytes that leave room for k blocks per CU on the current device
 // (none under DDP_OCCUPANCY_SHARED).
 unsigned lds_for_blocks(int k)
 {
     static std::atomic<int> lds_per_cu[kMaxDevices];   // 0: not queried yet, -1: unknown
-    if (k <= 0 || g_occupancy.load(std::memory_order_relaxed) != DDP_OCCUPANCY_TUNED) return 0;
+    if (k <= 0 || current_occupancy() != DDP_OCCUPANCY_TUNED) return 0;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     int v = lds_per_cu[dev].load(std::memory_order_relaxed);

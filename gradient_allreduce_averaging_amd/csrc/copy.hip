@@ -171,6 +171,7 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t first = bucket < 0 ? 0 : bd->bucket_first_unit[bucket];
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
+    const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
     // Every XCD gets the same number of units (the last round padded).  A
     // launch takes at most max_launch_items() work-items: a multiple of 4096,
     // so of the kXcds * bpu blocks that one round of units spans.

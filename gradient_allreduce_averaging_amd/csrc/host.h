@@ -99,4 +99,20 @@ int params_sgd_blocks_per_cu(int N, bool mom);
 constexpr int kCopyBlocksPerCU = 7;   // flatten / unflatten (256-thread blocks)
 unsigned lds_for_blocks(int k);
 
+// The occupancy policy of the launches made while it lives on this thread:
+// an object's own (DDP_OCCUPANCY_TUNED or _SHARED), or, for
+// DDP_OCCUPANCY_DEFAULT, the process-wide one.  Entry points that take a
+// plan or a per-parameter sync open one with that object's policy.
+class OccupancyScope {
+public:
+    explicit OccupancyScope(int policy);
+    ~OccupancyScope();
+    OccupancyScope(const OccupancyScope &) = delete;
+    OccupancyScope &operator=(const OccupancyScope &) = delete;
+
+private:
+    int prev_;
+};
+int current_occupancy();
+
 }  // namespace ddp_detail

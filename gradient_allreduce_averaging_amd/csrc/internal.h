@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -32,6 +33,7 @@ struct ddp_plan {
 
     int32_t n_buckets() const { return (int32_t)bucket_base.size() - 1; }
 
+    std::atomic<int> occupancy{DDP_OCCUPANCY_DEFAULT};   // of the launches over this plan
     std::mutex mu;                            // guards dev and ring_desc
     std::map<std::pair<int, int64_t>, ddp_dev_tables> dev;   // (device, tile elements)
     // (device, tile elements, ranks): device array of one ring-segment word per tile
@@ -67,6 +69,7 @@ struct ddp_param_sync {
     int in = 0, out = 0;                      // ddp_dtype_t of inputs and outputs
     bool sgd = false;                         // built by ddp_param_sgd_create
     bool momentum = false;                    // sgd: with a momentum buffer
+    std::atomic<int> occupancy{DDP_OCCUPANCY_DEFAULT};   // of its launches
     char *table = nullptr;                    // device array: tile records, then parameter entries
     int64_t n_tiles = 0;
     int64_t rstride = 0;                      // tile records per XCD stripe

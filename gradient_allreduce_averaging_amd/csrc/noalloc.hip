@@ -129,6 +129,7 @@ ddp_status_t ddp_sync_allreduce_avg_noalloc(ddp_plan_t *plan, const void *const 
     int32_t *tile_bucket = reinterpret_cast<int32_t *>(sp + off_tb);
     uint32_t *words = reinterpret_cast<uint32_t *>(sp + off_w);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
 
     BaseBatch batch;
     for (int64_t first = 0; first <= nb; first += kBasesPerLaunch) {

@@ -741,6 +741,7 @@ ddp_status_t run_sync(const ddp_param_sync_t *ps, int32_t b0, int32_t nb, void *
     TileRange tr;
     const ddp_status_t s = check_run(ps, false, b0, nb, &tr);
     if (s != DDP_OK || tr.count == 0) return s;
+    const OccupancyScope occ(ps->occupancy.load(std::memory_order_relaxed));
     hipStream_t st = static_cast<hipStream_t>(stream);
     return ps->order == DDP_ORDER_RING && ps->n_ranks > 1 ? launch_sync<true>(ps, tr, st)
                                                           : launch_sync<false>(ps, tr, st);
@@ -752,6 +753,7 @@ ddp_status_t run_sgd(const ddp_param_sync_t *ps, int32_t b0, int32_t nb, float l
     TileRange tr;
     const ddp_status_t s = check_run(ps, true, b0, nb, &tr);
     if (s != DDP_OK || tr.count == 0) return s;
+    const OccupancyScope occ(ps->occupancy.load(std::memory_order_relaxed));
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool ring = ps->order == DDP_ORDER_RING && ps->n_ranks > 1;
     if (ring)
@@ -809,6 +811,21 @@ ddp_status_t ddp_param_sgd_run_buckets(const ddp_param_sync_t *ps, int32_t first
 {
     if (n_buckets < 0) return DDP_ERR_INVALID_ARG;
     return run_sgd(ps, first_bucket, n_buckets, lr, momentum, stream);
+}
+
+ddp_status_t ddp_param_sync_set_occupancy(ddp_param_sync_t *ps, ddp_occupancy_t policy)
+{
+    if (!ps || (policy != DDP_OCCUPANCY_TUNED && policy != DDP_OCCUPANCY_SHARED &&
+                policy != DDP_OCCUPANCY_DEFAULT))
+        return DDP_ERR_INVALID_ARG;
+    ps->occupancy.store(policy, std::memory_order_relaxed);
+    return DDP_OK;
+}
+
+ddp_occupancy_t ddp_param_sync_get_occupancy(const ddp_param_sync_t *ps)
+{
+    return ps ? static_cast<ddp_occupancy_t>(ps->occupancy.load(std::memory_order_relaxed))
+              : DDP_OCCUPANCY_DEFAULT;
 }
 
 void ddp_param_sync_free(ddp_param_sync_t *ps)

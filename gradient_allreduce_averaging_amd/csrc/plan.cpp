@@ -195,6 +195,21 @@ ddp_status_t ddp_plan_param(const ddp_plan_t *plan, int32_t p, int32_t *bucket,
     return DDP_OK;
 }
 
+ddp_status_t ddp_plan_set_occupancy(ddp_plan_t *plan, ddp_occupancy_t policy)
+{
+    if (!plan || (policy != DDP_OCCUPANCY_TUNED && policy != DDP_OCCUPANCY_SHARED &&
+                  policy != DDP_OCCUPANCY_DEFAULT))
+        return DDP_ERR_INVALID_ARG;
+    plan->occupancy.store(policy, std::memory_order_relaxed);
+    return DDP_OK;
+}
+
+ddp_occupancy_t ddp_plan_get_occupancy(const ddp_plan_t *plan)
+{
+    return plan ? static_cast<ddp_occupancy_t>(plan->occupancy.load(std::memory_order_relaxed))
+                : DDP_OCCUPANCY_DEFAULT;
+}
+
 const char *ddp_status_string(ddp_status_t status)
 {
     switch (status) {

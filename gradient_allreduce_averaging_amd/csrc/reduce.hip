@@ -1,6 +1,7 @@
 // The reduce and the fused average + SGD step: kernels, their launches,
 // the plan's device tables, and the entry points ddp_bucket_allreduce_avg,
-// ddp_sync_allreduce_avg, ddp_sync_sgd_update, ddp_plan_prepare[_ranks].
+// ddp_sync_allreduce_avg[_bucket], ddp_sync_sgd_update,
+// ddp_plan_prepare[_ranks].
 //
 // Pages: [DDP] "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel);
 //        [TR24] "(24) NCCL通信与分布式数据并行" (tech-renaissance.cn).
@@ -574,6 +575,7 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
     if (stc != DDP_OK) return stc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (total == 0) return DDP_OK;
+    const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
     if (n_ranks == 1) return copy_single(rank_flat[0], total, dtype_size(in), out_flat, st);
 
     RankArgs ra;
@@ -609,6 +611,32 @@ ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const *rank_fl
     return launch_reduce(ra, n_ranks, total, order, in, out_dtype, bk, out_flat, st, true);
 }
 
+ddp_status_t ddp_sync_allreduce_avg_bucket(ddp_plan_t *plan, int32_t bucket,
+                                           const void *const *rank_flat, int32_t n_ranks,
+                                           ddp_order_t order, ddp_dtype_t out_dtype,
+                                           void *out_flat, void *stream)
+{
+    if (!plan || bucket < 0 || bucket >= plan->n_buckets()) return DDP_ERR_INVALID_ARG;
+    const int in = plan->dtype;
+    // the flat buffers as a whole are checked as by ddp_sync_allreduce_avg
+    ddp_status_t stc =
+        check_reduce(rank_flat, n_ranks, plan->total, order, in, out_dtype, out_flat);
+    if (stc != DDP_OK) return stc;
+    const int64_t base = plan->bucket_base[bucket], len = plan->bucket_base[bucket + 1] - base;
+    if (len == 0) return DDP_OK;
+    const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int isz = dtype_size(in), osz = dtype_size(out_dtype);
+    char *out_b = static_cast<char *>(out_flat) + base * osz;
+    if (n_ranks == 1)
+        return copy_single(static_cast<const char *>(rank_flat[0]) + base * isz, len, isz, out_b,
+                           st);
+    RankArgs sub;
+    std::memset(&sub, 0, sizeof(sub));
+    for (int r = 0; r < n_ranks; ++r) sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
+    return launch_one_bucket(sub, n_ranks, len, order, in, out_dtype, out_b, st);
+}
+
 ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
                                  float *param_flat, float *momentum_flat, float lr, float momentum,
@@ -638,6 +666,7 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
     if (momentum_flat && overlaps(pa, total * 4, ma, total * 4)) return DDP_ERR_ALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
     // the written buffers must sit on 16-byte boundaries for the vector

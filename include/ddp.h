@@ -257,6 +257,22 @@ DDP_API ddp_status_t ddp_sync_allreduce_avg(ddp_plan_t *plan, const void *const 
                                     ddp_dtype_t out_dtype, void *out_flat,
                                     void *stream);
 
+/* Bucket b of a plan on its own: ddp_bucket_allreduce_avg on the bucket's
+ * sub-ranges of the flat buffers (elements [base_b, base_b + len_b) of each
+ * rank_flat[r] and of out_flat), with the plan's occupancy policy.  DDP
+ * all-reduces each bucket as soon as backward has produced it, last layers
+ * first ([DDP] 3.2; [TR24] 十一): a caller runs bucket 0, 1, ... as they
+ * become ready.  The buckets of one step together give the bits of one
+ * ddp_sync_allreduce_avg.
+ *   rank_flat, n_ranks, order, out_dtype, out_flat  as ddp_sync_allreduce_avg
+ *   bucket  0..ddp_plan_num_buckets(plan) - 1
+ * Errors: as ddp_bucket_allreduce_avg, plus INVALID_ARG for a bucket out of
+ * range. */
+DDP_API ddp_status_t ddp_sync_allreduce_avg_bucket(ddp_plan_t *plan, int32_t bucket,
+                                                   const void *const *rank_flat, int32_t n_ranks,
+                                                   ddp_order_t order, ddp_dtype_t out_dtype,
+                                                   void *out_flat, void *stream);
+
 /* Every bucket's average folded into one SGD step on the flat parameters,
  * in one launch: the optimizer update [TR24] 九 suggests absorbing the 1/N
  * scale into, with the update rule theta <- theta - eta * g of [DDP] 5.3.
@@ -422,23 +438,48 @@ DDP_API ddp_status_t ddp_sync_allreduce_avg_noalloc(ddp_plan_t *plan,
 
 /* ------------------------------------------------------------------ occupancy
  * How many blocks of the streaming kernels (reduce, fused SGD step, flatten /
- * unflatten) may be resident on one CU.
- *   DDP_OCCUPANCY_TUNED   (default) each launch is capped at the number of
- *       resident blocks per CU measured fastest for its kernel and rank
- *       count, by asking for an unused share of the CU's LDS.  Best for a
+ * unflatten, per-parameter sync) may be resident on one CU.
+ *   DDP_OCCUPANCY_TUNED   each launch is capped at the number of resident
+ *       blocks per CU measured fastest for its kernel and rank count, by
+ *       asking for an unused share of the CU's LDS.  Best for a
  *       synchronisation that has the GPU to itself.
  *   DDP_OCCUPANCY_SHARED  no cap.  The reserved LDS keeps other kernels'
  *       LDS-using blocks (a GEMM's, say) off a CU while the reduce runs
  *       there; when syncs overlap compute on other streams this policy
  *       shortens the overlapped step by a few percent (more for the
  *       per-parameter sync, whose tuned cap is higher).
- * The policy is process-wide and applies to launches made after the call.
- * Results do not depend on it, only timing. */
-typedef enum { DDP_OCCUPANCY_TUNED = 0, DDP_OCCUPANCY_SHARED = 1 } ddp_occupancy_t;
+ *   DDP_OCCUPANCY_DEFAULT (objects only) follow the process-wide policy.
+ * The policy is a property of each plan and each per-parameter sync: the
+ * launches of a call that takes one (ddp_sync_allreduce_avg[_bucket,
+ * _noalloc], ddp_sync_sgd_update, ddp_flatten / ddp_unflatten with that
+ * plan; ddp_param_sync_run[_buckets], ddp_param_sgd_run[_buckets]) follow
+ * the object's, so that the syncs a caller overlaps with compute and those
+ * it runs alone can differ without touching shared state.  A new object
+ * has DDP_OCCUPANCY_DEFAULT; calls without an object (ddp_bucket_allreduce_avg,
+ * ddp_accumulate) and objects left at DEFAULT follow the process-wide
+ * policy, DDP_OCCUPANCY_TUNED unless ddp_set_occupancy changed it.
+ * Results do not depend on any of it, only timing. */
+typedef enum {
+    DDP_OCCUPANCY_TUNED = 0,
+    DDP_OCCUPANCY_SHARED = 1,
+    DDP_OCCUPANCY_DEFAULT = 2
+} ddp_occupancy_t;
 
-/* Errors: INVALID_ARG (not a ddp_occupancy_t value). */
+/* Process-wide policy (TUNED or SHARED), for launches made after the call.
+ * Errors: INVALID_ARG (not TUNED or SHARED). */
 DDP_API ddp_status_t ddp_set_occupancy(ddp_occupancy_t policy);
 DDP_API ddp_occupancy_t ddp_get_occupancy(void);
+
+/* A plan's own policy (TUNED, SHARED or DEFAULT), for the calls that take
+ * the plan, from the next call on.  Errors: INVALID_ARG (null plan, bad
+ * value). */
+DDP_API ddp_status_t ddp_plan_set_occupancy(ddp_plan_t *plan, ddp_occupancy_t policy);
+/* The plan's policy as set (DEFAULT if never set), or DEFAULT for NULL. */
+DDP_API ddp_occupancy_t ddp_plan_get_occupancy(const ddp_plan_t *plan);
+
+/* The same for a per-parameter sync or SGD step. */
+DDP_API ddp_status_t ddp_param_sync_set_occupancy(ddp_param_sync_t *sync, ddp_occupancy_t policy);
+DDP_API ddp_occupancy_t ddp_param_sync_get_occupancy(const ddp_param_sync_t *sync);
 
 /* ------------------------------------------------------------------ misc */
 DDP_API const char *ddp_status_string(ddp_status_t status);

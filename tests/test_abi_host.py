@@ -257,3 +257,38 @@ def test_occupancy_policy_round_trip():
     assert ddp.get_occupancy() == "tuned"
     with pytest.raises(ValueError):
         ddp.set_occupancy("fast")
+
+
+def test_object_occupancy_policies_round_trip():
+    """A plan carries its own policy; setting it leaves the process-wide one
+    alone.  DEFAULT (2) is valid for objects, not process-wide."""
+    L = ddp.lib
+    p = ddp.plan_buckets([3, 4], 1 << 20)
+    assert p.get_occupancy() == "default"
+    for pol in ("shared", "tuned", "default"):
+        p.set_occupancy(pol)
+        assert p.get_occupancy() == pol
+        assert ddp.get_occupancy() == "tuned"
+    assert L.ddp_plan_set_occupancy(p.handle, 3) == 1
+    assert L.ddp_plan_set_occupancy(None, 0) == 1
+    assert L.ddp_plan_get_occupancy(None) == 2
+    assert L.ddp_param_sync_set_occupancy(None, 0) == 1
+    assert L.ddp_param_sync_get_occupancy(None) == 2
+    with pytest.raises(KeyError):
+        p.set_occupancy("fast")
+
+
+def test_bucket_sync_argument_errors_are_host_side():
+    L = ddp.lib
+    P = lambda *a: (ctypes.c_void_p * len(a))(*[ctypes.c_void_p(x) for x in a])   # noqa: E731
+    f = L.ddp_sync_allreduce_avg_bucket
+    p = ddp.plan_buckets([3, 4, 5], 16)          # three buckets of one parameter each
+    two = P(0x200000, 0x300000)
+    out = ctypes.c_void_p(0x400000)
+    assert p.n_buckets == 3
+    assert f(None, 0, two, 2, 1, 0, out, None) == 1
+    assert f(p.handle, -1, two, 2, 1, 0, out, None) == 1
+    assert f(p.handle, 3, two, 2, 1, 0, out, None) == 1
+    assert f(p.handle, 0, two, 2, 2, 0, out, None) == 1                  # bad order
+    assert f(p.handle, 0, P(0x200000), 1, 1, 1, out, None) == 2          # N = 1, f32 -> bf16
+    assert f(p.handle, 0, two, 2, 1, 0, ctypes.c_void_p(0x200004), None) == 4

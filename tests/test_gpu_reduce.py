@@ -322,3 +322,45 @@ def test_concurrent_first_use_of_ring_tables(env):
     assert not errors, errors
     for n in counts:
         assert_bits_equal(to_host(outs[n], torch), oracle.sync_avg(op, xs[:n], "ring"), f"N={n}")
+
+
+def test_object_policies_and_bucket_calls_change_no_bit(env):
+    """A plan's own occupancy policy (shared, tuned, default) gives the bits of
+    the oracle and leaves the process-wide policy alone; the plan's buckets
+    averaged one call each (ddp_sync_allreduce_avg_bucket, last layers
+    first) give the one-launch bits; a per-parameter sync with its own
+    policy gives the same bits as with the default."""
+    torch, ddp = env
+    rng = np.random.default_rng(55)
+    numel = [int(v) for v in rng.integers(1, 40000, 60)]
+    lp = ddp.plan_buckets(numel, 150 << 10)
+    op = oracle.plan_cap(numel, 150 << 10, 4)
+    xs = random_inputs(rng, 5, op.total, "f32")
+    ts = [to_dev(x, torch) for x in xs]
+    want = {o: oracle.sync_avg(op, xs, o) for o in ("seq", "ring")}
+    for policy in ("shared", "tuned", "default"):
+        lp.set_occupancy(policy)
+        for order in ("seq", "ring"):
+            out = torch.full((op.total,), float("nan"), device="cuda:0")
+            ddp.sync_allreduce_avg(lp, ts, out, order)
+            per = torch.full((op.total,), float("nan"), device="cuda:0")
+            for b in range(lp.n_buckets):
+                ddp.sync_allreduce_avg_bucket(lp, b, ts, per, order)
+            torch.cuda.synchronize()
+            assert_bits_equal(to_host(out, torch), want[order], f"{policy} {order}")
+            assert_bits_equal(to_host(per, torch), want[order], f"{policy} {order} per bucket")
+        assert ddp.get_occupancy() == "tuned"
+    # per-parameter sync: its own policy against the default
+    grads = [list(torch.split(t, numel)) for t in ts]
+    binds = [ddp.bind_params(lp, g) for g in grads]
+    outs = {}
+    for policy in ("default", "shared"):
+        res = [torch.empty(n, device="cuda:0") for n in numel]
+        ps = ddp.param_sync(lp, binds, ddp.bind_params(lp, res), "ring")
+        ps.set_occupancy(policy)
+        assert ps.get_occupancy() == policy
+        ps()
+        torch.cuda.synchronize()
+        outs[policy] = np.concatenate([to_host(r, torch) for r in res])
+    assert_bits_equal(outs["shared"], outs["default"], "per-parameter sync policies")
+    assert ddp.get_occupancy() == "tuned"
