@@ -21,22 +21,35 @@ __device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, 
         *reinterpret_cast<uint16_t *>(dst + j) = *reinterpret_cast<const uint16_t *>(src + j);
 }
 
-// Block-wide copy of nbytes (a multiple of 2) between 2-byte aligned
-// addresses: 16-byte non-temporal accesses from the destination's first
-// 16-byte boundary, a thread's two loads before its stores.  The loads run
-// at whatever alignment the source has there (gfx9 and later global loads
-// take any address), so a tensor whose flat offset is not a multiple of 16
-// bytes still moves in 16-byte vectors.  A head and tail of under 16 bytes
-// move 2 bytes per thread.
+// Block-wide copy of nbytes (a multiple of 2, at most kCopyBlockBytes)
+// between 2-byte aligned addresses: 16-byte non-temporal accesses from the
+// destination's first 16-byte boundary, at most two per thread, a thread's
+// loads before its stores.  The loads run at whatever alignment the source
+// has (gfx9 and later global loads take any address), so a tensor whose flat
+// offset is not a multiple of 16 bytes still moves in 16-byte vectors; a head
+// and tail of under 16 bytes move 2 bytes per thread.  A piece with neither
+// (every piece of a 16-byte aligned tensor) takes a straight-line path; on
+// the others the head goes first, which measured faster there than issuing
+// the vector loads before it.
+static_assert(kCopyBlockBytes == 2 * 16 * kCopyThreads, "two vectors per thread cover a block");
 __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
 {
     const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
     const int tid = threadIdx.x;
     const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
-    copy16b(dst, src, 0, head);
-    const int64_t nvec = (nbytes - head) >> 4;
+    const int64_t nvec = (nbytes - head) >> 4;   // at most 2 * kCopyThreads
     const char *sv = src + head;
     u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    if (head == 0 && (nbytes & 15) == 0) {
+        const int64_t j0 = tid, j1 = tid + kCopyThreads;
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (j0 < nvec) a = ld_stream(sv + 16 * j0);
+        if (j1 < nvec) b = ld_stream(sv + 16 * j1);
+        if (j0 < nvec) __builtin_nontemporal_store(a, dv + j0);
+        if (j1 < nvec) __builtin_nontemporal_store(b, dv + j1);
+        return;
+    }
+    copy16b(dst, src, 0, head);
     int64_t j = tid;
     for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {
         const u32x4 a = ld_stream(sv + 16 * j);
