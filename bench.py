@@ -337,10 +337,11 @@ def leg_parity_per_parameter(c):
     """Per-parameter layout: the timed outputs against the flat sync of the
     same values (flatten every rank, ddp_sync_allreduce_avg, unflatten), bit
     for bit, where the flat copies fit beside the tensors (inputs up to
-    16 GB); the GPU tests check the rest against the oracle on samples."""
+    16 GB); the GPU tests check every workload against the oracle."""
     torch, ddp, plan, wl = c.torch, c.ddp, c.plan, c.wl
     if c.N * c.P * wl.in_bytes > (16 << 30):
-        return "not checked here (inputs above 16 GB); the GPU tests compare sampled elements"
+        return ("not checked here (inputs above 16 GB); tests/test_gpu_full_size.py compares every "
+                "element with the oracle")
     c.sync()
     flats = [torch.empty(c.P, dtype=c.tin, device=c.dev) for _ in range(c.N)]
     for g, f in zip(c.grads, flats):
