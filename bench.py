@@ -16,7 +16,9 @@ own; the parent never touches the GPU, idles --settle-seconds (20) before the
 first child and --config-settle-seconds (10) before each further one
 (buffers allocated within about 20 s of another process releasing tens of GB
 of device memory were measured to stream 1-5 % slower).  The headline's
-record is the line; the other workloads' records go under "configs".
+record is the line; the other workloads' records go under "configs",
+GPT-1.3B's one-kernel sync over per-parameter tensors among them
+("gpt1p3b:per-parameter").
 
 Per workload: a declared clock ramp (back-to-back syncs for --ramp-ms, the
 first K of them timed as "without_ramp"), W warm-up syncs, K timed syncs
@@ -207,7 +209,8 @@ def gbps(nbytes, ms):
     return round(nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-DEFAULT_CONFIGS = "resnet50,many_small,tiny,gpt1p3b_two_bucket,llama7b"
+DEFAULT_CONFIGS = ("resnet50,many_small,tiny,gpt1p3b_two_bucket,gpt1p3b:per-parameter,"
+                   "llama7b")
 
 
 def parse_args():
@@ -219,7 +222,8 @@ def parse_args():
                     help="the headline workload (default gpt1p3b: GPT-1.3B, 146 buckets, N=8)")
     ap.add_argument("--configs", default=DEFAULT_CONFIGS,
                     help="the other workloads measured after the headline, each in a fresh child "
-                         "process, comma-separated ('none' for the headline alone)")
+                         "process, comma-separated; NAME:per-parameter times the one-kernel sync over "
+                         "per-parameter tensors ('none' for the headline alone)")
     ap.add_argument("--child", action="store_true",
                     help="measure --workload in this process and print its JSON line (what the "
                          "parent runs per workload; the parent itself never touches the GPU)")
@@ -1242,7 +1246,7 @@ _SHARED_KEYS = ("metric", "unit", "n_gpus", "steps", "warmup", "higher_is_better
                 "vs_baseline", "data")
 
 
-def run_child(args, workload, cpu_seconds, headline):
+def run_child(args, workload, cpu_seconds, headline, layout=None):
     """Measures one workload in a fresh child process (started by this
     process, which has not touched the GPU) and returns its record."""
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--child", "--workload", workload,
@@ -1256,7 +1260,9 @@ def run_child(args, workload, cpu_seconds, headline):
         cmd += ["--extras", args.extras]
     if headline:
         cmd += ["--layout", args.layout] + (["--order", args.order] if args.order else [])
-    log(f"bench: {workload} in a child process")
+    elif layout:
+        cmd += ["--layout", layout]
+    log(f"bench: {workload} ({layout or 'bucket-view'}) in a child process")
     t0 = time.perf_counter()
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
     lines = [l for l in proc.stdout.splitlines() if l.startswith("{")]
@@ -1296,7 +1302,8 @@ def main():
     for w in names:
         if args.config_settle_seconds > 0:
             time.sleep(args.config_settle_seconds)
-        rec = run_child(args, w, args.config_cpu_seconds, headline=False)
+        name, _, layout = w.partition(":")
+        rec = run_child(args, name, args.config_cpu_seconds, headline=False, layout=layout or None)
         configs[w] = {k: v for k, v in rec.items() if k not in _SHARED_KEYS}
     line["configs"] = configs
     line["protocol"] = {

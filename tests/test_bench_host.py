@@ -68,7 +68,8 @@ def test_parser_defaults_and_layouts(monkeypatch):
     a = b.parse_args()
     assert (a.gpus, a.steps, a.warmup, a.workload, a.layout) == (1, 50, 10, "gpt1p3b", "bucket-view")
     assert a.order is None and a.settle_seconds == 20.0 and not a.child
-    assert a.configs.split(",") == ["resnet50", "many_small", "tiny", "gpt1p3b_two_bucket", "llama7b"]
+    assert a.configs.split(",") == ["resnet50", "many_small", "tiny", "gpt1p3b_two_bucket",
+                                    "gpt1p3b:per-parameter", "llama7b"]
     monkeypatch.setattr(sys, "argv", ["bench.py", "--layout", "per-parameter", "--settle-seconds", "0",
                                       "--workload", "tiny", "--order", "seq", "--child"])
     a = b.parse_args()

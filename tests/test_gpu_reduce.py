@@ -364,3 +364,46 @@ def test_object_policies_and_bucket_calls_change_no_bit(env):
         outs[policy] = np.concatenate([to_host(r, torch) for r in res])
     assert_bits_equal(outs["shared"], outs["default"], "per-parameter sync policies")
     assert ddp.get_occupancy() == "tuned"
+
+
+@pytest.mark.parametrize("pair", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=lambda p: f"{p[0]}-{p[1]}")
+@pytest.mark.parametrize("N", [1, 2, 3, 8, 13, 24])
+def test_bucket_calls_every_dtype_pair(env, pair, N):
+    """ddp_sync_allreduce_avg_bucket over every bucket of random plans (empty
+    parameters, buckets shorter than a tile, buckets at unaligned offsets),
+    every dtype pair, N from 1 to 24, both orders: the oracle's bits, and an
+    output outside the bucket left untouched."""
+    torch, ddp = env
+    in_dt, out_dt = pair
+    if N == 1 and in_dt != out_dt:
+        pytest.skip("one rank: the input is the output, so the dtypes must match")
+    rng = np.random.default_rng(600 + N)
+    eb = 4 if in_dt == "f32" else 2
+    sizes = [int(x) for x in rng.choice([0, 1, 3, 17, 255, 600, 5000, 40000], size=30)]
+    sizes[0] = max(sizes[0], 1)
+    cap = 8192
+    lp = ddp.plan_buckets(sizes, cap, in_dt)
+    op = oracle.plan_cap(sizes, cap, eb)
+    xs = random_inputs(rng, N, op.total, in_dt)
+    ts = [to_dev(x, torch) for x in xs]
+    tout = torch.float32 if out_dt == "f32" else torch.bfloat16
+    for order in ("seq", "ring"):
+        want = oracle.sync_avg(op, xs, order, in_dt, out_dt)
+        out = torch.full((op.total,), float("nan"), dtype=tout, device="cuda:0")
+        for b in range(lp.n_buckets):
+            ddp.sync_allreduce_avg_bucket(lp, b, ts, out, order)
+        torch.cuda.synchronize()
+        assert_bits_equal(to_host(out, torch), want, f"N={N} {pair} {order}")
+        # one bucket alone writes only its own range
+        b = lp.n_buckets // 2
+        ln, base, _, _ = lp.bucket(b)
+        one = torch.full((op.total,), float("nan"), dtype=tout, device="cuda:0")
+        ddp.sync_allreduce_avg_bucket(lp, b, ts, one, order)
+        torch.cuda.synchronize()
+        got = to_host(one, torch)
+        assert_bits_equal(got[base:base + ln], want[base:base + ln], f"bucket {b}")
+        rest = np.concatenate([got[:base], got[base + ln:]])
+        nan = ((rest & 0x7F80) == 0x7F80) & ((rest & 0x7F) != 0) if rest.dtype == np.uint16 \
+            else np.isnan(rest)
+        assert nan.all(), "a bucket call wrote outside its bucket"
