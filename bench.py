@@ -27,6 +27,7 @@ first K of them timed as "without_ramp"), W warm-up syncs, K timed syncs
   ceiling        a probe of the reduce's bare access pattern
   other_orders   the other summation order
   cpu_baseline   the CPU oracle on all host cores and on one, with parity
+  noalloc        the sync through the entry point that allocates nothing
 and for ResNet-50 only (--extras): per_bucket, copy_path, fused_sgd,
 overlap, rank_sweep_GBps, in_place, no_sync, small_means; for many-small
 copy_path; for tiny the latency of a sync (Python call, prepared call, graph
@@ -1084,6 +1085,24 @@ def latency(c, make_call, reps=2000):
     return res
 
 
+def leg_noalloc(c):
+    """The same synchronisation through ddp_sync_allreduce_avg_noalloc, which
+    rebuilds the plan's ring tables in its static device buffer on every
+    call (two small kernels before the reduce) instead of reading tables
+    uploaded once: the cost of allocating nothing."""
+    ddp = c.ddp
+    if c.args.layout != "bucket-view" or c.order != "ring" or c.sync_bytes < (64 << 20):
+        return None
+    call = lambda: ddp.sync_allreduce_avg_noalloc(c.plan, c.flats, c.out, "ring",   # noqa: E731
+                                                  stream=c.stream)
+    ms = stream_ms(c, call, c.args.steps, warm=3, settle=True)
+    res = {"ms_per_sync": round(ms, 5), "GBps": gbps(c.sync_bytes, ms),
+           "vs_prepared_tables": round(c.kern_ms / ms, 4),
+           "call": "ddp_sync_allreduce_avg_noalloc, K back-to-back calls between one event pair"}
+    log(f"no-allocation sync: {res}")
+    return res
+
+
 def leg_tiny_latency(c):
     """The latency-bound workload (tiny: 15 KB per sync): its sync through
     the plain Python call, the prepared call and graph replay."""
@@ -1187,6 +1206,7 @@ def measure(args, cpu_seconds):
     elif copy_only and not per_param:
         more = {"copy_path": leg_copy_path(c)}
     tiny = leg_tiny_latency(c)
+    noalloc = leg_noalloc(c)
 
     wl, P, np = c.wl, c.P, c.np
     kernel = "params_fast" if per_param else "reduce_fast"
@@ -1233,6 +1253,7 @@ def measure(args, cpu_seconds):
         "parity": parity,
         "other_orders": other,
         **({"latency": tiny} if tiny else {}),
+        **({"noalloc": noalloc} if noalloc else {}),
         **{k: v for k, v in more.items() if v is not None},
         "env": dict(run_environment(torch),
                     sensors={"before_timed_steps": sensors_before,

@@ -19,7 +19,7 @@ MIN_SUB = 1 << 19        # smallest sub-range handed to one host thread
 
 def host_threads():
     """Host threads to use: the CPUs this process may run on, at most 16
-    (a GPU machine shares its host between GPUs)."""
+    (a host shared by several GPUs gives each a share of its CPUs)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
