@@ -58,10 +58,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "effective HBM GB/s (N·P·bytes read + P written) and % of peak per sync"
 CSRC = os.path.join(ROOT, "gradient_allreduce_averaging_amd", "csrc")
-# the sources the flat reduce kernel (the one whose HBM counters are recorded)
-# is built and launched from: its kernels and launches, the shared device
-# code, the host helpers and the occupancy caps
+# the sources each timed kernel (the ones whose HBM counters are recorded) is
+# built and launched from: its kernels and launches, the shared device code,
+# the host helpers and the occupancy caps.  The flat reduce (bucket-view
+# layout) and the per-parameter sync are hashed apart, so a change to one
+# keeps the other's counter data.
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("common.hip", "device.h", "host.h", "reduce.hip")]
+PARAMS_KERNEL_SOURCES = [os.path.join(CSRC, f)
+                         for f in ("common.hip", "device.h", "host.h", "params.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -69,12 +73,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
-    """sha256[:16] of the kernel sources (in name order) with comments and
-    blank lines removed and each line stripped, so that only a change of code
-    invalidates the counter data taken on it."""
+def kernel_source_sha(layout="bucket-view"):
+    """sha256[:16] of the layout's kernel sources (in name order) with
+    comments and blank lines removed and each line stripped, so that only a
+    change of code invalidates the counter data taken on it."""
     code = []
-    for path in KERNEL_SOURCES:
+    for path in (PARAMS_KERNEL_SOURCES if layout == "per-parameter" else KERNEL_SOURCES):
         with open(path, encoding="utf-8") as f:
             text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
         lines = (re.sub(r"//.*", "", line).strip() for line in text.splitlines())
@@ -82,7 +86,13 @@ def kernel_source_sha():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload, order):
+def traffic_key(workload, order, layout="bucket-view"):
+    """The key of a workload's counter record in profiles/traffic.json."""
+    return f"{workload}:per-parameter/{order}" if layout == "per-parameter" else \
+        f"{workload}/{order}"
+
+
+def measured_traffic(workload, order, layout="bucket-view"):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (profiles/traffic.json) and where they come from, or None and the reason
     when there are none for this kernel source.  The counters are not taken
@@ -92,12 +102,14 @@ def measured_traffic(workload, order):
             table = json.load(f)
     except (OSError, ValueError):
         return None, "no counter file"
-    rec = table.get(f"{workload}/{order}")
+    key = traffic_key(workload, order, layout)
+    rec = table.get(key)
     if not rec:
-        return None, f"no counter run for {workload}/{order}"
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None, f"no counter run for {key}"
+    sha = kernel_source_sha(layout)
+    if rec.get("kernel_source_sha") != sha:
         return None, (f"counters taken on kernel source {rec.get('kernel_source_sha')}, not "
-                      f"this one ({kernel_source_sha()})")
+                      f"this one ({sha})")
     return rec.get("hbm_bytes_per_launch"), {
         "profile": rec.get("profile"), "kernel_source_sha": rec.get("kernel_source_sha"),
         "taken": rec.get("taken"), "read_bytes": rec.get("read_bytes"),
@@ -1210,8 +1222,7 @@ def measure(args, cpu_seconds):
 
     wl, P, np = c.wl, c.P, c.np
     kernel = "params_fast" if per_param else "reduce_fast"
-    traffic, traffic_source = (None, "not taken for the per-parameter layout") if per_param else \
-        measured_traffic(wl.name, c.order)
+    traffic, traffic_source = measured_traffic(wl.name, c.order, args.layout)
     record = {
         "metric": METRIC,
         "value": round(c.value, 1),

@@ -1,5 +1,5 @@
-"""bench.py on the host (no GPU): the one-GPU guard and the kernel-code hash
-that keys the committed HBM counter data."""
+"""bench.py on the host (no GPU): the one-GPU guard and the kernel-code hashes
+that key the committed HBM counter data."""
 import importlib.util
 import os
 import subprocess
@@ -60,6 +60,31 @@ def test_traffic_is_reported_only_for_the_hashed_code(tmp_path):
     f.write_text(json.dumps(rec))
     nbytes, why = b.measured_traffic("resnet50", "ring")
     assert nbytes is None and "0" * 16 in why
+
+
+def test_per_parameter_traffic_has_its_own_key_and_hash(tmp_path):
+    """The per-parameter sync's counters are keyed apart from the flat
+    reduce's and checked against the hash of its own sources."""
+    b = _bench()
+    import json
+    assert any(p.endswith("params.hip") for p in b.PARAMS_KERNEL_SOURCES)
+    assert not any(p.endswith("reduce.hip") for p in b.PARAMS_KERNEL_SOURCES)
+    assert b.kernel_source_sha("per-parameter") != b.kernel_source_sha()
+    assert b.traffic_key("gpt1p3b", "ring", "per-parameter") == "gpt1p3b:per-parameter/ring"
+    rec = {"gpt1p3b/ring": {"kernel_source_sha": b.kernel_source_sha(), "hbm_bytes_per_launch": 1},
+           "gpt1p3b:per-parameter/ring": {"kernel_source_sha": b.kernel_source_sha("per-parameter"),
+                                          "hbm_bytes_per_launch": 2}}
+    f = tmp_path / "t.json"
+    f.write_text(json.dumps(rec))
+    b.TRAFFIC_FILE = str(f)
+    assert b.measured_traffic("gpt1p3b", "ring")[0] == 1
+    assert b.measured_traffic("gpt1p3b", "ring", "per-parameter")[0] == 2
+    nbytes, why = b.measured_traffic("gpt1p3b", "seq", "per-parameter")
+    assert nbytes is None and "gpt1p3b:per-parameter/seq" in why
+    # a record taken on the flat reduce's hash does not serve the per-parameter sync
+    rec["gpt1p3b:per-parameter/ring"]["kernel_source_sha"] = b.kernel_source_sha()
+    f.write_text(json.dumps(rec))
+    assert b.measured_traffic("gpt1p3b", "ring", "per-parameter")[0] is None
 
 
 def test_parser_defaults_and_layouts(monkeypatch):
