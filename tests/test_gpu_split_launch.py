@@ -59,6 +59,16 @@ def launches(blocks, threads):
     return -(-blocks // per)
 
 
+def copy_units_per_launch(esize):
+    """Copy units one flatten/unflatten launch takes (same rule as the
+    library): the work-item limit's worth of 256-thread blocks, one per 8 KiB
+    of a 4096-element unit, rounded down to whole rounds of 8 runs of up to
+    64 consecutive units."""
+    cap = launch_items() // (256 * (4096 * esize // 8192))
+    run = min(64, cap // 8)
+    return cap // (8 * run) * (8 * run)
+
+
 @pytest.fixture(scope="module")
 def env():
     torch = torch_cuda()
@@ -210,7 +220,7 @@ def test_launch_count_follows_the_item_limit(env):
         ddp.flatten(lp, bind, out[:P])
     k, g = _kernel_nodes(torch, flat)
     units = sum(-(-n // 4096) for n in sizes)
-    assert k == -(-units // (launch_items() // 512)), ("flatten", k)   # 2 blocks of 256 a unit
+    assert k == -(-units // copy_units_per_launch(4)), ("flatten", k)
     _replay_equals_eager(torch, g, flat, [out], "flatten replay")
     del flats, out, params, mom, acc_dst, grads
     torch.cuda.empty_cache()
