@@ -15,7 +15,7 @@ namespace {
 
 // ---------------------------------------------------------------- copies
 
-constexpr int64_t kCopyRun = 64;   // consecutive copy units per XCD (copy_units)
+constexpr int64_t kCopyRun = 64;   // consecutive copy units per XCD (unit_of_block)
 
 __device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, int64_t hi)
 {
@@ -63,41 +63,176 @@ __device__ void block_copy(char *dst, const char *src, int64_t nbytes)
     copy16b(dst, src, head + (nvec << 4), nbytes);
 }
 
-// BPU blocks per copy unit (copy_blocks_per_unit: 8 KiB a block), each
-// moving its share of the unit (parts past a short unit's end return at
-// once); to_flat selects flatten (param -> flat) or unflatten (flat ->
-// param).  Workgroups are dealt to the XCDs round-robin (block b runs on
-// XCD b % 8).  Each XCD takes runs of `run` consecutive units (units
-// [(8k + x) run, (8k + x + 1) run) go to XCD x), and the blocks of one unit
-// run on one XCD, where the unit's table entry is then an L2 hit for all
-// but the first of them.  Consecutive units touch neighbouring bytes: where
-// a parameter's flat offset is not a multiple of the 128-byte line, the
-// line two units share is written whole by one XCD's L2 inside a run
-// instead of in two partial writes from two L2s, which measured 2-3 %
+// Block -> unit mapping of both copy kernels.  BPU blocks per copy unit
+// (copy_blocks_per_unit: 8 KiB a block), each moving its share of the unit
+// (parts past a short unit's end return at once).  Workgroups are dealt to
+// the XCDs round-robin (block b runs on XCD b % 8).  Each XCD takes runs of
+// `run` consecutive units (units [(8k + x) run, (8k + x + 1) run) go to XCD
+// x), and the blocks of one unit run on one XCD, where the unit's table
+// entry is then an L2 hit for all but the first of them.  Consecutive units
+// touch neighbouring bytes: where a parameter's flat offset is not a
+// multiple of the 128-byte line, the line two units share is written by one
+// XCD's L2 inside a run instead of from two L2s, which measured 2-3 %
 // faster with many small unaligned parameters (runs of 64; runs of 256, or
 // one contiguous span per XCD, measured slower on large ones).  Units hold
 // 4K elements: with many short parameters, bigger units mostly spawn blocks
 // that find no work.
 template <int BPU>
-__global__ void __launch_bounds__(kCopyThreads)
-copy_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run, char *flat,
-           int esize, int to_flat)
+__device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
 {
     constexpr int64_t kBlockElems = kCopyUnitElems / BPU;
     const unsigned m = blockIdx.x / kXcds, j = m / BPU;   // this XCD's j-th unit
-    const int64_t ui = (int64_t)((j / run) * kXcds + blockIdx.x % kXcds) * run + j % run;
+    *lo = (m % BPU) * kBlockElems;
+    return (int64_t)((j / run) * kXcds + blockIdx.x % kXcds) * run + j % run;
+}
+
+// Unflatten (flat -> param): each block copies its part of a unit into the
+// parameter, whose storage starts on the allocator's alignment, so every
+// piece but a parameter's last starts and ends on a 16-byte boundary.
+template <int BPU>
+__global__ void __launch_bounds__(kCopyThreads)
+unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
+                const char *flat, int esize)
+{
+    int64_t lo;
+    const int64_t ui = unit_of_block<BPU>(run, &lo);
     if (ui >= n_units) return;
     const ddp_copy_unit u = units[first + ui];
-    const int64_t lo = (m % BPU) * kBlockElems;
     if (lo >= u.count) return;
-    const int64_t n = min(u.count - lo, kBlockElems);
-    char *pp = reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize;
-    char *fp = flat + (u.flat_elem + lo) * esize;
-    const int64_t nbytes = n * esize;
-    if (to_flat)
-        block_copy(fp, pp, nbytes);
-    else
-        block_copy(pp, fp, nbytes);
+    const int64_t n = min(u.count - lo, kCopyUnitElems / BPU);
+    block_copy(reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize,
+               flat + (u.flat_elem + lo) * esize, n * esize);
+}
+
+// Loads through a generic pointer compile to flat instructions, which the
+// scalar-load counter also tracks, so a wait for a scalar load would wait
+// for them too; these take the global address space.
+__device__ __forceinline__ u32x4 ld_stream_global(const char *p)
+{
+    typedef __attribute__((address_space(1))) const u32x4_ua gvec;
+    return __builtin_nontemporal_load(reinterpret_cast<gvec *>(reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ uint16_t ld_u16_global(const char *p)
+{
+    typedef __attribute__((address_space(1))) const uint16_t g16;
+    return *reinterpret_cast<g16 *>(reinterpret_cast<uintptr_t>(p));
+}
+
+// A unit's flat bytes [beg, end) and the source address of beg.
+struct UnitSpan {
+    uintptr_t beg, end;
+    const char *src;
+};
+
+__device__ __forceinline__ UnitSpan unit_span(const ddp_copy_unit &u, uintptr_t flat, int esize)
+{
+    const uintptr_t beg = flat + (uintptr_t)(u.flat_elem * esize);
+    return {beg, beg + (uintptr_t)(u.count * esize),
+            reinterpret_cast<const char *>(u.param_addr) + u.param_elem * esize};
+}
+
+// Source of flat byte x >= d1 (past the block's own bytes): in unit v0
+// (cur), the unit after it (nxt, loaded with the block's own entry), or --
+// where units are shorter than a chunk -- one further on, walked to up to
+// range_end; null past the range's last unit.
+__device__ const char *source_past(const ddp_copy_unit *units, int64_t v0, int64_t range_end,
+                                   UnitSpan cur, UnitSpan nxt, uintptr_t flat, int esize,
+                                   uintptr_t x)
+{
+    if (x < cur.end) return cur.src + (x - cur.beg);
+    if (v0 + 1 >= range_end) return nullptr;
+    if (x < nxt.end) return nxt.src + (x - nxt.beg);
+    for (int64_t w = v0 + 2; w < range_end; ++w) {
+        const UnitSpan sp = unit_span(units[w], flat, esize);
+        if (x < sp.end) return sp.src + (x - sp.beg);
+    }
+    return nullptr;
+}
+
+// Flatten (param -> flat) with one writer per 16-byte chunk of the flat
+// buffer.  Parameters sit in the flat buffer at any element offset, so a
+// chunk often holds the end of one piece and the start of the next.  The
+// block whose flat bytes [d0, d1) hold a chunk's first byte writes the whole
+// chunk; the call's first block also writes the chunk holding the range's
+// first byte.  Chunks inside [d0, d1) take one vector load from the source
+// at its own alignment (any address) and an aligned store.  A chunk at an
+// edge (the head chunk, and the one that runs past d1) is written by 8
+// lanes, 2 bytes each, in one store instruction: bytes in [d0, d1) come
+// from this block's source, bytes from d1 on from the unit that holds them,
+// none before d0 (the head of a call's range) or past the range's last
+// unit.  The next unit's entry is loaded with the block's own, and the
+// edge lanes' loads go out with the vector loads, so a block makes one
+// round trip to memory.  Bytes before a block's first chunk are left to the
+// block before it.  Written in 2-byte pieces by two blocks each, as an
+// earlier version did, such chunks cost many small unaligned parameters 3 %
+// of their bandwidth.  A block with no edge chunk (every block of a tensor
+// whose flat offset is a multiple of 16 bytes) takes a straight-line path:
+// the edge bookkeeping ahead of its loads cost such tensors 5 %.
+template <int BPU>
+__global__ void __launch_bounds__(kCopyThreads)
+flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
+              int64_t range_first, int64_t range_end, char *flat, int esize)
+{
+    int64_t lo;
+    const int64_t ui = unit_of_block<BPU>(run, &lo);
+    if (ui >= n_units) return;
+    const int64_t v0 = first + ui;
+    const ddp_copy_unit u = units[v0];
+    const ddp_copy_unit un = units[min(v0 + 1, range_end - 1)];
+    // both entries arrive together, before any data load is in flight
+    asm volatile("" ::"s"(un.param_addr), "s"(un.param_elem), "s"(un.flat_elem), "s"(un.count));
+    if (lo >= u.count) return;
+    const int64_t n = min(u.count - lo, kCopyUnitElems / BPU);
+    const char *src = reinterpret_cast<const char *>(u.param_addr) + (u.param_elem + lo) * esize;
+    const uintptr_t fb = reinterpret_cast<uintptr_t>(flat);
+    const uintptr_t d0 = fb + (uintptr_t)((u.flat_elem + lo) * esize);
+    const uintptr_t d1 = d0 + (uintptr_t)(n * esize);
+    const bool head = v0 == range_first && lo == 0 && (d0 & 15);
+    const uintptr_t cf = head ? (d0 & ~(uintptr_t)15) : ((d0 + 15) & ~(uintptr_t)15);
+    if (cf >= d1) return;                                // no chunk starts here
+    const int64_t nch = (int64_t)((d1 - cf + 15) >> 4);  // chunks [cf, cf + 16 nch), <= 513
+    const bool spill = (d1 & 15) != 0;                   // the last chunk runs past d1
+    const int64_t kb = head ? 1 : 0, ke = spill ? nch - 1 : nch;   // whole chunks [kb, ke)
+    const int tid = threadIdx.x;
+    if (((d0 | d1) & 15) == 0) {   // [d0, d1) is whole chunks: cf = d0, kb = 0, ke = nch
+        const int64_t k0 = tid, k1 = tid + kCopyThreads;
+        u32x4 *dv = reinterpret_cast<u32x4 *>(d0);
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (k0 < ke) a = ld_stream(src + 16 * k0);
+        if (k1 < ke) b = ld_stream(src + 16 * k1);
+        if (k0 < ke) __builtin_nontemporal_store(a, dv + k0);
+        if (k1 < ke) __builtin_nontemporal_store(b, dv + k1);
+        return;
+    }
+    // edge lanes: 0-7 the head chunk, the last 8 the chunk past d1 (unless
+    // it is the head chunk too); their sources first, so that their loads
+    // go out with the vector loads
+    const int e = tid - (kCopyThreads - 8);
+    uintptr_t x = 0;
+    if (head && tid < 8) x = cf + 2 * (uintptr_t)tid;
+    else if (spill && (nch > 1 || !head) && e >= 0) x = cf + 16 * (uintptr_t)(nch - 1) + 2 * e;
+    const char *ps = nullptr;
+    if (x >= d0 && x < d1)
+        ps = src + (x - d0);
+    else if (x >= d1)
+        ps = source_past(units, v0, range_end, unit_span(u, fb, esize), unit_span(un, fb, esize),
+                         fb, esize, x);
+    const int64_t k0 = kb + tid, k1 = kb + tid + kCopyThreads;     // ke - kb <= 512
+    // Lanes past the last whole chunk load it again (their loads merge with
+    // its own), so both loads go out unconditionally and no lane waits for
+    // one before the other is issued; only the stores are predicated.
+    const int64_t klast = max(ke - 1, kb);
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (ke > kb) {
+        a = ld_stream_global(src + (cf + 16 * (uintptr_t)min(k0, klast) - d0));
+        b = ld_stream_global(src + (cf + 16 * (uintptr_t)min(k1, klast) - d0));
+    }
+    uint16_t piece = 0;
+    if (ps) piece = ld_u16_global(ps);
+    u32x4 *cv = reinterpret_cast<u32x4 *>(cf);
+    if (k0 < ke) __builtin_nontemporal_store(a, cv + k0);
+    if (k1 < ke) __builtin_nontemporal_store(b, cv + k1);
+    if (ps) *reinterpret_cast<uint16_t *>(x) = piece;
 }
 
 }  // namespace
@@ -209,10 +344,15 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
         const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
         char *fl = static_cast<char *>(flat);
         hipStream_t st = static_cast<hipStream_t>(stream);
-        if (bpu == 1)
-            copy_units<1><<<g, b, lds, st>>>(bd->units, u0, n, (unsigned)run, fl, esize, to_flat);
+        const unsigned r = (unsigned)run;
+        if (to_flat && bpu == 1)
+            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, first, last, fl, esize);
+        else if (to_flat)
+            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, first, last, fl, esize);
+        else if (bpu == 1)
+            unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
         else
-            copy_units<2><<<g, b, lds, st>>>(bd->units, u0, n, (unsigned)run, fl, esize, to_flat);
+            unflatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
         const ddp_status_t s = launched("copy kernel launch");
         if (s != DDP_OK) return s;
     }

@@ -119,3 +119,49 @@ def test_full_path_flatten_sync_unflatten_resnet50(env):
     want = oracle.unflatten(op, oracle.sync_avg(op, [oracle.flatten(op, h) for h in host], "ring"))
     for p in range(len(wl.numel)):
         assert_bits_equal(to_host(result[p], torch), want[p], f"param {p}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("flat_off", [0, 1, 3, 7])
+def test_flatten_tiny_tensors_at_any_offset(env, dt, flat_off):
+    """Tensors of 1-9 elements between longer ones, so that one 16-byte chunk
+    of the flat buffer holds pieces of up to eight tensors; the flat buffer
+    itself starts flat_off elements past an aligned allocation; small
+    buckets, so most bucket starts are unaligned.  Whole and per-bucket
+    calls against the oracle; bytes outside the bucket keep their
+    sentinel."""
+    torch, ddp = env
+    rng = np.random.default_rng(100 + flat_off + (dt == "bf16"))
+    pool = [1, 1, 2, 3, 5, 7, 8, 9, 63, 64, 65, 2047, 2049, 4095, 4096, 4097, 9001]
+    sizes = [int(rng.choice(pool)) for _ in range(400)]
+    eb = 4 if dt == "f32" else 2
+    cap = 3000 * eb
+    lp = ddp.plan_buckets(sizes, cap, dt)
+    op = oracle.plan_cap(sizes, cap, eb)
+    assert lp.buckets() == op.buckets
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    host = []
+    for n in sizes:
+        x = rng.standard_normal(n).astype(np.float32)
+        host.append(x if dt == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16))
+    big, views, _ = _carve(torch, sizes, tdt, rng, True)
+    for v, h in zip(views, host):
+        v.copy_(to_dev(h, torch))
+    binding = ddp.bind_params(lp, views)
+    want = oracle.flatten(op, host)
+    store = torch.full((flat_off + lp.total + 16,), 9.0, dtype=tdt, device="cuda:0")
+    flat = store[flat_off:flat_off + lp.total]
+    ddp.flatten(lp, binding, flat)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(flat, torch), want, f"{dt} flat+{flat_off} whole")
+    nine = to_host(torch.full((1,), 9.0, dtype=tdt, device="cuda:0"), torch)[0]
+    h = to_host(store, torch)
+    assert (h[:flat_off] == nine).all() and (h[flat_off + lp.total:] == nine).all()
+    for b in rng.choice(lp.n_buckets, size=min(12, lp.n_buckets), replace=False):
+        store.fill_(9.0)
+        ddp.flatten(lp, binding, flat, bucket=int(b))
+        torch.cuda.synchronize()
+        h = to_host(store, torch)[flat_off:flat_off + lp.total]
+        lo, hi = op.bucket_base[b], op.bucket_base[b] + op.bucket_len[b]
+        assert_bits_equal(h[lo:hi], want[lo:hi], f"{dt} flat+{flat_off} bucket {b}")
+        assert (h[:lo] == nine).all() and (h[hi:] == nine).all(), f"bucket {b} wrote outside"
