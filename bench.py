@@ -713,27 +713,29 @@ def rank_grads(c):
     return grads
 
 
-def copy_ceiling(c):
+def copy_ceiling(c, flats=None, out=None, esize=None):
     """A plain copy of one rank buffer (the bytes one flatten or unflatten
     launch moves), one launch per rank back to back, through the probe's
     one-load-one-store pattern (non-temporal 16-byte accesses, one-wave
     blocks): the ceiling of a copy of this size on this machine, best over
-    resident-block caps."""
+    resident-block caps.  Defaults: the workload's rank buffers and output."""
     import ctypes
     torch, N, wl = c.torch, c.N, c.wl
-    if wl.in_bytes != wl.out_bytes:
-        return None
+    if flats is None:
+        if wl.in_bytes != wl.out_bytes:
+            return None
+        flats, out, esize = c.flats, c.out, wl.in_bytes
     probe = ctypes.CDLL(os.path.join(ROOT, "gradient_allreduce_averaging_amd", "libddp_probe.so"))
     probe.ddp_probe_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     sink = torch.zeros(4, dtype=torch.int32, device=c.dev)
-    nvec = c.P * wl.in_bytes // 16
-    srcs = [(ctypes.c_void_p * 1)(ctypes.c_void_p(f.data_ptr())) for f in c.flats]
+    nvec = c.P * esize // 16
+    srcs = [(ctypes.c_void_p * 1)(ctypes.c_void_p(f.data_ptr())) for f in flats]
 
     def copies(k):
         for src in srcs:
-            rc = probe.ddp_probe_stream(src, 1, ctypes.c_void_p(c.out.data_ptr()), nvec, 1, k,
+            rc = probe.ddp_probe_stream(src, 1, ctypes.c_void_p(out.data_ptr()), nvec, 1, k,
                                         ctypes.c_void_p(sink.data_ptr()),
                                         ctypes.c_void_p(c.stream.cuda_stream))
             assert rc == 0, "probe launch failed"
@@ -747,6 +749,51 @@ def copy_ceiling(c):
             "probe": f"{N} launches, each a plain copy of one rank buffer ({nvec * 16} B) with the "
                      "one-load-one-store pattern, back to back; best over caps of 4..8 resident "
                      "blocks per CU and none"}
+
+
+def copy_rates_bf16(c, reps):
+    """Flatten and unflatten of the same parameter sizes in bf16: per-rank
+    bf16 tensors, a bf16 plan with the workload's cap, each copy timed back
+    to back (K repetitions between one event pair), GB/s by the bytes it
+    moves; the plain copy of one bf16 rank buffer beside them.  The
+    tensors are filled by unflattening the rank buffers, so flattening them
+    again must give those buffers back bit for bit."""
+    torch, ddp, wl, N = c.torch, c.ddp, c.wl, c.N
+    plan = ddp.plan_buckets(wl.numel, wl.bucket_cap_bytes, "bf16")
+    gen = torch.Generator(device=c.dev)
+    gen.manual_seed(5)
+    flats = [torch.empty(c.P, dtype=torch.bfloat16, device=c.dev).normal_(0, 1e-3, generator=gen)
+             for _ in range(N)]
+    grads = [[torch.empty(n, dtype=torch.bfloat16, device=c.dev) for n in wl.numel]
+             for _ in range(N)]
+    binds = [ddp.bind_params(plan, g) for g in grads]
+    for r in range(N):
+        ddp.unflatten(plan, binds[r], flats[r], stream=c.stream)
+    want = [f.clone() for f in flats]
+
+    def flatten_all():
+        for r in range(N):
+            ddp.flatten(plan, binds[r], flats[r], stream=c.stream)
+
+    def unflatten_one():
+        ddp.unflatten(plan, binds[0], flats[0], stream=c.stream)
+
+    tf = stream_ms(c, flatten_all, reps, settle=True)
+    tu = stream_ms(c, unflatten_one, reps, settle=True)
+    torch.cuda.synchronize()
+    same = all(torch.equal(f.view(torch.int16), w.view(torch.int16)) for f, w in zip(flats, want))
+    out = {"flatten_ms": round(tf, 4), "flatten_GBps": gbps(2 * N * c.P * 2, tf),
+           "unflatten_ms": round(tu, 4), "unflatten_GBps": gbps(2 * c.P * 2, tu),
+           "flatten_gives_the_rank_buffers_back": bool(same)}
+    scratch = torch.empty(c.P, dtype=torch.bfloat16, device=c.dev)
+    ceil = copy_ceiling(c, flats, scratch, 2)
+    if ceil:
+        out["copy_ceiling"] = ceil
+        out["flatten_frac_of_copy_ceiling"] = round(out["flatten_GBps"] / ceil["GBps"], 4)
+        out["unflatten_frac_of_copy_ceiling"] = round(out["unflatten_GBps"] / ceil["GBps"], 4)
+    del flats, grads, binds, want, scratch
+    torch.cuda.empty_cache()
+    return out
 
 
 def leg_copy_path(c):
@@ -821,6 +868,8 @@ def leg_copy_path(c):
         "same_bits_as_three_steps": bool(same),
         "step": "every rank's per-parameter gradients averaged into per-parameter outputs "
                 "in one launch (ddp_param_sync_run)"}
+    if wl.dtype == "f32":
+        out["bf16"] = copy_rates_bf16(c, reps)
     log(f"copy path: {out}")
     return out
 
