@@ -1,5 +1,11 @@
 // Flatten and unflatten: per-parameter gradients <-> flat bucket buffers
-// (ddp_bind_params, ddp_flatten, ddp_unflatten).
+// (ddp_bind_params, ddp_flatten, ddp_unflatten).  The flat buffer of a
+// bucket holds its parameters' gradients back to back at the plan's
+// offsets, with no padding; after the average it is viewed back onto the
+// parameters' gradients.
+//
+// Pages: [DDP] "DDP" (sgdbs.github.io, AI_Infra/1.DataParallel), 4.2
+//        (flat_grad built from the gradients, then viewed back).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -87,8 +93,10 @@ __device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
 }
 
 // Unflatten (flat -> param): each block copies its part of a unit into the
-// parameter, whose storage starts on the allocator's alignment, so every
-// piece but a parameter's last starts and ends on a 16-byte boundary.
+// parameter.  A parameter's storage usually starts on the allocator's
+// alignment, so its pieces, all but its last, start and end on a 16-byte
+// boundary and no two blocks share a chunk; block_copy takes any 2-byte
+// alignment all the same.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
