@@ -107,140 +107,105 @@ unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsi
     if (ui >= n_units) return;
     const ddp_copy_unit u = units[first + ui];
     if (lo >= u.count) return;
-    const int64_t n = min(u.count - lo, kCopyUnitElems / BPU);
+    const int64_t n = min((int64_t)u.count - lo, kCopyUnitElems / BPU);
     block_copy(reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize,
                flat + (u.flat_elem + lo) * esize, n * esize);
 }
 
-// Loads through a generic pointer compile to flat instructions, which the
-// scalar-load counter also tracks, so a wait for a scalar load would wait
-// for them too; these take the global address space.
-__device__ __forceinline__ u32x4 ld_stream_global(const char *p)
-{
-    typedef __attribute__((address_space(1))) const u32x4_ua gvec;
-    return __builtin_nontemporal_load(reinterpret_cast<gvec *>(reinterpret_cast<uintptr_t>(p)));
-}
-__device__ __forceinline__ uint16_t ld_u16_global(const char *p)
-{
-    typedef __attribute__((address_space(1))) const uint16_t g16;
-    return *reinterpret_cast<g16 *>(reinterpret_cast<uintptr_t>(p));
-}
-
-// A unit's flat bytes [beg, end) and the source address of beg.
-struct UnitSpan {
-    uintptr_t beg, end;
-    const char *src;
-};
-
-__device__ __forceinline__ UnitSpan unit_span(const ddp_copy_unit &u, uintptr_t flat, int esize)
-{
-    const uintptr_t beg = flat + (uintptr_t)(u.flat_elem * esize);
-    return {beg, beg + (uintptr_t)(u.count * esize),
-            reinterpret_cast<const char *>(u.param_addr) + u.param_elem * esize};
-}
-
-// Source of flat byte x >= d1 (past the block's own bytes): in unit v0
-// (cur), the unit after it (nxt, loaded with the block's own entry), or --
-// where units are shorter than a chunk -- one further on, walked to up to
-// range_end; null past the range's last unit.
-__device__ const char *source_past(const ddp_copy_unit *units, int64_t v0, int64_t range_end,
-                                   UnitSpan cur, UnitSpan nxt, uintptr_t flat, int esize,
-                                   uintptr_t x)
-{
-    if (x < cur.end) return cur.src + (x - cur.beg);
-    if (v0 + 1 >= range_end) return nullptr;
-    if (x < nxt.end) return nxt.src + (x - nxt.beg);
-    for (int64_t w = v0 + 2; w < range_end; ++w) {
-        const UnitSpan sp = unit_span(units[w], flat, esize);
-        if (x < sp.end) return sp.src + (x - sp.beg);
-    }
-    return nullptr;
-}
-
-// Flatten (param -> flat) with one writer per 16-byte chunk of the flat
-// buffer.  Parameters sit in the flat buffer at any element offset, so a
-// chunk often holds the end of one piece and the start of the next.  The
-// block whose flat bytes [d0, d1) hold a chunk's first byte writes the whole
-// chunk; the call's first block also writes the chunk holding the range's
-// first byte.  Chunks inside [d0, d1) take one vector load from the source
-// at its own alignment (any address) and an aligned store.  A chunk at an
-// edge (the head chunk, and the one that runs past d1) is written by 8
-// lanes, 2 bytes each, in one store instruction: bytes in [d0, d1) come
-// from this block's source, bytes from d1 on from the unit that holds them,
-// none before d0 (the head of a call's range) or past the range's last
-// unit.  The next unit's entry is loaded with the block's own, and the
-// edge lanes' loads go out with the vector loads, so a block makes one
-// round trip to memory.  Bytes before a block's first chunk are left to the
-// block before it.  Written in 2-byte pieces by two blocks each, as an
-// earlier version did, such chunks cost many small unaligned parameters 3 %
-// of their bandwidth.  A block with no edge chunk (every block of a tensor
-// whose flat offset is a multiple of 16 bytes) takes a straight-line path:
-// the edge bookkeeping ahead of its loads cost such tensors 5 %.
+// Flatten (param -> flat), the bulk.  Parameters sit in the flat buffer at
+// any element offset, so the 16-byte chunk that holds a parameter's last
+// bytes often holds the next one's first bytes too.  Each block writes the
+// chunks that start in its bytes [d0, d1) and end inside its parameter
+// (counting the parameter's bytes past d1, `more` of them past the unit):
+// one vector load from the source at its own alignment (any address) and
+// an aligned 16-byte store each.  The chunk that holds a parameter's end
+// when that end is not on a chunk boundary, and the chunk before the
+// range's first byte, are left to flatten_edges.  So every chunk has one
+// writer and every store is whole; these blocks do nothing else, and a
+// parameter whose bytes start and end on chunk boundaries needs no edge
+// pass at all.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
-              int64_t range_first, int64_t range_end, char *flat, int esize)
+              char *flat, int esize)
 {
     int64_t lo;
     const int64_t ui = unit_of_block<BPU>(run, &lo);
     if (ui >= n_units) return;
-    const int64_t v0 = first + ui;
-    const ddp_copy_unit u = units[v0];
-    const ddp_copy_unit un = units[min(v0 + 1, range_end - 1)];
-    // both entries arrive together, before any data load is in flight
-    asm volatile("" ::"s"(un.param_addr), "s"(un.param_elem), "s"(un.flat_elem), "s"(un.count));
+    const ddp_copy_unit u = units[first + ui];
     if (lo >= u.count) return;
-    const int64_t n = min(u.count - lo, kCopyUnitElems / BPU);
+    const int64_t n = min((int64_t)u.count - lo, kCopyUnitElems / BPU);
     const char *src = reinterpret_cast<const char *>(u.param_addr) + (u.param_elem + lo) * esize;
-    const uintptr_t fb = reinterpret_cast<uintptr_t>(flat);
-    const uintptr_t d0 = fb + (uintptr_t)((u.flat_elem + lo) * esize);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(flat) + (uintptr_t)((u.flat_elem + lo) * esize);
     const uintptr_t d1 = d0 + (uintptr_t)(n * esize);
-    const bool head = v0 == range_first && lo == 0 && (d0 & 15);
-    const uintptr_t cf = head ? (d0 & ~(uintptr_t)15) : ((d0 + 15) & ~(uintptr_t)15);
+    const uintptr_t after = (uintptr_t)(((int64_t)u.count - lo - n + u.more) * esize);
+    const uintptr_t cf = (d0 + 15) & ~(uintptr_t)15;
     if (cf >= d1) return;                                // no chunk starts here
-    const int64_t nch = (int64_t)((d1 - cf + 15) >> 4);  // chunks [cf, cf + 16 nch), <= 513
-    const bool spill = (d1 & 15) != 0;                   // the last chunk runs past d1
-    const int64_t kb = head ? 1 : 0, ke = spill ? nch - 1 : nch;   // whole chunks [kb, ke)
+    int64_t nch = (int64_t)((d1 - cf + 15) >> 4);        // chunks starting in [d0, d1), <= 512
+    if (cf + 16 * (uintptr_t)nch > d1 + after) --nch;    // the last holds the parameter's end
     const int tid = threadIdx.x;
-    if (((d0 | d1) & 15) == 0) {   // [d0, d1) is whole chunks: cf = d0, kb = 0, ke = nch
-        const int64_t k0 = tid, k1 = tid + kCopyThreads;
-        u32x4 *dv = reinterpret_cast<u32x4 *>(d0);
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (k0 < ke) a = ld_stream(src + 16 * k0);
-        if (k1 < ke) b = ld_stream(src + 16 * k1);
-        if (k0 < ke) __builtin_nontemporal_store(a, dv + k0);
-        if (k1 < ke) __builtin_nontemporal_store(b, dv + k1);
-        return;
-    }
-    // edge lanes: 0-7 the head chunk, the last 8 the chunk past d1 (unless
-    // it is the head chunk too); their sources first, so that their loads
-    // go out with the vector loads
-    const int e = tid - (kCopyThreads - 8);
-    uintptr_t x = 0;
-    if (head && tid < 8) x = cf + 2 * (uintptr_t)tid;
-    else if (spill && (nch > 1 || !head) && e >= 0) x = cf + 16 * (uintptr_t)(nch - 1) + 2 * e;
-    const char *ps = nullptr;
-    if (x >= d0 && x < d1)
-        ps = src + (x - d0);
-    else if (x >= d1)
-        ps = source_past(units, v0, range_end, unit_span(u, fb, esize), unit_span(un, fb, esize),
-                         fb, esize, x);
-    const int64_t k0 = kb + tid, k1 = kb + tid + kCopyThreads;     // ke - kb <= 512
-    // Lanes past the last whole chunk load it again (their loads merge with
-    // its own), so both loads go out unconditionally and no lane waits for
-    // one before the other is issued; only the stores are predicated.
-    const int64_t klast = max(ke - 1, kb);
+    const int64_t k0 = tid, k1 = tid + kCopyThreads;
+    const char *s = src + (cf - d0);
+    u32x4 *dv = reinterpret_cast<u32x4 *>(cf);
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (ke > kb) {
-        a = ld_stream_global(src + (cf + 16 * (uintptr_t)min(k0, klast) - d0));
-        b = ld_stream_global(src + (cf + 16 * (uintptr_t)min(k1, klast) - d0));
-    }
-    uint16_t piece = 0;
-    if (ps) piece = ld_u16_global(ps);
-    u32x4 *cv = reinterpret_cast<u32x4 *>(cf);
-    if (k0 < ke) __builtin_nontemporal_store(a, cv + k0);
-    if (k1 < ke) __builtin_nontemporal_store(b, cv + k1);
-    if (ps) *reinterpret_cast<uint16_t *>(x) = piece;
+    if (k0 < nch) a = ld_stream(s + 16 * k0);
+    if (k1 < nch) b = ld_stream(s + 16 * k1);
+    if (k0 < nch) __builtin_nontemporal_store(a, dv + k0);
+    if (k1 < nch) __builtin_nontemporal_store(b, dv + k1);
+}
+
+constexpr int kEdgeThreads = 256;
+
+// A parameter's start in the flat buffer: its first unit and flat element.
+struct TensorStart {
+    int64_t unit, flat_elem;
+};
+
+// The unit of [lo_unit, hi_unit) whose flat elements hold element f, found
+// from unit `w` (whose span is [wb, we)) by walking: one step in all but
+// layouts with parameters shorter than a 16-byte chunk.
+__device__ __forceinline__ ddp_copy_unit unit_holding(const ddp_copy_unit *units, int64_t w,
+                                                      int64_t f)
+{
+    ddp_copy_unit u = units[w];
+    while (f < u.flat_elem) u = units[--w];
+    while (f >= u.flat_elem + u.count) u = units[++w];
+    return u;
+}
+
+// Flatten, the chunks flatten_units leaves.  Boundary i of the range is the
+// first flat element of its i-th parameter, and after the last one the
+// range's end.  A boundary inside a 16-byte chunk (not on its first byte)
+// makes the chunk an edge chunk, which the chunk's first such boundary
+// takes.  Eight lanes serve boundary i, lane p the chunk's bytes
+// [2p, 2p + 2): bytes before the boundary come from the unit before it,
+// bytes from it on from its parameter's first unit (or, where parameters
+// are shorter than a chunk, a unit further off), none outside the range.
+// The eight lanes store in one instruction, so the chunk is written whole.
+__global__ void __launch_bounds__(kEdgeThreads)
+flatten_edges(const ddp_copy_unit *units, const TensorStart *starts, int64_t nb, int64_t first,
+              int64_t last, int64_t r0e, int64_t r1e, char *flat, int esize)
+{
+    const int64_t lane = (int64_t)blockIdx.x * kEdgeThreads + threadIdx.x;
+    const int64_t i = lane >> 3;
+    const int p = (int)(lane & 7);
+    if (i > nb) return;
+    const uintptr_t fb = reinterpret_cast<uintptr_t>(flat);
+    const TensorStart ts = i < nb ? starts[i] : TensorStart{last, r1e};
+    const uintptr_t b = fb + (uintptr_t)(ts.flat_elem * esize);
+    if ((b & 15) == 0) return;
+    const uintptr_t c = b & ~(uintptr_t)15;
+    if (i > 0 && fb + (uintptr_t)(starts[i - 1].flat_elem * esize) > c)
+        return;                                      // an earlier boundary in the chunk takes it
+    const uintptr_t x = c + 2 * (uintptr_t)p;
+    const uintptr_t r0 = fb + (uintptr_t)(r0e * esize), r1 = fb + (uintptr_t)(r1e * esize);
+    if (x < r0 || x >= r1) return;
+    // element f holds byte x; the unit before the boundary or the one at it
+    const int64_t f = (int64_t)((x - fb) / (uintptr_t)esize);
+    const ddp_copy_unit u = unit_holding(units, x < b ? ts.unit - 1 : ts.unit, f);
+    const char *s = reinterpret_cast<const char *>(u.param_addr) + u.param_elem * esize +
+                    (x - (fb + (uintptr_t)(u.flat_elem * esize)));
+    *reinterpret_cast<uint16_t *>(x) = *reinterpret_cast<const uint16_t *>(s);
 }
 
 }  // namespace
@@ -265,42 +230,59 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
         return hip_fail("hipGetDevice", e);
     }
     std::vector<ddp_copy_unit> units;
+    std::vector<TensorStart> tfirst;   // each parameter's first unit and flat element
     try {
         bd->param_addr.resize((size_t)plan->n_params);
         for (int32_t p = 0; p < plan->n_params; ++p)
             bd->param_addr[p] = reinterpret_cast<uint64_t>(param_grads[p]);
         const int32_t nb = plan->n_buckets();
         bd->bucket_first_unit.resize((size_t)nb + 1);
+        bd->bucket_first_tensor.resize((size_t)nb + 1);
+        bd->bucket_edge_mask.assign((size_t)nb, 0);
         for (int32_t b = 0; b < nb; ++b) {
             bd->bucket_first_unit[b] = (int64_t)units.size();
+            bd->bucket_first_tensor[b] = (int64_t)tfirst.size();
             int64_t flat = plan->bucket_base[b];
             for (int32_t s = plan->bucket_first_slot[b]; s < plan->bucket_first_slot[b + 1]; ++s) {
                 const int32_t p = plan->slot_param[s];
                 const int64_t n = plan->numel[p];
+                if (n > 0) {
+                    tfirst.push_back(TensorStart{(int64_t)units.size(), flat});
+                    bd->bucket_edge_mask[b] |= (uint8_t)(1u << (flat & 7));
+                }
                 for (int64_t off = 0; off < n; off += kCopyUnitElems) {
                     ddp_copy_unit u;
                     u.param_addr = reinterpret_cast<uint64_t>(param_grads[p]);
                     u.param_elem = off;
                     u.flat_elem = flat + off;
-                    u.count = std::min<int64_t>(kCopyUnitElems, n - off);
+                    u.count = (int32_t)std::min<int64_t>(kCopyUnitElems, n - off);
+                    u.more = (int32_t)std::min<int64_t>(16, n - off - u.count);
                     units.push_back(u);
                 }
                 flat += n;
             }
+            bd->bucket_edge_mask[b] |= (uint8_t)(1u << (flat & 7));   // the bucket's end
         }
         bd->bucket_first_unit[nb] = (int64_t)units.size();
+        bd->bucket_first_tensor[nb] = (int64_t)tfirst.size();
     } catch (...) {
         delete bd;
         return DDP_ERR_NOMEM;
     }
     bd->n_units = (int64_t)units.size();
     if (bd->n_units > 0) {
-        const size_t bytes = sizeof(ddp_copy_unit) * units.size();
+        // one allocation: the units, then the parameters' starts
+        const size_t ubytes = sizeof(ddp_copy_unit) * units.size();
+        const size_t bytes = ubytes + sizeof(TensorStart) * tfirst.size();
+        static_assert(sizeof(ddp_copy_unit) % alignof(TensorStart) == 0, "tensor_first alignment");
         if ((e = hipMalloc(&bd->units, bytes)) != hipSuccess) {
             delete bd;
             return hip_fail("hipMalloc (copy units)", e, DDP_ERR_NOMEM);
         }
-        if ((e = hipMemcpy(bd->units, units.data(), bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        bd->tensor_first = reinterpret_cast<int64_t *>(bd->units + units.size());
+        if ((e = hipMemcpy(bd->units, units.data(), ubytes, hipMemcpyHostToDevice)) != hipSuccess ||
+            (e = hipMemcpy(bd->tensor_first, tfirst.data(), sizeof(TensorStart) * tfirst.size(),
+                           hipMemcpyHostToDevice)) != hipSuccess) {
             (void)hipFree(bd->units);
             delete bd;
             return hip_fail("hipMemcpy (copy units)", e);
@@ -346,17 +328,17 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t cap = max_launch_items() / (kCopyThreads * bpu);
     const int64_t run = std::min<int64_t>(kCopyRun, cap / kXcds);
     const int64_t round = kXcds * run, per = cap / round * round;
+    char *fl = static_cast<char *>(flat);
+    hipStream_t st = static_cast<hipStream_t>(stream);
     for (int64_t u0 = first; u0 < last; u0 += per) {
         const int64_t n = std::min(per, last - u0);
         const dim3 g((unsigned)((n + round - 1) / round * round * bpu)), b(kCopyThreads);
         const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
-        char *fl = static_cast<char *>(flat);
-        hipStream_t st = static_cast<hipStream_t>(stream);
         const unsigned r = (unsigned)run;
         if (to_flat && bpu == 1)
-            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, first, last, fl, esize);
+            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
         else if (to_flat)
-            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, first, last, fl, esize);
+            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
         else if (bpu == 1)
             unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
         else
@@ -364,7 +346,24 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
         const ddp_status_t s = launched("copy kernel launch");
         if (s != DDP_OK) return s;
     }
-    return DDP_OK;
+    if (!to_flat) return DDP_OK;
+    // the edge pass, when a parameter of the range starts or the range ends
+    // off a 16-byte boundary of this flat buffer
+    const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
+    unsigned mask = 0;
+    for (int32_t b = b0; b < b1; ++b) mask |= bd->bucket_edge_mask[b];
+    bool edges = false;
+    for (int k = 0; k < 8; ++k)
+        if ((mask >> k & 1u) && ((reinterpret_cast<uintptr_t>(flat) + (uintptr_t)(k * esize)) & 15))
+            edges = true;
+    if (!edges) return DDP_OK;
+    const int64_t t0 = bd->bucket_first_tensor[b0], nt = bd->bucket_first_tensor[b1] - t0;
+    const TensorStart *ts = reinterpret_cast<const TensorStart *>(bd->tensor_first) + t0;
+    const int64_t lanes = 8 * (nt + 1);   // 8 lanes per boundary; n_params < 2^31
+    flatten_edges<<<dim3((unsigned)((lanes + kEdgeThreads - 1) / kEdgeThreads)), dim3(kEdgeThreads),
+                    0, st>>>(bd->units, ts, nt, first, last, plan->bucket_base[b0],
+                             plan->bucket_base[b1], fl, esize);
+    return launched("flatten edge launch");
 }
 
 ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,

@@ -47,15 +47,21 @@ struct ddp_copy_unit {
     uint64_t param_addr;   // device address of the parameter's gradient
     int64_t param_elem;    // first element of this unit inside the parameter
     int64_t flat_elem;     // first flat element of this unit
-    int64_t count;         // elements, 1..kCopyUnitElems
+    int32_t count;         // elements, 1..kCopyUnitElems
+    int32_t more;          // elements of the same parameter after this unit, at most 16
 };
 
 struct ddp_binding {
     const ddp_plan *plan = nullptr;
     int device = -1;
-    ddp_copy_unit *units = nullptr;           // device array
+    ddp_copy_unit *units = nullptr;           // device array: the units, then tensor_first
     int64_t n_units = 0;
+    int64_t *tensor_first = nullptr;          // device: each parameter's first unit and flat
+                                              // element (pairs of int64), in flat order
     std::vector<int64_t> bucket_first_unit;   // [n_buckets + 1]
+    std::vector<int64_t> bucket_first_tensor; // [n_buckets + 1] into tensor_first
+    std::vector<uint8_t> bucket_edge_mask;    // [n_buckets] bit f % 8 for every flat element f
+                                              // at which one of its parameters starts or it ends
     std::vector<uint64_t> param_addr;         // [n_params] the bound gradient pointers
 };
 
