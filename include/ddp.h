@@ -184,7 +184,8 @@ DDP_API ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
  *   stream                 unused for now (the table upload is synchronous)
  * The binding copies the pointer array; it does not own the gradients.  It
  * keeps a device table of 32 bytes per 4096 elements of each parameter
- * (rounded up per parameter) until ddp_binding_free.
+ * (rounded up per parameter), plus 16 bytes per parameter with elements,
+ * until ddp_binding_free.
  * Errors: INVALID_ARG (null plan/array/out, a null pointer for a parameter
  * with numel > 0, misaligned pointer), HIP, NOMEM. */
 DDP_API ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
@@ -192,10 +193,13 @@ DDP_API ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_
 DDP_API void ddp_binding_free(ddp_binding_t *binding);
 
 /* flat_buf[base_b + offset_p + j] = grad_p[j] for every parameter p of
- * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch.
- * flat_buf: device, ddp_plan_total(plan) elements, must not overlap any
- * parameter buffer.  Errors: INVALID_ARG (null, bucket out of range, bad
- * dtype, binding of another plan), HIP. */
+ * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch, and a
+ * second, small one when a parameter of the range starts, or the range
+ * ends, off a 16-byte boundary of flat_buf (it writes the 16-byte pieces
+ * that hold two parameters).  Bytes of flat_buf outside the range are not
+ * written.  flat_buf: device, ddp_plan_total(plan) elements, must not
+ * overlap any parameter buffer.  Errors: INVALID_ARG (null, bucket out of
+ * range, bad dtype, binding of another plan), HIP. */
 DDP_API ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
                          int32_t bucket, void *flat_buf, ddp_dtype_t dtype,
                          void *stream);
