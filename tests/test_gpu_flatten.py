@@ -165,3 +165,57 @@ def test_flatten_tiny_tensors_at_any_offset(env, dt, flat_off):
         lo, hi = op.bucket_base[b], op.bucket_base[b] + op.bucket_len[b]
         assert_bits_equal(h[lo:hi], want[lo:hi], f"{dt} flat+{flat_off} bucket {b}")
         assert (h[:lo] == nine).all() and (h[hi:] == nine).all(), f"bucket {b} wrote outside"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_flatten_random_layouts(env, seed):
+    """Seeded random layouts: 1-200 parameters of 0-9000 elements, a third
+    of them shorter than a 16-byte chunk; f32 or bf16; caps from a few
+    elements to whole-plan; the flat buffer at a random element offset; the
+    whole plan, then every bucket (up to 40) on its own, each against the
+    oracle, with nothing outside the call's range written."""
+    torch, ddp = env
+    rng = np.random.default_rng(500 + seed)
+    for case in range(4):
+        dt = "f32" if rng.random() < 0.5 else "bf16"
+        eb = 4 if dt == "f32" else 2
+        n = int(rng.integers(1, 201))
+        sizes = [int(rng.integers(0, 16)) if rng.random() < 1 / 3 else int(rng.integers(16, 9001))
+                 for _ in range(n)]
+        cap = int(rng.choice([4, 64, 1000, 40000, 1 << 30])) * eb
+        lp = ddp.plan_buckets(sizes, cap, dt)
+        op = oracle.plan_cap(sizes, cap, eb)
+        assert lp.buckets() == op.buckets
+        P = op.total
+        flat_off = int(rng.integers(0, 8))
+        tag = f"seed={seed} case={case} {dt} n={n} cap={cap} P={P} B={op.n_buckets} off={flat_off}"
+        print(tag, flush=True)
+        if P == 0:
+            continue
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        host = []
+        for k in sizes:
+            x = rng.standard_normal(k).astype(np.float32)
+            host.append(x if dt == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16))
+        big, views, _ = _carve(torch, sizes, tdt, rng, bool(rng.random() < 0.5))
+        for v, h in zip(views, host):
+            if h.size:
+                v.copy_(to_dev(h, torch))
+        binding = ddp.bind_params(lp, views)
+        want = oracle.flatten(op, host)
+        store = torch.full((flat_off + P + 16,), 9.0, dtype=tdt, device="cuda:0")
+        flat = store[flat_off:flat_off + P]
+        nine = to_host(torch.full((1,), 9.0, dtype=tdt, device="cuda:0"), torch)[0]
+        ddp.flatten(lp, binding, flat)
+        torch.cuda.synchronize()
+        h = to_host(store, torch)
+        assert_bits_equal(h[flat_off:flat_off + P], want, "whole " + tag)
+        assert (h[:flat_off] == nine).all() and (h[flat_off + P:] == nine).all(), tag
+        for b in range(min(lp.n_buckets, 40)):
+            store.fill_(9.0)
+            ddp.flatten(lp, binding, flat, bucket=b)
+            torch.cuda.synchronize()
+            h = to_host(store, torch)[flat_off:flat_off + P]
+            lo, hi = op.bucket_base[b], op.bucket_base[b] + op.bucket_len[b]
+            assert_bits_equal(h[lo:hi], want[lo:hi], f"bucket {b} " + tag)
+            assert (h[:lo] == nine).all() and (h[hi:] == nine).all(), f"bucket {b} wrote outside {tag}"
