@@ -262,6 +262,7 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
                 flat += n;
             }
             bd->bucket_edge_mask[b] |= (uint8_t)(1u << (flat & 7));   // the bucket's end
+            bd->edge_mask |= bd->bucket_edge_mask[b];
         }
         bd->bucket_first_unit[nb] = (int64_t)units.size();
         bd->bucket_first_tensor[nb] = (int64_t)tfirst.size();
@@ -350,8 +351,7 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     // the edge pass, when a parameter of the range starts or the range ends
     // off a 16-byte boundary of this flat buffer
     const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
-    unsigned mask = 0;
-    for (int32_t b = b0; b < b1; ++b) mask |= bd->bucket_edge_mask[b];
+    const unsigned mask = bucket < 0 ? bd->edge_mask : bd->bucket_edge_mask[bucket];
     bool edges = false;
     for (int k = 0; k < 8; ++k)
         if ((mask >> k & 1u) && ((reinterpret_cast<uintptr_t>(flat) + (uintptr_t)(k * esize)) & 15))

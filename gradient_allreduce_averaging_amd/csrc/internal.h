@@ -62,6 +62,7 @@ struct ddp_binding {
     std::vector<int64_t> bucket_first_tensor; // [n_buckets + 1] into tensor_first
     std::vector<uint8_t> bucket_edge_mask;    // [n_buckets] bit f % 8 for every flat element f
                                               // at which one of its parameters starts or it ends
+    uint8_t edge_mask = 0;                    // the union over all buckets
     std::vector<uint64_t> param_addr;         // [n_params] the bound gradient pointers
 };
 
