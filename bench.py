@@ -7,8 +7,9 @@ synchronisation of the workload: every bucket of the plan reduced over the N
 virtual ranks in the fixed order, scaled by 1/N and written -- one launch of
 ddp_sync_allreduce_avg.  Gradients sit in their bucket buffers (the
 gradient-as-bucket-view layout), so flatten and unflatten are not needed in
-the step; the ResNet-50 record also times the copy layout (flatten every
-rank, sync, unflatten) under "copy_path".
+the step; the ResNet-50 and many-small records also time the copy layout
+(flatten every rank, sync, unflatten; the copies in bf16 as well) under
+"copy_path".
 
 The headline is GPT-1.3B (1.3 G f32 gradients, 8 virtual ranks, 146 buckets
 of 25 MiB, ring order).  Every workload runs in a fresh child process of its
