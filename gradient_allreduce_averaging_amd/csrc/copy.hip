@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -23,51 +24,7 @@ namespace {
 
 constexpr int64_t kCopyRun = 64;   // consecutive copy units per XCD (unit_of_block)
 
-__device__ __forceinline__ void copy16b(char *dst, const char *src, int64_t lo, int64_t hi)
-{
-    for (int64_t j = lo + 2 * (int64_t)threadIdx.x; j < hi; j += 2 * kCopyThreads)
-        *reinterpret_cast<uint16_t *>(dst + j) = *reinterpret_cast<const uint16_t *>(src + j);
-}
-
-// Block-wide copy of nbytes (a multiple of 2, at most kCopyBlockBytes)
-// between 2-byte aligned addresses: 16-byte non-temporal accesses from the
-// destination's first 16-byte boundary, at most two per thread, a thread's
-// loads before its stores.  The loads run at whatever alignment the source
-// has (gfx9 and later global loads take any address), so a tensor whose flat
-// offset is not a multiple of 16 bytes still moves in 16-byte vectors; a head
-// and tail of under 16 bytes move 2 bytes per thread.  A piece with neither
-// (every piece of a 16-byte aligned tensor) takes a straight-line path; on
-// the others the head goes first, which measured faster there than issuing
-// the vector loads before it.
 static_assert(kCopyBlockBytes == 2 * 16 * kCopyThreads, "two vectors per thread cover a block");
-__device__ void block_copy(char *dst, const char *src, int64_t nbytes)
-{
-    const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
-    const int tid = threadIdx.x;
-    const int64_t head = min<int64_t>((16 - (d & 15)) & 15, nbytes);
-    const int64_t nvec = (nbytes - head) >> 4;   // at most 2 * kCopyThreads
-    const char *sv = src + head;
-    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
-    if (head == 0 && (nbytes & 15) == 0) {
-        const int64_t j0 = tid, j1 = tid + kCopyThreads;
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (j0 < nvec) a = ld_stream(sv + 16 * j0);
-        if (j1 < nvec) b = ld_stream(sv + 16 * j1);
-        if (j0 < nvec) __builtin_nontemporal_store(a, dv + j0);
-        if (j1 < nvec) __builtin_nontemporal_store(b, dv + j1);
-        return;
-    }
-    copy16b(dst, src, 0, head);
-    int64_t j = tid;
-    for (; j + kCopyThreads < nvec; j += 2 * kCopyThreads) {
-        const u32x4 a = ld_stream(sv + 16 * j);
-        const u32x4 b = ld_stream(sv + 16 * (j + kCopyThreads));
-        __builtin_nontemporal_store(a, dv + j);
-        __builtin_nontemporal_store(b, dv + j + kCopyThreads);
-    }
-    for (; j < nvec; j += kCopyThreads) __builtin_nontemporal_store(ld_stream(sv + 16 * j), dv + j);
-    copy16b(dst, src, head + (nvec << 4), nbytes);
-}
 
 // Block -> unit mapping of both copy kernels.  BPU blocks per copy unit
 // (copy_blocks_per_unit: 8 KiB a block), each moving its share of the unit
@@ -92,11 +49,18 @@ __device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
     return (int64_t)((j / run) * kXcds + blockIdx.x % kXcds) * run + j % run;
 }
 
-// Unflatten (flat -> param): each block copies its part of a unit into the
-// parameter.  A parameter's storage usually starts on the allocator's
-// alignment, so its pieces, all but its last, start and end on a 16-byte
-// boundary and no two blocks share a chunk; block_copy takes any 2-byte
-// alignment all the same.
+// Unflatten (flat -> param), the bulk: the mirror of flatten_units with the
+// roles of the buffers swapped.  Parameter views carved out of one buffer
+// sit at any alignment, so a 16-byte chunk of parameter storage can hold
+// bytes of two units of one parameter, or of two parameters.  Each block
+// writes the chunks that start in its bytes [d0, d1) of the parameter and
+// end inside it, one aligned store each, reading the flat buffer, where a
+// parameter's units are contiguous, at its own alignment.  The chunks at the
+// parameter's two ends are partial: one that holds no other parameter's
+// bytes is written here, 2 bytes per lane in one store instruction; one that
+// does (flags in the unit entry, for this element size) is left to
+// unflatten_edges.  Parameters that start on the allocator's alignment, as
+// separate tensors do, have no first partial chunk and share no chunk.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
@@ -108,8 +72,54 @@ unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsi
     const ddp_copy_unit u = units[first + ui];
     if (lo >= u.count) return;
     const int64_t n = min((int64_t)u.count - lo, kCopyUnitElems / BPU);
-    block_copy(reinterpret_cast<char *>(u.param_addr) + (u.param_elem + lo) * esize,
-               flat + (u.flat_elem + lo) * esize, n * esize);
+    const char *src = flat + (u.flat_elem + lo) * esize;
+    const uintptr_t d0 = (uintptr_t)u.param_addr + (uintptr_t)((u.param_elem + lo) * esize);
+    const uintptr_t d1 = d0 + (uintptr_t)(n * esize);
+    const int more = u.more & 0xff, sh = 8 + 2 * (esize >> 2);   // esize 2: bits 8-9, 4: 10-11
+    const uintptr_t pend = d1 + (uintptr_t)(((int64_t)u.count - lo - n + more) * esize);
+    const bool shared_head = (u.more >> sh) & 1, shared_tail = (u.more >> (sh + 1)) & 1;
+    const uintptr_t cf = (d0 + 15) & ~(uintptr_t)15;
+    const int tid = threadIdx.x;
+    // the parameter's first chunk, partial, when no other parameter shares it
+    if (u.param_elem + lo == 0 && cf != d0 && !shared_head) {
+        const uintptr_t x = d0 + 2 * (uintptr_t)tid, xe = min(cf, pend);
+        if (tid < 8 && x < xe)
+            *reinterpret_cast<uint16_t *>(x) = *reinterpret_cast<const uint16_t *>(src + (x - d0));
+    }
+    if (cf >= d1) return;                                // no chunk starts here
+    int64_t nch = (int64_t)((d1 - cf + 15) >> 4);        // chunks starting in [d0, d1), <= 512
+    const uintptr_t cl = cf + 16 * (uintptr_t)(nch - 1);
+    const bool tail = cl + 16 > pend;                    // the last holds the parameter's end
+    if (tail) --nch;
+    const int64_t k0 = tid, k1 = tid + kCopyThreads;
+    const char *s = src + (cf - d0);
+    u32x4 *dv = reinterpret_cast<u32x4 *>(cf);
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    uint16_t t = 0;
+    const uintptr_t xt = cl + 2 * (uintptr_t)(tid - (kCopyThreads - 8));
+    const bool tl = tail && !shared_tail && tid >= kCopyThreads - 8 && xt < pend;
+    if (k0 < nch) a = ld_stream(s + 16 * k0);
+    if (k1 < nch) b = ld_stream(s + 16 * k1);
+    if (tl) t = *reinterpret_cast<const uint16_t *>(src + (xt - d0));
+    if (k0 < nch) __builtin_nontemporal_store(a, dv + k0);
+    if (k1 < nch) __builtin_nontemporal_store(b, dv + k1);
+    if (tl) *reinterpret_cast<uint16_t *>(xt) = t;       // the last 8 lanes: one store
+}
+
+// Unflatten, the chunks two or more parameters share: eight lanes per chunk,
+// lane k copying the chunk's bytes [2k, 2k + 2) from the flat buffer where
+// they belong to a parameter of the bucket, in one store instruction.
+__global__ void __launch_bounds__(kCopyThreads)
+unflatten_edges(const ddp_unflatten_edge *edges, int64_t n, const char *flat)
+{
+    const int64_t lane = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    const int64_t i = lane >> 3;
+    if (i >= n) return;
+    const int k = (int)(lane & 7);
+    const int64_t off = edges[i].piece[k];
+    if (off < 0) return;
+    *reinterpret_cast<uint16_t *>(edges[i].chunk + 2 * (uint64_t)k) =
+        *reinterpret_cast<const uint16_t *>(flat + off);
 }
 
 // Flatten (param -> flat), the bulk.  Parameters sit in the flat buffer at
@@ -138,7 +148,7 @@ flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsign
     const char *src = reinterpret_cast<const char *>(u.param_addr) + (u.param_elem + lo) * esize;
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(flat) + (uintptr_t)((u.flat_elem + lo) * esize);
     const uintptr_t d1 = d0 + (uintptr_t)(n * esize);
-    const uintptr_t after = (uintptr_t)(((int64_t)u.count - lo - n + u.more) * esize);
+    const uintptr_t after = (uintptr_t)(((int64_t)u.count - lo - n + (u.more & 0xff)) * esize);
     const uintptr_t cf = (d0 + 15) & ~(uintptr_t)15;
     if (cf >= d1) return;                                // no chunk starts here
     int64_t nch = (int64_t)((d1 - cf + 15) >> 4);        // chunks starting in [d0, d1), <= 512
@@ -208,6 +218,72 @@ flatten_edges(const ddp_copy_unit *units, const TensorStart *starts, int64_t nb,
     *reinterpret_cast<uint16_t *>(x) = *reinterpret_cast<const uint16_t *>(s);
 }
 
+// Unflatten's shared chunks for elements of `es` bytes: every 16-byte chunk
+// of parameter storage that holds bytes of two or more bound parameters (a
+// parameter's first or last chunk when it starts or ends off a 16-byte
+// boundary).  Sets the parameters' shared-head and shared-tail flags and
+// returns the chunks' edge entries grouped by bucket, with the start of
+// each bucket's group in first[].
+std::vector<ddp_unflatten_edge> unflatten_edges_for(const ddp_plan *plan, void *const *grads,
+                                                    int64_t es, std::vector<uint8_t> &flags,
+                                                    int shift, std::vector<int64_t> &first)
+{
+    const int32_t nb = plan->n_buckets();
+    std::vector<int64_t> start((size_t)plan->n_params, 0);   // flat element of each parameter
+    std::vector<int32_t> bucket_of((size_t)plan->n_params, -1);
+    for (int32_t b = 0; b < nb; ++b) {
+        int64_t flat = plan->bucket_base[b];
+        for (int32_t sl = plan->bucket_first_slot[b]; sl < plan->bucket_first_slot[b + 1]; ++sl) {
+            const int32_t q = plan->slot_param[sl];
+            start[q] = flat;
+            bucket_of[q] = b;
+            flat += plan->numel[q];
+        }
+    }
+    std::map<uint64_t, std::vector<int32_t>> chunks;   // partial chunk -> its parameters
+    for (int32_t q = 0; q < plan->n_params; ++q) {
+        if (plan->numel[q] == 0) continue;
+        const uint64_t s0 = reinterpret_cast<uint64_t>(grads[q]), t = s0 + plan->numel[q] * es;
+        if (s0 & 15) chunks[s0 & ~15ull].push_back(q);
+        if ((t & 15) && (!(s0 & 15) || (t & ~15ull) != (s0 & ~15ull))) chunks[t & ~15ull].push_back(q);
+    }
+    std::vector<std::vector<ddp_unflatten_edge>> per((size_t)nb);
+    for (const auto &kv : chunks) {
+        if (kv.second.size() < 2) continue;
+        const uint64_t c = kv.first;
+        for (int32_t q : kv.second) {
+            const uint64_t s0 = reinterpret_cast<uint64_t>(grads[q]), t = s0 + plan->numel[q] * es;
+            if ((s0 & 15) && (s0 & ~15ull) == c) flags[q] |= (uint8_t)(1u << shift);
+            if ((t & 15) && (t & ~15ull) == c) flags[q] |= (uint8_t)(2u << shift);
+        }
+        std::vector<int32_t> bs;
+        for (int32_t q : kv.second)
+            if (std::find(bs.begin(), bs.end(), bucket_of[q]) == bs.end()) bs.push_back(bucket_of[q]);
+        for (int32_t b : bs) {
+            ddp_unflatten_edge ed;
+            ed.chunk = c;
+            for (int k = 0; k < 8; ++k) {
+                ed.piece[k] = -1;
+                const uint64_t x = c + 2 * (uint64_t)k;
+                for (int32_t q : kv.second) {
+                    const uint64_t s0 = reinterpret_cast<uint64_t>(grads[q]);
+                    if (bucket_of[q] == b && x >= s0 && x < s0 + plan->numel[q] * es)
+                        ed.piece[k] = start[q] * es + (int64_t)(x - s0);
+                }
+            }
+            per[b].push_back(ed);
+        }
+    }
+    std::vector<ddp_unflatten_edge> all;
+    first.assign((size_t)nb + 1, 0);
+    for (int32_t b = 0; b < nb; ++b) {
+        first[b] = (int64_t)all.size();
+        all.insert(all.end(), per[b].begin(), per[b].end());
+    }
+    first[nb] = (int64_t)all.size();
+    return all;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,7 +307,13 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
     }
     std::vector<ddp_copy_unit> units;
     std::vector<TensorStart> tfirst;   // each parameter's first unit and flat element
+    std::vector<ddp_unflatten_edge> uedges[2];
+    std::vector<uint8_t> pflags;       // per parameter: shared-chunk flags (unit `more` bits 8-11)
     try {
+        pflags.assign((size_t)plan->n_params, 0);
+        for (int k = 0; k < 2; ++k)
+            uedges[k] = unflatten_edges_for(plan, param_grads, (int64_t)2 << k, pflags, 2 * k,
+                                            bd->bucket_first_uedge[k]);
         bd->param_addr.resize((size_t)plan->n_params);
         for (int32_t p = 0; p < plan->n_params; ++p)
             bd->param_addr[p] = reinterpret_cast<uint64_t>(param_grads[p]);
@@ -256,7 +338,8 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
                     u.param_elem = off;
                     u.flat_elem = flat + off;
                     u.count = (int32_t)std::min<int64_t>(kCopyUnitElems, n - off);
-                    u.more = (int32_t)std::min<int64_t>(16, n - off - u.count);
+                    u.more = (int32_t)std::min<int64_t>(16, n - off - u.count) |
+                             (int32_t)pflags[p] << 8;
                     units.push_back(u);
                 }
                 flat += n;
@@ -272,18 +355,30 @@ ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads, v
     }
     bd->n_units = (int64_t)units.size();
     if (bd->n_units > 0) {
-        // one allocation: the units, then the parameters' starts
+        // one allocation: the units, the parameters' starts, unflatten's
+        // shared chunks for 2- and 4-byte elements
         const size_t ubytes = sizeof(ddp_copy_unit) * units.size();
-        const size_t bytes = ubytes + sizeof(TensorStart) * tfirst.size();
-        static_assert(sizeof(ddp_copy_unit) % alignof(TensorStart) == 0, "tensor_first alignment");
-        if ((e = hipMalloc(&bd->units, bytes)) != hipSuccess) {
+        const size_t tbytes = sizeof(TensorStart) * tfirst.size();
+        const size_t e0 = sizeof(ddp_unflatten_edge) * uedges[0].size();
+        const size_t e1 = sizeof(ddp_unflatten_edge) * uedges[1].size();
+        static_assert(sizeof(ddp_copy_unit) % alignof(TensorStart) == 0 &&
+                          sizeof(TensorStart) % alignof(ddp_unflatten_edge) == 0,
+                      "table alignment");
+        if ((e = hipMalloc(&bd->units, ubytes + tbytes + e0 + e1)) != hipSuccess) {
             delete bd;
             return hip_fail("hipMalloc (copy units)", e, DDP_ERR_NOMEM);
         }
-        bd->tensor_first = reinterpret_cast<int64_t *>(bd->units + units.size());
+        char *base = reinterpret_cast<char *>(bd->units);
+        bd->tensor_first = reinterpret_cast<int64_t *>(base + ubytes);
+        bd->uedges[0] = reinterpret_cast<ddp_unflatten_edge *>(base + ubytes + tbytes);
+        bd->uedges[1] = reinterpret_cast<ddp_unflatten_edge *>(base + ubytes + tbytes + e0);
         if ((e = hipMemcpy(bd->units, units.data(), ubytes, hipMemcpyHostToDevice)) != hipSuccess ||
-            (e = hipMemcpy(bd->tensor_first, tfirst.data(), sizeof(TensorStart) * tfirst.size(),
-                           hipMemcpyHostToDevice)) != hipSuccess) {
+            (e = hipMemcpy(bd->tensor_first, tfirst.data(), tbytes, hipMemcpyHostToDevice)) !=
+                hipSuccess ||
+            (e0 && (e = hipMemcpy(bd->uedges[0], uedges[0].data(), e0, hipMemcpyHostToDevice)) !=
+                       hipSuccess) ||
+            (e1 && (e = hipMemcpy(bd->uedges[1], uedges[1].data(), e1, hipMemcpyHostToDevice)) !=
+                       hipSuccess)) {
             (void)hipFree(bd->units);
             delete bd;
             return hip_fail("hipMemcpy (copy units)", e);
@@ -347,7 +442,15 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
         const ddp_status_t s = launched("copy kernel launch");
         if (s != DDP_OK) return s;
     }
-    if (!to_flat) return DDP_OK;
+    if (!to_flat) {   // the shared chunks of the range's parameters, if any
+        const int k = esize == 4 ? 1 : 0;
+        const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
+        const int64_t e0 = bd->bucket_first_uedge[k][b0], ne = bd->bucket_first_uedge[k][b1] - e0;
+        if (ne == 0) return DDP_OK;
+        unflatten_edges<<<dim3((unsigned)((8 * ne + kCopyThreads - 1) / kCopyThreads)),
+                          dim3(kCopyThreads), 0, st>>>(bd->uedges[k] + e0, ne, fl);
+        return launched("unflatten edge launch");
+    }
     // the edge pass, when a parameter of the range starts or the range ends
     // off a 16-byte boundary of this flat buffer
     const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;

@@ -48,7 +48,19 @@ struct ddp_copy_unit {
     int64_t param_elem;    // first element of this unit inside the parameter
     int64_t flat_elem;     // first flat element of this unit
     int32_t count;         // elements, 1..kCopyUnitElems
-    int32_t more;          // elements of the same parameter after this unit, at most 16
+    int32_t more;          // bits 0-7: elements of the same parameter after this unit, at
+                           // most 16; bits 8 + 2e, 9 + 2e: the parameter's first / last
+                           // 16-byte chunk in its own storage is shared with another
+                           // parameter, for elements of 2 << e bytes (unflatten)
+};
+
+// A 16-byte chunk of parameter storage that holds bytes of two or more bound
+// parameters (views carved out of one buffer), as unflatten writes it for
+// one bucket: piece[k] is the flat byte offset of the chunk's bytes
+// [2k, 2k + 2), or -1 where they belong to no parameter of that bucket.
+struct ddp_unflatten_edge {
+    uint64_t chunk;
+    int64_t piece[8];
 };
 
 struct ddp_binding {
@@ -63,6 +75,9 @@ struct ddp_binding {
     std::vector<uint8_t> bucket_edge_mask;    // [n_buckets] bit f % 8 for every flat element f
                                               // at which one of its parameters starts or it ends
     uint8_t edge_mask = 0;                    // the union over all buckets
+    ddp_unflatten_edge *uedges[2] = {nullptr, nullptr};   // device, per element size 2 << e,
+                                              // grouped by bucket (in the units' allocation)
+    std::vector<int64_t> bucket_first_uedge[2];   // [n_buckets + 1] into uedges[e]
     std::vector<uint64_t> param_addr;         // [n_params] the bound gradient pointers
 };
 

@@ -184,8 +184,10 @@ DDP_API ddp_status_t ddp_plan_prepare_ranks(ddp_plan_t *plan, int32_t n_ranks);
  *   stream                 unused for now (the table upload is synchronous)
  * The binding copies the pointer array; it does not own the gradients.  It
  * keeps a device table of 32 bytes per 4096 elements of each parameter
- * (rounded up per parameter), plus 16 bytes per parameter with elements,
- * until ddp_binding_free.
+ * (rounded up per parameter), plus 16 bytes per parameter with elements and
+ * 72 bytes per bucket and element size (2 and 4 bytes) for each 16-byte
+ * piece of storage that two parameters share (views carved out of one
+ * buffer), until ddp_binding_free.
  * Errors: INVALID_ARG (null plan/array/out, a null pointer for a parameter
  * with numel > 0, misaligned pointer), HIP, NOMEM. */
 DDP_API ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_grads,
@@ -205,7 +207,10 @@ DDP_API ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *bi
                          void *stream);
 
 /* grad_p[j] = flat_out[base_b + offset_p + j]: the inverse copy, elements of
- * `dtype` (the sync's output type).  Same arguments and errors. */
+ * `dtype` (the sync's output type).  One launch, and a second, small one
+ * when parameters of the range share 16-byte pieces of storage (it writes
+ * those pieces).  Bytes outside the range's parameters are not written.
+ * Same arguments and errors. */
 DDP_API ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
                            int32_t bucket, const void *flat_out, ddp_dtype_t dtype,
                            void *stream);

@@ -172,8 +172,10 @@ def test_flatten_random_layouts(env, seed):
     """Seeded random layouts: 1-200 parameters of 0-9000 elements, a third
     of them shorter than a 16-byte chunk; f32 or bf16; caps from a few
     elements to whole-plan; the flat buffer at a random element offset; the
-    whole plan, then every bucket (up to 40) on its own, each against the
-    oracle, with nothing outside the call's range written."""
+    parameters carved out of one buffer back to back or with gaps.  Flatten
+    and unflatten of the whole plan, then of every bucket (up to 40) on its
+    own, each against the oracle, with nothing outside the call's range (or
+    its parameters) written."""
     torch, ddp = env
     rng = np.random.default_rng(500 + seed)
     for case in range(4):
@@ -219,3 +221,38 @@ def test_flatten_random_layouts(env, seed):
             lo, hi = op.bucket_base[b], op.bucket_base[b] + op.bucket_len[b]
             assert_bits_equal(h[lo:hi], want[lo:hi], f"bucket {b} " + tag)
             assert (h[:lo] == nine).all() and (h[hi:] == nine).all(), f"bucket {b} wrote outside {tag}"
+
+        # unflatten a new flat buffer into the same views (carved back to back
+        # or with gaps, so neighbouring parameters share 16-byte chunks)
+        src = rng.standard_normal(P).astype(np.float32)
+        src_h = src if dt == "f32" else (src.view(np.uint32) >> 16).astype(np.uint16)
+        src_d = to_dev(src_h, torch)
+        back = oracle.unflatten(op, src_h)
+        before = to_host(big, torch).copy()
+        ddp.unflatten(lp, binding, src_d)
+        torch.cuda.synchronize()
+        for q, v in enumerate(views):
+            if sizes[q]:
+                assert_bits_equal(to_host(v, torch), back[q], f"unflatten p={q} " + tag)
+        hb = to_host(big, torch)
+        inside = np.zeros(hb.size, dtype=bool)
+        for v in views:
+            if v.numel():
+                o = (v.data_ptr() - big.data_ptr()) // v.element_size()
+                inside[o:o + v.numel()] = True
+        assert np.array_equal(hb[~inside].view(np.uint8), before[~inside].view(np.uint8)), \
+            "unflatten wrote outside the parameters " + tag
+        for b in range(min(lp.n_buckets, 40)):
+            big.copy_(to_dev(before, torch))
+            ddp.unflatten(lp, binding, src_d, bucket=b)
+            torch.cuda.synchronize()
+            hb = to_host(big, torch)
+            mine = np.zeros(hb.size, dtype=bool)
+            for q in op.buckets[b]:
+                v = views[q]
+                if v.numel():
+                    o = (v.data_ptr() - big.data_ptr()) // v.element_size()
+                    mine[o:o + v.numel()] = True
+                    assert_bits_equal(hb[o:o + v.numel()], back[q], f"unflatten bucket {b} p={q} " + tag)
+            assert np.array_equal(hb[~mine].view(np.uint8), before[~mine].view(np.uint8)), \
+                f"unflatten of bucket {b} wrote outside its parameters " + tag
