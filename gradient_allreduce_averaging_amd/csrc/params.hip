@@ -73,7 +73,7 @@ struct PsParamMeta {
     int64_t blen;         // length of that bucket
     int64_t first_tile;   // the parameter's first tile
     int64_t numel;        // its elements
-    uint32_t vec;         // 1: every written tensor of the parameter 4-byte aligned
+    uint32_t vec;         // 1: every written tensor of the parameter 2-byte aligned
     uint32_t pad;
 };
 
@@ -673,16 +673,16 @@ ddp_status_t create(const ddp_plan_t *plan, const ddp_binding_t *const *R, int32
             char *ent = ents.data() + q * pstride;
             uint64_t *addr = reinterpret_cast<uint64_t *>(ent);
             for (int r = 0; r < n_ranks; ++r) addr[r] = R[r]->param_addr[p];
-            // the vector path stores 8- or 16-byte vectors to the written
-            // tensors, which needs 4-byte alignment (views carved out of one
-            // buffer sit at any element offset: a 16-byte boundary is not
-            // needed, and requiring one sent such f32 views down the
-            // per-element path at 2.5 TB/s); the gradients are read at
-            // whatever element alignment they have
+            // the vector path loads and stores 8- or 16-byte vectors at the
+            // tensors' own element alignment, as gfx9 and later global
+            // accesses allow (views carved out of one buffer sit at any
+            // element offset; requiring a 16-byte boundary sent them down the
+            // per-element path at 2.5 TB/s), so every bound tensor (2-byte
+            // aligned) qualifies
             bool vec = true;
             for (int k = 0; k < nw; ++k) {
                 addr[n_ranks + k] = w[k].bd ? w[k].bd->param_addr[p] : 0;
-                vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 4 == 0);
+                vec = vec && (!w[k].bd || w[k].bd->param_addr[p] % 2 == 0);
             }
             PsParamMeta pm;
             std::memset(&pm, 0, sizeof(pm));
