@@ -338,10 +338,11 @@ DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *ra
  * an f32 tile of 8 ranks reads and writes) and, per parameter with elements,
  * its n_ranks + 1 addresses and 40 bytes of position, rounded up to 16
  * bytes (Llama-7B, 8 ranks: 105 MB in all).  The bindings' addresses are copied into it: bind
- * again if a gradient moves.  Parameters whose written tensors (outputs;
- * parameters, momentum and stored average of the SGD step) sit on 16-byte
- * boundaries take the vector path, reading the gradients at any element
- * alignment; others take the per-element path (same results).
+ * again if a gradient moves.  Every tensor is read and written in 16- or
+ * 8-byte vectors at its own element alignment (views carved out of one
+ * buffer at any offset run as fast as separate tensors, within 2-3 %);
+ * tile ends and ring cuts inside a vector take a per-element path (same
+ * results).
  * ddp_param_sync_run enqueues the sync on `stream` (current device = the
  * device it was created on); it allocates nothing, so it can be captured.
  * Errors: INVALID_ARG (null arguments, a binding of another plan or device,
