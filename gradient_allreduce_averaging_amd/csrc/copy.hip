@@ -171,9 +171,9 @@ struct TensorStart {
     int64_t unit, flat_elem;
 };
 
-// The unit of [lo_unit, hi_unit) whose flat elements hold element f, found
-// from unit `w` (whose span is [wb, we)) by walking: one step in all but
-// layouts with parameters shorter than a 16-byte chunk.
+// The unit whose flat elements hold element f, walked to from unit w (the
+// caller's first guess, right in all but layouts with parameters shorter
+// than a 16-byte chunk).
 __device__ __forceinline__ ddp_copy_unit unit_holding(const ddp_copy_unit *units, int64_t w,
                                                       int64_t f)
 {
