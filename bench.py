@@ -752,6 +752,39 @@ def copy_ceiling(c, flats=None, out=None, esize=None):
                      "blocks per CU and none"}
 
 
+def carved_view_rates(c, binds, reps, t_unflatten, t_param_sync):
+    """The outputs as views carved back to back, in registration order, out
+    of one buffer one element past an aligned allocation (a flat gradient
+    buffer viewed per parameter): neighbouring parameters then share 16-byte
+    pieces of storage.  Unflatten into them and the one-kernel sync writing
+    into them, timed as the separate tensors are, with the same bits."""
+    torch, ddp, plan, wl = c.torch, c.ddp, c.plan, c.wl
+    big = torch.empty(c.P + 1, dtype=c.tout, device=c.dev)
+    views, o = [], 1
+    for n in wl.numel:
+        views.append(big[o:o + n])
+        o += n
+    vb = ddp.bind_params(plan, views)
+    tu = stream_ms(c, lambda: ddp.unflatten(plan, vb, c.out, stream=c.stream), reps, settle=True)
+    ps = ddp.param_sync(plan, binds, vb, c.order)
+    t_ps = stream_ms(c, lambda: ps(c.stream), reps, warm=5, settle=True)
+    chk = [torch.empty_like(v) for v in views]
+    ddp.unflatten(plan, ddp.bind_params(plan, chk), c.out, stream=c.stream)
+    torch.cuda.synchronize()
+    same = all(torch.equal(x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32),
+                           y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32))
+               for x, y in zip(views, chk))
+    res = {"unflatten_ms": round(tu, 4), "unflatten_GBps": gbps(2 * c.P * wl.out_bytes, tu),
+           "unflatten_vs_separate_tensors": round(t_unflatten / tu, 4),
+           "param_sync_ms": round(t_ps, 4), "param_sync_GBps": gbps(c.sync_bytes, t_ps),
+           "param_sync_vs_separate_tensors": round(t_param_sync / t_ps, 4),
+           "same_bits_as_unflatten": bool(same),
+           "layout": "outputs carved back to back out of one buffer, 1 element past its start"}
+    del big, views, vb, ps, chk
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_rates_bf16(c, reps):
     """Flatten and unflatten of the same parameter sizes in bf16: per-rank
     bf16 tensors, a bf16 plan with the workload's cap, each copy timed back
@@ -869,6 +902,7 @@ def leg_copy_path(c):
         "same_bits_as_three_steps": bool(same),
         "step": "every rank's per-parameter gradients averaged into per-parameter outputs "
                 "in one launch (ddp_param_sync_run)"}
+    out["carved_views"] = carved_view_rates(c, binds, reps, tu, t_ps)
     if wl.dtype == "f32":
         out["bf16"] = copy_rates_bf16(c, reps)
     log(f"copy path: {out}")

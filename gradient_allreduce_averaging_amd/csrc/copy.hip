@@ -49,6 +49,27 @@ __device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
     return (int64_t)((j / run) * kXcds + blockIdx.x % kXcds) * run + j % run;
 }
 
+// Unflatten, the chunks two or more parameters share: eight lanes per chunk,
+// lane k copying the chunk's bytes [2k, 2k + 2) from the flat buffer where
+// they belong to a parameter of the bucket, in one store instruction.  Run
+// by the blocks of an unflatten launch past bulk_blocks.
+struct UnflatEdges {
+    const ddp_unflatten_edge *edges;
+    int64_t n;
+    unsigned bulk_blocks;   // the launch's copy blocks; the blocks after them take the edges
+};
+
+__device__ __forceinline__ void unflatten_edge(const UnflatEdges &ue, int64_t lane, const char *flat)
+{
+    const int64_t i = lane >> 3;
+    if (i >= ue.n) return;
+    const int k = (int)(lane & 7);
+    const int64_t off = ue.edges[i].piece[k];
+    if (off < 0) return;
+    *reinterpret_cast<uint16_t *>(ue.edges[i].chunk + 2 * (uint64_t)k) =
+        *reinterpret_cast<const uint16_t *>(flat + off);
+}
+
 // Unflatten (flat -> param), the bulk: the mirror of flatten_units with the
 // roles of the buffers swapped.  Parameter views carved out of one buffer
 // sit at any alignment, so a 16-byte chunk of parameter storage can hold
@@ -58,14 +79,18 @@ __device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
 // parameter's units are contiguous, at its own alignment.  The chunks at the
 // parameter's two ends are partial: one that holds no other parameter's
 // bytes is written here, 2 bytes per lane in one store instruction; one that
-// does (flags in the unit entry, for this element size) is left to
-// unflatten_edges.  Parameters that start on the allocator's alignment, as
+// does (flags in the unit entry, for this element size) is left to the edge
+// blocks (unflatten_edge).  Parameters that start on the allocator's alignment, as
 // separate tensors do, have no first partial chunk and share no chunk.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
-                const char *flat, int esize)
+                const char *flat, int esize, UnflatEdges ue)
 {
+    if (blockIdx.x >= ue.bulk_blocks) {
+        unflatten_edge(ue, (int64_t)(blockIdx.x - ue.bulk_blocks) * kCopyThreads + threadIdx.x, flat);
+        return;
+    }
     int64_t lo;
     const int64_t ui = unit_of_block<BPU>(run, &lo);
     if (ui >= n_units) return;
@@ -106,20 +131,63 @@ unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsi
     if (tl) *reinterpret_cast<uint16_t *>(xt) = t;       // the last 8 lanes: one store
 }
 
-// Unflatten, the chunks two or more parameters share: eight lanes per chunk,
-// lane k copying the chunk's bytes [2k, 2k + 2) from the flat buffer where
-// they belong to a parameter of the bucket, in one store instruction.
-__global__ void __launch_bounds__(kCopyThreads)
-unflatten_edges(const ddp_unflatten_edge *edges, int64_t n, const char *flat)
+// A parameter's start in the flat buffer: its first unit and flat element.
+struct TensorStart {
+    int64_t unit, flat_elem;
+};
+
+// The unit whose flat elements hold element f, walked to from unit w (the
+// caller's first guess, right in all but layouts with parameters shorter
+// than a 16-byte chunk).
+__device__ __forceinline__ ddp_copy_unit unit_holding(const ddp_copy_unit *units, int64_t w,
+                                                      int64_t f)
 {
-    const int64_t lane = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    ddp_copy_unit u = units[w];
+    while (f < u.flat_elem) u = units[--w];
+    while (f >= u.flat_elem + u.count) u = units[++w];
+    return u;
+}
+
+// Flatten, the chunks flatten_units leaves, run by the blocks of a flatten
+// launch past bulk_blocks.  Boundary i of the range is the first flat
+// element of its i-th parameter, and after the last one the range's end.  A
+// boundary inside a 16-byte chunk (not on its first byte) makes the chunk
+// an edge chunk, which the chunk's first such boundary takes.  Eight lanes
+// serve boundary i, lane p the chunk's bytes [2p, 2p + 2): bytes before the
+// boundary come from the unit before it, bytes from it on from its
+// parameter's first unit (or, where parameters are shorter than a chunk, a
+// unit further off), none outside the range.  The eight lanes store in one
+// instruction, so the chunk is written whole.
+struct FlatEdges {
+    const TensorStart *starts;   // the range's parameter starts
+    int64_t nb;                  // their number
+    int64_t first, last;         // the range's units
+    int64_t r0e, r1e;            // the range's flat elements
+    unsigned bulk_blocks;        // the launch's copy blocks; the blocks after them take the edges
+};
+
+__device__ __forceinline__ void flatten_edge(const ddp_copy_unit *units, const FlatEdges &fe,
+                                             int64_t lane, char *flat, int esize)
+{
     const int64_t i = lane >> 3;
-    if (i >= n) return;
-    const int k = (int)(lane & 7);
-    const int64_t off = edges[i].piece[k];
-    if (off < 0) return;
-    *reinterpret_cast<uint16_t *>(edges[i].chunk + 2 * (uint64_t)k) =
-        *reinterpret_cast<const uint16_t *>(flat + off);
+    const int p = (int)(lane & 7);
+    if (i > fe.nb) return;
+    const uintptr_t fb = reinterpret_cast<uintptr_t>(flat);
+    const TensorStart ts = i < fe.nb ? fe.starts[i] : TensorStart{fe.last, fe.r1e};
+    const uintptr_t b = fb + (uintptr_t)(ts.flat_elem * esize);
+    if ((b & 15) == 0) return;
+    const uintptr_t c = b & ~(uintptr_t)15;
+    if (i > 0 && fb + (uintptr_t)(fe.starts[i - 1].flat_elem * esize) > c)
+        return;                                      // an earlier boundary in the chunk takes it
+    const uintptr_t x = c + 2 * (uintptr_t)p;
+    const uintptr_t r0 = fb + (uintptr_t)(fe.r0e * esize), r1 = fb + (uintptr_t)(fe.r1e * esize);
+    if (x < r0 || x >= r1) return;
+    // element f holds byte x; the unit before the boundary or the one at it
+    const int64_t f = (int64_t)((x - fb) / (uintptr_t)esize);
+    const ddp_copy_unit u = unit_holding(units, x < b ? ts.unit - 1 : ts.unit, f);
+    const char *s = reinterpret_cast<const char *>(u.param_addr) + u.param_elem * esize +
+                    (x - (fb + (uintptr_t)(u.flat_elem * esize)));
+    *reinterpret_cast<uint16_t *>(x) = *reinterpret_cast<const uint16_t *>(s);
 }
 
 // Flatten (param -> flat), the bulk.  Parameters sit in the flat buffer at
@@ -130,15 +198,19 @@ unflatten_edges(const ddp_unflatten_edge *edges, int64_t n, const char *flat)
 // one vector load from the source at its own alignment (any address) and
 // an aligned 16-byte store each.  The chunk that holds a parameter's end
 // when that end is not on a chunk boundary, and the chunk before the
-// range's first byte, are left to flatten_edges.  So every chunk has one
-// writer and every store is whole; these blocks do nothing else, and a
-// parameter whose bytes start and end on chunk boundaries needs no edge
-// pass at all.
+// range's first byte, are left to the edge blocks (flatten_edge).  So every
+// chunk has one writer and every store is whole, and a parameter whose
+// bytes start and end on chunk boundaries needs no edge work at all.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
 flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
-              char *flat, int esize)
+              char *flat, int esize, FlatEdges fe)
 {
+    if (blockIdx.x >= fe.bulk_blocks) {
+        flatten_edge(units, fe, (int64_t)(blockIdx.x - fe.bulk_blocks) * kCopyThreads + threadIdx.x,
+                     flat, esize);
+        return;
+    }
     int64_t lo;
     const int64_t ui = unit_of_block<BPU>(run, &lo);
     if (ui >= n_units) return;
@@ -162,60 +234,6 @@ flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsign
     if (k1 < nch) b = ld_stream(s + 16 * k1);
     if (k0 < nch) __builtin_nontemporal_store(a, dv + k0);
     if (k1 < nch) __builtin_nontemporal_store(b, dv + k1);
-}
-
-constexpr int kEdgeThreads = 256;
-
-// A parameter's start in the flat buffer: its first unit and flat element.
-struct TensorStart {
-    int64_t unit, flat_elem;
-};
-
-// The unit whose flat elements hold element f, walked to from unit w (the
-// caller's first guess, right in all but layouts with parameters shorter
-// than a 16-byte chunk).
-__device__ __forceinline__ ddp_copy_unit unit_holding(const ddp_copy_unit *units, int64_t w,
-                                                      int64_t f)
-{
-    ddp_copy_unit u = units[w];
-    while (f < u.flat_elem) u = units[--w];
-    while (f >= u.flat_elem + u.count) u = units[++w];
-    return u;
-}
-
-// Flatten, the chunks flatten_units leaves.  Boundary i of the range is the
-// first flat element of its i-th parameter, and after the last one the
-// range's end.  A boundary inside a 16-byte chunk (not on its first byte)
-// makes the chunk an edge chunk, which the chunk's first such boundary
-// takes.  Eight lanes serve boundary i, lane p the chunk's bytes
-// [2p, 2p + 2): bytes before the boundary come from the unit before it,
-// bytes from it on from its parameter's first unit (or, where parameters
-// are shorter than a chunk, a unit further off), none outside the range.
-// The eight lanes store in one instruction, so the chunk is written whole.
-__global__ void __launch_bounds__(kEdgeThreads)
-flatten_edges(const ddp_copy_unit *units, const TensorStart *starts, int64_t nb, int64_t first,
-              int64_t last, int64_t r0e, int64_t r1e, char *flat, int esize)
-{
-    const int64_t lane = (int64_t)blockIdx.x * kEdgeThreads + threadIdx.x;
-    const int64_t i = lane >> 3;
-    const int p = (int)(lane & 7);
-    if (i > nb) return;
-    const uintptr_t fb = reinterpret_cast<uintptr_t>(flat);
-    const TensorStart ts = i < nb ? starts[i] : TensorStart{last, r1e};
-    const uintptr_t b = fb + (uintptr_t)(ts.flat_elem * esize);
-    if ((b & 15) == 0) return;
-    const uintptr_t c = b & ~(uintptr_t)15;
-    if (i > 0 && fb + (uintptr_t)(starts[i - 1].flat_elem * esize) > c)
-        return;                                      // an earlier boundary in the chunk takes it
-    const uintptr_t x = c + 2 * (uintptr_t)p;
-    const uintptr_t r0 = fb + (uintptr_t)(r0e * esize), r1 = fb + (uintptr_t)(r1e * esize);
-    if (x < r0 || x >= r1) return;
-    // element f holds byte x; the unit before the boundary or the one at it
-    const int64_t f = (int64_t)((x - fb) / (uintptr_t)esize);
-    const ddp_copy_unit u = unit_holding(units, x < b ? ts.unit - 1 : ts.unit, f);
-    const char *s = reinterpret_cast<const char *>(u.param_addr) + u.param_elem * esize +
-                    (x - (fb + (uintptr_t)(u.flat_elem * esize)));
-    *reinterpret_cast<uint16_t *>(x) = *reinterpret_cast<const uint16_t *>(s);
 }
 
 // Unflatten's shared chunks for elements of `es` bytes: every 16-byte chunk
@@ -426,47 +444,64 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t round = kXcds * run, per = cap / round * round;
     char *fl = static_cast<char *>(flat);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // The edge work of the call.  Flatten: the chunks that hold a parameter
+    // start or the range's end off a 16-byte boundary of this flat buffer.
+    // Unflatten: the pieces of storage two parameters share.  It runs as
+    // extra blocks after the last launch's copy blocks when they fit in the
+    // launch, else as a launch of its own.
+    const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
+    FlatEdges fe{nullptr, 0, first, last, plan->bucket_base[b0], plan->bucket_base[b1], 0u};
+    UnflatEdges ue{nullptr, 0, 0u};
+    int64_t edge_lanes = 0;
+    if (to_flat) {
+        const unsigned mask = bucket < 0 ? bd->edge_mask : bd->bucket_edge_mask[bucket];
+        bool edges = false;
+        for (int k = 0; k < 8; ++k)
+            if ((mask >> k & 1u) && ((reinterpret_cast<uintptr_t>(flat) + (uintptr_t)(k * esize)) & 15))
+                edges = true;
+        if (edges) {
+            const int64_t t0 = bd->bucket_first_tensor[b0];
+            fe.starts = reinterpret_cast<const TensorStart *>(bd->tensor_first) + t0;
+            fe.nb = bd->bucket_first_tensor[b1] - t0;
+            edge_lanes = 8 * (fe.nb + 1);   // 8 lanes per boundary; n_params < 2^31
+        }
+    } else {
+        const int k = esize == 4 ? 1 : 0;
+        const int64_t e0 = bd->bucket_first_uedge[k][b0];
+        ue.edges = bd->uedges[k] + e0;
+        ue.n = bd->bucket_first_uedge[k][b1] - e0;
+        edge_lanes = 8 * ue.n;
+    }
+    const int64_t eblocks = (edge_lanes + kCopyThreads - 1) / kCopyThreads;
+    bool edges_done = eblocks == 0;
+    const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
+    const unsigned r = (unsigned)run;
+    auto launch = [&](int64_t u0, int64_t n, unsigned bulk, unsigned extra) {
+        const dim3 g(bulk + extra), b(kCopyThreads);
+        fe.bulk_blocks = ue.bulk_blocks = bulk;
+        if (to_flat && bpu == 1)
+            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, fe);
+        else if (to_flat)
+            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, fe);
+        else if (bpu == 1)
+            unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, ue);
+        else
+            unflatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, ue);
+        return launched("copy kernel launch");
+    };
     for (int64_t u0 = first; u0 < last; u0 += per) {
         const int64_t n = std::min(per, last - u0);
-        const dim3 g((unsigned)((n + round - 1) / round * round * bpu)), b(kCopyThreads);
-        const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
-        const unsigned r = (unsigned)run;
-        if (to_flat && bpu == 1)
-            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
-        else if (to_flat)
-            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
-        else if (bpu == 1)
-            unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
-        else
-            unflatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize);
-        const ddp_status_t s = launched("copy kernel launch");
+        const int64_t bulk = (n + round - 1) / round * round * bpu;
+        int64_t extra = 0;
+        if (u0 + per >= last && !edges_done && (bulk + eblocks) * kCopyThreads <= max_launch_items()) {
+            extra = eblocks;
+            edges_done = true;
+        }
+        const ddp_status_t s = launch(u0, n, (unsigned)bulk, (unsigned)extra);
         if (s != DDP_OK) return s;
     }
-    if (!to_flat) {   // the shared chunks of the range's parameters, if any
-        const int k = esize == 4 ? 1 : 0;
-        const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
-        const int64_t e0 = bd->bucket_first_uedge[k][b0], ne = bd->bucket_first_uedge[k][b1] - e0;
-        if (ne == 0) return DDP_OK;
-        unflatten_edges<<<dim3((unsigned)((8 * ne + kCopyThreads - 1) / kCopyThreads)),
-                          dim3(kCopyThreads), 0, st>>>(bd->uedges[k] + e0, ne, fl);
-        return launched("unflatten edge launch");
-    }
-    // the edge pass, when a parameter of the range starts or the range ends
-    // off a 16-byte boundary of this flat buffer
-    const int32_t b0 = bucket < 0 ? 0 : bucket, b1 = bucket < 0 ? plan->n_buckets() : bucket + 1;
-    const unsigned mask = bucket < 0 ? bd->edge_mask : bd->bucket_edge_mask[bucket];
-    bool edges = false;
-    for (int k = 0; k < 8; ++k)
-        if ((mask >> k & 1u) && ((reinterpret_cast<uintptr_t>(flat) + (uintptr_t)(k * esize)) & 15))
-            edges = true;
-    if (!edges) return DDP_OK;
-    const int64_t t0 = bd->bucket_first_tensor[b0], nt = bd->bucket_first_tensor[b1] - t0;
-    const TensorStart *ts = reinterpret_cast<const TensorStart *>(bd->tensor_first) + t0;
-    const int64_t lanes = 8 * (nt + 1);   // 8 lanes per boundary; n_params < 2^31
-    flatten_edges<<<dim3((unsigned)((lanes + kEdgeThreads - 1) / kEdgeThreads)), dim3(kEdgeThreads),
-                    0, st>>>(bd->units, ts, nt, first, last, plan->bucket_base[b0],
-                             plan->bucket_base[b1], fl, esize);
-    return launched("flatten edge launch");
+    if (!edges_done) return launch(first, 0, 0u, (unsigned)eblocks);
+    return DDP_OK;
 }
 
 ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding, int32_t bucket,

@@ -195,11 +195,12 @@ DDP_API ddp_status_t ddp_bind_params(const ddp_plan_t *plan, void *const *param_
 DDP_API void ddp_binding_free(ddp_binding_t *binding);
 
 /* flat_buf[base_b + offset_p + j] = grad_p[j] for every parameter p of
- * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch, and a
- * second, small one when a parameter of the range starts, or the range
- * ends, off a 16-byte boundary of flat_buf (it writes the 16-byte pieces
- * that hold two parameters).  Bytes of flat_buf outside the range are not
- * written.  flat_buf: device, ddp_plan_total(plan) elements, must not
+ * bucket `bucket` (-1: all buckets), elements of `dtype`.  One launch; where
+ * a parameter of the range starts, or the range ends, off a 16-byte
+ * boundary of flat_buf, the 16-byte pieces that hold two parameters are
+ * written by extra blocks at its end (a second, small launch if they do not
+ * fit under the per-launch work-item limit).  Bytes of flat_buf outside the
+ * range are not written.  flat_buf: device, ddp_plan_total(plan) elements, must not
  * overlap any parameter buffer.  Errors: INVALID_ARG (null, bucket out of
  * range, bad dtype, binding of another plan), HIP. */
 DDP_API ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
@@ -207,9 +208,10 @@ DDP_API ddp_status_t ddp_flatten(const ddp_plan_t *plan, const ddp_binding_t *bi
                          void *stream);
 
 /* grad_p[j] = flat_out[base_b + offset_p + j]: the inverse copy, elements of
- * `dtype` (the sync's output type).  One launch, and a second, small one
- * when parameters of the range share 16-byte pieces of storage (it writes
- * those pieces).  Bytes outside the range's parameters are not written.
+ * `dtype` (the sync's output type).  One launch; 16-byte pieces of storage
+ * that two parameters share (views carved out of one buffer) are written
+ * by extra blocks at its end, as in ddp_flatten.  Bytes outside the range's
+ * parameters are not written.
  * Same arguments and errors. */
 DDP_API ddp_status_t ddp_unflatten(const ddp_plan_t *plan, const ddp_binding_t *binding,
                            int32_t bucket, const void *flat_out, ddp_dtype_t dtype,
