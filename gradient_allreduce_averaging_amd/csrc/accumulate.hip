@@ -12,7 +12,8 @@ namespace {
 // ---------------------------------------------------------------- accumulate
 // Local accumulation between synchronisations ([DDP] 5.2, no_sync):
 // dst[k] += src[k] for every buffer pair k (grid row k), one f32 add per
-// element (bf16: widened, added, rounded to nearest even).
+// element (bf16: widened, added, rounded to nearest even).  The buffers are
+// read and written at whatever element alignment they have.
 struct AccArgs {
     char *dst[DDP_MAX_RANKS];
     const char *src[DDP_MAX_RANKS];
@@ -50,14 +51,6 @@ __global__ void __launch_bounds__(kThreads) accumulate_vec(AccArgs a, int64_t le
     }
 }
 
-template <int DT>
-__global__ void __launch_bounds__(kThreads) accumulate_scalar(AccArgs a, int64_t len,
-                                                             int64_t first_block)
-{
-    const int64_t i = (first_block + blockIdx.x) * kThreads + threadIdx.x;
-    if (i < len) acc_elem<DT>(a.dst[blockIdx.y], a.src[blockIdx.y], i);
-}
-
 }  // namespace
 
 extern "C" {
@@ -74,7 +67,6 @@ ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_
     const int64_t nbytes = len * esz;
     AccArgs a;
     std::memset(&a, 0, sizeof(a));
-    bool vec_ok = true;
     for (int k = 0; k < n_bufs; ++k) {
         if (!dst[k] || !src[k] || !aligned(dst[k], esz) || !aligned(src[k], esz))
             return DDP_ERR_INVALID_ARG;
@@ -88,21 +80,17 @@ ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_
         }
         a.dst[k] = static_cast<char *>(dst[k]);
         a.src[k] = static_cast<const char *>(src[k]);
-        vec_ok = vec_ok && aligned(dst[k], 16) && aligned(src[k], 16);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t per = vec_ok ? (int64_t)kThreads * vec_elems(dtype) : kThreads;
+    const int64_t per = (int64_t)kThreads * vec_elems(dtype);
     const dim3 b(kThreads);
     return launch_split((len + per - 1) / per, kThreads, "accumulate kernel launch",
                         [&](int64_t b0, unsigned n) {
                             const dim3 g(n, (unsigned)n_bufs);
-                            if (dtype == DDP_F32) {
-                                if (vec_ok) accumulate_vec<kF32><<<g, b, 0, st>>>(a, len, b0);
-                                else accumulate_scalar<kF32><<<g, b, 0, st>>>(a, len, b0);
-                            } else {
-                                if (vec_ok) accumulate_vec<kBF16><<<g, b, 0, st>>>(a, len, b0);
-                                else accumulate_scalar<kBF16><<<g, b, 0, st>>>(a, len, b0);
-                            }
+                            if (dtype == DDP_F32)
+                                accumulate_vec<kF32><<<g, b, 0, st>>>(a, len, b0);
+                            else
+                                accumulate_vec<kBF16><<<g, b, 0, st>>>(a, len, b0);
                         });
 }
 

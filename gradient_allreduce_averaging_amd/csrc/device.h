@@ -176,12 +176,16 @@ struct Segs {
 
 // Streaming 16-byte accesses of the reduce.  Every byte is touched once, so
 // they are non-temporal (the `nt` cache policy): on gfx950 this lifts a pure
-// streaming read from ~6.5 to ~7.2 TB/s and the reduce by ~15 %.  Loads need
-// only element alignment (2 bytes): gfx9 and later global loads take any
-// address, and the under-aligned type tells the compiler so (the instruction
-// is the same global_load_dwordx4).  Rank buffers of a bucket therefore need
-// not share their offset from a 16-byte boundary.
+// streaming read from ~6.5 to ~7.2 TB/s and the reduce by ~15 %.  Loads and
+// stores need only element alignment (2 bytes): gfx9 and later global
+// accesses take any address, and the under-aligned types tell the compiler
+// so (the instructions are the same global_load_dwordx4 and
+// global_store_dwordx{2,4}).  Rank buffers of a bucket therefore need not
+// share their offset from a 16-byte boundary, nor written buffers sit on one.
 typedef u32x4 u32x4_ua __attribute__((aligned(2)));
+template <typename V> struct under_aligned;
+template <> struct under_aligned<u32x4> { typedef u32x4 type __attribute__((aligned(2))); };
+template <> struct under_aligned<u32x2> { typedef u32x2 type __attribute__((aligned(2))); };
 
 __device__ __forceinline__ u32x4 ld_stream(const char *p)
 {
@@ -191,7 +195,8 @@ __device__ __forceinline__ u32x4 ld_stream(const char *p)
 template <typename V>
 __device__ __forceinline__ void st_stream(void *p, const V &v)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+    typedef typename under_aligned<V>::type VU;
+    __builtin_nontemporal_store(static_cast<VU>(v), reinterpret_cast<VU *>(p));
 }
 
 // The same accesses at a base that is either a pointer (a kernel argument,
@@ -219,8 +224,9 @@ __device__ __forceinline__ void st_at(void *p, int64_t i, const V &v)
 template <typename T, typename V>
 __device__ __forceinline__ void st_at(uint64_t a, int64_t i, const V &v)
 {
-    typedef __attribute__((address_space(1))) V GV;
-    __builtin_nontemporal_store(v, reinterpret_cast<GV *>(a + (uint64_t)i * sizeof(T)));
+    typedef __attribute__((address_space(1))) typename under_aligned<V>::type GV;
+    __builtin_nontemporal_store(static_cast<typename under_aligned<V>::type>(v),
+                                reinterpret_cast<GV *>(a + (uint64_t)i * sizeof(T)));
 }
 
 // Plain (cached) accesses of element i of a T array at either kind of base,

@@ -123,17 +123,6 @@ reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
     }
 }
 
-// Fused average + SGD step, one element per thread, element-aligned buffers
-// of a single bucket, any N.
-template <bool RING, int IN, int OUT, bool MOM>
-__global__ void __launch_bounds__(kThreads)
-reduce_sgd_scalar(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArgs sa)
-{
-    const int64_t i = tile_of_block(bk) * kThreads + threadIdx.x;
-    if (i >= total) return;
-    sgd_elems<IN, OUT, RING, MOM>(ra, N, total, bk, 0, inv, sa, i, 1);
-}
-
 // Any N up to DDP_MAX_RANKS (launched for N > 16).  A wave makes one pass per ring segment its
 // lanes lie in (usually one), so the rank order of each pass is
 // wave-uniform, and folds with fold_looped.
@@ -318,55 +307,44 @@ ddp_status_t launch_one_bucket(const RankArgs &ra, int N, int64_t len, int order
 
 template <bool RING, int IN, int OUT, bool MOM>
 ddp_status_t launch_sgd_typed(const RankArgs &ra, int N, int64_t total, const Buckets &bk,
-                              float inv, const SgdArgs &sa, hipStream_t st, bool vec_ok)
+                              float inv, const SgdArgs &sa, hipStream_t st)
 {
     Buckets lb = bk;
     const dim3 b(kThreads);
-    const char *what = "fused SGD kernel launch";
-    if (vec_ok) {
-        const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
-        const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
-        return launch_split(tiles, kThreads, what, [&](int64_t b0, unsigned n) {
-            lb.first_block = b0;
-            const dim3 g(n);
-            const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
-                reduce_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(
-                    ra, total, lb, inv, sa);
-            });
-            if (!fixed)
-                reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, lb, inv, sa);
+    const int64_t tiles = (total + tile_elems(IN) - 1) / tile_elems(IN);
+    const unsigned lds = lds_for_blocks(sgd_blocks_per_cu(N, MOM));
+    return launch_split(tiles, kThreads, "fused SGD kernel launch", [&](int64_t b0, unsigned n) {
+        lb.first_block = b0;
+        const dim3 g(n);
+        const bool fixed = with_rank_count<1, 8>(N, [&](auto nr) {
+            reduce_sgd_fast<decltype(nr)::value, RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, total,
+                                                                                       lb, inv, sa);
         });
-    }
-    return launch_split((total + kThreads - 1) / kThreads, kThreads, what,
-                        [&](int64_t b0, unsigned n) {
-                            lb.first_block = b0;
-                            reduce_sgd_scalar<RING, IN, OUT, MOM><<<dim3(n), b, 0, st>>>(
-                                ra, N, total, lb, inv, sa);
-                        });
+        if (!fixed) reduce_sgd_many<RING, IN, OUT, MOM><<<g, b, lds, st>>>(ra, N, total, lb, inv, sa);
+    });
 }
 
 template <bool RING, bool MOM>
 ddp_status_t launch_sgd_pair(const RankArgs &ra, int N, int64_t total, int in, int out_dt,
-                             const Buckets &bk, float inv, const SgdArgs &sa, hipStream_t st,
-                             bool vec_ok)
+                             const Buckets &bk, float inv, const SgdArgs &sa, hipStream_t st)
 {
     if (in == DDP_F32 && out_dt == DDP_F32)
-        return launch_sgd_typed<RING, kF32, kF32, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
+        return launch_sgd_typed<RING, kF32, kF32, MOM>(ra, N, total, bk, inv, sa, st);
     if (in == DDP_BF16 && out_dt == DDP_BF16)
-        return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
-    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ra, N, total, bk, inv, sa, st, vec_ok);
+        return launch_sgd_typed<RING, kBF16, kBF16, MOM>(ra, N, total, bk, inv, sa, st);
+    return launch_sgd_typed<RING, kF32, kBF16, MOM>(ra, N, total, bk, inv, sa, st);
 }
 
 ddp_status_t launch_sgd(const RankArgs &ra, int N, int64_t total, int order, int in, int out_dt,
-                        const Buckets &bk, const SgdArgs &sa, hipStream_t st, bool vec_ok)
+                        const Buckets &bk, const SgdArgs &sa, hipStream_t st)
 {
     const float inv = 1.0f / (float)N;
     const bool ring = order == DDP_ORDER_RING, mom = sa.mom != nullptr;
     if (ring)
-        return mom ? launch_sgd_pair<true, true>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok)
-                   : launch_sgd_pair<true, false>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok);
-    return mom ? launch_sgd_pair<false, true>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok)
-               : launch_sgd_pair<false, false>(ra, N, total, in, out_dt, bk, inv, sa, st, vec_ok);
+        return mom ? launch_sgd_pair<true, true>(ra, N, total, in, out_dt, bk, inv, sa, st)
+                   : launch_sgd_pair<true, false>(ra, N, total, in, out_dt, bk, inv, sa, st);
+    return mom ? launch_sgd_pair<false, true>(ra, N, total, in, out_dt, bk, inv, sa, st)
+               : launch_sgd_pair<false, false>(ra, N, total, in, out_dt, bk, inv, sa, st);
 }
 
 }  // namespace
@@ -669,38 +647,16 @@ ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat,
     const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
     RankArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    // the written buffers must sit on 16-byte boundaries for the vector
-    // kernels; the rank buffers are read at whatever element alignment they have
-    const bool vec_ok = aligned(param_flat, 16) && (!momentum_flat || aligned(momentum_flat, 16)) &&
-                        (!grad_out || aligned(grad_out, 16));
+    // every buffer is read and written at whatever element alignment it has
     for (int r = 0; r < n_ranks; ++r) ra.p[r] = rank_flat[r];
-    if (!vec_ok) {
-        // element-aligned buffers: one per-element launch per bucket
-        for (int32_t b = 0; b < plan->n_buckets(); ++b) {
-            const int64_t base = plan->bucket_base[b], len = plan->bucket_base[b + 1] - base;
-            if (len == 0) continue;
-            RankArgs sub;
-            std::memset(&sub, 0, sizeof(sub));
-            for (int r = 0; r < n_ranks; ++r)
-                sub.p[r] = static_cast<const char *>(rank_flat[r]) + base * isz;
-            SgdArgs sa = {param_flat + base, momentum_flat ? momentum_flat + base : nullptr,
-                          grad_out ? static_cast<char *>(grad_out) + base * osz : nullptr, lr,
-                          momentum};
-            ddp_status_t s2 = launch_sgd(sub, n_ranks, len, order, in, out_dtype,
-                                         single_bucket(0, len), sa, st, false);
-            if (s2 != DDP_OK) return s2;
-        }
-        return DDP_OK;
-    }
     const SgdArgs sa = {param_flat, momentum_flat, grad_out, lr, momentum};
     if (order == DDP_ORDER_SEQUENTIAL || n_ranks == 1) {
         // neither depends on bucket boundaries (one rank: the input itself)
-        return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single_bucket(0, total), sa, st,
-                          true);
+        return launch_sgd(ra, n_ranks, total, order, in, out_dtype, single_bucket(0, total), sa, st);
     }
     Buckets bk;
     if ((stc = ring_buckets(plan, in, n_ranks, &bk)) != DDP_OK) return stc;
-    return launch_sgd(ra, n_ranks, total, order, in, out_dtype, bk, sa, st, true);
+    return launch_sgd(ra, n_ranks, total, order, in, out_dtype, bk, sa, st);
 }
 
 }  // extern "C"

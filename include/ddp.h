@@ -302,10 +302,10 @@ DDP_API ddp_status_t ddp_sync_allreduce_avg_bucket(ddp_plan_t *plan, int32_t buc
  *                  place (start from zeros), or NULL for plain SGD
  *   lr, momentum   learning rate and momentum factor (f32)
  * param_flat and momentum_flat may overlap no other buffer (DDP_ERR_ALIAS).
- * N == 1 takes the input as the average, bit for bit.  With param_flat,
- * momentum_flat and grad_out on 16-byte boundaries the vector kernels run
- * (N <= 8 unrolled, N > 8 looped; the rank buffers need only element
- * alignment), otherwise a per-element kernel with identical results.
+ * N == 1 takes the input as the average, bit for bit.  One launch of the
+ * vector kernel (N <= 8 unrolled, N > 8 looped) at any element alignment of
+ * every buffer: each is read and written with 16-byte accesses that need
+ * not sit on a 16-byte boundary.
  * Errors: as ddp_sync_allreduce_avg. */
 DDP_API ddp_status_t ddp_sync_sgd_update(ddp_plan_t *plan, const void *const *rank_flat, int32_t n_ranks,
                                  ddp_order_t order, ddp_dtype_t out_dtype, void *grad_out,
@@ -413,7 +413,8 @@ DDP_API void ddp_param_sync_free(ddp_param_sync_t *sync);
  *                             of dtype; n_bufs 1..DDP_MAX_RANKS (one pair
  *                             per virtual rank)
  * dst[k] may be exactly src[k]; any other overlap between the buffers is
- * rejected (DDP_ERR_ALIAS).  len == 0 does nothing.
+ * rejected (DDP_ERR_ALIAS).  Buffers need only element alignment (one
+ * vector kernel for any offset).  len == 0 does nothing.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERFLOW, ALIAS, HIP. */
 DDP_API ddp_status_t ddp_accumulate(void *const *dst, const void *const *src, int32_t n_bufs, int64_t len,
                             ddp_dtype_t dtype, void *stream);

@@ -2,7 +2,8 @@
 against the oracle's synchronisation followed by its SGD step, bit for bit:
 parameters, momentum buffer and the stored average, for every rank count
 1..9, 13, 16, 40 and 64 (N > 8: the looped kernel), all dtype pairs, both orders, with and without
-momentum and average output, misaligned buffers, in-place average output,
+momentum and average output, buffers off 16-byte boundaries (all at one offset,
+or each at its own), in-place average output,
 the ResNet-50 and many-small workloads at full size, and Llama-7B (bf16
 gradients, 27 GB of f32 parameters) on sampled positions."""
 import numpy as np
@@ -36,25 +37,27 @@ def _case(env, sizes, N, in_dt, out_dt, order, mom, write_avg, seed, misalign=Fa
     lr, mu = 0.05, 0.9
     tdt = torch.float32 if in_dt == "f32" else torch.bfloat16
     odt = torch.float32 if out_dt == "f32" else torch.bfloat16
-    off = 1 if misalign else 0
+    # element offsets of (rank r's buffer - r % 3, params, momentum, average)
+    offs = misalign if isinstance(misalign, tuple) else (1, 1, 1, 1) if misalign else (0, 0, 0, 0)
     ranks = []
-    for x in xs:
-        big = torch.empty(P + 4, dtype=tdt, device="cuda:0")
+    for r, x in enumerate(xs):
+        off = offs[0] + (r % 3 if isinstance(misalign, tuple) else 0)
+        big = torch.empty(P + 8, dtype=tdt, device="cuda:0")
         big[off:off + P].copy_(to_dev(x, torch))
         ranks.append(big[off:off + P])
-    pb = torch.empty(P + 4, dtype=torch.float32, device="cuda:0")
-    params = pb[off:off + P]
+    pb = torch.empty(P + 8, dtype=torch.float32, device="cuda:0")
+    params = pb[offs[1]:offs[1] + P]
     params.copy_(to_dev(p0, torch))
-    mb = torch.empty(P + 4, dtype=torch.float32, device="cuda:0")
-    mbuf = mb[off:off + P] if mom else None
+    mb = torch.empty(P + 8, dtype=torch.float32, device="cuda:0")
+    mbuf = mb[offs[2]:offs[2] + P] if mom else None
     if mom:
         mbuf.copy_(to_dev(m0, torch))
     gout = None
     if in_place:
         gout = ranks[N - 1]
     elif write_avg:
-        gb = torch.empty(P + 4, dtype=odt, device="cuda:0")
-        gout = gb[off:off + P]
+        gb = torch.empty(P + 8, dtype=odt, device="cuda:0")
+        gout = gb[offs[3]:offs[3] + P]
     ddp.sync_sgd_update(lp, ranks, params, lr, order, grad_out=gout, momentum_buf=mbuf,
                         momentum=mu, out_dtype=out_dt)
     torch.cuda.synchronize()
@@ -92,6 +95,22 @@ def test_fused_sgd_misaligned_and_in_place(env, order):
     _case(env, SIZES, 4, "f32", "f32", order, True, True, seed=1, misalign=True)
     _case(env, SIZES, 8, "bf16", "bf16", order, True, True, seed=2, misalign=True)
     _case(env, SIZES, 4, "f32", "f32", order, True, False, seed=3, in_place=True)
+
+
+MIXED = [(0, 1, 2, 3), (1, 3, 0, 1), (2, 0, 3, 0), (3, 2, 1, 2)]
+
+
+@pytest.mark.parametrize("order", ["seq", "ring"])
+@pytest.mark.parametrize("offs", MIXED, ids=lambda o: "off" + "".join(map(str, o)))
+def test_fused_sgd_mixed_alignment(env, order, offs):
+    """Every buffer at its own element offset from a 16-byte boundary (rank
+    buffers among themselves too): the vector kernels read and write at
+    element alignment, through the unrolled (N <= 8) and looped kernels."""
+    for k, (N, in_dt, out_dt) in enumerate([(4, "f32", "f32"), (8, "bf16", "bf16"),
+                                            (5, "f32", "bf16"), (12, "f32", "f32"),
+                                            (12, "bf16", "bf16")]):
+        for mom in (False, True):
+            _case(env, SIZES, N, in_dt, out_dt, order, mom, True, seed=40 + k, misalign=offs)
 
 
 @pytest.mark.parametrize("name", ["resnet50", "many_small"])

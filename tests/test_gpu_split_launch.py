@@ -8,17 +8,17 @@ These tests check that the split changes no bit:
 
 * the launch count: kernel nodes of captured graphs, for the one-launch
   synchronisation, an unaligned single bucket (head block in the last
-  launch), ranks at mixed offsets, the fused SGD step (vector and
-  per-element), accumulate and flatten, each replay equal to the eager call;
+  launch), ranks at mixed offsets, the fused SGD step (buffers on and off
+  16-byte boundaries), accumulate and flatten, each replay equal to the
+  eager call;
 * the parity suites (flat and per-parameter) once more in a child process whose limit is 4096
   work-items (64 reduce blocks, 8 copy units per launch), so that every
   small case spans many launches and is compared with the oracle there;
 * at the real limit: N = 2 f32 ranks of 4.3 G elements (past element 2^32,
   where the one-launch sync, the head-peeled and mixed-offset buckets, the
-  fused step and accumulate split) and a per-element fused SGD launch past
-  element 2^30, checked on
-  sampled positions around every launch edge, bucket edge and ring-chunk
-  edge against the oracle.
+  fused step with buffers on and off 16-byte boundaries and accumulate
+  split), checked on sampled positions around every launch edge, bucket edge
+  and ring-chunk edge against the oracle.
 """
 import ctypes
 import os
@@ -182,23 +182,24 @@ def test_launch_count_follows_the_item_limit(env):
     assert k == launches(-(-P // 256), 64), ("sgd, ranks off 16 B", k)
     _replay_equals_eager(torch, g, sgd_mixed, [params, mom], "SGD replay, ranks off 16 B", sgd_reset)
 
-    # parameters off a 16-byte boundary: the per-element fused kernel, one
-    # grid per bucket
+    # parameters and momentum off a 16-byte boundary (1 and 3 elements): the
+    # same vector grid, stores at element alignment
     pbig = torch.empty(P + 4, device=dev)
     p_off = pbig[1:P + 1]
+    mbig = torch.zeros(P + 4, device=dev)
+    m_off = mbig[3:P + 3]
 
     def p_reset():
         p_off.copy_(p0)
-        mom.zero_()
+        m_off.zero_()
         torch.cuda.synchronize()
 
-    def sgd_elems():
-        ddp.sync_sgd_update(lp, [f[:P] for f in flats], p_off, 0.1, "ring", momentum_buf=mom,
+    def sgd_off():
+        ddp.sync_sgd_update(lp, [f[:P] for f in flats], p_off, 0.1, "ring", momentum_buf=m_off,
                             momentum=0.9)
-    k, g = _kernel_nodes(torch, sgd_elems)
-    lens = [lp.bucket(b)[0] for b in range(lp.n_buckets)]
-    assert k == sum(launches(-(-n // 64), 64) for n in lens if n), ("per-element sgd", k)
-    _replay_equals_eager(torch, g, sgd_elems, [p_off, mom], "per-element SGD replay", p_reset)
+    k, g = _kernel_nodes(torch, sgd_off)
+    assert k == launches(-(-P // 256), 64), ("sgd, parameters off 16 B", k)
+    _replay_equals_eager(torch, g, sgd_off, [p_off, m_off], "SGD replay, parameters off 16 B", p_reset)
 
     acc_dst = [torch.empty(P, device=dev) for _ in range(2)]
 
@@ -342,28 +343,20 @@ def test_real_limit_past_element_2_32(env):
     del out
     torch.cuda.empty_cache()
 
-    print("real limit: per-element fused SGD kernel past element 2^30", flush=True)
-    L3 = 1_100_000_000
-    lp3 = ddp.plan_buckets([L3], 25 << 20, "f32")
-    p3big = torch.empty(L3 + 4, dtype=torch.float32, device=dev)
-    p3 = p3big[1:L3 + 1]                          # off a 16-byte boundary
+    print("real limit: fused SGD step, parameters and momentum off a 16-byte boundary", flush=True)
+    p3big = torch.empty(P + 4, dtype=torch.float32, device=dev)
+    p3 = p3big[1:P + 1]                           # 4 bytes past a 16-byte boundary
     W.device_normal_(p3, 78, 3, 1.0)
-    m3 = torch.zeros(L3, dtype=torch.float32, device=dev)
-    tpos = set(int(x) for x in rng.integers(0, L3, 4000))
-    tpos |= _near([1 << 30, 0, L3 - 1, L3 // 2], 0, L3)
-    tpos = np.array(sorted(tpos), dtype=np.int64)
-    tidx = torch.from_numpy(tpos).to(dev)
-    tv = np.stack([to_host(flats[r].index_select(0, tidx + 1), torch) for r in range(N)], axis=1)
-    wp3 = to_host(p3.index_select(0, tidx), torch).copy()
-    wm3 = np.zeros(tpos.size, np.float32)
-    avg3 = oracle.sampled_avg(tv, tpos, np.full(tpos.size, L3), "ring")
-    ddp.sync_sgd_update(lp3, [f[1:L3 + 1] for f in flats], p3, 0.1, "ring", momentum_buf=m3,
-                        momentum=0.9)
-    oracle.sgd_step(wp3, avg3, 0.1, "f32", wm3, 0.9)
+    m3big = torch.zeros(P + 4, dtype=torch.float32, device=dev)
+    m3 = m3big[3:P + 3]                           # 12 bytes past one
+    wp3 = to_host(p3.index_select(0, idx), torch).copy()
+    wm3 = np.zeros(pos.size, np.float32)
+    ddp.sync_sgd_update(lp, flats, p3, 0.1, "ring", momentum_buf=m3, momentum=0.9)
+    oracle.sgd_step(wp3, avg_ring, 0.1, "f32", wm3, 0.9)
     torch.cuda.synchronize()
-    assert_bits_equal(to_host(p3.index_select(0, tidx), torch), wp3, "per-element SGD params")
-    assert_bits_equal(to_host(m3.index_select(0, tidx), torch), wm3, "per-element SGD momentum")
-    del p3, p3big, m3, tidx
+    assert_bits_equal(to_host(p3.index_select(0, idx), torch), wp3, "offset SGD params")
+    assert_bits_equal(to_host(m3.index_select(0, idx), torch), wm3, "offset SGD momentum")
+    del p3, p3big, m3, m3big
     torch.cuda.empty_cache()
 
     print("real limit: fused SGD step with momentum", flush=True)
