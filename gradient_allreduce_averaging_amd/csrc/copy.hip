@@ -37,16 +37,25 @@ static_assert(kCopyBlockBytes == 2 * 16 * kCopyThreads, "two vectors per thread 
 // multiple of the 128-byte line, the line two units share is written by one
 // XCD's L2 inside a run instead of from two L2s, which measured 2-3 %
 // faster with many small unaligned parameters (runs of 64; runs of 256, or
-// one contiguous span per XCD, measured slower on large ones).  Units hold
-// 4K elements: with many short parameters, bigger units mostly spawn blocks
-// that find no work.
+// one contiguous span per XCD, measured slower on large ones).  The units
+// after the last whole round of 8 runs are shared out in runs of last_run =
+// ceil(rest / 8), so that no XCD ends the launch with a whole run more than
+// the others.  Units hold 4K elements: with many short parameters, bigger
+// units mostly spawn blocks that find no work.
+struct CopyMap {
+    unsigned run, last_run;   // units per XCD run: whole rounds, the last round
+    unsigned full_j;          // units of one XCD in whole rounds
+};
+
 template <int BPU>
-__device__ __forceinline__ int64_t unit_of_block(unsigned run, int64_t *lo)
+__device__ __forceinline__ int64_t unit_of_block(const CopyMap &cm, int64_t *lo)
 {
     constexpr int64_t kBlockElems = kCopyUnitElems / BPU;
     const unsigned m = blockIdx.x / kXcds, j = m / BPU;   // this XCD's j-th unit
+    const unsigned x = blockIdx.x % kXcds;
     *lo = (m % BPU) * kBlockElems;
-    return (int64_t)((j / run) * kXcds + blockIdx.x % kXcds) * run + j % run;
+    if (j < cm.full_j) return (int64_t)((j / cm.run) * kXcds + x) * cm.run + j % cm.run;
+    return (int64_t)cm.full_j * kXcds + (int64_t)x * cm.last_run + (j - cm.full_j);
 }
 
 // Unflatten, the chunks two or more parameters share: eight lanes per chunk,
@@ -84,7 +93,7 @@ __device__ __forceinline__ void unflatten_edge(const UnflatEdges &ue, int64_t la
 // separate tensors do, have no first partial chunk and share no chunk.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
-unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
+unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, CopyMap cm,
                 const char *flat, int esize, UnflatEdges ue)
 {
     if (blockIdx.x >= ue.bulk_blocks) {
@@ -92,7 +101,7 @@ unflatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsi
         return;
     }
     int64_t lo;
-    const int64_t ui = unit_of_block<BPU>(run, &lo);
+    const int64_t ui = unit_of_block<BPU>(cm, &lo);
     if (ui >= n_units) return;
     const ddp_copy_unit u = units[first + ui];
     if (lo >= u.count) return;
@@ -203,7 +212,7 @@ __device__ __forceinline__ void flatten_edge(const ddp_copy_unit *units, const F
 // bytes start and end on chunk boundaries needs no edge work at all.
 template <int BPU>
 __global__ void __launch_bounds__(kCopyThreads)
-flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsigned run,
+flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, CopyMap cm,
               char *flat, int esize, FlatEdges fe)
 {
     if (blockIdx.x >= fe.bulk_blocks) {
@@ -212,7 +221,7 @@ flatten_units(const ddp_copy_unit *units, int64_t first, int64_t n_units, unsign
         return;
     }
     int64_t lo;
-    const int64_t ui = unit_of_block<BPU>(run, &lo);
+    const int64_t ui = unit_of_block<BPU>(cm, &lo);
     if (ui >= n_units) return;
     const ddp_copy_unit u = units[first + ui];
     if (lo >= u.count) return;
@@ -433,11 +442,10 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t last = bucket < 0 ? bd->n_units : bd->bucket_first_unit[bucket + 1];
     if (last <= first) return DDP_OK;
     const OccupancyScope occ(plan->occupancy.load(std::memory_order_relaxed));
-    // Every XCD gets the same number of runs (the last round of kXcds runs
-    // padded).  A launch takes at most max_launch_items() work-items, a
-    // multiple of 4096, so cap (units per launch) is a multiple of kXcds; the
-    // run is shortened where cap is below kXcds * kCopyRun, and a launch
-    // takes whole rounds.
+    // A launch takes at most max_launch_items() work-items, a multiple of
+    // 4096, so cap (units per launch) is a multiple of kXcds; the run is
+    // shortened where cap is below kXcds * kCopyRun, and every launch but the
+    // last takes whole rounds of kXcds runs.
     const int esize = dtype_size(dtype), bpu = copy_blocks_per_unit(esize);
     const int64_t cap = max_launch_items() / (kCopyThreads * bpu);
     const int64_t run = std::min<int64_t>(kCopyRun, cap / kXcds);
@@ -475,32 +483,33 @@ static ddp_status_t run_copy(const ddp_plan_t *plan, const ddp_binding_t *bd, in
     const int64_t eblocks = (edge_lanes + kCopyThreads - 1) / kCopyThreads;
     bool edges_done = eblocks == 0;
     const unsigned lds = lds_for_blocks(kCopyBlocksPerCU);
-    const unsigned r = (unsigned)run;
-    auto launch = [&](int64_t u0, int64_t n, unsigned bulk, unsigned extra) {
+    auto launch = [&](int64_t u0, int64_t n, const CopyMap &cm, unsigned bulk, unsigned extra) {
         const dim3 g(bulk + extra), b(kCopyThreads);
         fe.bulk_blocks = ue.bulk_blocks = bulk;
         if (to_flat && bpu == 1)
-            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, fe);
+            flatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, cm, fl, esize, fe);
         else if (to_flat)
-            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, fe);
+            flatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, cm, fl, esize, fe);
         else if (bpu == 1)
-            unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, ue);
+            unflatten_units<1><<<g, b, lds, st>>>(bd->units, u0, n, cm, fl, esize, ue);
         else
-            unflatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, r, fl, esize, ue);
+            unflatten_units<2><<<g, b, lds, st>>>(bd->units, u0, n, cm, fl, esize, ue);
         return launched("copy kernel launch");
     };
     for (int64_t u0 = first; u0 < last; u0 += per) {
         const int64_t n = std::min(per, last - u0);
-        const int64_t bulk = (n + round - 1) / round * round * bpu;
+        const int64_t whole = n / round, rest = n % round;
+        const CopyMap cm{(unsigned)run, (unsigned)((rest + kXcds - 1) / kXcds), (unsigned)(whole * run)};
+        const int64_t bulk = (whole * run + cm.last_run) * kXcds * bpu;
         int64_t extra = 0;
         if (u0 + per >= last && !edges_done && (bulk + eblocks) * kCopyThreads <= max_launch_items()) {
             extra = eblocks;
             edges_done = true;
         }
-        const ddp_status_t s = launch(u0, n, (unsigned)bulk, (unsigned)extra);
+        const ddp_status_t s = launch(u0, n, cm, (unsigned)bulk, (unsigned)extra);
         if (s != DDP_OK) return s;
     }
-    if (!edges_done) return launch(first, 0, 0u, (unsigned)eblocks);
+    if (!edges_done) return launch(first, 0, CopyMap{(unsigned)run, 0u, 0u}, 0u, (unsigned)eblocks);
     return DDP_OK;
 }
 

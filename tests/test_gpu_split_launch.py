@@ -235,7 +235,9 @@ def test_launch_count_follows_the_item_limit(env):
     per = copy_units_per_launch(4)
     run = min(64, launch_items() // 512 // 8)
     n_last = units - (-(-units // per) - 1) * per
-    bulk_last = -(-n_last // (8 * run)) * 8 * run * 2          # 2 blocks per f32 unit
+    # whole rounds of 8 runs, then the rest shared out in 8 runs of ceil(rest / 8)
+    whole, rest = divmod(n_last, 8 * run)
+    bulk_last = (whole * run + -(-rest // 8)) * 8 * 2          # 2 blocks per f32 unit
     eblocks = -(-8 * (len(starts) + 1) // 256)
     alone = edge and (bulk_last + eblocks) * 256 > launch_items()
     assert k == -(-units // per) + alone, ("flatten", k, edge, alone)
