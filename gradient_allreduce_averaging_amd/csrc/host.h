@@ -82,8 +82,9 @@ bool with_rank_count(int n, F &&f)
 
 // reduce.hip: the validation every reduce entry point shares (the output
 // may be null only when out_optional is set), the N == 1 copy, and the
-// reduce launch over the buckets bk (vec_ok: every written buffer on a
-// 16-byte boundary).
+// reduce launch over the buckets bk (vec_ok: the vector kernels, else one
+// element per thread; the bits are the same, the callers choose by output
+// alignment and bucket length).
 ddp_status_t check_reduce(const void *const *ptrs, int32_t n, int64_t len, int order, int in,
                           int out_dt, const void *out, bool out_optional = false);
 ddp_status_t copy_single(const void *in, int64_t len, int esize, void *out, hipStream_t st);

@@ -36,9 +36,8 @@
  *     own descriptor tables (plans, bindings) and frees it in *_free.
  *   - Element counts and offsets are int64 everywhere.  A dispatch counts
  *     its grid in 32-bit work-items, so a grid of more than 2^30 work-items
- *     (a one-launch f32 reduce past 2^32 elements, a per-element one past
- *     2^30) runs as consecutive launches on the same stream; results are
- *     the same bits.  DDP_ERR_HIP from a later launch may follow earlier
+ *     (a one-launch f32 reduce past 2^32 elements, bf16 past 2^33) runs as
+ *     consecutive launches on the same stream; results are the same bits.  DDP_ERR_HIP from a later launch may follow earlier
  *     ones already enqueued.  The environment variable DDP_MAX_LAUNCH_ITEMS,
  *     read once per process, lowers the limit (at least 4096, rounded down
  *     to a multiple of 4096), so that tests can split small grids.
