@@ -192,6 +192,13 @@ __device__ __forceinline__ u32x4 ld_stream(const char *p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_ua *>(p));
 }
 
+// An 8-byte streaming load (four bf16 gradients of the fused step's split
+// lane layout, sgd_vec_split).
+__device__ __forceinline__ u32x2 ld_stream8(const char *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const typename under_aligned<u32x2>::type *>(p));
+}
+
 template <typename V>
 __device__ __forceinline__ void st_stream(void *p, const V &v)
 {
@@ -213,6 +220,21 @@ __device__ __forceinline__ u32x4 ld_at(const void *p, int64_t off)
 __device__ __forceinline__ u32x4 ld_at(uint64_t a, int64_t off)
 {
     return __builtin_nontemporal_load(reinterpret_cast<const g_u32x4_ua *>(a + (uint64_t)off));
+}
+// Two 8-byte loads at byte offsets offA and offB, as one vector (the fused
+// step's split lane layout for bf16 gradients).
+__device__ __forceinline__ u32x4 ld_split(const void *p, int64_t offA, int64_t offB)
+{
+    const char *c = static_cast<const char *>(p);
+    const u32x2 lo = ld_stream8(c + offA), hi = ld_stream8(c + offB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ u32x4 ld_split(uint64_t a, int64_t offA, int64_t offB)
+{
+    typedef __attribute__((address_space(1))) typename under_aligned<u32x2>::type g_u32x2_ua;
+    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const g_u32x2_ua *>(a + (uint64_t)offA));
+    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const g_u32x2_ua *>(a + (uint64_t)offB));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // Stores take the element index i of a T array at the base.
@@ -572,6 +594,37 @@ __device__ __forceinline__ void fold_looped(const Ptrs &p, int N, int s, int64_t
     }
 }
 
+// fold_looped for bf16 gradients in the split lane layout: each rank's
+// vector is four elements at byte offset offA and four at offB.
+template <bool RING, class Ptrs>
+__device__ __forceinline__ void fold_looped_split(const Ptrs &p, int N, int s, int64_t offA,
+                                                  int64_t offB, float *acc)
+{
+    constexpr int G = 8;
+#pragma unroll 1
+    for (int k0 = 0; k0 < N; k0 += G) {
+        u32x4 v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (k0 + j < N) {
+                int r = s + k0 + j;
+                r = r >= N ? r - N : r;
+                v[j] = ld_split(p[r], offA, offB);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (k0 + j < N) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = lane<kBF16>(v[j], e);
+                    acc[e] = k0 + j > 0 ? acc[e] + x : (RING ? x : 0.0f + x);
+                }
+            }
+        }
+    }
+}
+
 // Convert and store one vector of scaled averages y at element i0 of the
 // tensor at `out` (a pointer or a table address; nothing is written unless
 // `write`); for a bf16 output y becomes the stored value widened back to f32
@@ -645,6 +698,43 @@ __device__ __forceinline__ void sgd_vec(const SgdArgs &sa, int64_t i0, float *y,
 {
     sgd_vec<IN, OUT, MOM>(sa.grad_out, static_cast<void *>(sa.param),
                           static_cast<void *>(sa.mom), i0, y, pv, mv, sa.lr, sa.mu);
+}
+
+// The fused step's epilogue for bf16 gradients in the split lane layout: the
+// lane's eight elements are [iA, iA + 4) and [iB, iB + 4), y[0..3] and
+// y[4..7], with parameter (and momentum) vectors pv[0], pv[1] (mv) loaded
+// from those two places.  With eight consecutive elements per lane a lane's
+// two 16-byte parameter stores sit 32 bytes apart and each store instruction
+// covers every other 16 bytes of its wave's range, so memory received a
+// quarter of the 64-byte pieces in two halves; here every store instruction
+// of a wave writes one contiguous range.  The average is rounded to bf16 and
+// the step takes the rounded value, as store_y does.
+template <bool MOM, class A>
+__device__ __forceinline__ void sgd_vec_split(A gout, A param, A mom, int64_t iA, int64_t iB, float *y,
+                                              const u32x4 *pv, const u32x4 *mv, float lr, float mu)
+{
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = bf16_rne(y[e]);
+        y[e] = widen_bf16(h[e]);
+    }
+    if (gout != A()) {
+        st_at<uint16_t>(gout, iA, u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
+        st_at<uint16_t>(gout, iB, u32x2{h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        u32x4 po, mo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float m = MOM ? __uint_as_float(mv[j][w]) : 0.0f;
+            po[w] = __float_as_uint(sgd_elem<MOM>(__uint_as_float(pv[j][w]), y[4 * j + w], m, lr, mu));
+            mo[w] = __float_as_uint(m);
+        }
+        st_at<float>(param, j ? iB : iA, po);
+        if (MOM) st_at<float>(mom, j ? iB : iA, mo);
+    }
 }
 
 }  // namespace ddp_detail

@@ -345,10 +345,72 @@ params_many(PsTable tb, int N, int64_t first_block, float inv)
 // average folded and scaled, optionally stored, and the parameters updated.
 // Parameters are f32: one 16-byte vector per 4 elements, so a bf16 lane (8
 // elements) moves two.
+// bf16 gradients: the split lane layout of the flat step (sgd_vec_split).
+// Lane L takes the tile's elements [4L, 4L + 4) and [256 + 4L, 256 + 4L + 4),
+// so that every parameter and momentum store of a wave writes one contiguous
+// range.  A lane whose two groups are not in one ring segment of the tile,
+// or reach past the parameter's end, folds them element by element.
+template <int NR, bool RING, bool MOM>
+__device__ __forceinline__ void params_sgd_tile_bf16(const PsTable &tb, int64_t first_block,
+                                                     float inv, float lr, float mu)
+{
+    static_assert(kPsUnroll == 1, "one vector per lane");
+    constexpr int H = kThreads * 4;   // the second group, 256 elements on
+    const int64_t tile = first_block + blockIdx.x;
+    const uint32_t pf = prefetch_record<NR>(tb, tile);
+    const PsEntry<NR + kSgdExtra> t = ps_entry<NR + kSgdExtra>(tb, tile);
+    const PsMeta &m = t.m;
+    const uint64_t gout = t.ad[NR], param = t.ad[NR + 1], mom = t.ad[NR + 2];
+    const uint64_t dummy = reinterpret_cast<uint64_t>(t.pe);
+    const int64_t cnt = m.count;
+    const int64_t iA = 4 * (int64_t)threadIdx.x, iB = iA + H;
+    const bool vec = m.vec && cnt >= 8;
+    // a lane past the parameter's end reads the tile's first elements (or,
+    // without the vector path, the entry) and drops them
+    const bool whole = iB + 4 <= cnt;
+    const int64_t ja = m.j0 + (whole ? iA : 0), jb = m.j0 + (whole ? iB : 0);
+    u32x4 v[NR], pv[2], mv[2];
+    const int64_t oa = vec ? 2 * ja : 0, ob = vec ? 2 * jb : 0;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) v[k] = ld_split(vec ? t.ad[k] : dummy, oa, ob);
+    pv[0] = gld_stream(vec ? param + (uint64_t)(4 * ja) : dummy);
+    pv[1] = gld_stream(vec ? param + (uint64_t)(4 * jb) : dummy);
+    if (MOM) {
+        mv[0] = gld_stream(vec ? mom + (uint64_t)(4 * ja) : dummy);
+        mv[1] = gld_stream(vec ? mom + (uint64_t)(4 * jb) : dummy);
+    }
+    const PsSegs sg = ps_segs<RING>(m);
+    const bool in_a = vec && iB + 4 <= sg.a_hi;
+    const bool in_b = RING && vec && iA >= sg.b_lo && iB + 4 <= sg.b_hi;
+    if (in_a || in_b) {
+        float y[8];
+        if (!RING || NR == 1)
+            fold_seq<NR, kBF16>(v, y);
+        else
+            fold_ring<NR, kBF16>(v, in_a ? sg.sa : sg.sb, y);
+        if (NR > 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * inv;
+        }
+        consume(pf);
+        sgd_vec_split<MOM>(gout, param, mom, m.j0 + iA, m.j0 + iB, y, pv, mv, lr, mu);
+    } else {
+        consume(pf);
+        const uint64_t *a = reinterpret_cast<const uint64_t *>(t.pe);
+        if (iA < cnt) params_sgd_elems<kBF16, kBF16, RING, MOM>(a, NR, m, inv, lr, mu, iA, 4);
+        if (iB < cnt) params_sgd_elems<kBF16, kBF16, RING, MOM>(a, NR, m, inv, lr, mu, iB, 4);
+    }
+}
+
 template <int NR, bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
 params_sgd_fast(PsTable tb, int64_t first_block, float inv, float lr, float mu)
 {
+    if constexpr (IN == kBF16) {
+        static_assert(OUT == kBF16, "bf16 gradients average to bf16");
+        params_sgd_tile_bf16<NR, RING, MOM>(tb, first_block, inv, lr, mu);
+        return;
+    }
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
@@ -426,6 +488,43 @@ params_sgd_many(PsTable tb, int N, int64_t first_block, float inv, float lr, flo
     const int64_t cnt = m.count;
     const bool vec = m.vec && cnt >= VEC;
     const PsSegs sg = ps_segs<RING>(m);
+    if constexpr (IN == kBF16) {
+        // the split lane layout of params_sgd_tile_bf16
+        static_assert(OUT == kBF16 && kPsUnroll == 1, "bf16 gradients average to bf16");
+        constexpr int H = kThreads * 4;
+        const int64_t iA = 4 * (int64_t)threadIdx.x, iB = iA + H;
+        const bool in_a = vec && iB + 4 <= sg.a_hi;
+        const bool in_b = RING && vec && iA >= sg.b_lo && iB + 4 <= sg.b_hi;
+        u32x4 pv[2], mv[2];
+        if (vec) {   // a lane past the end reads the tile's first elements and drops them
+            const bool whole = iB + 4 <= cnt;
+            const int64_t ja = m.j0 + (whole ? iA : 0), jb = m.j0 + (whole ? iB : 0);
+            pv[0] = gld_stream(param + (uint64_t)(4 * ja));
+            pv[1] = gld_stream(param + (uint64_t)(4 * jb));
+            if (MOM) {
+                mv[0] = gld_stream(mom + (uint64_t)(4 * ja));
+                mv[1] = gld_stream(mom + (uint64_t)(4 * jb));
+            }
+        }
+#pragma unroll 1
+        for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+            const bool mine = pass == 0 ? in_a : in_b;
+            if (!__builtin_amdgcn_ballot_w64(mine)) continue;
+            float y[8];
+            fold_looped_split<RING>(a, N, pass == 0 ? sg.sa : sg.sb, 2 * (m.j0 + (mine ? iA : 0)),
+                                    2 * (m.j0 + (mine ? iB : 0)), y);
+            if (mine) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = y[k] * inv;
+                sgd_vec_split<MOM>(gout, param, mom, m.j0 + iA, m.j0 + iB, y, pv, mv, lr, mu);
+            }
+        }
+        if (!in_a && !in_b) {
+            if (iA < cnt) params_sgd_elems<kBF16, kBF16, RING, MOM>(a, N, m, inv, lr, mu, iA, 4);
+            if (iB < cnt) params_sgd_elems<kBF16, kBF16, RING, MOM>(a, N, m, inv, lr, mu, iB, 4);
+        }
+        return;
+    }
 #pragma unroll 1
     for (int u = 0; u < kPsUnroll; ++u) {
         const int64_t i0 = ((int64_t)u * kThreads + threadIdx.x) * VEC;

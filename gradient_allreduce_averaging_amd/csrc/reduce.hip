@@ -76,11 +76,67 @@ reduce_fast(RankArgs ra, int64_t total, Buckets bk, float inv, void *out)
 // together, the average is folded and scaled, optionally stored, and the
 // parameters updated in place.  Parameters are f32: one 16-byte vector per 4
 // elements, so a bf16 lane (8 elements) moves two.
+// bf16 gradients, the split lane layout of sgd_vec_split: lane L of a tile
+// takes elements [4L, 4L + 4) and [256 + 4L, 256 + 4L + 4), loaded as two
+// 8-byte vectors per rank, so that each of its parameter and momentum
+// stores is one 16-byte piece of a 1 KiB contiguous wave store.  A lane
+// whose two groups do not lie in one ring segment of the tile (a tile that
+// holds a ring cut), or reach past the end, folds them element by element.
+template <int NR, bool RING, bool MOM>
+__device__ __forceinline__ void sgd_tile_bf16(const RankArgs &ra, int64_t total, const Buckets &bk,
+                                              float inv, const SgdArgs &sa)
+{
+    constexpr int H = kThreads * 4;   // the second group, 256 elements on
+    const int64_t tile = tile_of_block(bk);
+    const int64_t tile0 = tile * (2 * H);
+    const int64_t iA = tile0 + 4 * (int64_t)threadIdx.x, iB = iA + H;
+    u32x4 v[NR], pv[2], mv[2];
+    if (total >= 8) {   // a lane past the end reads the first elements and drops them
+        const bool whole = iB + 4 <= total;
+        const int64_t a = whole ? iA : 0, b = whole ? iB : 0;
+#pragma unroll
+        for (int k = 0; k < NR; ++k) v[k] = ld_split(ra.p[k], 2 * a, 2 * b);
+        const char *pp = reinterpret_cast<const char *>(sa.param);
+        pv[0] = ld_stream(pp + 4 * a);
+        pv[1] = ld_stream(pp + 4 * b);
+        if (MOM) {
+            const char *mp = reinterpret_cast<const char *>(sa.mom);
+            mv[0] = ld_stream(mp + 4 * a);
+            mv[1] = ld_stream(mp + 4 * b);
+        }
+    }
+    const Segs sg = tile_segs<RING>(bk, total, NR, tile, tile0);
+    const bool in_a = iA >= sg.a_lo && iB + 4 <= sg.a_hi;
+    const bool in_b = RING && iA >= sg.b_lo && iB + 4 <= sg.b_hi;
+    if (in_a || in_b) {
+        float y[8];
+        if (!RING || NR == 1)
+            fold_seq<NR, kBF16>(v, y);
+        else
+            fold_ring<NR, kBF16>(v, in_a ? sg.sa : sg.sb, y);
+        if (NR > 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * inv;
+        }
+        sgd_vec_split<MOM>(sa.grad_out, static_cast<void *>(sa.param), static_cast<void *>(sa.mom),
+                           iA, iB, y, pv, mv, sa.lr, sa.mu);
+    } else {
+        const int32_t b0 = first_bucket(bk, tile);
+        if (iA < total) sgd_elems<kBF16, kBF16, RING, MOM>(ra, NR, total, bk, b0, inv, sa, iA, 4);
+        if (iB < total) sgd_elems<kBF16, kBF16, RING, MOM>(ra, NR, total, bk, b0, inv, sa, iB, 4);
+    }
+}
+
 template <int NR, bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
 reduce_sgd_fast(RankArgs ra, int64_t total, Buckets bk, float inv, SgdArgs sa)
 {
     static_assert(kUnroll == 1, "the fused kernel processes one vector per lane");
+    if constexpr (IN == kBF16) {
+        static_assert(OUT == kBF16, "bf16 gradients average to bf16");
+        sgd_tile_bf16<NR, RING, MOM>(ra, total, bk, inv, sa);
+        return;
+    }
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
@@ -152,6 +208,53 @@ reduce_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, void *out)
     head_block<IN, OUT, RING>(ra, N, total, bk, inv, out, tile0);
 }
 
+// reduce_sgd_many for bf16 gradients, in the split lane layout of
+// sgd_tile_bf16.
+template <bool RING, bool MOM>
+__device__ __forceinline__ void sgd_many_bf16(const RankArgs &ra, int N, int64_t total,
+                                              const Buckets &bk, float inv, const SgdArgs &sa)
+{
+    constexpr int H = kThreads * 4;
+    const int64_t tile = tile_of_block(bk);
+    const int64_t tile0 = tile * (2 * H);
+    const int64_t iA = tile0 + 4 * (int64_t)threadIdx.x, iB = iA + H;
+    u32x4 pv[2], mv[2];
+    if (total >= 8) {   // a lane past the end reads the first elements and drops them
+        const bool whole = iB + 4 <= total;
+        const int64_t a = whole ? iA : 0, b = whole ? iB : 0;
+        const char *pp = reinterpret_cast<const char *>(sa.param);
+        pv[0] = ld_stream(pp + 4 * a);
+        pv[1] = ld_stream(pp + 4 * b);
+        if (MOM) {
+            const char *mp = reinterpret_cast<const char *>(sa.mom);
+            mv[0] = ld_stream(mp + 4 * a);
+            mv[1] = ld_stream(mp + 4 * b);
+        }
+    }
+    const Segs sg = tile_segs<RING>(bk, total, N, tile, tile0);
+    const bool in_a = iA >= sg.a_lo && iB + 4 <= sg.a_hi;
+    const bool in_b = RING && iA >= sg.b_lo && iB + 4 <= sg.b_hi;
+#pragma unroll 1
+    for (int pass = 0; pass < (RING ? 2 : 1); ++pass) {
+        const bool mine = pass == 0 ? in_a : in_b;
+        if (!__builtin_amdgcn_ballot_w64(mine)) continue;
+        float y[8];
+        fold_looped_split<RING>(ra.p, N, pass == 0 ? sg.sa : sg.sb, mine ? 2 * iA : 0,
+                                mine ? 2 * iB : 0, y);
+        if (mine) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * inv;
+            sgd_vec_split<MOM>(sa.grad_out, static_cast<void *>(sa.param),
+                               static_cast<void *>(sa.mom), iA, iB, y, pv, mv, sa.lr, sa.mu);
+        }
+    }
+    if (!in_a && !in_b) {
+        const int32_t b0 = first_bucket(bk, tile);
+        if (iA < total) sgd_elems<kBF16, kBF16, RING, MOM>(ra, N, total, bk, b0, inv, sa, iA, 4);
+        if (iB < total) sgd_elems<kBF16, kBF16, RING, MOM>(ra, N, total, bk, b0, inv, sa, iB, 4);
+    }
+}
+
 // The fused average + SGD step for any N up to DDP_MAX_RANKS: the lane's
 // parameter (and momentum) vectors are issued first, then the ranks are
 // folded as in reduce_many and the epilogue of reduce_sgd_fast applied.
@@ -159,6 +262,11 @@ template <bool RING, int IN, int OUT, bool MOM>
 __global__ void __launch_bounds__(kThreads)
 reduce_sgd_many(RankArgs ra, int N, int64_t total, Buckets bk, float inv, SgdArgs sa)
 {
+    if constexpr (IN == kBF16) {
+        static_assert(OUT == kBF16, "bf16 gradients average to bf16");
+        sgd_many_bf16<RING, MOM>(ra, N, total, bk, inv, sa);
+        return;
+    }
     constexpr int VEC = IN == kF32 ? 4 : 8;
     constexpr int ISZ = IN == kF32 ? 4 : 2;
     constexpr int PV = VEC / 4;
