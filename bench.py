@@ -31,8 +31,8 @@ first K of them timed as "without_ramp"), W warm-up syncs, K timed syncs
   noalloc        the sync through the entry point that allocates nothing
 and for ResNet-50 only (--extras): per_bucket, copy_path, fused_sgd,
 overlap, rank_sweep_GBps, in_place, no_sync, small_means; for many-small
-copy_path; for tiny the latency of a sync (Python call, prepared call, graph
-replay).
+copy_path; for Llama-7B fused_sgd (the step on bf16 gradients); for tiny the
+latency of a sync (Python call, prepared call, graph replay).
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with 2.
 
@@ -915,7 +915,7 @@ def leg_fused_sgd(c):
     optimizer reading the averaged gradient back (torch's in-place ops); and
     the same step on per-parameter tensors."""
     torch, ddp, plan, wl, N, P = c.torch, c.ddp, c.plan, c.wl, c.N, c.P
-    if c.args.no_fused_sgd or wl.out_dtype != "f32":
+    if c.args.no_fused_sgd:
         return None
     params = torch.empty(P, dtype=torch.float32, device=c.dev)
     c.W.device_normal_(params, 99, 7, 1.0)
@@ -936,7 +936,8 @@ def leg_fused_sgd(c):
     fb = N * P * wl.in_bytes + 4 * P * 4
     res = {"ms": round(t_f, 5), "GBps": gbps(fb, t_f), "bytes": fb, "unfused_ms": round(t_u, 5),
            "speedup_vs_unfused": round(t_u / t_f, 3),
-           "step": "momentum SGD (mu 0.9) on f32 parameters; unfused = sync + torch mul_/add_"}
+           "step": f"momentum SGD (mu 0.9) on f32 parameters from {wl.dtype} gradients (the average "
+                   f"as stored in {wl.out_dtype}); unfused = sync + torch mul_/add_"}
     # the same step on per-parameter tensors (gradients, parameters and
     # momentum buffers as autograd and the optimizer keep them)
     if N * P * wl.in_bytes <= (16 << 30):
@@ -1286,6 +1287,7 @@ def measure(args, cpu_seconds):
     per_param = args.layout == "per-parameter"
     extras = (args.extras == "on") if args.extras else c.wl.name == "resnet50"
     copy_only = args.extras is None and c.wl.name == "many_small"   # the copies of many tensors
+    sgd_only = args.extras is None and c.wl.name == "llama7b"       # the fused step on bf16 gradients
     cold = leg_cold_mall(c)
     ceiling = None if per_param else leg_ceiling(c)
     other = leg_other_orders(c)
@@ -1301,6 +1303,8 @@ def measure(args, cpu_seconds):
                 "no_sync": leg_no_sync(c), "small_means": leg_small_means(c)}
     elif copy_only and not per_param:
         more = {"copy_path": leg_copy_path(c)}
+    elif sgd_only and not per_param:
+        more = {"fused_sgd": leg_fused_sgd(c)}
     tiny = leg_tiny_latency(c)
     noalloc = leg_noalloc(c)
 
