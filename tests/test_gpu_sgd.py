@@ -97,6 +97,19 @@ def test_fused_sgd_misaligned_and_in_place(env, order):
     _case(env, SIZES, 4, "f32", "f32", order, True, False, seed=3, in_place=True)
 
 
+@pytest.mark.parametrize("total", [1, 3, 7, 8, 9, 255, 257, 511, 512, 513, 777])
+def test_fused_sgd_short_totals(env, total):
+    """Totals shorter than a vector, a tile (256 f32 / 512 bf16 elements) and
+    a little past one: the lanes past the end, the split bf16 layout's second
+    group and the per-element paths, in both orders, N = 3, 8 and 12."""
+    sizes = [total] if total < 9 else [total // 3, total - total // 3]
+    for k, (N, in_dt, out_dt) in enumerate([(3, "bf16", "bf16"), (8, "bf16", "bf16"),
+                                            (12, "bf16", "bf16"), (8, "f32", "f32"),
+                                            (8, "f32", "bf16")]):
+        for order in ("seq", "ring"):
+            _case(env, sizes, N, in_dt, out_dt, order, True, True, seed=total * 7 + k, cap=64)
+
+
 MIXED = [(0, 1, 2, 3), (1, 3, 0, 1), (2, 0, 3, 0), (3, 2, 1, 2)]
 
 
